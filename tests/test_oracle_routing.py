@@ -1,0 +1,108 @@
+"""Pins of the oracle's routing: brute force, a library stable sort, invariants, edge cases."""
+
+import numpy as np
+import pytest
+
+from mixture_experts_ffn_int32_amd import synth
+from oracle.routing import check_ids, permute_rows, route, unpermute_rows
+
+
+def brute_force(ids, E):
+    """O(S^2) restatement: row = offset of the expert + number of earlier slots of that expert."""
+    flat = np.asarray(ids).reshape(-1)
+    S = flat.size
+    counts = np.array([sum(1 for s in range(S) if flat[s] == e) for e in range(E)])
+    offsets = np.array([sum(counts[:e]) for e in range(E + 1)])
+    rows = np.array([offsets[flat[s]] + sum(1 for q in range(s) if flat[q] == flat[s])
+                     for s in range(S)], dtype=np.int64)
+    return counts, offsets, rows
+
+
+def check_invariants(ids, E, r):
+    flat = np.asarray(ids).reshape(-1).astype(np.int64)
+    S = flat.size
+    c, off, ss, ros = r["counts"], r["offsets"], r["sorted_slot"], r["row_of_slot"]
+    assert all(a.dtype == np.int32 for a in (c, off, ss, ros))
+    assert c.sum() == S and off[0] == 0 and off[E] == S
+    assert np.all(np.diff(off) == c)
+    assert np.array_equal(np.sort(ss), np.arange(S))
+    assert np.array_equal(ros[ss], np.arange(S))
+    for e in range(E):
+        seg = ss[off[e]:off[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)
+
+
+@pytest.mark.parametrize("T,E,K,seed", [(5, 3, 2, 0), (17, 4, 3, 1), (9, 1, 1, 2), (8, 5, 5, 3), (1, 6, 2, 4)])
+def test_route_matches_brute_force(T, E, K, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=(T, K))           # duplicates inside a token allowed
+    r = route(ids, E)
+    counts, offsets, rows = brute_force(ids, E)
+    assert np.array_equal(r["counts"], counts)
+    assert np.array_equal(r["offsets"], offsets)
+    assert np.array_equal(r["row_of_slot"], rows)
+    check_invariants(ids, E, r)
+
+
+@pytest.mark.parametrize("name", ["tiny", "sample", "skewed"])
+def test_route_matches_stable_sort_on_workloads(name):
+    spec = synth.WORKLOADS[name]
+    ids, _, _ = synth.make_routing(spec, seed=0)
+    r = route(ids, spec["E"])
+    flat = ids.reshape(-1)
+    assert np.array_equal(r["sorted_slot"], np.argsort(flat, kind="stable"))
+    assert np.array_equal(r["counts"], np.bincount(flat, minlength=spec["E"]))
+    check_invariants(ids, spec["E"], r)
+
+
+def test_route_edge_cases():
+    # no tokens
+    r = route(np.zeros((0, 2), np.int32), 4)
+    assert r["counts"].tolist() == [0, 0, 0, 0] and r["offsets"].tolist() == [0] * 5
+    assert r["sorted_slot"].size == 0
+    # all slots on one expert, others empty
+    ids = np.full((7, 3), 2)
+    r = route(ids, 4)
+    assert r["counts"].tolist() == [0, 0, 21, 0]
+    assert np.array_equal(r["sorted_slot"], np.arange(21))
+    # K = E: every token visits every expert
+    ids = np.array([[2, 0, 1], [1, 2, 0]])
+    r = route(ids, 3)
+    assert r["sorted_slot"].tolist() == [1, 5, 2, 3, 0, 4]
+    assert r["row_of_slot"].tolist() == [4, 0, 2, 3, 5, 1]
+
+
+def test_route_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        check_ids(np.array([[0, 4]]), 4)
+    with pytest.raises(ValueError):
+        route(np.array([[-1, 0]]), 4)
+
+
+def test_permute_unpermute_identity():
+    rng = np.random.default_rng(5)
+    T, K, E, H = 13, 3, 5, 7
+    ids = rng.integers(0, E, size=(T, K))
+    x = rng.standard_normal((T, H))
+    r = route(ids, E)
+    xp = permute_rows(x, r["sorted_slot"], K)
+    assert np.array_equal(unpermute_rows(xp, r["row_of_slot"]), np.repeat(x, K, axis=0))
+
+
+def test_workload_routing_structures():
+    s = synth.WORKLOADS["skewed"]
+    ids, w, _ = synth.make_routing(s, 0)
+    counts = np.bincount(ids.reshape(-1), minlength=s["E"])
+    assert (counts == 0).sum() >= s["n_empty"]
+    assert all(len(set(row)) == s["K"] for row in ids)          # distinct per token
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+    h = synth.spec_with("hotspot", T=512)
+    ids, _, info = synth.make_routing(h, 0)
+    assert all((row == info["hot_expert"]).sum() == 1 for row in ids)
+    assert all(len(set(row)) == h["K"] for row in ids)
+    ids, _, info = synth.make_routing(synth.spec_with(h, routing="hot_dup"), 0)
+    assert all((row == info["hot_expert"]).sum() == 2 for row in ids)
+    u = synth.WORKLOADS["sample"]
+    ids, _, _ = synth.make_routing(u, 0)
+    assert all(len(set(row)) == u["K"] for row in ids)
