@@ -1,0 +1,274 @@
+"""Benchmark of the fused MoE-FFN forward + backward on one MI355X.
+
+One step = hmm_forward + hmm_backward (routing, up-projection + SwiGLU,
+down-projection, weighted combine; act_grad + SwiGLUGrad, input_grad,
+combine(dX), d_topk_weights, W2Grad, W1Grad) over one batch of seeded
+synthetic input already resident in HBM, through the C ABI of libhmm.
+
+Prints ONE JSON line on stdout; details go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot]
+
+Timing: W untimed warm-up steps (the first one's time is reported as
+first_step_ms), then K steps between two synchronisations, timed with HIP
+events on the stream the kernels run on -> ms_per_step and tokens/s.  A
+second pass of K steps records HIP events around every kernel launch (the
+library's stage timing) and gives each kernel's average duration for the
+roofline figures.  The CPU oracle is then timed on a bounded sample of the
+same workload on the host's cores.
+"""
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(stage, T, H, I, E, K):
+    """Algorithmic work of one launch of a stage: (bound, amount, unit)."""
+    S = T * K
+    flops = {
+        "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
+        "gmm2": 2 * S * I * H,          # [S,I] x [I,H]
+        "act_grad": 2 * S * H * I,      # [S,H] x [H,I]
+        "input_grad": 4 * S * I * H,    # [S,2I] x [2I,H]
+        "dw2": 2 * S * I * H,           # [I,S] x [S,H]
+        "dw1": 4 * S * H * I,           # [H,S] x [S,2I]
+    }
+    if stage in flops:
+        return "mfma", flops[stage], "TFLOP/s"
+    nbytes = {
+        # read K gathered rows per token + row index + weight, write one row
+        "combine": S * H * 2 + S * 8 + T * H * 2,
+        "combine_dx": S * H * 2 + S * 4 + T * H * 2,
+        # ids read twice, histograms, sorted_slot + row_of_slot written
+        "route": S * 4 * 2 + S * 8,
+        "dw_finalize": S * 4,
+    }
+    if stage in nbytes:
+        return "hbm", nbytes[stage], "GB/s"
+    return None, 0, None
+
+
+class Runner:
+    """Preallocated buffers and raw C-ABI calls for one workload."""
+
+    def __init__(self, spec, seed, device, validate_ids=True):
+        import torch
+        from mixture_experts_ffn_int32_amd import _lib, synth
+        self.torch = torch
+        self.lib = _lib.load()
+        self._lib = _lib
+        self.spec = spec
+        T, H, I, E, K = (spec[k] for k in "THIEK")
+        self.dims = (T, H, I, E, K)
+        t0 = time.time()
+        inp = synth.make_inputs(spec, seed=seed)
+        log("[bench] inputs generated in %.1fs" % (time.time() - t0))
+        self.inp = inp
+
+        def bf(bits):
+            import numpy as np
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+        self.x = bf(inp["x"])
+        self.dy = bf(inp["dY"])
+        self.W1 = bf(inp["up_proj_weight"])
+        self.W2 = bf(inp["down_proj_weight"])
+        self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
+        self.w = torch.from_numpy(inp["topk_weights"]).to(device)
+        flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, _lib.HMM_BF16, flags, 0)
+        fws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        _lib.check(self.lib.hmm_forward_sizes(ctypes.byref(self.prob), ctypes.byref(fws), ctypes.byref(sv)))
+        _lib.check(self.lib.hmm_backward_sizes(ctypes.byref(self.prob), ctypes.byref(bws)))
+        u8 = torch.uint8
+        self.y = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        self.saved = torch.empty(sv.value, dtype=u8, device=device)
+        self.fwork = torch.empty(fws.value, dtype=u8, device=device)
+        self.bwork = torch.empty(bws.value, dtype=u8, device=device)
+        self.dx = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        self.dW1 = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=device)
+        self.dW2 = torch.empty((E, I, H), dtype=torch.bfloat16, device=device)
+        self.dw = torch.empty((T, K), dtype=torch.float32, device=device)
+        self.sizes = (fws.value, sv.value, bws.value)
+        self.stream = torch.cuda.current_stream(device)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.fargs = (ctypes.byref(self.prob), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2), P(self.y),
+                      P(self.saved), sv.value, P(self.fwork), fws.value, ctypes.c_void_p(self.stream.cuda_stream))
+        self.bargs = (ctypes.byref(self.prob), P(self.dy), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2),
+                      P(self.saved), sv.value, P(self.dx), P(self.dW1), P(self.dW2), P(self.dw), P(self.bwork),
+                      bws.value, ctypes.c_void_p(self.stream.cuda_stream))
+
+    def step(self):
+        self._lib.check(self.lib.hmm_forward(*self.fargs))
+        self._lib.check(self.lib.hmm_backward(*self.bargs))
+
+    def timed(self, n):
+        torch = self.torch
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(n):
+            self.step()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+
+def cpu_baseline(spec, seed, budget_s=12.0):
+    """Time the oracle (faithful fwd + full bwd) on a bounded prefix of the workload's tokens."""
+    import numpy as np
+    from mixture_experts_ffn_int32_amd import synth
+    from oracle.moe_ffn import MoEFFN
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    inp = synth.make_inputs(spec, seed=seed)
+    T = spec["T"]
+
+    def run(tp):
+        d = dict(x=synth.bits_to_f32(inp["x"][:tp]), topk_ids=inp["topk_ids"][:tp],
+                 topk_weights=inp["topk_weights"][:tp], up_proj_weight=synth.bits_to_f32(inp["up_proj_weight"]),
+                 down_proj_weight=synth.bits_to_f32(inp["down_proj_weight"]), dY=synth.bits_to_f32(inp["dY"][:tp]))
+        t0 = time.perf_counter()
+        m = MoEFFN(**d, mode="faithful")
+        m.forward()
+        m.backward()
+        return time.perf_counter() - t0
+
+    tp = min(T, 8)
+    el = run(tp)
+    while el < budget_s / 4 and tp < T:
+        tp = min(T, int(tp * max(2.0, min(8.0, budget_s / 2 / max(el, 1e-3)))))
+        el = run(tp)
+    return {"value": tp / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "first %d of %d tokens of the same workload, FAITHFUL float64 forward + full backward "
+                      "(numpy, %d BLAS threads), %.1f s" % (tp, T, cores, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sample")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-validate", action="store_true", help="skip the id check's device-to-host read-back")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_ffn_int32_amd import _lib, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    spec = dict(synth.WORKLOADS[args.workload])
+    if spec.get("gmm1", "bf16") != "bf16":
+        print("workload %s needs the FP8 up-projection, which this build does not run yet" % args.workload,
+              file=sys.stderr)
+        sys.exit(1)
+    T, H, I, E, K = (spec[k] for k in "THIEK")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate)
+    log("[bench] workload %s T=%d H=%d I=%d E=%d K=%d; workspace fwd %.1f MB, saved %.1f MB, bwd %.1f MB"
+        % (args.workload, T, H, I, E, K, r.sizes[0] / 1e6, r.sizes[1] / 1e6, r.sizes[2] / 1e6))
+
+    first_ms = r.timed(1)
+    for _ in range(max(0, args.warmup - 1)):
+        r.step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    total_ms = r.timed(args.steps)
+    wall = time.perf_counter() - wall0
+    ms = total_ms / args.steps
+    log("[bench] %d steps: %.4f ms/step (host wall %.4f ms/step), first step %.3f ms"
+        % (args.steps, ms, wall * 1e3 / args.steps, first_ms))
+
+    # second pass: per-kernel device time from the library's stage events
+    _lib.profile_read()
+    _lib.profile_enable(True)
+    prof_ms = r.timed(args.steps)
+    _lib.profile_enable(False)
+    stages, dropped = _lib.profile_read()
+    log("[bench] profiled pass %.4f ms/step; %d launches untimed" % (prof_ms / args.steps, dropped))
+    S = T * K
+    gemm_ms = 0.0
+    rows = []
+    for name, (n, tot) in sorted(stages.items(), key=lambda kv: -kv[1][1]):
+        avg = tot / max(n, 1)
+        bound, work, unit = stage_work(name, T, H, I, E, K)
+        rate = (work / (avg * 1e-3) / (1e12 if bound == "mfma" else 1e9)) if bound else None
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+        if bound == "mfma":
+            gemm_ms += tot / args.steps
+        rows.append((name, n, avg, bound, work, rate, unit, (rate / peak) if rate else None))
+        log("[bench]   %-12s launches %4d  avg %9.4f ms  %s" % (
+            name, n, avg, ("%.1f %s (%.1f%% of peak)" % (rate, unit, 100 * rate / peak)) if rate else ""))
+    dom = max((x for x in rows if x[3]), key=lambda x: x[2] * x[1])
+    gemm_flops = 18 * S * H * I
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+    roofline = {
+        "kernel": dom[0],
+        "bound": dom[3],
+        "achieved": round(dom[5], 3),
+        "peak": PEAK_BF16_TFLOPS if dom[3] == "mfma" else PEAK_HBM_GBS,
+        "unit": dom[6],
+        "frac": round(dom[7], 5),
+        "traffic": None,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(spec, args.seed, args.cpu_budget)
+        log("[bench] cpu baseline %.1f tokens/s (%s) in %.1fs" % (cpu["value"], cpu["sample"], time.time() - t0))
+
+    out = {
+        "metric": "MoE-FFN fwd+bwd tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), 1xMI355X",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "first_step_ms": round(first_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
+                   "routing": spec.get("routing"), "seed": args.seed, "validate_ids": not args.no_validate},
+        "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
+        "gemm_frac_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 5) if gemm_tflops else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * hmm.h -- C ABI of the MI355X (gfx950) fused MoE-FFN expert library, libhmm.so.
+ *
+ * The operation is the one of the HyperMegaMoE RFC ("HyperParallel Multicore
+ * HyperMegaMoE fused forward/backward operator"):
+ *
+ *   forward  (section 2.1, 3.1, 4.1): for every token t and every k < K, with
+ *            e = topk_ids[t,k]:  [g|u] = x[t] . up_proj_weight[e];
+ *            a = silu(g) * u;  o = a . down_proj_weight[e];
+ *            y[t] = sum_k topk_weights[t,k] * o.
+ *   backward (section 2.2): dx, d_up_proj_weight, d_down_proj_weight and
+ *            d_topk_weights of that function; topk_ids gets no gradient.
+ *
+ * Like the RFC's two-phase interface (section 2.3 and 10: a workspace-size
+ * query, then the execution call, for the forward and for the grad op), each
+ * call has a *_sizes query.  Everything except the five user tensors (offsets,
+ * group lists, tile tables, intermediate buffers) lives in caller-provided
+ * workspace and saved buffers (section 3.3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as tensors are DEVICE pointers (HBM of the current HIP
+ *   device); all are caller-owned and caller-allocated.  The library never
+ *   allocates device memory.  Its only state is, per host thread, one pinned
+ *   host word for the id read-back and the optional stage-timing events.
+ * - All tensors are dense, row-major (last index fastest), with no padding.
+ *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
+ *   be 16-byte aligned.
+ * - ``stream`` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *   is enqueued asynchronously on it, in order; outputs are valid once the
+ *   stream reaches that point.  Only HMM_FLAG_VALIDATE_IDS adds a host wait.
+ * - Every check that needs only host data (null pointers, shapes, dtypes,
+ *   alignment, workspace size) runs before any HIP call: on failure nothing is
+ *   enqueued (RFC section 4.2: invalid input is rejected at the host boundary
+ *   and never reaches a device kernel).
+ * - Errors are returned as hmm_status; nothing is thrown across the ABI.
+ *   hmm_last_error_message() gives a per-thread text for the last failure.
+ *   A failed call leaves no state behind: the next call behaves like a fresh
+ *   one (RFC section 5.3 and 7.3).
+ * - Calls that share a workspace or saved buffer must be ordered by the caller
+ *   (same stream, or events); concurrent calls from several host threads on the
+ *   same buffers are not supported.
+ */
+#ifndef HMM_H
+#define HMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hmm_status {
+  HMM_OK = 0,
+  HMM_ERR_NULL_POINTER = 1,          /* a required pointer is NULL */
+  HMM_ERR_BAD_SHAPE = 2,             /* T,H,I,E,K inconsistent or out of the supported range */
+  HMM_ERR_BAD_DTYPE = 3,             /* unknown or unsupported dtype selection */
+  HMM_ERR_MISALIGNED = 4,            /* a device pointer is not 16-byte aligned */
+  HMM_ERR_UNSUPPORTED = 5,           /* valid problem this build does not implement */
+  HMM_ERR_WORKSPACE_TOO_SMALL = 6,   /* workspace_bytes below the *_sizes figure */
+  HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7,/* some topk_ids value is outside [0, E) */
+  HMM_ERR_HIP = 8                    /* a HIP runtime call failed */
+} hmm_status;
+
+typedef enum hmm_dtype {
+  HMM_BF16 = 0,
+  HMM_F32 = 1,
+  HMM_FP8_E4M3 = 2
+} hmm_dtype;
+
+/* Check topk_ids on the device before any matrix product: the routing kernel
+ * raises a flag, the host reads it back (one small device-to-host copy and a
+ * stream wait) and returns HMM_ERR_EXPERT_ID_OUT_OF_RANGE without launching
+ * the products.  Without the flag, slots with an invalid id are dropped (they
+ * contribute zero) and the flag is recorded in ``saved`` (hmm_saved_layout.id_error). */
+#define HMM_FLAG_VALIDATE_IDS 1u
+
+/* Problem description.
+ *   T  tokens (>= 0; T = 0 is a no-op that still writes zero weight gradients)
+ *   H  hidden size, multiple of 64, 64 <= H <= 65536
+ *   I  intermediate size, multiple of 64, 64 <= I <= 65536
+ *   E  experts held by this device, 1 <= E <= 1024
+ *   K  experts per token, 1 <= K <= 16  (the dispatch op's top-k bound)
+ *   T*K must stay below 2^31.
+ *   out_dtype   HMM_BF16 (y and dx in bf16).  HMM_F32 is reserved (UNSUPPORTED).
+ *   gmm1_dtype  HMM_BF16, or HMM_FP8_E4M3 for the FP8 up-projection: tokens
+ *               are quantised per row, the up-projection weight per
+ *               (expert, column), both as scale = 448 / max|.| (the per-token
+ *               dynamic quantisation of MoeDistributeDispatchV2, case 3).
+ *   flags       HMM_FLAG_* bits. */
+typedef struct hmm_problem {
+  int64_t T, H, I, E, K;
+  int32_t out_dtype;
+  int32_t gmm1_dtype;
+  uint32_t flags;
+  uint32_t reserved; /* must be 0 */
+} hmm_problem;
+
+/* Byte offsets of the arrays a forward call records in ``saved`` (for tests
+ * and tools; the backward reads them).  S = T*K.
+ *   counts[E] int32      tokens per expert (the per-expert histogram)
+ *   offsets[E+1] int32   exclusive prefix sum of counts; offsets[E] = S
+ *   sorted_slot[S] int32 slot (t*K+k) placed at permuted row p; slots of one
+ *                        expert are contiguous and in ascending slot order
+ *   row_of_slot[S] int32 inverse of sorted_slot (-1 for a dropped slot)
+ *   tiles                int32 tile table of the grouped products
+ *   h[S,2I] bf16         up-projection output per permuted row ([gate | up])
+ *   a[S,I] bf16          SwiGLU output per permuted row
+ *   aw[S,I] bf16         topk weight * a, the W2-gradient operand
+ *   id_error int32       1 if an id was out of range on the recording call */
+typedef struct hmm_saved_layout {
+  size_t counts, offsets, sorted_slot, row_of_slot, tiles, h, a, aw, id_error, total;
+} hmm_saved_layout;
+
+/* Sizes of the forward's workspace and saved buffers for ``p`` (bytes). */
+hmm_status hmm_forward_sizes(const hmm_problem* p, size_t* workspace_bytes, size_t* saved_bytes);
+
+/* Byte offsets of the arrays inside ``saved``. */
+hmm_status hmm_saved_layout_of(const hmm_problem* p, hmm_saved_layout* out);
+
+/* Forward (RFC section 2.1: Dispatch -> GMM1 -> SwiGLU -> GMM2 -> Combine).
+ *   x             bf16 [T,H]       tokens of this device
+ *   topk_ids      int32 [T,K]      global expert ids (here: 0 <= id < E)
+ *   topk_weights  float32 [T,K]    routing weights
+ *   up_w          bf16 [E,H,2I]    up_proj_weight; columns [0,I) gate, [I,2I) up
+ *   down_w        bf16 [E,I,H]     down_proj_weight
+ *   y             bf16 [T,H]       output (overwritten)
+ *   saved         forward_sizes' saved_bytes; filled for the backward, must
+ *                 stay untouched until the matching backward has run
+ *   workspace     forward_sizes' workspace_bytes of scratch (free after the
+ *                 call has executed on the stream)
+ * On HMM_ERR_EXPERT_ID_OUT_OF_RANGE (with HMM_FLAG_VALIDATE_IDS) y is not
+ * written. */
+hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids,
+                       const float* topk_weights, const void* up_w, const void* down_w, void* y,
+                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Size of the backward's workspace (bytes). */
+hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes);
+
+/* Backward (RFC section 2.2: Dispatch(dY) -> act_grad (dY . W2^T) -> SwiGLUGrad
+ * -> input_grad GMM -> Combine(dX); W2Grad and W1Grad GMMs; d_topk_weights).
+ *   dy              bf16 [T,H]       gradient of y
+ *   x, topk_ids, topk_weights, up_w, down_w   the forward's inputs (topk_ids
+ *                   is only shape-checked: the routing recorded in ``saved``
+ *                   is used)
+ *   saved           the buffer filled by the matching forward
+ *   dx              bf16 [T,H]       overwritten
+ *   d_up_w          bf16 [E,H,2I]    overwritten (experts without tokens: zeros)
+ *   d_down_w        bf16 [E,I,H]     overwritten (experts without tokens: zeros)
+ *   d_topk_weights  float32 [T,K]    overwritten (0 for dropped slots) */
+hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* up_w, const void* down_w,
+                        const void* saved, size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w,
+                        float* d_topk_weights, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Routing alone (RFC section 4.1 top-k expand; 3.1 offset construction; 6.2
+ * sort by expert): writes counts[E], offsets[E+1], sorted_slot[S] and
+ * row_of_slot[S] (int32 device arrays) as described for hmm_saved_layout.
+ * ``workspace`` needs hmm_route_workspace_size bytes.  With
+ * HMM_FLAG_VALIDATE_IDS an out-of-range id returns
+ * HMM_ERR_EXPERT_ID_OUT_OF_RANGE after the routing has been written. */
+hmm_status hmm_route_workspace_size(const hmm_problem* p, size_t* workspace_bytes);
+hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_slot, int32_t* row_of_slot, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Names of statuses, and the calling thread's last error text. */
+const char* hmm_status_string(hmm_status s);
+const char* hmm_last_error_message(void);
+
+/* Build identification: the offload target the kernels were compiled for. */
+const char* hmm_build_info(void);
+
+/* Stage timing, for benchmarks and tools.  While enabled on the calling
+ * thread, every kernel launch (and the id read-back) of hmm_forward,
+ * hmm_backward and hmm_route is bracketed by two HIP events recorded on the
+ * call's stream, so the timings cover exactly that stage as it ran in the
+ * stream.  hmm_profile_read waits for the recorded events and returns, per
+ * stage name, the number of launches and their summed device time; it then
+ * clears the record.  Events are created on first use (at most 16384 per
+ * thread; beyond that further launches are not timed and ``dropped`` counts
+ * them).  Enabling costs two event records per launch; disabled, nothing. */
+typedef struct hmm_stage_time {
+  char name[32];
+  int32_t launches;
+  double ms;
+} hmm_stage_time;
+hmm_status hmm_profile_enable(int32_t on);
+hmm_status hmm_profile_read(hmm_stage_time* out, int32_t max_stages, int32_t* n_stages, int32_t* dropped);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HMM_H */

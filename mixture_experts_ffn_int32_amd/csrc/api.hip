@@ -1,0 +1,467 @@
+// Host side of libhmm: validation, buffer layouts and the kernel sequences of
+// the forward and backward calls declared in include/hmm.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/hmm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hmm_status fail(hmm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hmm_status fail(hmm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hmm_status hip_fail(hipError_t e, const char* what) {
+  return fail(HMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Dims {
+  int64_t T, H, I, E, K, S;
+};
+
+hmm_status validate(const hmm_problem* p, Dims* d) {
+  if (!p) return fail(HMM_ERR_NULL_POINTER, "problem is NULL");
+  if (p->reserved != 0) return fail(HMM_ERR_BAD_SHAPE, "hmm_problem.reserved must be 0");
+  if (p->T < 0) return fail(HMM_ERR_BAD_SHAPE, "T must be >= 0 (got %lld)", (long long)p->T);
+  if (p->K < 1 || p->K > 16) return fail(HMM_ERR_BAD_SHAPE, "K must be in [1, 16] (got %lld)", (long long)p->K);
+  if (p->E < 1 || p->E > hmm::MAX_EXPERTS)
+    return fail(HMM_ERR_BAD_SHAPE, "E must be in [1, %d] (got %lld)", hmm::MAX_EXPERTS, (long long)p->E);
+  if (p->H < 64 || p->H > 65536 || p->H % 64)
+    return fail(HMM_ERR_BAD_SHAPE, "H must be a multiple of 64 in [64, 65536] (got %lld)", (long long)p->H);
+  if (p->I < 64 || p->I > 65536 || p->I % 64)
+    return fail(HMM_ERR_BAD_SHAPE, "I must be a multiple of 64 in [64, 65536] (got %lld)", (long long)p->I);
+  if (p->T > (int64_t)0x7fffffff / p->K)
+    return fail(HMM_ERR_BAD_SHAPE, "T*K must stay below 2^31 (T=%lld, K=%lld)", (long long)p->T, (long long)p->K);
+  if (p->flags & ~HMM_FLAG_VALIDATE_IDS) return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
+  if (p->out_dtype != HMM_BF16 && p->out_dtype != HMM_F32)
+    return fail(HMM_ERR_BAD_DTYPE, "out_dtype must be HMM_BF16 or HMM_F32 (got %d)", p->out_dtype);
+  if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3)
+    return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16 or HMM_FP8_E4M3 (got %d)", p->gmm1_dtype);
+  if (p->out_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is not implemented");
+  if (p->gmm1_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "gmm1_dtype HMM_FP8_E4M3 is not implemented");
+  d->T = p->T;
+  d->H = p->H;
+  d->I = p->I;
+  d->E = p->E;
+  d->K = p->K;
+  d->S = p->T * p->K;
+  return HMM_OK;
+}
+
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+// A pointer to an array that may legitimately be empty may be NULL.
+hmm_status need(const void* ptr, bool nonempty, const char* name) {
+  if (!ptr && nonempty) return fail(HMM_ERR_NULL_POINTER, "%s is NULL", name);
+  if (ptr && misaligned(ptr)) return fail(HMM_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return HMM_OK;
+}
+
+int64_t n_route_blocks(const Dims& d) { return (d.S + hmm::RT_SLOTS - 1) / hmm::RT_SLOTS; }
+int64_t n_tiles_max(const Dims& d) { return hmm::max_row_tiles(d.S, d.E, hmm::GEMM_BM); }
+
+hmm_saved_layout saved_layout(const Dims& d) {
+  hmm_saved_layout L{};
+  size_t o = 0;
+  L.counts = o;        o += up(d.E * 4);
+  L.offsets = o;       o += up((d.E + 1) * 4);
+  L.sorted_slot = o;   o += up(d.S * 4);
+  L.row_of_slot = o;   o += up(d.S * 4);
+  L.tiles = o;         o += up((2 + 2 * n_tiles_max(d)) * 4);
+  L.h = o;             o += up(d.S * 2 * d.I * 2);
+  L.a = o;             o += up(d.S * d.I * 2);
+  L.aw = o;            o += up(d.S * d.I * 2);
+  L.id_error = o;      o += up(4);
+  L.total = o;
+  return L;
+}
+
+// routing scratch: per-block histograms and bases, per-block error bits
+struct RouteScratch {
+  size_t blockhist, blockbase, blockerr, total;
+};
+RouteScratch route_scratch(const Dims& d, size_t base) {
+  RouteScratch r{};
+  const int64_t nb = n_route_blocks(d);
+  size_t o = base;
+  r.blockhist = o; o += up(nb * d.E * 4);
+  r.blockbase = o; o += up(nb * d.E * 4);
+  r.blockerr = o;  o += up(nb * 4 + 4);
+  r.total = o;
+  return r;
+}
+
+struct FwdWork {
+  RouteScratch rs;
+  size_t o, total;
+};
+FwdWork fwd_work(const Dims& d) {
+  FwdWork w{};
+  w.rs = route_scratch(d, 0);
+  size_t o = w.rs.total;
+  w.o = o; o += up(d.S * d.H * 2);
+  w.total = o;
+  return w;
+}
+
+struct BwdWork {
+  size_t dh, dxp, dwpart, total;
+  int dw_cols;
+};
+BwdWork bwd_work(const Dims& d) {
+  BwdWork w{};
+  w.dw_cols = hmm::act_grad_dw_cols(d.I);
+  size_t o = 0;
+  w.dh = o;     o += up(d.S * 2 * d.I * 2);
+  w.dxp = o;    o += up(d.S * d.H * 2);
+  w.dwpart = o; o += up(d.S * w.dw_cols * 4);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <class T>
+const T* at(const void* base, size_t off) { return reinterpret_cast<const T*>(static_cast<const char*>(base) + off); }
+
+// ------------------------------------------------------------- stage timing
+struct Prof {
+  bool on = false;
+  int dropped = 0;
+  std::vector<hipEvent_t> pool;           // events created so far (reused after a read)
+  size_t used = 0;                        // events handed out since the last read
+  std::vector<std::pair<std::string, std::pair<size_t, size_t>>> marks;  // name, (start, end) indices
+};
+constexpr size_t PROF_MAX_EVENTS = 16384;
+thread_local Prof g_prof;
+
+hipEvent_t prof_event() {
+  Prof& P = g_prof;
+  if (P.used == P.pool.size()) {
+    if (P.pool.size() >= PROF_MAX_EVENTS) return nullptr;
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    P.pool.push_back(ev);
+  }
+  return P.pool[P.used++];
+}
+
+// Brackets one launch with events when timing is on.
+struct Stage {
+  const char* name;
+  hipStream_t st;
+  size_t i0 = 0;
+  bool live = false;
+  Stage(const char* n, hipStream_t s) : name(n), st(s) {
+    if (!g_prof.on) return;
+    hipEvent_t e = prof_event();
+    if (!e) { ++g_prof.dropped; return; }
+    i0 = g_prof.used - 1;
+    live = hipEventRecord(e, st) == hipSuccess;
+  }
+  ~Stage() {
+    if (!live) return;
+    hipEvent_t e = prof_event();
+    if (!e) { ++g_prof.dropped; return; }
+    if (hipEventRecord(e, st) == hipSuccess) g_prof.marks.push_back({name, {i0, g_prof.used - 1}});
+  }
+};
+
+// One pinned host word per thread for the id-validation read-back.
+int32_t* pinned_word() {
+  thread_local int32_t* w = nullptr;
+  if (!w) {
+    if (hipHostMalloc((void**)&w, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) w = nullptr;
+  }
+  return w;
+}
+
+hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                     int32_t* row_of_slot, int32_t* tiles, int32_t* err, void* scratch, const RouteScratch& rs,
+                     bool validate_ids, hipStream_t stream) {
+  hipError_t e;
+  {
+    Stage stage("route", stream);
+    e = hmm::launch_route(ids, d.S, (int)d.E, hmm::GEMM_BM, counts, offsets, sorted_slot, row_of_slot, tiles, err,
+                          at<int32_t>(scratch, rs.blockhist), at<int32_t>(scratch, rs.blockbase),
+                          at<int32_t>(scratch, rs.blockerr), stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "routing launch");
+  if (validate_ids) {
+    int32_t* host = pinned_word();
+    if (!host) return fail(HMM_ERR_HIP, "hipHostMalloc of the validation word failed");
+    *host = 0;
+    {
+      Stage stage("id_readback", stream);
+      e = hipMemcpyAsync(host, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "id-validation read-back");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "id-validation wait");
+    if (*host) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
+  }
+  return HMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hmm_status_string(hmm_status s) {
+  switch (s) {
+    case HMM_OK: return "HMM_OK";
+    case HMM_ERR_NULL_POINTER: return "HMM_ERR_NULL_POINTER";
+    case HMM_ERR_BAD_SHAPE: return "HMM_ERR_BAD_SHAPE";
+    case HMM_ERR_BAD_DTYPE: return "HMM_ERR_BAD_DTYPE";
+    case HMM_ERR_MISALIGNED: return "HMM_ERR_MISALIGNED";
+    case HMM_ERR_UNSUPPORTED: return "HMM_ERR_UNSUPPORTED";
+    case HMM_ERR_WORKSPACE_TOO_SMALL: return "HMM_ERR_WORKSPACE_TOO_SMALL";
+    case HMM_ERR_EXPERT_ID_OUT_OF_RANGE: return "HMM_ERR_EXPERT_ID_OUT_OF_RANGE";
+    case HMM_ERR_HIP: return "HMM_ERR_HIP";
+  }
+  return "HMM_ERR_UNKNOWN";
+}
+
+const char* hmm_last_error_message(void) { return g_last_error.c_str(); }
+
+const char* hmm_build_info(void) { return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16, 128x128x64 tiles"; }
+
+hmm_status hmm_forward_sizes(const hmm_problem* p, size_t* workspace_bytes, size_t* saved_bytes) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (!workspace_bytes || !saved_bytes) return fail(HMM_ERR_NULL_POINTER, "size outputs are NULL");
+  *workspace_bytes = fwd_work(d).total;
+  *saved_bytes = saved_layout(d).total;
+  return HMM_OK;
+}
+
+hmm_status hmm_saved_layout_of(const hmm_problem* p, hmm_saved_layout* out) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (!out) return fail(HMM_ERR_NULL_POINTER, "layout output is NULL");
+  *out = saved_layout(d);
+  return HMM_OK;
+}
+
+hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (!workspace_bytes) return fail(HMM_ERR_NULL_POINTER, "size output is NULL");
+  *workspace_bytes = bwd_work(d).total;
+  return HMM_OK;
+}
+
+hmm_status hmm_route_workspace_size(const hmm_problem* p, size_t* workspace_bytes) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (!workspace_bytes) return fail(HMM_ERR_NULL_POINTER, "size output is NULL");
+  RouteScratch rs = route_scratch(d, 0);
+  size_t o = rs.total;
+  o += up((2 + 2 * n_tiles_max(d)) * 4);  // tile table
+  o += up(4);                             // error word
+  *workspace_bytes = o;
+  return HMM_OK;
+}
+
+hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_slot, int32_t* row_of_slot, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  const bool ne = d.S > 0;
+  if ((s = need(topk_ids, ne, "topk_ids")) || (s = need(counts, true, "counts")) ||
+      (s = need(offsets, true, "offsets")) || (s = need(sorted_slot, ne, "sorted_slot")) ||
+      (s = need(row_of_slot, ne, "row_of_slot")) || (s = need(workspace, true, "workspace")))
+    return s;
+  size_t need_ws = 0;
+  hmm_route_workspace_size(p, &need_ws);
+  if (workspace_bytes < need_ws)
+    return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need_ws);
+  RouteScratch rs = route_scratch(d, 0);
+  int32_t* tiles = at<int32_t>(workspace, rs.total);
+  int32_t* err = at<int32_t>(workspace, rs.total + up((2 + 2 * n_tiles_max(d)) * 4));
+  return run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tiles, err, workspace, rs,
+                   (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, (hipStream_t)stream);
+}
+
+hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                       const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  const bool ne = d.S > 0;
+  if ((s = need(x, ne, "x")) || (s = need(topk_ids, ne, "topk_ids")) || (s = need(topk_weights, ne, "topk_weights")) ||
+      (s = need(up_w, true, "up_proj_weight")) || (s = need(down_w, true, "down_proj_weight")) ||
+      (s = need(y, ne, "y")) || (s = need(saved, true, "saved")) || (s = need(workspace, true, "workspace")))
+    return s;
+  const hmm_saved_layout L = saved_layout(d);
+  const FwdWork W = fwd_work(d);
+  if (saved_bytes < L.total) return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "saved %zu < %zu bytes", saved_bytes, L.total);
+  if (workspace_bytes < W.total)
+    return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, W.total);
+  hipStream_t st = (hipStream_t)stream;
+
+  int32_t* offsets = at<int32_t>(saved, L.offsets);
+  int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
+  int32_t* tiles = at<int32_t>(saved, L.tiles);
+  s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
+                tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, st);
+  if (s != HMM_OK) return s;
+  if (!ne) return HMM_OK;
+
+  hmm::RowGroups g{tiles, offsets, sorted_slot, n_tiles_max(d), (int)d.K};
+  uint16_t* h = at<uint16_t>(saved, L.h);
+  uint16_t* a = at<uint16_t>(saved, L.a);
+  uint16_t* aw = at<uint16_t>(saved, L.aw);
+  uint16_t* o = at<uint16_t>(workspace, W.o);
+  hipError_t e;
+  {
+    Stage stage("gmm1_swiglu", st);
+    e = hmm::launch_gmm1_swiglu(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a,
+                                         aw, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  {
+    Stage stage("gmm2", st);
+    e = hmm::launch_gmm2(g, a, (const uint16_t*)down_w, d.H, d.I, o, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+  {
+    Stage stage("combine", st);
+    e = hmm::launch_combine(o, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, (uint16_t*)y, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return HMM_OK;
+}
+
+hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* up_w, const void* down_w, const void* saved,
+                        size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w, float* d_topk_weights,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  const bool ne = d.S > 0;
+  if ((s = need(dy, ne, "dy")) || (s = need(x, ne, "x")) || (s = need(topk_ids, ne, "topk_ids")) ||
+      (s = need(topk_weights, ne, "topk_weights")) || (s = need(up_w, true, "up_proj_weight")) ||
+      (s = need(down_w, true, "down_proj_weight")) || (s = need(saved, true, "saved")) ||
+      (s = need(dx, ne, "dx")) || (s = need(d_up_w, true, "d_up_proj_weight")) ||
+      (s = need(d_down_w, true, "d_down_proj_weight")) || (s = need(d_topk_weights, ne, "d_topk_weights")) ||
+      (s = need(workspace, true, "workspace")))
+    return s;
+  const hmm_saved_layout L = saved_layout(d);
+  const BwdWork W = bwd_work(d);
+  if (saved_bytes < L.total) return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "saved %zu < %zu bytes", saved_bytes, L.total);
+  if (workspace_bytes < W.total)
+    return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, W.total);
+  hipStream_t st = (hipStream_t)stream;
+
+  const int32_t* offsets = at<int32_t>(saved, L.offsets);
+  const int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
+  const int32_t* row_of_slot = at<int32_t>(saved, L.row_of_slot);
+  hmm::RowGroups g{at<int32_t>(saved, L.tiles), offsets, sorted_slot, n_tiles_max(d), (int)d.K};
+  const uint16_t* h = at<uint16_t>(saved, L.h);
+  const uint16_t* a = at<uint16_t>(saved, L.a);
+  const uint16_t* aw = at<uint16_t>(saved, L.aw);
+  uint16_t* dh = at<uint16_t>(workspace, W.dh);
+  uint16_t* dxp = at<uint16_t>(workspace, W.dxp);
+  float* dwpart = at<float>(workspace, W.dwpart);
+  hipError_t e;
+  if (ne) {
+    {
+      Stage stage("act_grad", st);
+      e = hmm::launch_act_grad(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh, dwpart,
+                             W.dw_cols, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+    {
+      Stage stage("input_grad", st);
+      e = hmm::launch_input_grad(g, dh, (const uint16_t*)up_w, d.H, d.I, dxp, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+    {
+      Stage stage("combine_dx", st);
+      e = hmm::launch_combine(dxp, row_of_slot, nullptr, d.T, (int)d.K, d.H, (uint16_t*)dx, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
+    {
+      Stage stage("dw_finalize", st);
+      e = hmm::launch_dw_finalize(dwpart, W.dw_cols, row_of_slot, d.S, d_topk_weights, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "d_topk_weights launch");
+  }
+  {
+    Stage stage("dw2", st);
+    e = hmm::launch_dw2(offsets, sorted_slot, (int)d.K, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+  {
+    Stage stage("dw1", st);
+    e = hmm::launch_dw1(offsets, sorted_slot, (int)d.K, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
+  return HMM_OK;
+}
+
+hmm_status hmm_profile_enable(int32_t on) {
+  g_prof.on = on != 0;
+  return HMM_OK;
+}
+
+hmm_status hmm_profile_read(hmm_stage_time* out, int32_t max_stages, int32_t* n_stages, int32_t* dropped) {
+  if (!n_stages) return fail(HMM_ERR_NULL_POINTER, "n_stages is NULL");
+  Prof& P = g_prof;
+  std::vector<hmm_stage_time> acc;
+  for (auto& m : P.marks) {
+    hipEvent_t a = P.pool[m.second.first], b = P.pool[m.second.second];
+    hipError_t e = hipEventSynchronize(b);
+    if (e != hipSuccess) return hip_fail(e, "profile event wait");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess) return hip_fail(e, "profile event time");
+    hmm_stage_time* slot = nullptr;
+    for (auto& x : acc)
+      if (m.first == x.name) slot = &x;
+    if (!slot) {
+      acc.push_back(hmm_stage_time{});
+      slot = &acc.back();
+      std::snprintf(slot->name, sizeof slot->name, "%s", m.first.c_str());
+    }
+    slot->launches += 1;
+    slot->ms += ms;
+  }
+  *n_stages = (int32_t)acc.size();
+  if (dropped) *dropped = P.dropped;
+  if (out)
+    for (int32_t i = 0; i < (int32_t)acc.size() && i < max_stages; ++i) out[i] = acc[i];
+  P.marks.clear();
+  P.used = 0;
+  P.dropped = 0;
+  return HMM_OK;
+}
+
+}  // extern "C"

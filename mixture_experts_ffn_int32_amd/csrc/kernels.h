@@ -1,0 +1,62 @@
+// Launchers of the libhmm kernels (host-callable), and the constants the host
+// planner shares with them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hmm {
+
+constexpr int MAX_EXPERTS = 1024;     // E limit (the dispatch op's moeExpertNum bound)
+constexpr int RT_THREADS = 256;       // routing block size
+constexpr int RT_SLOTS = 1024;        // slots per routing block
+constexpr int RT_SCAN_THREADS = 1024; // the single scan block (>= MAX_EXPERTS)
+
+constexpr int GEMM_BM = 128;          // rows of a grouped-product tile (tile table granularity)
+
+// Upper bound of the tile-table length for S routed rows over E experts with
+// BM-row tiles: sum_e ceil(c_e / BM) <= (S + E * (BM - 1)) / BM.
+inline int64_t max_row_tiles(int64_t S, int64_t E, int BM) { return (S + E * (BM - 1)) / BM; }
+
+// routing (route.hip)
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int BM, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tiles, int32_t* err,
+                        int32_t* blockhist, int32_t* blockbase, int32_t* blockerr, hipStream_t stream);
+
+// grouped products (gemm.hip).  All matrices bf16 (uint16_t storage).
+struct RowGroups {
+  const int32_t* tiles;        // [2 + 2*max_tiles]: count, BM, then (expert, first row) pairs
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted_slot;  // [S]
+  int64_t max_tiles;
+  int K;                       // top-k (token of permuted row p = sorted_slot[p] / K)
+};
+
+// h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
+hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
+                              int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream);
+// o = a . W2[e]                                                (forward down-projection)
+hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
+                       uint16_t* o, hipStream_t stream);
+// G = dY[tok] . W2[e]^T; dH = SwiGLUGrad(w G); dwpart = partial sums of G a
+hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
+                           const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
+                           float* dwpart, int dw_cols, hipStream_t stream);
+// dXp = dH . W1[e]^T
+hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
+                             uint16_t* dxp, hipStream_t stream);
+// dW1[e] = sum_p x[tok(p)]^T dH[p];  dW2[e] = sum_p aw[p]^T dY[tok(p)]
+hipError_t launch_dw1(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* x,
+                      const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream);
+hipError_t launch_dw2(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* aw,
+                      const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream);
+// number of d_topk_weights partial columns written by launch_act_grad for a given I
+int act_grad_dw_cols(int64_t I);
+
+// pointwise (pointwise.hip)
+hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
+                          int K, int64_t H, uint16_t* out, hipStream_t stream);
+hipError_t launch_dw_finalize(const float* dwpart, int dw_cols, const int32_t* row_of_slot, int64_t S,
+                              float* dw, hipStream_t stream);
+
+}  // namespace hmm

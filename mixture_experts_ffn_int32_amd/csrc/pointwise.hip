@@ -1,0 +1,84 @@
+// Bandwidth-bound steps of the path:
+//   combine      (HyperMegaMoE RFC section 2.1 Combine and 4.1: outputs return to
+//                 their token and are summed with the top-k weights; section 2.2
+//                 Combine(dX): the same gather without weights)
+//                 out[t] = sum_k w[t,k] * rows[row_of_slot[t*K+k]]   (w = 1 if NULL)
+//                 in float32, k ascending, then one bf16 rounding; no atomics, so
+//                 the result is deterministic.
+//   dw_finalize  d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c], c ascending.
+#include "device.h"
+#include "kernels.h"
+
+namespace hmm {
+
+constexpr int PW_THREADS = 256;
+
+// One thread per 8 consecutive hidden elements of one token (16-byte loads).
+template <bool WEIGHTED>
+__global__ void __launch_bounds__(PW_THREADS) combine_kernel(const uint16_t* __restrict__ rows,
+                                                             const int32_t* __restrict__ row_of_slot,
+                                                             const float* __restrict__ tw, int64_t T, int K,
+                                                             int64_t H, uint16_t* __restrict__ out) {
+  const int64_t chunks_per_row = H >> 3;
+  const int64_t total = T * chunks_per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * PW_THREADS + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * PW_THREADS) {
+    const int64_t t = idx / chunks_per_row;
+    const int64_t c = idx - t * chunks_per_row;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const int64_t s = t * K + k;
+      const int r = row_of_slot[s];
+      if (r < 0) continue;
+      const float wk = WEIGHTED ? tw[s] : 1.f;
+      float v[8];
+      unpack8(*reinterpret_cast<const u32x4*>(rows + (int64_t)r * H + c * 8), v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = WEIGHTED ? __builtin_fmaf(wk, v[j], acc[j]) : acc[j] + v[j];
+    }
+    *reinterpret_cast<u32x4*>(out + t * H + c * 8) = pack8(acc);
+  }
+}
+
+__global__ void __launch_bounds__(PW_THREADS) dw_finalize_kernel(const float* __restrict__ dwpart, int dw_cols,
+                                                                 const int32_t* __restrict__ row_of_slot,
+                                                                 int64_t S, float* __restrict__ dw) {
+  const int64_t s = (int64_t)blockIdx.x * PW_THREADS + threadIdx.x;
+  if (s >= S) return;
+  const int r = row_of_slot[s];
+  float acc = 0.f;
+  if (r >= 0) {
+    const float* p = dwpart + (int64_t)r * dw_cols;
+    for (int c = 0; c < dw_cols; ++c) acc += p[c];
+  }
+  dw[s] = acc;
+}
+
+static unsigned grid_for(int64_t work, int64_t cap) {
+  int64_t g = (work + PW_THREADS - 1) / PW_THREADS;
+  if (g > cap) g = cap;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
+                          int K, int64_t H, uint16_t* out, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const unsigned g = grid_for(T * (H / 8), 1 << 20);
+  if (topk_w)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
+                       K, H, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
+                       K, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_finalize(const float* dwpart, int dw_cols, const int32_t* row_of_slot, int64_t S, float* dw,
+                              hipStream_t stream) {
+  if (S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dw_finalize_kernel, dim3(grid_for(S, 1 << 30)), dim3(PW_THREADS), 0, stream, dwpart, dw_cols,
+                     row_of_slot, S, dw);
+  return hipGetLastError();
+}
+
+}  // namespace hmm

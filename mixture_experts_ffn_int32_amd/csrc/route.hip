@@ -1,0 +1,171 @@
+// Routing: top-k expand, per-expert int32 histogram, exclusive prefix offsets,
+// stable scatter of slots into expert order, and the tile table of the grouped
+// products.  (HyperMegaMoE RFC section 4.1: each token expands into K expert
+// slots; section 3.1: offsets are built inside the operator; section 6.2:
+// slots are sorted by expert and un-sorted afterwards.)
+//
+// Slot s = t*K + k.  Three kernels, all integer and deterministic:
+//   route_hist     one block per RT_SLOTS slots: LDS histogram -> blockhist[b][e]
+//   route_scan     one block: counts, per-block bases, offsets, tile table
+//   route_scatter  one block per RT_SLOTS slots: stable rank inside the block
+//                  (wave multisplit over the id bits with ballots, then a
+//                  fixed-order sum over the waves) -> sorted_slot, row_of_slot
+#include "device.h"
+#include "kernels.h"
+
+namespace hmm {
+
+__global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                         int32_t* __restrict__ blockhist,
+                                                         int32_t* __restrict__ blockerr) {
+  __shared__ int32_t hist[MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += RT_THREADS) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RT_SLOTS;
+  int bad = 0;
+#pragma unroll
+  for (int r = 0; r < RT_SLOTS / RT_THREADS; ++r) {
+    const int64_t s = base + r * RT_THREADS + tid;
+    if (s < S) {
+      const int e = ids[s];
+      if (e >= 0 && e < E)
+        atomicAdd(&hist[e], 1);
+      else
+        bad = 1;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  for (int e = tid; e < E; e += RT_THREADS) blockhist[(int64_t)blockIdx.x * E + e] = hist[e];
+  if (tid == 0) blockerr[blockIdx.x] = bad;
+}
+
+// One block of RT_SCAN_THREADS threads (>= E).
+__global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __restrict__ blockhist,
+                                                              const int32_t* __restrict__ blockerr, int nblk,
+                                                              int E, int BM, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ blockbase,
+                                                              int32_t* __restrict__ tiles,
+                                                              int32_t* __restrict__ err) {
+  __shared__ int32_t scan_c[RT_SCAN_THREADS];
+  __shared__ int32_t scan_t[RT_SCAN_THREADS];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int v = blockhist[(int64_t)b * E + e];
+      blockbase[(int64_t)b * E + e] = c;
+      c += v;
+    }
+  }
+  const int nt = (c + BM - 1) / BM;
+  scan_c[e] = (e < E) ? c : 0;
+  scan_t[e] = (e < E) ? nt : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scans over the experts (integers: order-free)
+  for (int d = 1; d < RT_SCAN_THREADS; d <<= 1) {
+    const int vc = (e >= d) ? scan_c[e - d] : 0;
+    const int vt = (e >= d) ? scan_t[e - d] : 0;
+    __syncthreads();
+    scan_c[e] += vc;
+    scan_t[e] += vt;
+    __syncthreads();
+  }
+  const int off = scan_c[e] - ((e < E) ? c : 0);
+  const int tstart = scan_t[e] - ((e < E) ? nt : 0);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    for (int i = 0; i < nt; ++i) {
+      tiles[2 + 2 * (tstart + i)] = e;
+      tiles[2 + 2 * (tstart + i) + 1] = off + i * BM;
+    }
+  }
+  if (e == RT_SCAN_THREADS - 1) {
+    offsets[E] = scan_c[e];
+    tiles[0] = scan_t[e];  // number of tiles
+    tiles[1] = BM;
+  }
+  int bad = 0;
+  for (int b = e; b < nblk; b += RT_SCAN_THREADS) bad |= blockerr[b];
+  bad = __syncthreads_or(bad);
+  if (e == 0) *err = bad;
+}
+
+__global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                            int nbits, const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ blockbase,
+                                                            int32_t* __restrict__ sorted_slot,
+                                                            int32_t* __restrict__ row_of_slot) {
+  __shared__ int32_t running[MAX_EXPERTS];
+  __shared__ int32_t wcnt[RT_THREADS / 64][MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  for (int e = tid; e < E; e += RT_THREADS) {
+    running[e] = offsets[e] + blockbase[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < RT_THREADS / 64; ++q) wcnt[q][e] = 0;
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RT_SLOTS;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < RT_SLOTS / RT_THREADS; ++r) {
+    const int64_t s = base + r * RT_THREADS + tid;
+    int e = -1;
+    bool valid = false;
+    if (s < S) {
+      e = ids[s];
+      valid = (e >= 0 && e < E);
+      if (!valid) row_of_slot[s] = -1;
+    }
+    // lanes of this wave holding the same expert id
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    if (!valid) peers = 0;
+    const int rank = __popcll(peers & lt_mask);
+    const int cnt = __popcll(peers);
+    const int tag = (r + 1) << 16;
+    if (valid && rank == 0) wcnt[w][e] = tag | cnt;
+    __syncthreads();
+    if (valid) {
+      int row = running[e] + rank;
+      for (int q = 0; q < w; ++q) {
+        const int v = wcnt[q][e];
+        if ((v >> 16) == r + 1) row += v & 0xffff;
+      }
+      sorted_slot[row] = (int32_t)s;
+      row_of_slot[s] = row;
+    }
+    __syncthreads();
+    if (valid && rank == 0) atomicAdd(&running[e], cnt);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int BM, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tiles, int32_t* err,
+                        int32_t* blockhist, int32_t* blockbase, int32_t* blockerr, hipStream_t stream) {
+  const int nblk = (int)((S + RT_SLOTS - 1) / RT_SLOTS);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (nblk > 0) {
+    hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr);
+  }
+  hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, BM,
+                     counts, offsets, blockbase, tiles, err);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, nbits, offsets,
+                       blockbase, sorted_slot, row_of_slot);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hmm

@@ -1,0 +1,205 @@
+"""Python binding of libhmm: ``hyper_mega_moe`` and its autograd Function.
+
+Argument marshalling only.  Every step of the path (routing, the grouped
+products, SwiGLU and its gradient, the combines) runs in the HIP kernels behind
+the C ABI of include/hmm.h; torch supplies device memory and the current HIP
+stream.  (HyperMegaMoE RFC section 3.1: the public call takes exactly x,
+topk_ids, topk_weights, up_proj_weight and down_proj_weight and returns y;
+section 3.2: the backward returns one gradient per public argument, None for
+topk_ids; section 3.3: offsets, tiling and buffers are internal.)
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+
+def _problem(T, H, I, E, K, flags=_lib.HMM_FLAG_VALIDATE_IDS, out_dtype=_lib.HMM_BF16, gmm1_dtype=_lib.HMM_BF16):
+    return _lib.Problem(int(T), int(H), int(I), int(E), int(K), out_dtype, gmm1_dtype, flags, 0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if (t is not None and t.numel() > 0) else 0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight):
+    """Shape/dtype/device checks of the public arguments (RFC section 4.2)."""
+    for name, t in (("x", x), ("topk_ids", topk_ids), ("topk_weights", topk_weights),
+                    ("up_proj_weight", up_proj_weight), ("down_proj_weight", down_proj_weight)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on a HIP device (got %s)" % (name, t.device))
+        if t.device != x.device:
+            raise ValueError("%s is on %s, x on %s" % (name, t.device, x.device))
+    if x.dtype != torch.bfloat16 or up_proj_weight.dtype != torch.bfloat16 or down_proj_weight.dtype != torch.bfloat16:
+        raise TypeError("x, up_proj_weight and down_proj_weight must be bfloat16")
+    if topk_ids.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_ids must be int32 or int64")
+    if not topk_weights.is_floating_point():
+        raise TypeError("topk_weights must be floating point")
+    if x.dim() != 2 or topk_ids.dim() != 2 or up_proj_weight.dim() != 3 or down_proj_weight.dim() != 3:
+        raise ValueError("expected x [T,H], topk_ids [T,K], up_proj_weight [E,H,2I], down_proj_weight [E,I,H]")
+    T, H = x.shape
+    E, H1, I2 = up_proj_weight.shape
+    I = I2 // 2
+    if topk_weights.shape != topk_ids.shape or topk_ids.shape[0] != T:
+        raise ValueError("topk_ids and topk_weights must both be [T, K] with T = x.shape[0]")
+    if H1 != H or I2 != 2 * I or tuple(down_proj_weight.shape) != (E, I, H):
+        raise ValueError("up_proj_weight must be [E,H,2I] and down_proj_weight [E,I,H] (got %s, %s, H=%d)"
+                         % (tuple(up_proj_weight.shape), tuple(down_proj_weight.shape), H))
+    return T, H, I, E, topk_ids.shape[1]
+
+
+def _contig(t, dtype=None):
+    if dtype is not None and t.dtype != dtype:
+        t = t.to(dtype)
+    return t.contiguous()
+
+
+def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags):
+    lib = _lib.load()
+    prob = _problem(T, H, I, E, K, flags)
+    ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
+    dev = x.device
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    saved = torch.empty(sv.value, dtype=torch.uint8, device=dev)
+    work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
+    _lib.check(lib.hmm_forward(ctypes.byref(prob), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2), _ptr(y),
+                               _ptr(saved), sv.value, _ptr(work), ws.value, _stream(dev)))
+    return y, saved
+
+
+def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags):
+    lib = _lib.load()
+    prob = _problem(T, H, I, E, K, flags)
+    ws = ctypes.c_size_t()
+    _lib.check(lib.hmm_backward_sizes(ctypes.byref(prob), ctypes.byref(ws)))
+    dev = x.device
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dW1 = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=dev)
+    dW2 = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
+    _lib.check(lib.hmm_backward(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2),
+                                _ptr(saved), saved.numel(), _ptr(dx), _ptr(dW1), _ptr(dW2), _ptr(dw),
+                                _ptr(work), ws.value, _stream(dev)))
+    return dx, dW1, dW2, dw
+
+
+class HyperMegaMoEFunction(torch.autograd.Function):
+    """Forward calls hmm_forward and keeps the saved buffer; backward calls hmm_backward."""
+
+    @staticmethod
+    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags):
+        T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+        x_ = _contig(x)
+        ids = _contig(topk_ids, torch.int32)
+        w = _contig(topk_weights, torch.float32)
+        W1 = _contig(up_proj_weight)
+        W2 = _contig(down_proj_weight)
+        with torch.cuda.device(x.device):
+            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags)
+        ctx.save_for_backward(x_, ids, w, W1, W2, saved)
+        ctx.dims = (T, H, I, E, K, flags)
+        ctx.w_dtype = topk_weights.dtype
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x_, ids, w, W1, W2, saved = ctx.saved_tensors
+        T, H, I, E, K, flags = ctx.dims
+        dy = _contig(dy, torch.bfloat16)
+        with torch.cuda.device(x_.device):
+            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags)
+        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None
+
+
+def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True):
+    """y [T,H] = sum_k topk_weights[t,k] * SwiGLU-FFN_{topk_ids[t,k]}(x[t]), on the GPU.
+
+    x bf16 [T,H]; topk_ids int32/int64 [T,K] (0 <= id < E); topk_weights float [T,K];
+    up_proj_weight bf16 [E,H,2I] (gate columns first, then up); down_proj_weight
+    bf16 [E,I,H].  Differentiable in x, topk_weights and both weights.
+    ``validate_ids`` checks the ids on the device before the matrix products
+    (one small device-to-host read-back) and raises ValueError if one is out
+    of range.
+    """
+    flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+    return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags)
+
+
+# ----------------------------------------------------------------------------- stage entry points (tests, tools)
+
+def route(topk_ids, E, validate_ids=True):
+    """Routing alone: dict(counts[E], offsets[E+1], sorted_slot[S], row_of_slot[S]) int32 tensors."""
+    if topk_ids.device.type != "cuda":
+        raise ValueError("topk_ids must be on a HIP device")
+    ids = _contig(topk_ids, torch.int32)
+    T, K = ids.shape
+    lib = _lib.load()
+    prob = _problem(T, 64, 64, E, K, _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0)
+    ws = ctypes.c_size_t()
+    _lib.check(lib.hmm_route_workspace_size(ctypes.byref(prob), ctypes.byref(ws)))
+    dev = ids.device
+    out = {
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "sorted_slot": torch.empty(T * K, dtype=torch.int32, device=dev),
+        "row_of_slot": torch.empty(T * K, dtype=torch.int32, device=dev),
+    }
+    work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.hmm_route(ctypes.byref(prob), _ptr(ids), _ptr(out["counts"]), _ptr(out["offsets"]),
+                                 _ptr(out["sorted_slot"]), _ptr(out["row_of_slot"]), _ptr(work), ws.value,
+                                 _stream(dev)))
+    return out
+
+
+def saved_views(saved, T, H, I, E, K):
+    """Typed views of the arrays a forward recorded in its saved buffer."""
+    lib = _lib.load()
+    prob = _problem(T, H, I, E, K)
+    L = _lib.SavedLayout()
+    _lib.check(lib.hmm_saved_layout_of(ctypes.byref(prob), ctypes.byref(L)))
+    S = T * K
+
+    def view(off, n, dtype, shape):
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return saved[off:off + nbytes].view(dtype).view(shape)
+
+    return {
+        "counts": view(L.counts, E, torch.int32, (E,)),
+        "offsets": view(L.offsets, E + 1, torch.int32, (E + 1,)),
+        "sorted_slot": view(L.sorted_slot, S, torch.int32, (S,)),
+        "row_of_slot": view(L.row_of_slot, S, torch.int32, (S,)),
+        "h": view(L.h, S * 2 * I, torch.bfloat16, (S, 2 * I)),
+        "a": view(L.a, S * I, torch.bfloat16, (S, I)),
+        "aw": view(L.aw, S * I, torch.bfloat16, (S, I)),
+        "id_error": view(L.id_error, 1, torch.int32, (1,)),
+    }
+
+
+def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True):
+    """Forward without autograd; returns (y, saved buffer) for stage-level checks."""
+    T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+    with torch.cuda.device(x.device):
+        return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
+                            _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags)
+
+
+def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved):
+    """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights)."""
+    T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    with torch.cuda.device(x.device):
+        return _backward_raw(_contig(dy, torch.bfloat16), _contig(x), _contig(topk_ids, torch.int32),
+                             _contig(topk_weights, torch.float32), _contig(up_proj_weight),
+                             _contig(down_proj_weight), saved, T, H, I, E, K, 0)

@@ -46,6 +46,30 @@ Modes
   R9 dW1 = bf16(sum x^T dH), dW2 = bf16(sum aw^T dY)
   d_topk_weights = sum_i G_i * a_i, float32 output, no rounding.
 
+Admissible deviation (faithful mode)
+------------------------------------
+A pipeline that evaluates the value in front of a rounding point in float32
+(any summation order) can land on the other side of a bfloat16 rounding
+boundary when the exact value lies within its evaluation error of that
+boundary; both neighbours are then correct results, and the choice propagates
+downstream.  Next to every faithful value the oracle therefore carries
+``dev``, a bound on how far an admissible result may lie from it:
+
+  * at a value v with upstream deviation d_up, the float32 evaluation error is
+    estimated as  eps = C_ACC * u * sqrt(n/2) * sqrt(sum_i t_i^2) + C_EL * u * |v|
+    for a sum of n terms t_i (u = 2^-24; sqrt(n/2) sqrt(sum t^2) is the typical
+    size of the partial sums' rounding errors; C_ACC = 8 is a wide margin) and
+    d = d_up + eps;
+  * rounding maps [v - d, v + d] onto the bfloat16 values between
+    RNE(v - d) and RNE(v + d), so the rounded value's bound is
+    max(|RNE(v + d) - RNE(v)|, |RNE(v) - RNE(v - d)|);
+  * downstream, bounds propagate to first order through |derivatives|, times
+    C_PROP = 1.25 to cover the curvature over the few-ulp steps involved.
+
+For almost every element dev is 0; it is one or a few ulps where a rounding
+decision is genuinely open.  Parity checks accept |gpu - ref| <= atol +
+rtol |ref| + dev.  In pure mode dev is 0.
+
 The FP8 variant (``gmm1="fp8"``) quantises each token row and each
 (expert, column) of the up-projection weight to E4M3 (see ``quant``) before
 the up-projection; everything after R1, and the whole backward, stays as in
@@ -58,6 +82,16 @@ from .numerics import round_bf16, sigmoid, silu
 from .quant import quantize_columns, quantize_rows
 from .routing import check_ids
 
+U32 = 2.0 ** -24     # unit roundoff of float32
+C_ACC = 8.0          # margin on the typical accumulated rounding error of a float32 sum
+C_EL = 8.0           # float32 evaluation error of an elementwise formula, in ulps
+C_PROP = 1.25        # margin on first-order propagation (covers curvature over a few ulps)
+
+
+def acc_eps(sq_sum, n):
+    """Evaluation-error estimate of a float32 sum of n terms whose squares sum to sq_sum."""
+    return C_ACC * U32 * np.sqrt(max(n, 1) / 2.0) * np.sqrt(sq_sum)
+
 
 class MoEFFN:
     """One problem instance.  Inputs are float arrays holding exact bf16 values.
@@ -65,6 +99,8 @@ class MoEFFN:
     x [T,H], topk_ids [T,K] int, topk_weights [T,K] float32,
     up_proj_weight [E,H,2I], down_proj_weight [E,I,H], dY [T,H] (optional).
     Weights are converted to float64 one expert at a time, on first use.
+    Methods return values; the ``*_dev`` variants also return the admissible
+    deviation bound described in the module text.
     """
 
     def __init__(self, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
@@ -80,6 +116,7 @@ class MoEFFN:
         self.W2 = np.asarray(down_proj_weight)
         self.dY = None if dY is None else np.asarray(dY)
         self.mode, self.gmm1 = mode, gmm1
+        self.faithful = mode == "faithful"
         self.T, self.H = self.x.shape
         self.K = self.ids.shape[1]
         self.E, _, two_i = self.W1.shape
@@ -92,8 +129,14 @@ class MoEFFN:
         self._w1, self._w2, self._w1q = {}, {}, {}
 
     # -- helpers ---------------------------------------------------------------
-    def _r(self, v):
-        return round_bf16(v) if self.mode == "faithful" else np.asarray(v, np.float64)
+    def _round(self, v, d):
+        """Rounding point: (bf16(v), admissible deviation) in faithful mode; (v, 0) in pure mode."""
+        v = np.asarray(v, np.float64)
+        if not self.faithful:
+            return v, np.zeros_like(v)
+        r = round_bf16(v)
+        dev = np.maximum(np.abs(round_bf16(v + d) - r), np.abs(r - round_bf16(v - d)))
+        return r, dev
 
     def _W1(self, e):
         if e not in self._w1:
@@ -115,104 +158,155 @@ class MoEFFN:
         return np.flatnonzero(self.ids.reshape(-1) == e)
 
     # -- per-slot stages (rows: any number of slots of ONE expert) ------------
-    def up(self, e, xrows, cols=None):
+    def up_dev(self, e, xrows, cols=None):
         """R1: h = x . W1[e] for the given rows (optionally a subset of columns)."""
         cols = slice(None) if cols is None else cols
+        xr = np.asarray(xrows, np.float64)
         if self.gmm1 == "fp8":
             q, _, dsx = quantize_rows(xrows)
             wq, _, dsw = self._W1q(e)
-            acc = q @ wq[:, cols]
-            h = acc * dsx.astype(np.float64)[:, None] * dsw.astype(np.float64)[cols][None, :]
+            wqc = wq[:, cols]
+            scale = dsx.astype(np.float64)[:, None] * dsw.astype(np.float64)[cols][None, :]
+            h = (q @ wqc) * scale
+            eps = acc_eps((q * q) @ (wqc * wqc), self.H) * scale + 2 * C_EL * U32 * np.abs(h)
         else:
-            h = np.asarray(xrows, np.float64) @ self._W1(e)[:, cols]
-        return self._r(h)
+            W = self._W1(e)[:, cols]
+            h = xr @ W
+            eps = acc_eps((xr * xr) @ (W * W), self.H)
+        return self._round(h, eps)
 
-    def swiglu(self, g, u):
-        """R2: a = silu(g) * u."""
-        return self._r(silu(g) * u)
+    def up(self, e, xrows, cols=None):
+        return self.up_dev(e, xrows, cols)[0]
+
+    def hidden_dev(self, e, xrows, icols=None):
+        """(g, u, a) and their deviations for gate columns ``icols`` (default all)."""
+        icols = np.arange(self.I) if icols is None else np.asarray(icols)
+        h, hd = self.up_dev(e, xrows, np.concatenate([icols, icols + self.I]))
+        n = icols.size
+        g, u, gd, ud = h[:, :n], h[:, n:], hd[:, :n], hd[:, n:]
+        s = sigmoid(g)
+        v = g * s * u                                           # R2
+        d = C_PROP * (np.abs(u * (s + g * s * (1 - s))) * gd + np.abs(g * s) * ud) + C_EL * U32 * np.abs(v)
+        a, ad = self._round(v, d)
+        return (g, u, a), (gd, ud, ad)
 
     def hidden(self, e, xrows, icols=None):
-        """Return (g, u, a) of the rows for gate columns ``icols`` (default all)."""
-        icols = np.arange(self.I) if icols is None else np.asarray(icols)
-        h = self.up(e, xrows, np.concatenate([icols, icols + self.I]))
-        n = icols.size
-        g, u = h[:, :n], h[:, n:]
-        return g, u, self.swiglu(g, u)
+        return self.hidden_dev(e, xrows, icols)[0]
 
-    def down(self, e, a):
+    def down_dev(self, e, a, ad):
         """R3: o = a . W2[e]."""
-        return self._r(a @ self._W2(e))
+        W2 = self._W2(e)
+        v = a @ W2
+        d = C_PROP * (ad @ np.abs(W2)) + acc_eps((a * a) @ (W2 * W2), self.I)
+        return self._round(v, d)
 
     def act_grad(self, e, dyrows, icols=None):
-        """G = dY . W2[e]^T (unrounded) for gate columns ``icols``."""
+        """G = dY . W2[e]^T (unrounded) and its float32 evaluation error, for gate columns ``icols``."""
         W2 = self._W2(e)
         W2 = W2 if icols is None else W2[np.asarray(icols)]
-        return np.asarray(dyrows, np.float64) @ W2.T
+        dyr = np.asarray(dyrows, np.float64)
+        return dyr @ W2.T, acc_eps((dyr * dyr) @ (W2 * W2).T, self.H)
 
-    def swiglu_grad(self, dA, g, u):
-        """SwiGLUGrad, R5: dH = [dg | du]."""
+    def swiglu_grad_dev(self, w, G, Ge, g, u, gd, ud):
+        """SwiGLUGrad with dA = w G; R5: dH = [dg | du] and deviations."""
         s = sigmoid(g)
-        dg = dA * u * s * (1.0 + g * (1.0 - s))
-        du = dA * g * s
-        return self._r(dg), self._r(du)
+        q = s * (1.0 + g * (1.0 - s))              # d silu / dg
+        dA = w * G
+        vg = dA * u * q
+        vu = dA * g * s
+        dq = s * (1 - s) * (2.0 + g * (1.0 - 2.0 * s))  # d q / dg
+        dvg = C_PROP * (np.abs(dA * u * dq) * gd + np.abs(dA * q) * ud + np.abs(w * u * q) * Ge) + C_EL * U32 * np.abs(vg)
+        dvu = C_PROP * (np.abs(dA * q) * gd + np.abs(w * g * s) * Ge) + C_EL * U32 * np.abs(vu)
+        return self._round(vg, dvg), self._round(vu, dvu)
 
     # -- forward ---------------------------------------------------------------
-    def forward(self, tokens=None, out_dtype="bf16"):
-        """y for the given tokens (default all), per-token loop over K slots."""
+    def forward_dev(self, tokens=None, out_dtype="bf16"):
+        """(y, dev) for the given tokens (default all), per-token loop over K slots."""
         toks = np.arange(self.T) if tokens is None else np.asarray(tokens)
         y = np.zeros((toks.size, self.H))
+        yd = np.zeros((toks.size, self.H))
         for j, t in enumerate(toks):
             acc = np.zeros(self.H)
+            accd = np.zeros(self.H)
+            sq = np.zeros(self.H)
             for k in range(self.K):
                 e = self.ids[t, k]
-                _, _, a = self.hidden(e, self.x[t:t + 1])
-                o = self.down(e, a)[0]
-                acc = acc + self.w[t, k] * o
-            y[j] = round_bf16(acc) if (out_dtype == "bf16" and self.mode == "faithful") else acc
-        return y
+                (_, _, a), (_, _, ad) = self.hidden_dev(e, self.x[t:t + 1])
+                o, od = self.down_dev(e, a, ad)
+                acc = acc + self.w[t, k] * o[0]
+                accd = accd + abs(self.w[t, k]) * od[0]
+                sq = sq + (self.w[t, k] * o[0]) ** 2
+            if out_dtype == "bf16":
+                y[j], yd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, self.K))      # R4
+            else:
+                y[j], yd[j] = acc, accd
+        return y, yd
+
+    def forward(self, tokens=None, out_dtype="bf16"):
+        return self.forward_dev(tokens, out_dtype)[0]
 
     def slot_intermediates(self, slots):
         """h (= [g|u]), a and o of the given slots, one row per slot (for checks)."""
+        return self.slot_intermediates_dev(slots)[0]
+
+    def slot_intermediates_dev(self, slots):
         slots = np.asarray(slots)
-        h = np.zeros((slots.size, 2 * self.I))
-        a = np.zeros((slots.size, self.I))
-        o = np.zeros((slots.size, self.H))
+        out = [np.zeros((slots.size, 2 * self.I)), np.zeros((slots.size, self.I)), np.zeros((slots.size, self.H))]
+        dev = [np.zeros_like(z) for z in out]
         for j, s in enumerate(slots):
             t, k = divmod(int(s), self.K)
             e = self.ids[t, k]
-            g, u, aa = self.hidden(e, self.x[t:t + 1])
-            h[j, :self.I], h[j, self.I:], a[j] = g[0], u[0], aa[0]
-            o[j] = self.down(e, aa)[0]
-        return h, a, o
+            (g, u, a), (gd, ud, ad) = self.hidden_dev(e, self.x[t:t + 1])
+            o, od = self.down_dev(e, a, ad)
+            out[0][j, :self.I], out[0][j, self.I:], out[1][j], out[2][j] = g[0], u[0], a[0], o[0]
+            dev[0][j, :self.I], dev[0][j, self.I:], dev[1][j], dev[2][j] = gd[0], ud[0], ad[0], od[0]
+        return out, dev
 
     # -- backward --------------------------------------------------------------
-    def backward_tokens(self, tokens=None, out_dtype="bf16"):
-        """(dx, d_topk_weights) for the given tokens, per-token loop over K slots."""
+    def backward_tokens_dev(self, tokens=None, out_dtype="bf16"):
+        """((dx, d_topk_weights), (dx_dev, dw_dev)) for the given tokens."""
         if self.dY is None:
             raise ValueError("dY required")
         toks = np.arange(self.T) if tokens is None else np.asarray(tokens)
         dx = np.zeros((toks.size, self.H))
+        dxd = np.zeros((toks.size, self.H))
         dw = np.zeros((toks.size, self.K))
+        dwd = np.zeros((toks.size, self.K))
         for j, t in enumerate(toks):
             acc = np.zeros(self.H)
+            accd = np.zeros(self.H)
+            sq = np.zeros(self.H)
             for k in range(self.K):
                 e = self.ids[t, k]
-                g, u, a = self.hidden(e, self.x[t:t + 1])
-                G = self.act_grad(e, self.dY[t:t + 1])
+                (g, u, a), (gd, ud, ad) = self.hidden_dev(e, self.x[t:t + 1])
+                G, Ge = self.act_grad(e, self.dY[t:t + 1])
                 dw[j, k] = float(np.sum(G * a))
-                dg, du = self.swiglu_grad(self.w[t, k] * G, g, u)
+                dwd[j, k] = float(C_PROP * np.sum(np.abs(G) * ad + np.abs(a) * Ge) + acc_eps(np.sum((G * a) ** 2), self.I))
+                (dg, dgd), (du, dud) = self.swiglu_grad_dev(self.w[t, k], G, Ge, g, u, gd, ud)
                 dH = np.concatenate([dg, du], axis=1)
-                dxp = self._r(dH @ self._W1(e).T)[0]             # R6
-                acc = acc + dxp
-            dx[j] = round_bf16(acc) if (out_dtype == "bf16" and self.mode == "faithful") else acc
-        return dx, dw
+                dHd = np.concatenate([dgd, dud], axis=1)
+                W1 = self._W1(e)
+                v = dH @ W1.T
+                xp, xpd = self._round(v, C_PROP * (dHd @ np.abs(W1.T)) + acc_eps((dH * dH) @ (W1 * W1).T, 2 * self.I))  # R6
+                acc = acc + xp[0]
+                accd = accd + xpd[0]
+                sq = sq + xp[0] ** 2
+            if out_dtype == "bf16":
+                dx[j], dxd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, self.K))     # R7
+            else:
+                dx[j], dxd[j] = acc, accd
+        return (dx, dw), (dxd, dwd)
 
-    def weight_grads_expert(self, e, icols=None, out_dtype="bf16"):
-        """Weight gradients of expert e restricted to gate columns ``icols``.
+    def backward_tokens(self, tokens=None, out_dtype="bf16"):
+        """(dx, d_topk_weights) for the given tokens, per-token loop over K slots."""
+        return self.backward_tokens_dev(tokens, out_dtype)[0]
 
-        Returns (dW1_gate[H, n], dW1_up[H, n], dW2_rows[n, H]) where n =
-        len(icols): columns i and I+i of d_up_proj_weight[e] and rows i of
-        d_down_proj_weight[e].  The sum runs over the slots routed to e in
+    def weight_grads_expert_dev(self, e, icols=None, out_dtype="bf16"):
+        """Weight gradients of expert e restricted to gate columns ``icols``, with deviations.
+
+        Returns ((dW1_gate[H, n], dW1_up[H, n], dW2_rows[n, H]), (their devs))
+        where n = len(icols): columns i and I+i of d_up_proj_weight[e] and rows i
+        of d_down_proj_weight[e].  The sum runs over the slots routed to e in
         ascending slot order; an expert with no slot gets exact zeros.
         """
         if self.dY is None:
@@ -222,29 +316,43 @@ class MoEFFN:
         n = icols.size
         if slots.size == 0:
             z = np.zeros((self.H, n))
-            return z, z.copy(), np.zeros((n, self.H))
+            zr = np.zeros((n, self.H))
+            return (z, z.copy(), zr), (z.copy(), z.copy(), zr.copy())
         t = slots // self.K
         k = slots % self.K
         xr = self.x[t].astype(np.float64)
         dyr = self.dY[t].astype(np.float64)
         w = self.w[t, k][:, None]
-        g, u, a = self.hidden(e, xr, icols)
-        G = self.act_grad(e, dyr, icols)
-        dg, du = self.swiglu_grad(w * G, g, u)
-        aw = self._r(w * a)                                       # R8
-        dW1g = xr.T @ dg                                          # R9
-        dW1u = xr.T @ du
-        dW2r = aw.T @ dyr
-        if out_dtype == "bf16" and self.mode == "faithful":
-            dW1g, dW1u, dW2r = round_bf16(dW1g), round_bf16(dW1u), round_bf16(dW2r)
-        return dW1g, dW1u, dW2r
+        (g, u, a), (gd, ud, ad) = self.hidden_dev(e, xr, icols)
+        G, Ge = self.act_grad(e, dyr, icols)
+        (dg, dgd), (du, dud) = self.swiglu_grad_dev(w, G, Ge, g, u, gd, ud)
+        aw, awd = self._round(w * a, C_PROP * np.abs(w) * ad + C_EL * U32 * np.abs(w * a))    # R8
+        m = slots.size
+        ax = np.abs(xr)
+        res = [xr.T @ dg, xr.T @ du, aw.T @ dyr]                                      # R9
+        devs = [C_PROP * (ax.T @ dgd) + acc_eps((xr * xr).T @ (dg * dg), m),
+                C_PROP * (ax.T @ dud) + acc_eps((xr * xr).T @ (du * du), m),
+                C_PROP * (awd.T @ np.abs(dyr)) + acc_eps((aw * aw).T @ (dyr * dyr), m)]
+        if out_dtype == "bf16":
+            pairs = [self._round(v, d) for v, d in zip(res, devs)]
+            res, devs = [p[0] for p in pairs], [p[1] for p in pairs]
+        return tuple(res), tuple(devs)
+
+    def weight_grads_expert(self, e, icols=None, out_dtype="bf16"):
+        return self.weight_grads_expert_dev(e, icols, out_dtype)[0]
+
+    def backward_dev(self, out_dtype="bf16"):
+        """Full backward with deviations: ((dx, dw, dW1, dW2), (their devs))."""
+        (dx, dw), (dxd, dwd) = self.backward_tokens_dev(None, out_dtype)
+        dW1 = np.zeros((self.E, self.H, 2 * self.I))
+        dW2 = np.zeros((self.E, self.I, self.H))
+        dW1d, dW2d = np.zeros_like(dW1), np.zeros_like(dW2)
+        for e in range(self.E):
+            (g, u, r), (gd, ud, rd) = self.weight_grads_expert_dev(e, None, out_dtype)
+            dW1[e, :, :self.I], dW1[e, :, self.I:], dW2[e] = g, u, r
+            dW1d[e, :, :self.I], dW1d[e, :, self.I:], dW2d[e] = gd, ud, rd
+        return (dx, dw, dW1, dW2), (dxd, dwd, dW1d, dW2d)
 
     def backward(self, out_dtype="bf16"):
         """Full backward: dx [T,H], d_topk_weights [T,K], dW1 [E,H,2I], dW2 [E,I,H]."""
-        dx, dw = self.backward_tokens(None, out_dtype)
-        dW1 = np.zeros((self.E, self.H, 2 * self.I))
-        dW2 = np.zeros((self.E, self.I, self.H))
-        for e in range(self.E):
-            g, u, r = self.weight_grads_expert(e, None, out_dtype)
-            dW1[e, :, :self.I], dW1[e, :, self.I:], dW2[e] = g, u, r
-        return dx, dw, dW1, dW2
+        return self.backward_dev(out_dtype)[0]
