@@ -37,6 +37,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def source_sha():
+    """sha256[:16] of the library sources (the key of the recorded traffic counters)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_ffn_int32_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc figures, or None if absent or stale."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha():
+        return None
+    ent = rec.get("per_workload", {}).get(workload, {}).get(kernel)
+    return None if ent is None else int(round(ent["bytes"]))
+
+
 def stage_work(stage, T, H, I, E, K):
     """Algorithmic work of one launch of a stage: (bound, amount, unit)."""
     S = T * K
@@ -173,6 +197,8 @@ def main():
     ap.add_argument("--no-validate", action="store_true", help="skip the id check's device-to-host read-back")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times (scale for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
@@ -184,6 +210,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied %d MiB 5 times (reads %d KiB, writes %d KiB per copy)" % (n >> 20, n >> 10, n >> 10))
+        return
     spec = dict(synth.WORKLOADS[args.workload])
     if spec.get("gmm1", "bf16") != "bf16":
         print("workload %s needs the FP8 up-projection, which this build does not run yet" % args.workload,
@@ -237,7 +272,8 @@ def main():
         "peak": PEAK_BF16_TFLOPS if dom[3] == "mfma" else PEAK_HBM_GBS,
         "unit": dom[6],
         "frac": round(dom[7], 5),
-        "traffic": None,
+        "algorithmic": dom[4],
+        "traffic": recorded_traffic(args.workload, dom[0]),
     }
 
     cpu = None

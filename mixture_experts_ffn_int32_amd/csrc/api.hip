@@ -370,11 +370,11 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
       (s = need(topk_weights, ne, "topk_weights")) || (s = need(up_w, true, "up_proj_weight")) ||
       (s = need(down_w, true, "down_proj_weight")) || (s = need(saved, true, "saved")) ||
       (s = need(dx, ne, "dx")) || (s = need(d_up_w, true, "d_up_proj_weight")) ||
-      (s = need(d_down_w, true, "d_down_proj_weight")) || (s = need(d_topk_weights, ne, "d_topk_weights")) ||
-      (s = need(workspace, true, "workspace")))
+      (s = need(d_down_w, true, "d_down_proj_weight")) || (s = need(d_topk_weights, ne, "d_topk_weights")))
     return s;
   const hmm_saved_layout L = saved_layout(d);
   const BwdWork W = bwd_work(d);
+  if ((s = need(workspace, W.total > 0, "workspace"))) return s;  // T = 0 needs no workspace
   if (saved_bytes < L.total) return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "saved %zu < %zu bytes", saved_bytes, L.total);
   if (workspace_bytes < W.total)
     return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, W.total);
