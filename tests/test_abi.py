@@ -1,0 +1,101 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and its
+host-side checks reject bad problems before any HIP call (no GPU is touched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_int32_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hmm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_ffn_int32_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hmm_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings(lib):
+    assert lib.hmm_status_string(0) == b"HMM_OK"
+    assert lib.hmm_status_string(7) == b"HMM_ERR_EXPERT_ID_OUT_OF_RANGE"
+    assert b"gfx950" in lib.hmm_build_info()
+
+
+def _prob(**kw):
+    d = dict(T=1024, H=512, I=128, E=4, K=2, out_dtype=_lib.HMM_BF16, gmm1_dtype=_lib.HMM_BF16,
+             flags=_lib.HMM_FLAG_VALIDATE_IDS, reserved=0)
+    d.update(kw)
+    return _lib.Problem(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=500), _lib.HMM_ERR_BAD_SHAPE), (dict(I=32), _lib.HMM_ERR_BAD_SHAPE), (dict(K=0), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(K=17), _lib.HMM_ERR_BAD_SHAPE), (dict(E=0), _lib.HMM_ERR_BAD_SHAPE), (dict(E=1025), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(T=-1), _lib.HMM_ERR_BAD_SHAPE), (dict(T=1 << 28, K=16), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(out_dtype=7), _lib.HMM_ERR_BAD_DTYPE), (dict(gmm1_dtype=9), _lib.HMM_ERR_BAD_DTYPE),
+    (dict(out_dtype=_lib.HMM_F32), _lib.HMM_ERR_UNSUPPORTED), (dict(flags=8), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(reserved=1), _lib.HMM_ERR_BAD_SHAPE),
+])
+def test_sizes_reject_bad_problems(lib, kw, status):
+    ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
+    p = _prob(**kw)
+    assert lib.hmm_forward_sizes(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(sv)) == status
+    assert lib.hmm_last_error_message()
+
+
+def test_sizes_and_layout(lib):
+    ws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    p = _prob()
+    assert lib.hmm_forward_sizes(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(sv)) == 0
+    assert lib.hmm_backward_sizes(ctypes.byref(p), ctypes.byref(bws)) == 0
+    L = _lib.SavedLayout()
+    assert lib.hmm_saved_layout_of(ctypes.byref(p), ctypes.byref(L)) == 0
+    S, I = 1024 * 2, 128
+    assert L.total == sv.value
+    offs = [L.counts, L.offsets, L.sorted_slot, L.row_of_slot, L.tiles, L.h, L.a, L.aw, L.id_error]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.a - L.h >= S * 2 * I * 2 and L.aw - L.a >= S * I * 2
+    assert ws.value >= S * 512 * 2          # o [S, H] bf16
+    assert bws.value >= S * (2 * I + 512) * 2
+
+
+def test_null_and_misaligned_pointers_rejected_without_launch(lib):
+    p = _prob()
+    z = ctypes.c_void_p(0)
+    st = lib.hmm_forward(ctypes.byref(p), z, z, z, z, z, z, z, 0, z, 0, z)
+    assert st == _lib.HMM_ERR_NULL_POINTER
+    bad = ctypes.c_void_p(0x1001)             # never dereferenced: the check fails first
+    st = lib.hmm_forward(ctypes.byref(p), bad, bad, bad, bad, bad, bad, bad, 1 << 30, bad, 1 << 30, z)
+    assert st == _lib.HMM_ERR_MISALIGNED
+    ok = ctypes.c_void_p(0x1000)              # aligned, but the buffers are declared too small
+    st = lib.hmm_forward(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, 16, ok, 16, z)
+    assert st == _lib.HMM_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_profile_read_without_launches(lib):
+    lib.hmm_profile_enable(1)
+    buf = (_lib.StageTime * 8)()
+    n, dropped = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert lib.hmm_profile_read(buf, 8, ctypes.byref(n), ctypes.byref(dropped)) == 0
+    assert n.value == 0 and dropped.value == 0
+    lib.hmm_profile_enable(0)
