@@ -104,13 +104,14 @@ typedef struct hmm_problem {
  *   sorted_slot[S] int32 slot (t*K+k) placed at permuted row p; slots of one
  *                        expert are contiguous and in ascending slot order
  *   row_of_slot[S] int32 inverse of sorted_slot (-1 for a dropped slot)
- *   tiles                int32 tile table of the grouped products
+ *   tok_of_row[S] int32  token of permuted row p (sorted_slot[p] / K)
+ *   tiles                int32 tile tables of the grouped products
  *   h[S,2I] bf16         up-projection output per permuted row ([gate | up])
  *   a[S,I] bf16          SwiGLU output per permuted row
  *   aw[S,I] bf16         topk weight * a, the W2-gradient operand
  *   id_error int32       1 if an id was out of range on the recording call */
 typedef struct hmm_saved_layout {
-  size_t counts, offsets, sorted_slot, row_of_slot, tiles, h, a, aw, id_error, total;
+  size_t counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, h, a, aw, id_error, total;
 } hmm_saved_layout;
 
 /* Sizes of the forward's workspace and saved buffers for ``p`` (bytes). */

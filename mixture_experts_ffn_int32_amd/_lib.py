@@ -40,7 +40,8 @@ class Problem(ctypes.Structure):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("counts", "offsets", "sorted_slot", "row_of_slot", "tiles", "h", "a", "aw", "id_error", "total")]
+                ("counts", "offsets", "sorted_slot", "row_of_slot", "tok_of_row", "tiles", "h", "a", "aw", "id_error",
+                 "total")]
 
 
 class StageTime(ctypes.Structure):

@@ -55,6 +55,13 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_DTYPE, "out_dtype must be HMM_BF16 or HMM_F32 (got %d)", p->out_dtype);
   if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3)
     return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16 or HMM_FP8_E4M3 (got %d)", p->gmm1_dtype);
+  {
+    // every array a product reads through a buffer resource must stay below 4 GiB
+    const int64_t S = p->T * p->K, lim = (int64_t)0xFFFFFF00;
+    const int64_t ext[] = {p->T * p->H * 2, S * 2 * p->I * 2, S * p->H * 2, p->H * 2 * p->I * 2};
+    for (int64_t x : ext)
+      if (x > lim) return fail(HMM_ERR_UNSUPPORTED, "an operand array exceeds 4 GiB (%lld bytes)", (long long)x);
+  }
   if (p->out_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is not implemented");
   if (p->gmm1_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "gmm1_dtype HMM_FP8_E4M3 is not implemented");
   d->T = p->T;
@@ -76,7 +83,7 @@ hmm_status need(const void* ptr, bool nonempty, const char* name) {
 }
 
 int64_t n_route_blocks(const Dims& d) { return (d.S + hmm::RT_SLOTS - 1) / hmm::RT_SLOTS; }
-int64_t n_tiles_max(const Dims& d) { return hmm::max_row_tiles(d.S, d.E, hmm::GEMM_BM); }
+int64_t tile_ints(const Dims& d) { return hmm::tile_table_ints(d.S, d.E); }
 
 hmm_saved_layout saved_layout(const Dims& d) {
   hmm_saved_layout L{};
@@ -85,7 +92,8 @@ hmm_saved_layout saved_layout(const Dims& d) {
   L.offsets = o;       o += up((d.E + 1) * 4);
   L.sorted_slot = o;   o += up(d.S * 4);
   L.row_of_slot = o;   o += up(d.S * 4);
-  L.tiles = o;         o += up((2 + 2 * n_tiles_max(d)) * 4);
+  L.tok_of_row = o;    o += up(d.S * 4);
+  L.tiles = o;         o += up(tile_ints(d) * 4);
   L.h = o;             o += up(d.S * 2 * d.I * 2);
   L.a = o;             o += up(d.S * d.I * 2);
   L.aw = o;            o += up(d.S * d.I * 2);
@@ -195,14 +203,14 @@ int32_t* pinned_word() {
 }
 
 hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
-                     int32_t* row_of_slot, int32_t* tiles, int32_t* err, void* scratch, const RouteScratch& rs,
-                     bool validate_ids, hipStream_t stream) {
+                     int32_t* row_of_slot, int32_t* tok_of_row, int32_t* tiles, int32_t* err, void* scratch,
+                     const RouteScratch& rs, bool validate_ids, hipStream_t stream) {
   hipError_t e;
   {
     Stage stage("route", stream);
-    e = hmm::launch_route(ids, d.S, (int)d.E, hmm::GEMM_BM, counts, offsets, sorted_slot, row_of_slot, tiles, err,
-                          at<int32_t>(scratch, rs.blockhist), at<int32_t>(scratch, rs.blockbase),
-                          at<int32_t>(scratch, rs.blockerr), stream);
+    e = hmm::launch_route(ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E), counts, offsets,
+                          sorted_slot, row_of_slot, tok_of_row, tiles, err, at<int32_t>(scratch, rs.blockhist),
+                          at<int32_t>(scratch, rs.blockbase), at<int32_t>(scratch, rs.blockerr), stream);
   }
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   if (validate_ids) {
@@ -242,7 +250,9 @@ const char* hmm_status_string(hmm_status s) {
 
 const char* hmm_last_error_message(void) { return g_last_error.c_str(); }
 
-const char* hmm_build_info(void) { return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16, 128x128x64 tiles"; }
+const char* hmm_build_info(void) {
+  return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16; 256x256x64 and 64x256x64 tiles, grouped rasterisation";
+}
 
 hmm_status hmm_forward_sizes(const hmm_problem* p, size_t* workspace_bytes, size_t* saved_bytes) {
   Dims d;
@@ -279,8 +289,9 @@ hmm_status hmm_route_workspace_size(const hmm_problem* p, size_t* workspace_byte
   if (!workspace_bytes) return fail(HMM_ERR_NULL_POINTER, "size output is NULL");
   RouteScratch rs = route_scratch(d, 0);
   size_t o = rs.total;
-  o += up((2 + 2 * n_tiles_max(d)) * 4);  // tile table
-  o += up(4);                             // error word
+  o += up(tile_ints(d) * 4);  // tile table
+  o += up(4);                 // error word
+  o += up(d.S * 4);           // token of each permuted row
   *workspace_bytes = o;
   return HMM_OK;
 }
@@ -302,8 +313,9 @@ hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* cou
     return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need_ws);
   RouteScratch rs = route_scratch(d, 0);
   int32_t* tiles = at<int32_t>(workspace, rs.total);
-  int32_t* err = at<int32_t>(workspace, rs.total + up((2 + 2 * n_tiles_max(d)) * 4));
-  return run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tiles, err, workspace, rs,
+  int32_t* err = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4));
+  int32_t* tok = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4) + up(4));
+  return run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tok, tiles, err, workspace, rs,
                    (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, (hipStream_t)stream);
 }
 
@@ -328,12 +340,15 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   int32_t* offsets = at<int32_t>(saved, L.offsets);
   int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
   int32_t* tiles = at<int32_t>(saved, L.tiles);
+  int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
   s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
-                tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, st);
+                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs,
+                (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, st);
   if (s != HMM_OK) return s;
   if (!ne) return HMM_OK;
 
-  hmm::RowGroups g{tiles, offsets, sorted_slot, n_tiles_max(d), (int)d.K};
+  hmm::RowGroups g{tiles, offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E),
+                   hmm::max_small_tiles(d.S, d.E), d.T, d.S};
   uint16_t* h = at<uint16_t>(saved, L.h);
   uint16_t* a = at<uint16_t>(saved, L.a);
   uint16_t* aw = at<uint16_t>(saved, L.aw);
@@ -383,7 +398,9 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   const int32_t* offsets = at<int32_t>(saved, L.offsets);
   const int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
   const int32_t* row_of_slot = at<int32_t>(saved, L.row_of_slot);
-  hmm::RowGroups g{at<int32_t>(saved, L.tiles), offsets, sorted_slot, n_tiles_max(d), (int)d.K};
+  const int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
+  hmm::RowGroups g{at<int32_t>(saved, L.tiles), offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E),
+                   hmm::max_small_tiles(d.S, d.E), d.T, d.S};
   const uint16_t* h = at<uint16_t>(saved, L.h);
   const uint16_t* a = at<uint16_t>(saved, L.a);
   const uint16_t* aw = at<uint16_t>(saved, L.aw);
@@ -416,12 +433,14 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   }
   {
     Stage stage("dw2", st);
-    e = hmm::launch_dw2(offsets, sorted_slot, (int)d.K, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w, st);
+    e = hmm::launch_dw2(offsets, tok_of_row, d.T, d.S, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w,
+                        st);
   }
   if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
   {
     Stage stage("dw1", st);
-    e = hmm::launch_dw1(offsets, sorted_slot, (int)d.K, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w, st);
+    e = hmm::launch_dw1(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w,
+                        st);
   }
   if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
   return HMM_OK;

@@ -13,34 +13,53 @@
 //   dw1         reduction x[tok(p)]^T (M-major, gather) dH[p] (N-major)        store dW1[e]
 //   dw2         reduction aw[p]^T    (M-major)          dY[tok(p)] (N-major)   store dW2[e]
 //
-// "rows" products take their work from the tile table built by the routing
-// (one 128-row tile of one expert per entry; the last tile of an expert is
-// ragged).  "reduction" products run one tile per (expert, M-tile, N-tile) and
-// reduce over that expert's rows; an expert without rows writes zeros.
+// Tile shapes (each wave owns MB x NB accumulator blocks of 32 x 32):
+//   Big   256 x 256 x 64, 8 waves as 2 x 4, 128 x 64 per wave (one workgroup per CU,
+//         two waves per SIMD)
+//   Small  64 x 256 x 64, 4 waves as 1 x 4,  64 x 64 per wave (expert remainders, small experts)
+// "rows" products run over the routing's tile tables: each expert's rows are
+// covered by big tiles, and a remainder of at most 128 rows by small tiles, so
+// a small or long-tail expert does not pay for a 256-row tile (RFC 6.3, expert
+// x block granularity).  "reduction" products run one big tile per (expert,
+// M-tile, N-tile) and reduce over that expert's rows; an expert without rows
+// writes zeros.
 //
-// Tile: 128 x 128 x 64, 256 threads = 4 waves in 2 x 2, each wave a 64 x 64
-// block of 2 x 2 MFMA 32x32 accumulators.  Both operand tiles go through LDS,
-// double buffered, with global loads of the next K step issued before the MFMAs
-// of the current one.  K-major tiles sit in LDS as [row][k] (row pitch 72
-// elements) and are read with ds_read_b128; M/N-major tiles sit as [k][m]
-// (pitch 144) and are read with the gfx950 transposing ds_read_b64_tr_b16, so
-// no operand is transposed in memory.  Workgroup ids are remapped so that
-// consecutive logical tiles land on the same XCD (one L2 each).
+// Both operand tiles go through LDS, double buffered.  Global loads are buffer
+// loads (32-bit per-thread offsets against a resource of the operand, the K step
+// in the scalar offset; an offset past the resource's end reads zeros) and run
+// two K steps ahead of the MFMAs (registers hold step k+1 while LDS holds step k).
+// K-major tiles sit in LDS as [row][k] (pitch 72 elements) and are read with
+// ds_read_b128; M/N-major tiles sit as [k][m] (pitch BM+16) and are read with
+// the gfx950 transposing ds_read_b64_tr_b16, so no operand is transposed in
+// memory.  Work is rasterised in groups of 8 row tiles walked column by column,
+// and workgroup ids are remapped so that the consecutive logical tiles of such
+// a group run on one XCD and share its L2.
 #include "device.h"
 #include "kernels.h"
 
 namespace hmm {
 namespace {
 
-constexpr int BM = GEMM_BM;  // 128
-constexpr int BN = 128;
 constexpr int BK = 64;
-constexpr int NTHR = 256;
-constexpr int LDK = BK + 8;      // pitch of a K-major LDS tile (elements)
-constexpr int LDMN = BM + 16;    // pitch of an M/N-major LDS tile (elements)
-constexpr int TILE_ELEMS = 128 * LDK;  // == 64 * LDMN == 9216
-static_assert(TILE_ELEMS == 64 * LDMN, "both LDS tile layouts have the same footprint");
-constexpr int CHUNKS = 4;        // 16-byte chunks per thread per operand tile (128*64*2 B / 16 B / 256)
+constexpr int LDK = BK + 8;   // pitch of a K-major LDS tile (elements)
+constexpr int GROUP_M = 8;    // row tiles per rasterisation group
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int MB = TM / 32, NB = TN / 32;  // 32x32 accumulator blocks per wave
+  static constexpr int CA = BM * BK / 8 / NTHR;     // 16-byte chunks of A per thread per K step
+  static constexpr int CB = BN * BK / 8 / NTHR;
+  static constexpr int LDA_MN = BM + 16, LDB_MN = BN + 16;
+  static constexpr int A_ELEMS = (BM * LDK > BK * LDA_MN) ? BM * LDK : BK * LDA_MN;
+  static constexpr int B_ELEMS = (BN * LDK > BK * LDB_MN) ? BN * LDK : BK * LDB_MN;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static_assert(CA >= 1 && CB >= 1 && MB >= 1 && NB >= 1, "tile too small for the workgroup");
+};
+typedef Cfg<256, 256, 2, 4> Big;
+typedef Cfg<64, 256, 1, 4> Small;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -49,27 +68,46 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid & 7) * (nblocks >> 3) + (bid >> 3);
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x4 zero16() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
+// logical index -> (row tile r, column tile c) of an R x C grid, walking groups
+// of GROUP_M row tiles column by column (a bijection on [0, R*C))
+__device__ __forceinline__ void raster(int idx, int R, int C, int& r, int& c) {
+  const int per_group = GROUP_M * C;
+  const int g = idx / per_group;
+  const int first = g * GROUP_M;
+  const int gsz = min(GROUP_M, R - first);
+  const int w = idx - g * per_group;
+  r = first + w % gsz;
+  c = w / gsz;
+}
 
-// LDS placement of the 16-byte chunk c (0..1023) of a tile
-template <bool KMAJ>
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// buffer resource over [base, base + bytes); bytes < 2^32
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// LDS placement of 16-byte chunk c of a tile with R rows (K-major) or R columns (M/N-major)
+template <bool KMAJ, int R>
 __device__ __forceinline__ int lds_chunk_off(int c) {
-  if constexpr (KMAJ) return (c >> 3) * LDK + (c & 7) * 8;     // [128 rows][64 k]
-  else return (c >> 4) * LDMN + (c & 15) * 8;                  // [64 k][128 cols]
+  if constexpr (KMAJ) return (c >> 3) * LDK + (c & 7) * 8;               // [R rows][64 k]
+  else return (c / (R / 8)) * (R + 16) + (c % (R / 8)) * 8;              // [64 k][R cols]
 }
 
 // MFMA operand fragment (8 bf16 along k) of a 32-row block starting at row0
-template <bool KMAJ>
+template <bool KMAJ, int R>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row0, int kk, int lane) {
   if constexpr (KMAJ) {
     const uint16_t* p = tile + (row0 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5);
     return *reinterpret_cast<const bf16x8*>(p);
   } else {
+    constexpr int LD = R + 16;
     const int k = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int m = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const uint16_t* p0 = tile + k * LDMN + m;
-    const uint16_t* p1 = p0 + 4 * LDMN;
+    const uint16_t* p0 = tile + k * LD + m;
+    const uint16_t* p1 = p0 + 4 * LD;
     bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
     bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
     bf16x8 r;
@@ -79,70 +117,74 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row0, int kk, i
   }
 }
 
-// Row and column (within the 128x128 tile) of accumulator element r of block (mb, nb)
+// Row (within the tile) of accumulator element r of block mb of wave row wm
+template <class C>
 __device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
-  return wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+template <class C, class P>
+__device__ __forceinline__ void store_stage(uint16_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i)
+    *reinterpret_cast<u32x4*>(st + lds_chunk_off<P::A_KMAJ, C::BM>(tid + i * C::NTHR)) = ra[i];
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i)
+    *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
 }
 
 template <class P>
-__global__ void __launch_bounds__(NTHR, 2) gemm_kernel(const typename P::Args args) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE_ELEMS];
+__global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::Args args) {
+  typedef typename P::C C;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
   P pol;
   if (!pol.init(args, xcd_remap(blockIdx.x, gridDim.x))) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int nk = pol.nk;
 
-  f32x16 acc[2][2];
+  f32x16 acc[C::MB][C::NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (nk > 0) {
-    u32x4 ra[CHUNKS], rb[CHUNKS];
+    u32x4 ra[C::CA], rb[C::CB];
     pol.load_a(0, ra);
     pol.load_b(0, rb);
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      *reinterpret_cast<u32x4*>(smem + lds_chunk_off<P::A_KMAJ>(c)) = ra[i];
-      *reinterpret_cast<u32x4*>(smem + TILE_ELEMS + lds_chunk_off<P::B_KMAJ>(c)) = rb[i];
+    store_stage<C, P>(smem, ra, rb);
+    if (nk > 1) {
+      pol.load_a(1, ra);
+      pol.load_b(1, rb);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-      uint16_t* sa = smem + (kt & 1) * 2 * TILE_ELEMS;
-      uint16_t* sb = sa + TILE_ELEMS;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        pol.load_a(kt + 1, ra);
-        pol.load_b(kt + 1, rb);
+      // registers hold step kt+1: park it in the other buffer, then fetch step kt+2
+      if (kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, ra, rb);
+      if (kt + 2 < nk) {
+        pol.load_a(kt + 2, ra);
+        pol.load_b(kt + 2, rb);
       }
+      const uint16_t* sa = smem + (kt & 1) * C::STAGE;
+      const uint16_t* sb = sa + C::A_ELEMS;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 fa[2], fb[2];
+        bf16x8 fa[C::MB], fb[C::NB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) fa[mb] = frag<P::A_KMAJ>(sa, wm * 64 + mb * 32, kk, lane);
+        for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<P::A_KMAJ, C::BM>(sa, wm * C::TM + mb * 32, kk, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) fb[nb] = frag<P::B_KMAJ>(sb, P::ncol0(wn, nb), kk, lane);
+        for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<P::B_KMAJ, C::BN>(sb, P::ncol0(wn, nb), kk, lane);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < C::NB; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
-      }
-      if (more) {
-        uint16_t* na = smem + ((kt + 1) & 1) * 2 * TILE_ELEMS;
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-          const int c = tid + i * NTHR;
-          *reinterpret_cast<u32x4*>(na + lds_chunk_off<P::A_KMAJ>(c)) = ra[i];
-          *reinterpret_cast<u32x4*>(na + TILE_ELEMS + lds_chunk_off<P::B_KMAJ>(c)) = rb[i];
-        }
       }
       __syncthreads();
     }
@@ -150,155 +192,198 @@ __global__ void __launch_bounds__(NTHR, 2) gemm_kernel(const typename P::Args ar
   pol.epilogue(acc, wm, wn, lane, smem);
 }
 
-// Column base of the 32-wide accumulator block nb of wave column wn (plain tiles)
+// Column base (within the tile) of accumulator block nb of wave column wn
+template <class C>
 struct PlainCols {
-  __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * 64 + nb * 32; }
+  __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
 };
 
 // ------------------------------------------------------------- row-grouped base
-// Tile j of the routing's table: expert e, permuted rows [row0, row0 + rows).
+// Tile j of one of the routing's tables: expert e, permuted rows [row0, row0 + rows).
+template <class Cc, bool SMALL>
 struct RowTile {
-  int e, row0, rows, n0, nk;
+  typedef Cc C;
+  int e, row0, rows, n0, nk, nt;
   __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
-    const int j = logical / n_ntiles;
-    const int nt = logical - j * n_ntiles;
-    if (j >= g.tiles[0]) return false;
-    e = g.tiles[2 + 2 * j];
-    row0 = g.tiles[3 + 2 * j];
-    rows = min(BM, g.offsets[e + 1] - row0);
-    n0 = nt * BN;
+    const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+    if (logical >= R * n_ntiles) return false;
+    int j;
+    raster(logical, R, n_ntiles, j, nt);
+    if (j >= g.tiles[SMALL ? 1 : 0]) return false;
+    const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
+    e = tab[2 * j];
+    row0 = tab[2 * j + 1];
+    rows = min(C::BM, g.offsets[e + 1] - row0);
+    n0 = nt * C::BN;
     return true;
+  }
+  // K-major A rows of this tile: byte offset of chunk i (the tile's rows past the
+  // expert's end repeat its last row; their results are not stored)
+  template <bool GATHER>
+  __device__ __forceinline__ void a_rows(const RowGroups& g, int64_t ld, uint32_t (&off)[C::CA]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int p = row0 + min(c >> 3, rows - 1);
+      const int64_t row = GATHER ? (int64_t)g.tok_of_row[p] : (int64_t)p;
+      off[i] = (uint32_t)((row * ld + (c & 7) * 8) * 2);
+    }
+  }
+  // K-major B rows n0 + r (clamped to N - 1), offsets within the expert's slice
+  __device__ __forceinline__ void b_rows(int64_t ld, int64_t N, uint32_t (&off)[C::CB]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int64_t n = min((int64_t)(n0 + (c >> 3)), N - 1);
+      off[i] = (uint32_t)((n * ld + (c & 7) * 8) * 2);
+    }
   }
 };
 
 // ------------------------------------------------------------- gmm1 + SwiGLU
-struct Gmm1 : RowTile {
+template <class Cc, bool SMALL>
+struct Gmm1 : RowTile<Cc, SMALL> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::nt;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
   struct Args {
     RowGroups g;
     const uint16_t* x;
     const uint16_t* w1;
     const float* tw;
-    int64_t H, I;
+    int64_t T, H, I;
     uint16_t *h, *a, *aw;
     int n_ntiles;
   };
   const Args* ar;
-  const uint16_t* arow[CHUNKS];
-  const uint16_t* bbase;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
   int i0;
-  // the B tile holds 64 gate columns then the 64 matching up columns
-  __device__ static __forceinline__ int ncol0(int wn, int nb) { return nb * 64 + wn * 32; }
+  // the B tile holds BN/2 gate columns then the BN/2 matching up columns; each
+  // wave takes TN/2 of each, so one lane holds g and u of the same (row, i)
+  __device__ static __forceinline__ int ncol0(int wn, int nb) {
+    return (nb >= C::NB / 2 ? C::BN / 2 : 0) + wn * (C::TN / 2) + (nb % (C::NB / 2)) * 32;
+  }
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
-    if (!init_rows(A.g, logical, A.n_ntiles)) return false;
-    i0 = n0 / 2;  // 64 gate columns per tile
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    i0 = nt * (C::BN / 2);
+    ra_ = make_rsrc(A.x, A.T * A.H * 2);
+    this->template a_rows<true>(A.g, A.H, aoff);
+    rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
     const int tid = threadIdx.x;
+    constexpr int CPR = C::BN / 8, HALF = C::BN / 16;
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = min(c >> 3, rows - 1);
-      const int tok = A.g.sorted_slot[row0 + r] / A.g.K;
-      arow[i] = A.x + (int64_t)tok * A.H + (c & 7) * 8;
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
+      const int64_t gi = min((int64_t)(i0 + (c8 % HALF) * 8), A.I - 8);   // gate column (clamped)
+      const int64_t col = (c8 < HALF) ? gi : A.I + gi;
+      boff[i] = (uint32_t)((kr * 2 * A.I + col) * 2);
     }
-    bbase = A.w1 + (int64_t)e * A.H * 2 * A.I;
     nk = (int)(A.H / BK);
     return true;
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(arow[i] + kt * BK);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[CHUNKS]) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    const uint32_t so = (uint32_t)(kt * BK * 2 * ar->I * 2);
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int kr = c >> 4, c8 = c & 15;
-      const int64_t col = (c8 < 8) ? (i0 + c8 * 8) : (ar->I + i0 + (c8 - 8) * 8);
-      r[i] = ld16(bbase + (int64_t)(kt * BK + kr) * 2 * ar->I + col);
-    }
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[2][2], int wm, int wn, int lane, uint16_t* smem) {
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
     float* wrow = reinterpret_cast<float*>(smem);
     const int tid = threadIdx.x;
-    if (tid < BM) wrow[tid] = (tid < rows) ? ar->tw[ar->g.sorted_slot[row0 + tid]] : 0.f;
+    for (int t = tid; t < C::BM; t += C::NTHR) wrow[t] = (t < rows) ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
     __syncthreads();
     const int64_t I = ar->I;
-    const int64_t i = i0 + wn * 32 + (lane & 31);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < C::NB / 2; ++nb) {
+      const int64_t i = i0 + wn * (C::TN / 2) + nb * 32 + (lane & 31);
+      if (i >= I) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rt = acc_row(wm, mb, r, lane);
-        if (rt < rows) {
-          const int64_t p = row0 + rt;
-          const float g = round_bf(acc[mb][0][r]);
-          const float u = round_bf(acc[mb][1][r]);
-          const float av = round_bf(g * sigmoidf_(g) * u);
-          const float awv = wrow[rt] * av;
-          ar->h[p * 2 * I + i] = f2bf(g);
-          ar->h[p * 2 * I + I + i] = f2bf(u);
-          ar->a[p * I + i] = f2bf(av);
-          ar->aw[p * I + i] = f2bf(awv);
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rt = acc_row<C>(wm, mb, r, lane);
+          if (rt < rows) {
+            const int64_t p = row0 + rt;
+            const float g = round_bf(acc[mb][nb][r]);
+            const float u = round_bf(acc[mb][nb + C::NB / 2][r]);
+            const float av = round_bf(g * sigmoidf_(g) * u);
+            const float awv = wrow[rt] * av;
+            ar->h[p * 2 * I + i] = f2bf(g);
+            ar->h[p * 2 * I + I + i] = f2bf(u);
+            ar->a[p * I + i] = f2bf(av);
+            ar->aw[p * I + i] = f2bf(awv);
+          }
         }
-      }
+    }
   }
 };
 
 // ------------------------------------------------------------- gmm2
-struct Gmm2 : RowTile, PlainCols {
+template <class Cc, bool SMALL>
+struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
+  using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
   struct Args {
     RowGroups g;
     const uint16_t* a;
     const uint16_t* w2;
-    int64_t H, I;
+    int64_t S, H, I;
     uint16_t* o;
     int n_ntiles;
   };
   const Args* ar;
-  const uint16_t* arow[CHUNKS];
-  const uint16_t* bbase;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
-    if (!init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.a, A.S * A.I * 2);
+    this->template a_rows<false>(A.g, A.I, aoff);
+    rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
     const int tid = threadIdx.x;
+    constexpr int CPR = C::BN / 8;
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = min(c >> 3, rows - 1);
-      arow[i] = A.a + (int64_t)(row0 + r) * A.I + (c & 7) * 8;
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
+      const int64_t col = min((int64_t)(n0 + c8 * 8), A.H - 8);
+      boff[i] = (uint32_t)((kr * A.H + col) * 2);
     }
-    bbase = A.w2 + (int64_t)e * A.I * A.H;
     nk = (int)(A.I / BK);
     return true;
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(arow[i] + kt * BK);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[CHUNKS]) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    const uint32_t so = (uint32_t)(kt * BK * ar->H * 2);
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int kr = c >> 4, c8 = c & 15;
-      const int64_t col = min((int64_t)(n0 + c8 * 8), ar->H - 8);
-      r[i] = ld16(bbase + (int64_t)(kt * BK + kr) * ar->H + col);
-    }
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[2][2], int wm, int wn, int lane, uint16_t*) {
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
     const int64_t H = ar->H;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < C::NB; ++nb) {
       const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
       if (col >= H) continue;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rt = acc_row(wm, mb, r, lane);
+          const int rt = acc_row<C>(wm, mb, r, lane);
           if (rt < rows) ar->o[(int64_t)(row0 + rt) * H + col] = f2bf(acc[mb][nb][r]);
         }
     }
@@ -306,7 +391,12 @@ struct Gmm2 : RowTile, PlainCols {
 };
 
 // ------------------------------------------------------------- act_grad + SwiGLUGrad
-struct ActGrad : RowTile, PlainCols {
+template <class Cc, bool SMALL>
+struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0; using B_::nt;
+  using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   struct Args {
     RowGroups g;
@@ -315,133 +405,133 @@ struct ActGrad : RowTile, PlainCols {
     const float* tw;
     const uint16_t* h;
     const uint16_t* a;
-    int64_t H, I;
+    int64_t T, H, I;
     uint16_t* dh;
     float* dwpart;
     int dw_cols;
     int n_ntiles;
   };
   const Args* ar;
-  const uint16_t* arow[CHUNKS];
-  const uint16_t* brow[CHUNKS];
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
-    if (!init_rows(A.g, logical, A.n_ntiles)) return false;
-    const int tid = threadIdx.x;
-    const uint16_t* w2e = A.w2 + (int64_t)e * A.I * A.H;
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = min(c >> 3, rows - 1);
-      const int tok = A.g.sorted_slot[row0 + r] / A.g.K;
-      arow[i] = A.dy + (int64_t)tok * A.H + (c & 7) * 8;
-      const int64_t n = min((int64_t)(n0 + (c >> 3)), A.I - 1);
-      brow[i] = w2e + n * A.H + (c & 7) * 8;
-    }
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.dy, A.T * A.H * 2);
+    this->template a_rows<true>(A.g, A.H, aoff);
+    rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
+    this->b_rows(A.H, A.I, boff);
     nk = (int)(A.H / BK);
     return true;
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(arow[i] + kt * BK);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(brow[i] + kt * BK);
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[2][2], int wm, int wn, int lane, uint16_t* smem) {
-    float* wrow = reinterpret_cast<float*>(smem);
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    float* wrow = reinterpret_cast<float*>(smem);           // [BM] routing weights
+    float* part = wrow + C::BM;                             // [WN][BM] per-wave partials of sum G*a
     const int tid = threadIdx.x;
-    if (tid < BM) wrow[tid] = (tid < rows) ? ar->tw[ar->g.sorted_slot[row0 + tid]] : 0.f;
+    for (int t = tid; t < C::BM; t += C::NTHR) wrow[t] = (t < rows) ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
     __syncthreads();
     const int64_t I = ar->I;
-    const int nt = n0 / BN;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rt = acc_row(wm, mb, r, lane);
+        const int rt = acc_row<C>(wm, mb, r, lane);
         const bool rv = rt < rows;
         const int64_t p = row0 + (rv ? rt : 0);
         const float wp = wrow[rt];
-        float part = 0.f;
+        float s = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < C::NB; ++nb) {
           const int64_t i = n0 + ncol0(wn, nb) + (lane & 31);
           if (rv && i < I) {
             const float G = acc[mb][nb][r];
             const float g = bf2f(ar->h[p * 2 * I + i]);
             const float u = bf2f(ar->h[p * 2 * I + I + i]);
             const float av = bf2f(ar->a[p * I + i]);
-            part += G * av;
+            s += G * av;
             const float dA = wp * G;
-            const float s = sigmoidf_(g);
-            const float dg = dA * u * s * (1.f + g * (1.f - s));
-            const float du = dA * g * s;
+            const float sg = sigmoidf_(g);
+            const float dg = dA * u * sg * (1.f + g * (1.f - sg));
+            const float du = dA * g * sg;
             ar->dh[p * 2 * I + i] = f2bf(dg);
             ar->dh[p * 2 * I + I + i] = f2bf(du);
           }
         }
         // fixed-order butterfly over the 32 columns held by this half-wave
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 8);
-        part += __shfl_xor(part, 4);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 1);
-        if (rv && (lane & 31) == 0) ar->dwpart[p * ar->dw_cols + nt * 2 + wn] = part;
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 8);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        if ((lane & 31) == 0) part[wn * C::BM + rt] = s;
       }
+    __syncthreads();
+    // one partial per (row, N tile): the WN wave columns summed in order
+    for (int t = tid; t < rows; t += C::NTHR) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < C::WN; ++q) s += part[q * C::BM + t];
+      ar->dwpart[(int64_t)(row0 + t) * ar->dw_cols + nt] = s;
+    }
   }
 };
 
 // ------------------------------------------------------------- input_grad
-struct InputGrad : RowTile, PlainCols {
+template <class Cc, bool SMALL>
+struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
+  using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   struct Args {
     RowGroups g;
     const uint16_t* dh;
     const uint16_t* w1;
-    int64_t H, I;
+    int64_t S, H, I;
     uint16_t* dxp;
     int n_ntiles;
   };
   const Args* ar;
-  const uint16_t* arow[CHUNKS];
-  const uint16_t* brow[CHUNKS];
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
-    if (!init_rows(A.g, logical, A.n_ntiles)) return false;
-    const int tid = threadIdx.x;
-    const uint16_t* w1e = A.w1 + (int64_t)e * A.H * 2 * A.I;
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = min(c >> 3, rows - 1);
-      arow[i] = A.dh + (int64_t)(row0 + r) * 2 * A.I + (c & 7) * 8;
-      const int64_t n = min((int64_t)(n0 + (c >> 3)), A.H - 1);
-      brow[i] = w1e + n * 2 * A.I + (c & 7) * 8;
-    }
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.dh, A.S * 2 * A.I * 2);
+    this->template a_rows<false>(A.g, 2 * A.I, aoff);
+    rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
+    this->b_rows(2 * A.I, A.H, boff);
     nk = (int)(2 * A.I / BK);
     return true;
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(arow[i] + kt * BK);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[CHUNKS]) {
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) r[i] = ld16(brow[i] + kt * BK);
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[2][2], int wm, int wn, int lane, uint16_t*) {
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
     const int64_t H = ar->H;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < C::NB; ++nb) {
       const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
       if (col >= H) continue;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rt = acc_row(wm, mb, r, lane);
+          const int rt = acc_row<C>(wm, mb, r, lane);
           if (rt < rows) ar->dxp[(int64_t)(row0 + rt) * H + col] = f2bf(acc[mb][nb][r]);
         }
     }
@@ -451,74 +541,80 @@ struct InputGrad : RowTile, PlainCols {
 // ------------------------------------------------------------- weight gradients
 // C[e][m][n] = sum over the expert's rows p of A[p][m] * B[p][n]; both operands
 // are read along their row (m or n contiguous) and transposed by the LDS read.
-struct DwBase : PlainCols {
-  static constexpr bool A_KMAJ = false, B_KMAJ = false;
-  int e, m0, n0, nk, p0, p1;
-  __device__ __forceinline__ bool init_dw(const int32_t* offsets, int64_t E, int mt_count, int nt_count,
-                                          int logical) {
-    const int per_e = mt_count * nt_count;
-    e = logical / per_e;
-    if (e >= E) return false;
-    const int rest = logical - e * per_e;
-    m0 = (rest / nt_count) * BM;
-    n0 = (rest % nt_count) * BN;
-    p0 = offsets[e];
-    p1 = offsets[e + 1];
-    nk = (p1 - p0 + BK - 1) / BK;
-    return true;
-  }
-};
-
 template <bool GATHER_A, bool GATHER_B>
-struct Dw : DwBase {
+struct Dw : PlainCols<Big> {
+  typedef Big C;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false;
   struct Args {
     const int32_t* offsets;
-    const int32_t* sorted_slot;
-    int K;
+    const int32_t* tok_of_row;
     int64_t E;
     const uint16_t* A;  // [rows or tokens][M]
     const uint16_t* B;  // [rows or tokens][N]
+    int64_t a_rows, b_rows;  // rows held by A and B
     int64_t M, N;
-    uint16_t* C;        // [E][M][N]
+    uint16_t* Cout;     // [E][M][N]
     int mt, nt;
   };
   const Args* ar;
+  rsrc_t ra_, rb_;
+  int e, m0, n0, nk, p0, p1;
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
-    return init_dw(A.offsets, A.E, A.mt, A.nt, logical);
+    const int per_e = A.mt * A.nt;
+    e = logical / per_e;
+    if (e >= A.E) return false;
+    int r, c;
+    raster(logical - e * per_e, A.mt, A.nt, r, c);
+    m0 = r * C::BM;
+    n0 = c * C::BN;
+    p0 = A.offsets[e];
+    p1 = A.offsets[e + 1];
+    nk = (p1 - p0 + BK - 1) / BK;
+    ra_ = make_rsrc(A.A, A.a_rows * A.M * 2);
+    rb_ = make_rsrc(A.B, A.b_rows * A.N * 2);
+    return true;
   }
-  template <bool GATHER>
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int64_t c0, int kt, u32x4 (&r)[CHUNKS]) {
+  // rows p past the expert's end and columns past the matrix read zeros (offset
+  // at the resource's end)
+  template <bool GATHER, int R, int CN>
+  __device__ __forceinline__ void load(rsrc_t rs, int64_t nrows, int64_t ld, int64_t c0, int kt, u32x4 (&r)[CN]) {
     const int tid = threadIdx.x;
+    constexpr int CPR = R / 8;
+    const uint32_t end = (uint32_t)(nrows * ld * 2);
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTHR;
-      const int kr = c >> 4, c8 = c & 15;
+    for (int i = 0; i < CN; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
       const int p = p0 + kt * BK + kr;
       const int64_t col = c0 + c8 * 8;
+      uint32_t off = end;
       if (p < p1 && col < ld) {
-        const int64_t row = GATHER ? (int64_t)(ar->sorted_slot[p] / ar->K) : (int64_t)p;
-        r[i] = ld16(base + row * ld + col);
-      } else {
-        r[i] = zero16();
+        const int64_t row = GATHER ? (int64_t)ar->tok_of_row[p] : (int64_t)p;
+        off = (uint32_t)((row * ld + col) * 2);
       }
+      r[i] = bload(rs, off, 0);
     }
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[CHUNKS]) { load<GATHER_A>(ar->A, ar->M, m0, kt, r); }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[CHUNKS]) { load<GATHER_B>(ar->B, ar->N, n0, kt, r); }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[2][2], int wm, int wn, int lane, uint16_t*) {
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+    load<GATHER_A, C::BM, C::CA>(ra_, ar->a_rows, ar->M, m0, kt, r);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    load<GATHER_B, C::BN, C::CB>(rb_, ar->b_rows, ar->N, n0, kt, r);
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
     const int64_t M = ar->M, N = ar->N;
-    uint16_t* C = ar->C + (int64_t)e * M * N;
+    uint16_t* Co = ar->Cout + (int64_t)e * M * N;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < C::NB; ++nb) {
       const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + acc_row(wm, mb, r, lane);
-          if (m < M) C[m * N + col] = f2bf(acc[mb][nb][r]);
+          const int64_t m = m0 + acc_row<C>(wm, mb, r, lane);
+          if (m < M) Co[m * N + col] = f2bf(acc[mb][nb][r]);
         }
     }
   }
@@ -531,50 +627,74 @@ hipError_t launch(const typename P::Args& args, int64_t logical_blocks, hipStrea
   if (logical_blocks <= 0) return hipSuccess;
   const int64_t g = round8(logical_blocks);
   if (g > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_kernel<P>, dim3((unsigned)g), dim3(NTHR), 0, stream, args);
+  hipLaunchKernelGGL(gemm_kernel<P>, dim3((unsigned)g), dim3(P::C::NTHR), 0, stream, args);
   return hipGetLastError();
+}
+
+// big-tile launch, then small-tile launch, of a row-grouped product
+template <template <class, bool> class P, class ArgsFill>
+hipError_t launch_rows(const RowGroups& g, int64_t n_ntiles, ArgsFill fill, hipStream_t stream) {
+  typedef P<Big, false> PB;
+  typedef P<Small, true> PS;
+  typename PB::Args ab;
+  fill(ab);
+  hipError_t e = launch<PB>(ab, g.max_big * n_ntiles, stream);
+  if (e != hipSuccess) return e;
+  typename PS::Args as;
+  fill(as);
+  return launch<PS>(as, g.max_small * n_ntiles, stream);
 }
 
 }  // namespace
 
-int act_grad_dw_cols(int64_t I) { return (int)(2 * ((I + BN - 1) / BN)); }
+int act_grad_dw_cols(int64_t I) { return (int)((I + 255) / 256); }
 
 hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
                               int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  Gmm1::Args A{g, x, w1, topk_w, H, I, h, a, aw, (int)(I / 64)};
-  return launch<Gmm1>(A, g.max_tiles * A.n_ntiles, stream);
+  const int nnt = (int)((I + 127) / 128);  // 128 gate columns (and their up columns) per N tile
+  return launch_rows<Gmm1>(g, nnt, [&](auto& A) {
+    A.g = g; A.x = x; A.w1 = w1; A.tw = topk_w; A.T = g.T; A.H = H; A.I = I; A.h = h; A.a = a; A.aw = aw;
+    A.n_ntiles = nnt;
+  }, stream);
 }
 
 hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
                        uint16_t* o, hipStream_t stream) {
-  Gmm2::Args A{g, a, w2, H, I, o, (int)((H + BN - 1) / BN)};
-  return launch<Gmm2>(A, g.max_tiles * A.n_ntiles, stream);
+  const int nnt = (int)((H + 255) / 256);
+  return launch_rows<Gmm2>(g, nnt, [&](auto& A) {
+    A.g = g; A.a = a; A.w2 = w2; A.S = g.S; A.H = H; A.I = I; A.o = o; A.n_ntiles = nnt;
+  }, stream);
 }
 
 hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
                            const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
                            float* dwpart, int dw_cols, hipStream_t stream) {
-  ActGrad::Args A{g, dy, w2, topk_w, h, a, H, I, dh, dwpart, dw_cols, (int)((I + BN - 1) / BN)};
-  return launch<ActGrad>(A, g.max_tiles * A.n_ntiles, stream);
+  const int nnt = (int)((I + 255) / 256);
+  return launch_rows<ActGrad>(g, nnt, [&](auto& A) {
+    A.g = g; A.dy = dy; A.w2 = w2; A.tw = topk_w; A.h = h; A.a = a; A.T = g.T; A.H = H; A.I = I; A.dh = dh;
+    A.dwpart = dwpart; A.dw_cols = dw_cols; A.n_ntiles = nnt;
+  }, stream);
 }
 
 hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
                              uint16_t* dxp, hipStream_t stream) {
-  InputGrad::Args A{g, dh, w1, H, I, dxp, (int)((H + BN - 1) / BN)};
-  return launch<InputGrad>(A, g.max_tiles * A.n_ntiles, stream);
+  const int nnt = (int)((H + 255) / 256);
+  return launch_rows<InputGrad>(g, nnt, [&](auto& A) {
+    A.g = g; A.dh = dh; A.w1 = w1; A.S = g.S; A.H = H; A.I = I; A.dxp = dxp; A.n_ntiles = nnt;
+  }, stream);
 }
 
-hipError_t launch_dw1(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* x,
-                      const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream) {
+hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream) {
   typedef Dw<true, false> P;
-  P::Args A{offsets, sorted_slot, K, E, x, dh, H, 2 * I, dw1, (int)((H + BM - 1) / BM), (int)((2 * I + BN - 1) / BN)};
+  P::Args A{offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, (int)((H + 255) / 256), (int)((2 * I + 255) / 256)};
   return launch<P>(A, E * A.mt * A.nt, stream);
 }
 
-hipError_t launch_dw2(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* aw,
-                      const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream) {
+hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream) {
   typedef Dw<false, true> P;
-  P::Args A{offsets, sorted_slot, K, E, aw, dy, I, H, dw2, (int)((I + BM - 1) / BM), (int)((H + BN - 1) / BN)};
+  P::Args A{offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, (int)((I + 255) / 256), (int)((H + 255) / 256)};
   return launch<P>(A, E * A.mt * A.nt, stream);
 }
 

@@ -12,24 +12,36 @@ constexpr int RT_THREADS = 256;       // routing block size
 constexpr int RT_SLOTS = 1024;        // slots per routing block
 constexpr int RT_SCAN_THREADS = 1024; // the single scan block (>= MAX_EXPERTS)
 
-constexpr int GEMM_BM = 128;          // rows of a grouped-product tile (tile table granularity)
+constexpr int TILE_BIG = 256;         // rows of a big row-grouped product tile
+constexpr int TILE_SMALL = 64;        // rows of a small tile (expert remainders, small experts)
 
-// Upper bound of the tile-table length for S routed rows over E experts with
-// BM-row tiles: sum_e ceil(c_e / BM) <= (S + E * (BM - 1)) / BM.
-inline int64_t max_row_tiles(int64_t S, int64_t E, int BM) { return (S + E * (BM - 1)) / BM; }
+// Upper bounds of the tile-table lengths for S routed rows over E experts.
+// An expert with c rows gets floor(c/256) big tiles, one more if the remainder
+// r = c mod 256 exceeds 128 rows, else ceil(r/64) <= 2 small tiles.  So
+// #big <= sum_e (c_e + 127) / 256 <= (S + 127 E) / 256, and, since ceil(r/64)
+// <= 1 + (r - 1)/64 for r > 0 and at most min(E, S) experts have rows,
+// #small <= min(2 E, min(E, S) + S / 64).
+inline int64_t max_big_tiles(int64_t S, int64_t E) { return (S + (TILE_BIG / 2 - 1) * E) / TILE_BIG; }
+inline int64_t max_small_tiles(int64_t S, int64_t E) {
+  const int64_t a = 2 * E, b = (E < S ? E : S) + S / TILE_SMALL;
+  return a < b ? a : b;
+}
+inline int64_t tile_table_ints(int64_t S, int64_t E) { return 4 + 2 * (max_big_tiles(S, E) + max_small_tiles(S, E)); }
 
 // routing (route.hip)
-hipError_t launch_route(const int32_t* ids, int64_t S, int E, int BM, int32_t* counts, int32_t* offsets,
-                        int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tiles, int32_t* err,
-                        int32_t* blockhist, int32_t* blockbase, int32_t* blockerr, hipStream_t stream);
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
+                        int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
+                        hipStream_t stream);
 
 // grouped products (gemm.hip).  All matrices bf16 (uint16_t storage).
 struct RowGroups {
-  const int32_t* tiles;        // [2 + 2*max_tiles]: count, BM, then (expert, first row) pairs
+  const int32_t* tiles;        // tile table written by route_scan (layout in route.hip)
   const int32_t* offsets;      // [E+1]
-  const int32_t* sorted_slot;  // [S]
-  int64_t max_tiles;
-  int K;                       // top-k (token of permuted row p = sorted_slot[p] / K)
+  const int32_t* sorted_slot;  // [S] slot of permuted row p
+  const int32_t* tok_of_row;   // [S] token of permuted row p (= sorted_slot[p] / K)
+  int64_t max_big, max_small;  // table capacities
+  int64_t T, S;                // tokens, routed rows (extents of the buffer resources)
 };
 
 // h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
@@ -46,10 +58,10 @@ hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_
 hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
                              uint16_t* dxp, hipStream_t stream);
 // dW1[e] = sum_p x[tok(p)]^T dH[p];  dW2[e] = sum_p aw[p]^T dY[tok(p)]
-hipError_t launch_dw1(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* x,
-                      const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream);
-hipError_t launch_dw2(const int32_t* offsets, const int32_t* sorted_slot, int K, int64_t E, const uint16_t* aw,
-                      const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream);
+hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream);
+hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream);
 // number of d_topk_weights partial columns written by launch_act_grad for a given I
 int act_grad_dw_cols(int64_t I);
 

@@ -6,10 +6,11 @@
 //
 // Slot s = t*K + k.  Three kernels, all integer and deterministic:
 //   route_hist     one block per RT_SLOTS slots: LDS histogram -> blockhist[b][e]
-//   route_scan     one block: counts, per-block bases, offsets, tile table
+//   route_scan     one block: counts, per-block bases, offsets, tile tables
 //   route_scatter  one block per RT_SLOTS slots: stable rank inside the block
 //                  (wave multisplit over the id bits with ballots, then a
-//                  fixed-order sum over the waves) -> sorted_slot, row_of_slot
+//                  fixed-order sum over the waves) -> sorted_slot, row_of_slot,
+//                  and the token of every permuted row (tok_of_row)
 #include "device.h"
 #include "kernels.h"
 
@@ -40,16 +41,22 @@ __global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restri
   if (tid == 0) blockerr[blockIdx.x] = bad;
 }
 
-// One block of RT_SCAN_THREADS threads (>= E).
+// One block of RT_SCAN_THREADS threads (>= E).  Besides counts and offsets it
+// builds the tile table of the row-grouped products: each expert's rows are
+// covered by TILE_BIG-row tiles, and a remainder of at most TILE_BIG/2 rows by
+// TILE_SMALL-row tiles (a larger remainder gets one more, partly filled, big
+// tile).  Layout: tiles[0] = #big, tiles[1] = #small, then max_big (expert,
+// first row) pairs from tiles[4], then the small pairs from tiles[4 + 2*max_big].
 __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __restrict__ blockhist,
                                                               const int32_t* __restrict__ blockerr, int nblk,
-                                                              int E, int BM, int32_t* __restrict__ counts,
+                                                              int E, int max_big, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ blockbase,
                                                               int32_t* __restrict__ tiles,
                                                               int32_t* __restrict__ err) {
   __shared__ int32_t scan_c[RT_SCAN_THREADS];
-  __shared__ int32_t scan_t[RT_SCAN_THREADS];
+  __shared__ int32_t scan_b[RT_SCAN_THREADS];
+  __shared__ int32_t scan_s[RT_SCAN_THREADS];
   const int e = threadIdx.x;
   int c = 0;
   if (e < E) {
@@ -59,33 +66,47 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
       c += v;
     }
   }
-  const int nt = (c + BM - 1) / BM;
+  const int rem = c % TILE_BIG;
+  const int nbig = c / TILE_BIG + (rem > TILE_BIG / 2 ? 1 : 0);
+  const int nsmall = (rem > TILE_BIG / 2) ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
   scan_c[e] = (e < E) ? c : 0;
-  scan_t[e] = (e < E) ? nt : 0;
+  scan_b[e] = (e < E) ? nbig : 0;
+  scan_s[e] = (e < E) ? nsmall : 0;
   __syncthreads();
   // inclusive Hillis-Steele scans over the experts (integers: order-free)
   for (int d = 1; d < RT_SCAN_THREADS; d <<= 1) {
     const int vc = (e >= d) ? scan_c[e - d] : 0;
-    const int vt = (e >= d) ? scan_t[e - d] : 0;
+    const int vb = (e >= d) ? scan_b[e - d] : 0;
+    const int vs = (e >= d) ? scan_s[e - d] : 0;
     __syncthreads();
     scan_c[e] += vc;
-    scan_t[e] += vt;
+    scan_b[e] += vb;
+    scan_s[e] += vs;
     __syncthreads();
   }
-  const int off = scan_c[e] - ((e < E) ? c : 0);
-  const int tstart = scan_t[e] - ((e < E) ? nt : 0);
   if (e < E) {
+    const int off = scan_c[e] - c;
+    const int b0 = scan_b[e] - nbig;
+    const int s0 = scan_s[e] - nsmall;
     counts[e] = c;
     offsets[e] = off;
-    for (int i = 0; i < nt; ++i) {
-      tiles[2 + 2 * (tstart + i)] = e;
-      tiles[2 + 2 * (tstart + i) + 1] = off + i * BM;
+    for (int i = 0; i < nbig; ++i) {
+      tiles[4 + 2 * (b0 + i)] = e;
+      tiles[4 + 2 * (b0 + i) + 1] = off + i * TILE_BIG;
+    }
+    int32_t* small = tiles + 4 + 2 * max_big;
+    const int srow = off + nbig * TILE_BIG;
+    for (int i = 0; i < nsmall; ++i) {
+      small[2 * (s0 + i)] = e;
+      small[2 * (s0 + i) + 1] = srow + i * TILE_SMALL;
     }
   }
   if (e == RT_SCAN_THREADS - 1) {
     offsets[E] = scan_c[e];
-    tiles[0] = scan_t[e];  // number of tiles
-    tiles[1] = BM;
+    tiles[0] = scan_b[e];
+    tiles[1] = scan_s[e];
+    tiles[2] = TILE_BIG;
+    tiles[3] = TILE_SMALL;
   }
   int bad = 0;
   for (int b = e; b < nblk; b += RT_SCAN_THREADS) bad |= blockerr[b];
@@ -96,8 +117,9 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
 __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __restrict__ ids, int64_t S, int E,
                                                             int nbits, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ blockbase,
-                                                            int32_t* __restrict__ sorted_slot,
-                                                            int32_t* __restrict__ row_of_slot) {
+                                                            int K, int32_t* __restrict__ sorted_slot,
+                                                            int32_t* __restrict__ row_of_slot,
+                                                            int32_t* __restrict__ tok_of_row) {
   __shared__ int32_t running[MAX_EXPERTS];
   __shared__ int32_t wcnt[RT_THREADS / 64][MAX_EXPERTS];
   const int tid = threadIdx.x;
@@ -140,6 +162,7 @@ __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __res
         if ((v >> 16) == r + 1) row += v & 0xffff;
       }
       sorted_slot[row] = (int32_t)s;
+      tok_of_row[row] = (int32_t)(s / K);
       row_of_slot[s] = row;
     }
     __syncthreads();
@@ -150,20 +173,21 @@ __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __res
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_route(const int32_t* ids, int64_t S, int E, int BM, int32_t* counts, int32_t* offsets,
-                        int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tiles, int32_t* err,
-                        int32_t* blockhist, int32_t* blockbase, int32_t* blockerr, hipStream_t stream) {
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
+                        int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
+                        hipStream_t stream) {
   const int nblk = (int)((S + RT_SLOTS - 1) / RT_SLOTS);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   if (nblk > 0) {
     hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr);
   }
-  hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, BM,
+  hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, max_big,
                      counts, offsets, blockbase, tiles, err);
   if (nblk > 0) {
     hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, nbits, offsets,
-                       blockbase, sorted_slot, row_of_slot);
+                       blockbase, K, sorted_slot, row_of_slot, tok_of_row);
   }
   return hipGetLastError();
 }

@@ -180,6 +180,7 @@ def saved_views(saved, T, H, I, E, K):
         "offsets": view(L.offsets, E + 1, torch.int32, (E + 1,)),
         "sorted_slot": view(L.sorted_slot, S, torch.int32, (S,)),
         "row_of_slot": view(L.row_of_slot, S, torch.int32, (S,)),
+        "tok_of_row": view(L.tok_of_row, S, torch.int32, (S,)),
         "h": view(L.h, S * 2 * I, torch.bfloat16, (S, 2 * I)),
         "a": view(L.a, S * I, torch.bfloat16, (S, I)),
         "aw": view(L.aw, S * I, torch.bfloat16, (S, I)),

@@ -72,7 +72,7 @@ def test_sizes_and_layout(lib):
     assert lib.hmm_saved_layout_of(ctypes.byref(p), ctypes.byref(L)) == 0
     S, I = 1024 * 2, 128
     assert L.total == sv.value
-    offs = [L.counts, L.offsets, L.sorted_slot, L.row_of_slot, L.tiles, L.h, L.a, L.aw, L.id_error]
+    offs = [L.counts, L.offsets, L.sorted_slot, L.row_of_slot, L.tok_of_row, L.tiles, L.h, L.a, L.aw, L.id_error]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L.a - L.h >= S * 2 * I * 2 and L.aw - L.a >= S * I * 2
     assert ws.value >= S * 512 * 2          # o [S, H] bf16
