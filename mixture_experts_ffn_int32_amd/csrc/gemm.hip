@@ -27,11 +27,15 @@
 // Both operand tiles go through LDS, double buffered.  Global loads are buffer
 // loads (32-bit per-thread offsets against a resource of the operand, the K step
 // in the scalar offset; an offset past the resource's end reads zeros) and run
-// two K steps ahead of the MFMAs (registers hold step k+1 while LDS holds step k).
+// three K steps ahead of the MFMAs: while LDS holds step k, two register sets
+// hold steps k+1 and k+2.  Row indices of gathered reduction operands are
+// fetched one step before their data.
 // K-major tiles sit in LDS as [row][k] (pitch 72 elements) and are read with
-// ds_read_b128; M/N-major tiles sit as [k][m] (pitch BM+16) and are read with
-// the gfx950 transposing ds_read_b64_tr_b16, so no operand is transposed in
-// memory.  Work is rasterised in groups of 8 row tiles walked column by column,
+// ds_read_b128; M/N-major tiles sit as [k][m] and are read with the gfx950
+// transposing ds_read_b64_tr_b16, so no operand is transposed in memory.  LDS
+// has 64 banks of 4 bytes and serves 32 lanes of a 64-bit read per pass: the
+// four k rows such a pass touches (64 bytes each) fall in distinct banks when
+// the row pitch is 64 bytes past a multiple of 256, hence pitch BM+32.  Work is rasterised in groups of 8 row tiles walked column by column,
 // and workgroup ids are remapped so that the consecutive logical tiles of such
 // a group run on one XCD and share its L2.
 #include "device.h"
@@ -52,7 +56,7 @@ struct Cfg {
   static constexpr int MB = TM / 32, NB = TN / 32;  // 32x32 accumulator blocks per wave
   static constexpr int CA = BM * BK / 8 / NTHR;     // 16-byte chunks of A per thread per K step
   static constexpr int CB = BN * BK / 8 / NTHR;
-  static constexpr int LDA_MN = BM + 16, LDB_MN = BN + 16;
+  static constexpr int LDA_MN = BM + 32, LDB_MN = BN + 32;
   static constexpr int A_ELEMS = (BM * LDK > BK * LDA_MN) ? BM * LDK : BK * LDA_MN;
   static constexpr int B_ELEMS = (BN * LDK > BK * LDB_MN) ? BN * LDK : BK * LDB_MN;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
@@ -93,7 +97,7 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
 template <bool KMAJ, int R>
 __device__ __forceinline__ int lds_chunk_off(int c) {
   if constexpr (KMAJ) return (c >> 3) * LDK + (c & 7) * 8;               // [R rows][64 k]
-  else return (c / (R / 8)) * (R + 16) + (c % (R / 8)) * 8;              // [64 k][R cols]
+  else return (c / (R / 8)) * (R + 32) + (c % (R / 8)) * 8;              // [64 k][R cols]
 }
 
 // MFMA operand fragment (8 bf16 along k) of a 32-row block starting at row0
@@ -103,7 +107,7 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row0, int kk, i
     const uint16_t* p = tile + (row0 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5);
     return *reinterpret_cast<const bf16x8*>(p);
   } else {
-    constexpr int LD = R + 16;
+    constexpr int LD = R + 32;
     const int k = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int m = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const uint16_t* p0 = tile + k * LD + m;
@@ -155,22 +159,32 @@ __global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::A
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (nk > 0) {
-    u32x4 ra[C::CA], rb[C::CB];
-    pol.load_a(0, ra);
-    pol.load_b(0, rb);
-    store_stage<C, P>(smem, ra, rb);
+    u32x4 ra0[C::CA], rb0[C::CB], ra1[C::CA], rb1[C::CB];
+    pol.index(0);
+    pol.load_a(0, ra0);
+    pol.load_b(0, rb0);
     if (nk > 1) {
-      pol.load_a(1, ra);
-      pol.load_b(1, rb);
+      pol.index(1);
+      pol.load_a(1, ra1);
+      pol.load_b(1, rb1);
     }
+    store_stage<C, P>(smem, ra0, rb0);
+    if (nk > 2) {
+      pol.index(2);
+      pol.load_a(2, ra0);
+      pol.load_b(2, rb0);
+    }
+    if (nk > 3) pol.index(3);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      // registers hold step kt+1: park it in the other buffer, then fetch step kt+2
-      if (kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, ra, rb);
-      if (kt + 2 < nk) {
-        pol.load_a(kt + 2, ra);
-        pol.load_b(kt + 2, rb);
+    // one K step: park step kt+1 (in set `nx`) in the other LDS buffer, refill
+    // that set with step kt+3, fetch the indices of step kt+4, then multiply step kt
+    auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB]) {
+      if (kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
+      if (kt + 3 < nk) {
+        pol.load_a(kt + 3, nxa);
+        pol.load_b(kt + 3, nxb);
       }
+      if (kt + 4 < nk) pol.index(kt + 4);
       const uint16_t* sa = smem + (kt & 1) * C::STAGE;
       const uint16_t* sb = sa + C::A_ELEMS;
 #pragma unroll
@@ -187,9 +201,43 @@ __global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::A
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
       }
       __syncthreads();
+    };
+    // register set 1 holds odd steps, set 0 even steps
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, ra1, rb1);
+      step(kt + 1, ra0, rb0);
     }
+    if (kt < nk) step(kt, ra1, rb1);
   }
   pol.epilogue(acc, wm, wn, lane, smem);
+}
+
+// Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
+// [BM][BN] tile and written out as 16-byte row chunks (rows < valid_rows,
+// columns < ncols), so every global store is a full, coalesced vector.
+template <class C, class P>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem,
+                                           uint16_t* out, int64_t ld, int64_t row_base, int valid_rows,
+                                           int64_t col_base, int64_t ncols) {
+  constexpr int LD = C::BN + 8;
+  static_assert(C::BM * LD <= 2 * C::STAGE, "staging tile must fit in the LDS buffers");
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        smem[acc_row<C>(wm, mb, r, lane) * LD + P::ncol0(wn, nb) + (lane & 31)] = f2bf(acc[mb][nb][r]);
+  __syncthreads();
+  constexpr int CPR = C::BN / 8;
+  for (int c = threadIdx.x; c < C::BM * CPR; c += C::NTHR) {
+    const int row = c / CPR, c8 = c % CPR;
+    const int64_t col = col_base + c8 * 8;
+    if (row < valid_rows && col < ncols)
+      *reinterpret_cast<u32x4*>(out + (row_base + row) * ld + col) =
+          *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+  }
 }
 
 // Column base (within the tile) of accumulator block nb of wave column wn
@@ -204,6 +252,7 @@ template <class Cc, bool SMALL>
 struct RowTile {
   typedef Cc C;
   int e, row0, rows, n0, nk, nt;
+  __device__ __forceinline__ void index(int) {}  // K-major rows are fixed for the whole tile
   __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
     const int R = SMALL ? (int)g.max_small : (int)g.max_big;
     if (logical >= R * n_ntiles) return false;
@@ -373,20 +422,8 @@ struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
-    const int64_t H = ar->H;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
-      if (col >= H) continue;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rt = acc_row<C>(wm, mb, r, lane);
-          if (rt < rows) ar->o[(int64_t)(row0 + rt) * H + col] = f2bf(acc[mb][nb][r]);
-        }
-    }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, Gmm2>(acc, wm, wn, lane, smem, ar->o, ar->H, row0, rows, n0, ar->H);
   }
 };
 
@@ -521,20 +558,8 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
-    const int64_t H = ar->H;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
-      if (col >= H) continue;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rt = acc_row<C>(wm, mb, r, lane);
-          if (rt < rows) ar->dxp[(int64_t)(row0 + rt) * H + col] = f2bf(acc[mb][nb][r]);
-        }
-    }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, InputGrad>(acc, wm, wn, lane, smem, ar->dxp, ar->H, row0, rows, n0, ar->H);
   }
 };
 
@@ -559,13 +584,25 @@ struct Dw : PlainCols<Big> {
   const Args* ar;
   rsrc_t ra_, rb_;
   int e, m0, n0, nk, p0, p1;
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  // byte offsets of the rows of the next step to be loaded (computed by index())
+  uint32_t rowoff_a[C::CA], rowoff_b[C::CB];
+  // The cost of a tile grows with its expert's row count, so every XCD gets an
+  // equal slice of every expert's tiles (not a contiguous run of experts): XCD x
+  // (workgroups b with b % 8 == x) walks the experts in order and takes tiles
+  // [x * per, (x + 1) * per) of each, per = ceil(mt * nt / 8); inside a slice the
+  // tiles are rasterised in groups of GROUP_M row tiles.
+  __device__ __forceinline__ bool init(const Args& A, int) {
     ar = &A;
     const int per_e = A.mt * A.nt;
-    e = logical / per_e;
+    const int per = (per_e + 7) / 8;
+    const int b = blockIdx.x;
+    const int j = b >> 3;
+    e = j / per;
     if (e >= A.E) return false;
+    const int t = (b & 7) * per + (j - e * per);
+    if (t >= per_e) return false;
     int r, c;
-    raster(logical - e * per_e, A.mt, A.nt, r, c);
+    raster(t, A.mt, A.nt, r, c);
     m0 = r * C::BM;
     n0 = c * C::BN;
     p0 = A.offsets[e];
@@ -575,10 +612,10 @@ struct Dw : PlainCols<Big> {
     rb_ = make_rsrc(A.B, A.b_rows * A.N * 2);
     return true;
   }
-  // rows p past the expert's end and columns past the matrix read zeros (offset
-  // at the resource's end)
+  // row part of the offsets of step kt: rows p past the expert's end and columns
+  // past the matrix get the resource's end (reads zeros)
   template <bool GATHER, int R, int CN>
-  __device__ __forceinline__ void load(rsrc_t rs, int64_t nrows, int64_t ld, int64_t c0, int kt, u32x4 (&r)[CN]) {
+  __device__ __forceinline__ void rows_of(int64_t nrows, int64_t ld, int64_t c0, int kt, uint32_t (&ro)[CN]) {
     const int tid = threadIdx.x;
     constexpr int CPR = R / 8;
     const uint32_t end = (uint32_t)(nrows * ld * 2);
@@ -593,30 +630,24 @@ struct Dw : PlainCols<Big> {
         const int64_t row = GATHER ? (int64_t)ar->tok_of_row[p] : (int64_t)p;
         off = (uint32_t)((row * ld + col) * 2);
       }
-      r[i] = bload(rs, off, 0);
+      ro[i] = off;
     }
   }
-  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
-    load<GATHER_A, C::BM, C::CA>(ra_, ar->a_rows, ar->M, m0, kt, r);
+  __device__ __forceinline__ void index(int kt) {
+    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->M, m0, kt, rowoff_a);
+    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->N, n0, kt, rowoff_b);
   }
-  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    load<GATHER_B, C::BN, C::CB>(rb_, ar->b_rows, ar->N, n0, kt, r);
+  __device__ __forceinline__ void load_a(int, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, rowoff_a[i], 0);
   }
-  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t*) {
-    const int64_t M = ar->M, N = ar->N;
-    uint16_t* Co = ar->Cout + (int64_t)e * M * N;
+  __device__ __forceinline__ void load_b(int, u32x4 (&r)[C::CB]) {
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const int64_t col = n0 + ncol0(wn, nb) + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + acc_row<C>(wm, mb, r, lane);
-          if (m < M) Co[m * N + col] = f2bf(acc[mb][nb][r]);
-        }
-    }
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, rowoff_b[i], 0);
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, Dw>(acc, wm, wn, lane, smem, ar->Cout + (int64_t)e * ar->M * ar->N, ar->N, m0,
+                      (int)min((int64_t)C::BM, ar->M - m0), n0, ar->N);
   }
 };
 
@@ -688,14 +719,14 @@ hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t
                       const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream) {
   typedef Dw<true, false> P;
   P::Args A{offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, (int)((H + 255) / 256), (int)((2 * I + 255) / 256)};
-  return launch<P>(A, E * A.mt * A.nt, stream);
+  return launch<P>(A, E * 8 * ((A.mt * A.nt + 7) / 8), stream);
 }
 
 hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
                       const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream) {
   typedef Dw<false, true> P;
   P::Args A{offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, (int)((I + 255) / 256), (int)((H + 255) / 256)};
-  return launch<P>(A, E * A.mt * A.nt, stream);
+  return launch<P>(A, E * 8 * ((A.mt * A.nt + 7) / 8), stream);
 }
 
 }  // namespace hmm
