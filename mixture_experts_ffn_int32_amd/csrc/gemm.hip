@@ -345,33 +345,45 @@ struct Gmm1 : RowTile<Cc, SMALL> {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
+  // g and u (rounded to bf16) are staged in LDS as the [BM][BN] tile (gate
+  // columns first); then each thread takes 8 consecutive columns of one row and
+  // writes h (both halves), a = bf16(silu(g) u) and aw = bf16(w a) as 16-byte chunks.
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
-    float* wrow = reinterpret_cast<float*>(smem);
+    constexpr int LD = C::BN + 8;
+    static_assert(C::BM * LD * 2 + C::BM * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    float* wrow = reinterpret_cast<float*>(smem + C::BM * LD);
     const int tid = threadIdx.x;
     for (int t = tid; t < C::BM; t += C::NTHR) wrow[t] = (t < rows) ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          smem[acc_row<C>(wm, mb, r, lane) * LD + ncol0(wn, nb) + (lane & 31)] = f2bf(acc[mb][nb][r]);
     __syncthreads();
     const int64_t I = ar->I;
+    constexpr int CPR = C::BN / 16;  // 8-column chunks of the gate half
+    for (int c = tid; c < C::BM * CPR; c += C::NTHR) {
+      const int row = c / CPR, c8 = c % CPR;
+      const int64_t i = i0 + c8 * 8;
+      if (row >= rows || i >= I) continue;
+      const int64_t p = row0 + row;
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(smem + row * LD + C::BN / 2 + c8 * 8);
+      float g[8], u[8], av[8], aw[8];
+      unpack8(gv, g);
+      unpack8(uv, u);
+      const float w = wrow[row];
 #pragma unroll
-    for (int nb = 0; nb < C::NB / 2; ++nb) {
-      const int64_t i = i0 + wn * (C::TN / 2) + nb * 32 + (lane & 31);
-      if (i >= I) continue;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rt = acc_row<C>(wm, mb, r, lane);
-          if (rt < rows) {
-            const int64_t p = row0 + rt;
-            const float g = round_bf(acc[mb][nb][r]);
-            const float u = round_bf(acc[mb][nb + C::NB / 2][r]);
-            const float av = round_bf(g * sigmoidf_(g) * u);
-            const float awv = wrow[rt] * av;
-            ar->h[p * 2 * I + i] = f2bf(g);
-            ar->h[p * 2 * I + I + i] = f2bf(u);
-            ar->a[p * I + i] = f2bf(av);
-            ar->aw[p * I + i] = f2bf(awv);
-          }
-        }
+      for (int j = 0; j < 8; ++j) {
+        av[j] = round_bf(g[j] * sigmoidf_(g[j]) * u[j]);
+        aw[j] = w * av[j];
+      }
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
+      *reinterpret_cast<u32x4*>(ar->a + p * I + i) = pack8(av);
+      *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
     }
   }
 };
@@ -469,54 +481,73 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
   }
+  // G stays in float32: one wave column (TN columns) at a time it is staged in
+  // LDS, then each thread takes 8 consecutive columns of one row, reads g, u and
+  // a as 16-byte chunks, writes dH = [dg | du] as 16-byte chunks and adds its
+  // share of sum_i G a.  The row sums are reduced in a fixed order (8-lane
+  // butterfly, then wave columns in order): one partial per (row, N tile).
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
-    float* wrow = reinterpret_cast<float*>(smem);           // [BM] routing weights
-    float* part = wrow + C::BM;                             // [WN][BM] per-wave partials of sum G*a
+    constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
+    constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
+    constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
+    static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
+    static_assert((C::BM * LDF + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    float* gst = reinterpret_cast<float*>(smem);
+    float* wrow = gst + C::BM * LDF;
     const int tid = threadIdx.x;
     for (int t = tid; t < C::BM; t += C::NTHR) wrow[t] = (t < rows) ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
-    __syncthreads();
     const int64_t I = ar->I;
+    float part[PER];
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int k = 0; k < PER; ++k) part[k] = 0.f;
+    for (int q = 0; q < C::WN; ++q) {
+      if (wn == q) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rt = acc_row<C>(wm, mb, r, lane);
-        const bool rv = rt < rows;
-        const int64_t p = row0 + (rv ? rt : 0);
-        const float wp = wrow[rt];
-        float s = 0.f;
+        for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const int64_t i = n0 + ncol0(wn, nb) + (lane & 31);
-          if (rv && i < I) {
-            const float G = acc[mb][nb][r];
-            const float g = bf2f(ar->h[p * 2 * I + i]);
-            const float u = bf2f(ar->h[p * 2 * I + I + i]);
-            const float av = bf2f(ar->a[p * I + i]);
-            s += G * av;
-            const float dA = wp * G;
-            const float sg = sigmoidf_(g);
-            const float dg = dA * u * sg * (1.f + g * (1.f - sg));
-            const float du = dA * g * sg;
-            ar->dh[p * 2 * I + i] = f2bf(dg);
-            ar->dh[p * 2 * I + I + i] = f2bf(du);
-          }
-        }
-        // fixed-order butterfly over the 32 columns held by this half-wave
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        if ((lane & 31) == 0) part[wn * C::BM + rt] = s;
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              gst[acc_row<C>(wm, mb, r, lane) * LDF + nb * 32 + (lane & 31)] = acc[mb][nb][r];
       }
-    __syncthreads();
-    // one partial per (row, N tile): the WN wave columns summed in order
-    for (int t = tid; t < rows; t += C::NTHR) {
-      float s = 0.f;
+      __syncthreads();
 #pragma unroll
-      for (int q = 0; q < C::WN; ++q) s += part[q * C::BM + t];
-      ar->dwpart[(int64_t)(row0 + t) * ar->dw_cols + nt] = s;
+      for (int k = 0; k < PER; ++k) {
+        const int c = tid + k * C::NTHR;
+        const int row = c / CPR, c8 = c % CPR;
+        const int64_t i = n0 + q * C::TN + c8 * 8;
+        float s = 0.f;
+        if (row < rows && i < I) {
+          const int64_t p = row0 + row;
+          float g[8], u[8], av[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + i), g);
+          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + I + i), u);
+          unpack8(*reinterpret_cast<const u32x4*>(ar->a + p * I + i), av);
+          const float w = wrow[row];
+          const float* G = gst + row * LDF + c8 * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            s += G[j] * av[j];
+            const float dA = w * G[j];
+            const float sg = sigmoidf_(g[j]);
+            dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
+            du[j] = dA * g[j] * sg;
+          }
+          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + i) = pack8(dg);
+          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + I + i) = pack8(du);
+        }
+        // the CPR threads of a row are consecutive lanes: fixed-order butterfly
+#pragma unroll
+        for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+        part[k] += s;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = tid + k * C::NTHR;
+      const int row = c / CPR;
+      if (c % CPR == 0 && row < rows) ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
     }
   }
 };
