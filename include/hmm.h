@@ -69,12 +69,23 @@ typedef enum hmm_dtype {
   HMM_FP8_E4M3 = 2
 } hmm_dtype;
 
-/* Check topk_ids on the device before any matrix product: the routing kernel
- * raises a flag, the host reads it back (one small device-to-host copy and a
- * stream wait) and returns HMM_ERR_EXPERT_ID_OUT_OF_RANGE without launching
- * the products.  Without the flag, slots with an invalid id are dropped (they
- * contribute zero) and the flag is recorded in ``saved`` (hmm_saved_layout.id_error). */
+/* Check topk_ids: the routing kernel raises a device flag for an id outside
+ * [0, E), and the host reads it back (one 4-byte device-to-host copy) and
+ * returns HMM_ERR_EXPERT_ID_OUT_OF_RANGE.  The host waits for that copy only
+ * after the call's kernels are enqueued, so the check adds no idle time on the
+ * GPU; the products of a failing call run with the invalid slots dropped, and
+ * its outputs are unspecified.  Without the flag, slots with an invalid id are
+ * dropped (they contribute zero) and the flag is recorded in ``saved``
+ * (hmm_saved_layout.id_error). */
 #define HMM_FLAG_VALIDATE_IDS 1u
+
+/* Tiling of the grouped products.  By default the library picks: 256-row tiles
+ * (plus 64-row tiles for expert remainders) when the problem fills the chip,
+ * 64x64 tiles when it is small.  These flags force one choice (for tuning and
+ * tests); at most one may be set.  A backward must be given the same flags as
+ * the forward that filled its ``saved`` buffer. */
+#define HMM_FLAG_TILES_LARGE 2u
+#define HMM_FLAG_TILES_NARROW 4u
 
 /* Problem description.
  *   T  tokens (>= 0; T = 0 is a no-op that still writes zero weight gradients)
@@ -88,7 +99,7 @@ typedef enum hmm_dtype {
  *               are quantised per row, the up-projection weight per
  *               (expert, column), both as scale = 448 / max|.| (the per-token
  *               dynamic quantisation of MoeDistributeDispatchV2, case 3).
- *   flags       HMM_FLAG_* bits. */
+ *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward. */
 typedef struct hmm_problem {
   int64_t T, H, I, E, K;
   int32_t out_dtype;
@@ -131,8 +142,8 @@ hmm_status hmm_saved_layout_of(const hmm_problem* p, hmm_saved_layout* out);
  *                 stay untouched until the matching backward has run
  *   workspace     forward_sizes' workspace_bytes of scratch (free after the
  *                 call has executed on the stream)
- * On HMM_ERR_EXPERT_ID_OUT_OF_RANGE (with HMM_FLAG_VALIDATE_IDS) y is not
- * written. */
+ * On HMM_ERR_EXPERT_ID_OUT_OF_RANGE (with HMM_FLAG_VALIDATE_IDS) the contents
+ * of y and saved are unspecified. */
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids,
                        const float* topk_weights, const void* up_w, const void* down_w, void* y,
                        void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,

@@ -23,6 +23,9 @@ HMM_ERR_HIP = 8
 
 HMM_BF16, HMM_F32, HMM_FP8_E4M3 = 0, 1, 2
 HMM_FLAG_VALIDATE_IDS = 1
+HMM_FLAG_TILES_LARGE = 2
+HMM_FLAG_TILES_NARROW = 4
+TILE_FLAGS = {"auto": 0, "large": HMM_FLAG_TILES_LARGE, "narrow": HMM_FLAG_TILES_NARROW}
 
 # every symbol include/hmm.h declares
 EXPORTS = (

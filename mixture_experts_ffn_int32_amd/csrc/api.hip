@@ -35,6 +35,7 @@ inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
   int64_t T, H, I, E, K, S;
+  bool small;  // small-problem mode (narrow tiles; see kernels.h)
 };
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
@@ -50,7 +51,10 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_SHAPE, "I must be a multiple of 64 in [64, 65536] (got %lld)", (long long)p->I);
   if (p->T > (int64_t)0x7fffffff / p->K)
     return fail(HMM_ERR_BAD_SHAPE, "T*K must stay below 2^31 (T=%lld, K=%lld)", (long long)p->T, (long long)p->K);
-  if (p->flags & ~HMM_FLAG_VALIDATE_IDS) return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
+  if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW))
+    return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
+  if ((p->flags & HMM_FLAG_TILES_LARGE) && (p->flags & HMM_FLAG_TILES_NARROW))
+    return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
   if (p->out_dtype != HMM_BF16 && p->out_dtype != HMM_F32)
     return fail(HMM_ERR_BAD_DTYPE, "out_dtype must be HMM_BF16 or HMM_F32 (got %d)", p->out_dtype);
   if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3)
@@ -70,6 +74,9 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->E = p->E;
   d->K = p->K;
   d->S = p->T * p->K;
+  d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
+             : (p->flags & HMM_FLAG_TILES_LARGE) ? false
+             : hmm::small_mode(d->S, d->H, d->I);
   return HMM_OK;
 }
 
@@ -83,7 +90,12 @@ hmm_status need(const void* ptr, bool nonempty, const char* name) {
 }
 
 int64_t n_route_blocks(const Dims& d) { return (d.S + hmm::RT_SLOTS - 1) / hmm::RT_SLOTS; }
-int64_t tile_ints(const Dims& d) { return hmm::tile_table_ints(d.S, d.E); }
+int64_t tile_ints(const Dims& d) { return hmm::tile_table_ints(d.S, d.E, d.small); }
+hmm::RowGroups row_groups(const Dims& d, const int32_t* tiles, const int32_t* offsets, const int32_t* sorted_slot,
+                          const int32_t* tok_of_row) {
+  return hmm::RowGroups{tiles, offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E, d.small),
+                        hmm::max_small_tiles(d.S, d.E, d.small), d.T, d.S, d.small};
+}
 
 hmm_saved_layout saved_layout(const Dims& d) {
   hmm_saved_layout L{};
@@ -136,7 +148,7 @@ struct BwdWork {
 };
 BwdWork bwd_work(const Dims& d) {
   BwdWork w{};
-  w.dw_cols = hmm::act_grad_dw_cols(d.I);
+  w.dw_cols = hmm::act_grad_dw_cols(d.I, d.small);
   size_t o = 0;
   w.dh = o;     o += up(d.S * 2 * d.I * 2);
   w.dxp = o;    o += up(d.S * d.H * 2);
@@ -193,39 +205,60 @@ struct Stage {
   }
 };
 
-// One pinned host word per thread for the id-validation read-back.
-int32_t* pinned_word() {
-  thread_local int32_t* w = nullptr;
-  if (!w) {
-    if (hipHostMalloc((void**)&w, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) w = nullptr;
+// Per-thread objects of the id check: a pinned host word and an event that
+// marks the word's arrival.
+struct IdCheck {
+  int32_t* word = nullptr;
+  hipEvent_t ev = nullptr;
+};
+IdCheck* id_check() {
+  thread_local IdCheck c;
+  if (!c.word) {
+    if (hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) c.word = nullptr;
   }
-  return w;
+  if (c.word && !c.ev) {
+    if (hipEventCreateWithFlags(&c.ev, hipEventDisableTiming) != hipSuccess) c.ev = nullptr;
+  }
+  return (c.word && c.ev) ? &c : nullptr;
 }
 
+// Enqueue the routing; with validate_ids also enqueue the 4-byte copy of the
+// error word to pinned host memory and an event after it.  The caller waits
+// with finish_id_check (after enqueueing its products, so the GPU never idles
+// while the host waits).
 hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                      int32_t* row_of_slot, int32_t* tok_of_row, int32_t* tiles, int32_t* err, void* scratch,
                      const RouteScratch& rs, bool validate_ids, hipStream_t stream) {
   hipError_t e;
   {
     Stage stage("route", stream);
-    e = hmm::launch_route(ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E), counts, offsets,
-                          sorted_slot, row_of_slot, tok_of_row, tiles, err, at<int32_t>(scratch, rs.blockhist),
-                          at<int32_t>(scratch, rs.blockbase), at<int32_t>(scratch, rs.blockerr), stream);
+    e = hmm::launch_route(ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E, d.small), d.small ? 0 : 1,
+                          counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err,
+                          at<int32_t>(scratch, rs.blockhist), at<int32_t>(scratch, rs.blockbase),
+                          at<int32_t>(scratch, rs.blockerr), stream);
   }
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   if (validate_ids) {
-    int32_t* host = pinned_word();
-    if (!host) return fail(HMM_ERR_HIP, "hipHostMalloc of the validation word failed");
-    *host = 0;
+    IdCheck* c = id_check();
+    if (!c) return fail(HMM_ERR_HIP, "could not create the id-check word or event");
+    *c->word = 0;
     {
       Stage stage("id_readback", stream);
-      e = hipMemcpyAsync(host, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+      e = hipMemcpyAsync(c->word, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "id-validation read-back");
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "id-validation wait");
-    if (*host) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
+    e = hipEventRecord(c->ev, stream);
+    if (e != hipSuccess) return hip_fail(e, "id-validation event");
   }
+  return HMM_OK;
+}
+
+hmm_status finish_id_check(const Dims& d) {
+  IdCheck* c = id_check();
+  if (!c) return fail(HMM_ERR_HIP, "id-check state missing");
+  hipError_t e = hipEventSynchronize(c->ev);
+  if (e != hipSuccess) return hip_fail(e, "id-validation wait");
+  if (*c->word) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
   return HMM_OK;
 }
 
@@ -315,8 +348,11 @@ hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* cou
   int32_t* tiles = at<int32_t>(workspace, rs.total);
   int32_t* err = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4));
   int32_t* tok = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4) + up(4));
-  return run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tok, tiles, err, workspace, rs,
-                   (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, (hipStream_t)stream);
+  const bool v = (p->flags & HMM_FLAG_VALIDATE_IDS) != 0;
+  s = run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tok, tiles, err, workspace, rs, v,
+                (hipStream_t)stream);
+  if (s != HMM_OK || !v) return s;
+  return finish_id_check(d);
 }
 
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
@@ -341,14 +377,13 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
   int32_t* tiles = at<int32_t>(saved, L.tiles);
   int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
+  const bool validate_ids = (p->flags & HMM_FLAG_VALIDATE_IDS) != 0;
   s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
-                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs,
-                (p->flags & HMM_FLAG_VALIDATE_IDS) != 0, st);
+                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, st);
   if (s != HMM_OK) return s;
-  if (!ne) return HMM_OK;
+  if (!ne) return validate_ids ? finish_id_check(d) : HMM_OK;
 
-  hmm::RowGroups g{tiles, offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E),
-                   hmm::max_small_tiles(d.S, d.E), d.T, d.S};
+  hmm::RowGroups g = row_groups(d, tiles, offsets, sorted_slot, tok_of_row);
   uint16_t* h = at<uint16_t>(saved, L.h);
   uint16_t* a = at<uint16_t>(saved, L.a);
   uint16_t* aw = at<uint16_t>(saved, L.aw);
@@ -370,7 +405,7 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
     e = hmm::launch_combine(o, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, (uint16_t*)y, st);
   }
   if (e != hipSuccess) return hip_fail(e, "combine launch");
-  return HMM_OK;
+  return validate_ids ? finish_id_check(d) : HMM_OK;
 }
 
 hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
@@ -399,8 +434,7 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   const int32_t* sorted_slot = at<int32_t>(saved, L.sorted_slot);
   const int32_t* row_of_slot = at<int32_t>(saved, L.row_of_slot);
   const int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
-  hmm::RowGroups g{at<int32_t>(saved, L.tiles), offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E),
-                   hmm::max_small_tiles(d.S, d.E), d.T, d.S};
+  hmm::RowGroups g = row_groups(d, at<int32_t>(saved, L.tiles), offsets, sorted_slot, tok_of_row);
   const uint16_t* h = at<uint16_t>(saved, L.h);
   const uint16_t* a = at<uint16_t>(saved, L.a);
   const uint16_t* aw = at<uint16_t>(saved, L.aw);
@@ -434,13 +468,13 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   {
     Stage stage("dw2", st);
     e = hmm::launch_dw2(offsets, tok_of_row, d.T, d.S, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w,
-                        st);
+                        d.small, st);
   }
   if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
   {
     Stage stage("dw1", st);
     e = hmm::launch_dw1(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w,
-                        st);
+                        d.small, st);
   }
   if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
   return HMM_OK;

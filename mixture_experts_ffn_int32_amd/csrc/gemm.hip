@@ -17,6 +17,8 @@
 //   Big   256 x 256 x 64, 8 waves as 2 x 4, 128 x 64 per wave (one workgroup per CU,
 //         two waves per SIMD)
 //   Small  64 x 256 x 64, 4 waves as 1 x 4,  64 x 64 per wave (expert remainders, small experts)
+//   Narrow 64 x  64 x 64, 4 waves as 2 x 2,  32 x 32 per wave (whole problem small: many
+//         workgroups instead of a few big tiles)
 // "rows" products run over the routing's tile tables: each expert's rows are
 // covered by big tiles, and a remainder of at most 128 rows by small tiles, so
 // a small or long-tail expert does not pay for a 256-row tile (RFC 6.3, expert
@@ -64,6 +66,7 @@ struct Cfg {
 };
 typedef Cfg<256, 256, 2, 4> Big;
 typedef Cfg<64, 256, 1, 4> Small;
+typedef Cfg<64, 64, 2, 2> Narrow;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -311,11 +314,9 @@ struct Gmm1 : RowTile<Cc, SMALL> {
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
   int i0;
-  // the B tile holds BN/2 gate columns then the BN/2 matching up columns; each
-  // wave takes TN/2 of each, so one lane holds g and u of the same (row, i)
-  __device__ static __forceinline__ int ncol0(int wn, int nb) {
-    return (nb >= C::NB / 2 ? C::BN / 2 : 0) + wn * (C::TN / 2) + (nb % (C::NB / 2)) * 32;
-  }
+  // the B tile holds BN/2 gate columns then the BN/2 matching up columns; the
+  // epilogue pairs them through LDS
+  __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
     if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
@@ -597,9 +598,10 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 // ------------------------------------------------------------- weight gradients
 // C[e][m][n] = sum over the expert's rows p of A[p][m] * B[p][n]; both operands
 // are read along their row (m or n contiguous) and transposed by the LDS read.
-template <bool GATHER_A, bool GATHER_B>
-struct Dw : PlainCols<Big> {
-  typedef Big C;
+template <class Cc, bool GATHER_A, bool GATHER_B>
+struct Dw : PlainCols<Cc> {
+  typedef Cc C;
+  using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
   struct Args {
     const int32_t* offsets;
@@ -693,28 +695,38 @@ hipError_t launch(const typename P::Args& args, int64_t logical_blocks, hipStrea
   return hipGetLastError();
 }
 
-// big-tile launch, then small-tile launch, of a row-grouped product
-template <template <class, bool> class P, class ArgsFill>
-hipError_t launch_rows(const RowGroups& g, int64_t n_ntiles, ArgsFill fill, hipStream_t stream) {
+// big-tile launch, then small-tile launch, of a row-grouped product (n_ntiles
+// is a function of the tile width); in narrow mode one launch of 64x64 tiles
+template <template <class, bool> class P, class ArgsFill, class NTiles>
+hipError_t launch_rows(const RowGroups& g, NTiles n_ntiles, ArgsFill fill, hipStream_t stream) {
+  if (g.narrow) {
+    typedef P<Narrow, true> PN;
+    typename PN::Args an;
+    fill(an, n_ntiles(Narrow::BN));
+    return launch<PN>(an, g.max_small * n_ntiles(Narrow::BN), stream);
+  }
   typedef P<Big, false> PB;
   typedef P<Small, true> PS;
   typename PB::Args ab;
-  fill(ab);
-  hipError_t e = launch<PB>(ab, g.max_big * n_ntiles, stream);
+  fill(ab, n_ntiles(Big::BN));
+  hipError_t e = launch<PB>(ab, g.max_big * n_ntiles(Big::BN), stream);
   if (e != hipSuccess) return e;
   typename PS::Args as;
-  fill(as);
-  return launch<PS>(as, g.max_small * n_ntiles, stream);
+  fill(as, n_ntiles(Small::BN));
+  return launch<PS>(as, g.max_small * n_ntiles(Small::BN), stream);
 }
 
 }  // namespace
 
-int act_grad_dw_cols(int64_t I) { return (int)((I + 255) / 256); }
+int act_grad_dw_cols(int64_t I, bool narrow) {
+  const int64_t bn = narrow ? Narrow::BN : Big::BN;  // Big and Small share BN
+  return (int)((I + bn - 1) / bn);
+}
 
 hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
                               int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  const int nnt = (int)((I + 127) / 128);  // 128 gate columns (and their up columns) per N tile
-  return launch_rows<Gmm1>(g, nnt, [&](auto& A) {
+  // BN/2 gate columns (and their up columns) per N tile
+  return launch_rows<Gmm1>(g, [&](int bn) { return (int)((I + bn / 2 - 1) / (bn / 2)); }, [&](auto& A, int nnt) {
     A.g = g; A.x = x; A.w1 = w1; A.tw = topk_w; A.T = g.T; A.H = H; A.I = I; A.h = h; A.a = a; A.aw = aw;
     A.n_ntiles = nnt;
   }, stream);
@@ -722,8 +734,7 @@ hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint1
 
 hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
                        uint16_t* o, hipStream_t stream) {
-  const int nnt = (int)((H + 255) / 256);
-  return launch_rows<Gmm2>(g, nnt, [&](auto& A) {
+  return launch_rows<Gmm2>(g, [&](int bn) { return (int)((H + bn - 1) / bn); }, [&](auto& A, int nnt) {
     A.g = g; A.a = a; A.w2 = w2; A.S = g.S; A.H = H; A.I = I; A.o = o; A.n_ntiles = nnt;
   }, stream);
 }
@@ -731,8 +742,7 @@ hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2
 hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
                            const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
                            float* dwpart, int dw_cols, hipStream_t stream) {
-  const int nnt = (int)((I + 255) / 256);
-  return launch_rows<ActGrad>(g, nnt, [&](auto& A) {
+  return launch_rows<ActGrad>(g, [&](int bn) { return (int)((I + bn - 1) / bn); }, [&](auto& A, int nnt) {
     A.g = g; A.dy = dy; A.w2 = w2; A.tw = topk_w; A.h = h; A.a = a; A.T = g.T; A.H = H; A.I = I; A.dh = dh;
     A.dwpart = dwpart; A.dw_cols = dw_cols; A.n_ntiles = nnt;
   }, stream);
@@ -740,24 +750,33 @@ hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_
 
 hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
                              uint16_t* dxp, hipStream_t stream) {
-  const int nnt = (int)((H + 255) / 256);
-  return launch_rows<InputGrad>(g, nnt, [&](auto& A) {
+  return launch_rows<InputGrad>(g, [&](int bn) { return (int)((H + bn - 1) / bn); }, [&](auto& A, int nnt) {
     A.g = g; A.dh = dh; A.w1 = w1; A.S = g.S; A.H = H; A.I = I; A.dxp = dxp; A.n_ntiles = nnt;
   }, stream);
 }
 
-hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream) {
-  typedef Dw<true, false> P;
-  P::Args A{offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, (int)((H + 255) / 256), (int)((2 * I + 255) / 256)};
+template <class C, bool GA, bool GB>
+hipError_t launch_dw(const int32_t* offsets, const int32_t* tok_of_row, int64_t E, const uint16_t* A_,
+                     const uint16_t* B_, int64_t a_rows, int64_t b_rows, int64_t M, int64_t N, uint16_t* out,
+                     hipStream_t stream) {
+  typedef Dw<C, GA, GB> P;
+  typename P::Args A{offsets, tok_of_row, E, A_, B_, a_rows, b_rows, M, N, out,
+                     (int)((M + C::BM - 1) / C::BM), (int)((N + C::BN - 1) / C::BN)};
   return launch<P>(A, E * 8 * ((A.mt * A.nt + 7) / 8), stream);
 }
 
+hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, bool narrow,
+                      hipStream_t stream) {
+  if (narrow) return launch_dw<Narrow, true, false>(offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, stream);
+  return launch_dw<Big, true, false>(offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, stream);
+}
+
 hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream) {
-  typedef Dw<false, true> P;
-  P::Args A{offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, (int)((I + 255) / 256), (int)((H + 255) / 256)};
-  return launch<P>(A, E * 8 * ((A.mt * A.nt + 7) / 8), stream);
+                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, bool narrow,
+                      hipStream_t stream) {
+  if (narrow) return launch_dw<Narrow, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
+  return launch_dw<Big, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
 }
 
 }  // namespace hmm

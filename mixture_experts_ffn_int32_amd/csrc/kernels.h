@@ -21,15 +21,28 @@ constexpr int TILE_SMALL = 64;        // rows of a small tile (expert remainders
 // #big <= sum_e (c_e + 127) / 256 <= (S + 127 E) / 256, and, since ceil(r/64)
 // <= 1 + (r - 1)/64 for r > 0 and at most min(E, S) experts have rows,
 // #small <= min(2 E, min(E, S) + S / 64).
-inline int64_t max_big_tiles(int64_t S, int64_t E) { return (S + (TILE_BIG / 2 - 1) * E) / TILE_BIG; }
-inline int64_t max_small_tiles(int64_t S, int64_t E) {
-  const int64_t a = 2 * E, b = (E < S ? E : S) + S / TILE_SMALL;
+// Small problems (few big tiles for the whole chip) use only TILE_SMALL-row tiles
+// and narrow 64x64 product tiles; then #small = sum_e ceil(c_e / 64) <=
+// (S + 63 min(E, S)) / 64.
+inline bool small_mode(int64_t S, int64_t H, int64_t I) {
+  const int64_t n = (H > 2 * I ? H : 2 * I);
+  return ((S + TILE_BIG - 1) / TILE_BIG) * ((n + 255) / 256) < 256;
+}
+inline int64_t max_big_tiles(int64_t S, int64_t E, bool small) {
+  return small ? 0 : (S + (TILE_BIG / 2 - 1) * E) / TILE_BIG;
+}
+inline int64_t max_small_tiles(int64_t S, int64_t E, bool small) {
+  const int64_t ne = E < S ? E : S;
+  if (small) return (S + (TILE_SMALL - 1) * ne) / TILE_SMALL;
+  const int64_t a = 2 * E, b = ne + S / TILE_SMALL;
   return a < b ? a : b;
 }
-inline int64_t tile_table_ints(int64_t S, int64_t E) { return 4 + 2 * (max_big_tiles(S, E) + max_small_tiles(S, E)); }
+inline int64_t tile_table_ints(int64_t S, int64_t E, bool small) {
+  return 4 + 2 * (max_big_tiles(S, E, small) + max_small_tiles(S, E, small));
+}
 
 // routing (route.hip)
-hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int32_t* counts,
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
                         hipStream_t stream);
@@ -42,6 +55,7 @@ struct RowGroups {
   const int32_t* tok_of_row;   // [S] token of permuted row p (= sorted_slot[p] / K)
   int64_t max_big, max_small;  // table capacities
   int64_t T, S;                // tokens, routed rows (extents of the buffer resources)
+  bool narrow;                 // small-problem mode: 64x64 tiles over the small table only
 };
 
 // h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
@@ -59,11 +73,13 @@ hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint1
                              uint16_t* dxp, hipStream_t stream);
 // dW1[e] = sum_p x[tok(p)]^T dH[p];  dW2[e] = sum_p aw[p]^T dY[tok(p)]
 hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, hipStream_t stream);
+                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, bool narrow,
+                      hipStream_t stream);
 hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, hipStream_t stream);
+                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, bool narrow,
+                      hipStream_t stream);
 // number of d_topk_weights partial columns written by launch_act_grad for a given I
-int act_grad_dw_cols(int64_t I);
+int act_grad_dw_cols(int64_t I, bool narrow);
 
 // pointwise (pointwise.hip)
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,

@@ -45,11 +45,13 @@ __global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restri
 // builds the tile table of the row-grouped products: each expert's rows are
 // covered by TILE_BIG-row tiles, and a remainder of at most TILE_BIG/2 rows by
 // TILE_SMALL-row tiles (a larger remainder gets one more, partly filled, big
-// tile).  Layout: tiles[0] = #big, tiles[1] = #small, then max_big (expert,
+// tile).  With big_on = 0 (small problems) every row goes to TILE_SMALL-row
+// tiles.  Layout: tiles[0] = #big, tiles[1] = #small, then max_big (expert,
 // first row) pairs from tiles[4], then the small pairs from tiles[4 + 2*max_big].
 __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __restrict__ blockhist,
                                                               const int32_t* __restrict__ blockerr, int nblk,
-                                                              int E, int max_big, int32_t* __restrict__ counts,
+                                                              int E, int max_big, int big_on,
+                                                              int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ blockbase,
                                                               int32_t* __restrict__ tiles,
@@ -66,9 +68,9 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
       c += v;
     }
   }
-  const int rem = c % TILE_BIG;
-  const int nbig = c / TILE_BIG + (rem > TILE_BIG / 2 ? 1 : 0);
-  const int nsmall = (rem > TILE_BIG / 2) ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
+  const int rem = big_on ? c % TILE_BIG : c;
+  const int nbig = big_on ? c / TILE_BIG + (rem > TILE_BIG / 2 ? 1 : 0) : 0;
+  const int nsmall = (big_on && rem > TILE_BIG / 2) ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
   scan_c[e] = (e < E) ? c : 0;
   scan_b[e] = (e < E) ? nbig : 0;
   scan_s[e] = (e < E) ? nsmall : 0;
@@ -173,7 +175,7 @@ __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __res
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int32_t* counts,
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
                         hipStream_t stream) {
@@ -184,7 +186,7 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big
     hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr);
   }
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, max_big,
-                     counts, offsets, blockbase, tiles, err);
+                     big_on, counts, offsets, blockbase, tiles, err);
   if (nblk > 0) {
     hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, nbits, offsets,
                        blockbase, K, sorted_slot, row_of_slot, tok_of_row);

@@ -163,10 +163,10 @@ def route(topk_ids, E, validate_ids=True):
     return out
 
 
-def saved_views(saved, T, H, I, E, K):
+def saved_views(saved, T, H, I, E, K, tiles="auto"):
     """Typed views of the arrays a forward recorded in its saved buffer."""
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K)
+    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles])
     L = _lib.SavedLayout()
     _lib.check(lib.hmm_saved_layout_of(ctypes.byref(prob), ctypes.byref(L)))
     S = T * K
@@ -188,19 +188,24 @@ def saved_views(saved, T, H, I, E, K):
     }
 
 
-def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True):
-    """Forward without autograd; returns (y, saved buffer) for stage-level checks."""
+def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True,
+                       tiles="auto"):
+    """Forward without autograd; returns (y, saved buffer) for stage-level checks.
+
+    ``tiles`` forces the tiling of the grouped products ("auto", "large" or
+    "narrow"); the matching backward_from_saved call must use the same value.
+    """
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
-    flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+    flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | _lib.TILE_FLAGS[tiles]
     with torch.cuda.device(x.device):
         return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
                             _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags)
 
 
-def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved):
+def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto"):
     """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights)."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     with torch.cuda.device(x.device):
         return _backward_raw(_contig(dy, torch.bfloat16), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
-                             _contig(down_proj_weight), saved, T, H, I, E, K, 0)
+                             _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles])

@@ -54,7 +54,7 @@ def _prob(**kw):
     (dict(T=-1), _lib.HMM_ERR_BAD_SHAPE), (dict(T=1 << 28, K=16), _lib.HMM_ERR_BAD_SHAPE),
     (dict(out_dtype=7), _lib.HMM_ERR_BAD_DTYPE), (dict(gmm1_dtype=9), _lib.HMM_ERR_BAD_DTYPE),
     (dict(out_dtype=_lib.HMM_F32), _lib.HMM_ERR_UNSUPPORTED), (dict(flags=8), _lib.HMM_ERR_BAD_SHAPE),
-    (dict(reserved=1), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(reserved=1), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=6), _lib.HMM_ERR_BAD_SHAPE),
 ])
 def test_sizes_reject_bad_problems(lib, kw, status):
     ws, sv = ctypes.c_size_t(), ctypes.c_size_t()

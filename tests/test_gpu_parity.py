@@ -18,13 +18,13 @@ from oracle.routing import route as oracle_route
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(g):
+def run_gpu(g, tiles="auto"):
     import torch
     from mixture_experts_ffn_int32_amd import backward_from_saved, forward_with_saved
     y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
-                                  g["down_proj_weight"])
+                                  g["down_proj_weight"], tiles=tiles)
     dx, dW1, dW2, dw = backward_from_saved(g["dY"], g["x"], g["topk_ids"], g["topk_weights"],
-                                           g["up_proj_weight"], g["down_proj_weight"], saved)
+                                           g["up_proj_weight"], g["down_proj_weight"], saved, tiles=tiles)
     torch.cuda.synchronize()
     return y, saved, dx, dW1, dW2, dw
 
@@ -40,13 +40,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("tiles", ["large", "narrow"])
 @pytest.mark.parametrize("name,over", SMALL, ids=[s[0] for s in SMALL])
-def test_small_full_parity(name, over):
+def test_small_full_parity(name, over, tiles):
     spec = synth.spec_with("tiny", **over)
     inp = synth.make_inputs(spec, seed=11)
-    announce("full parity %s %s" % (name, {k: spec[k] for k in "THIEK"}))
+    announce("full parity %s %s tiles=%s" % (name, {k: spec[k] for k in "THIEK"}, tiles))
     g = gpu_inputs(inp, "cuda")
-    y, saved, dx, dW1, dW2, dw = run_gpu(g)
+    y, saved, dx, dW1, dW2, dw = run_gpu(g, tiles)
     o = MoEFFN(**oracle_inputs(inp), mode="faithful")
     ry, ryd = o.forward_dev()
     assert_close(to_f64(y), ry, name + " y", ryd)
@@ -61,14 +62,15 @@ def test_small_full_parity(name, over):
         assert not to_f64(dW1[e]).any() and not to_f64(dW2[e]).any()
 
 
-def test_saved_intermediates_match_oracle():
+@pytest.mark.parametrize("tiles", ["large", "narrow"])
+def test_saved_intermediates_match_oracle(tiles):
     from mixture_experts_ffn_int32_amd import saved_views
     spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3)
     inp = synth.make_inputs(spec, seed=3)
-    announce("saved intermediates")
+    announce("saved intermediates tiles=%s" % tiles)
     g = gpu_inputs(inp, "cuda")
-    y, saved, *_ = run_gpu(g)
-    v = saved_views(saved, *(spec[k] for k in "THIEK"))
+    y, saved, *_ = run_gpu(g, tiles)
+    v = saved_views(saved, *(spec[k] for k in "THIEK"), tiles=tiles)
     ref_route = oracle_route(inp["topk_ids"], spec["E"])
     for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
         assert np.array_equal(v[k].cpu().numpy(), ref_route[k]), k
