@@ -77,10 +77,9 @@ def stage_work(stage, T, H, I, E, K):
     nbytes = {
         # read K gathered rows per token + row index + weight, write one row
         "combine": S * H * 2 + S * 8 + T * H * 2,
-        "combine_dx": S * H * 2 + S * 4 + T * H * 2,
+        "combine_dx": S * H * 2 + S * 4 + T * H * 2,   # (+ d_topk_weights partials, small)
         # ids read twice, histograms, sorted_slot + row_of_slot written
         "route": S * 4 * 2 + S * 8,
-        "dw_finalize": S * 4,
     }
     if stage in nbytes:
         return "hbm", nbytes[stage], "GB/s"

@@ -22,7 +22,7 @@
  * - Pointers named as tensors are DEVICE pointers (HBM of the current HIP
  *   device); all are caller-owned and caller-allocated.  The library never
  *   allocates device memory.  Its only state is, per host thread, one pinned
- *   host word for the id read-back and the optional stage-timing events.
+ *   host word and event for the id check, and the optional stage-timing events.
  * - All tensors are dense, row-major (last index fastest), with no padding.
  *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
  *   be 16-byte aligned.
@@ -69,8 +69,8 @@ typedef enum hmm_dtype {
   HMM_FP8_E4M3 = 2
 } hmm_dtype;
 
-/* Check topk_ids: the routing kernel raises a device flag for an id outside
- * [0, E), and the host reads it back (one 4-byte device-to-host copy) and
+/* Check topk_ids: the routing kernel raises a flag for an id outside [0, E)
+ * and also stores it into a pinned host word; the host reads that word and
  * returns HMM_ERR_EXPERT_ID_OUT_OF_RANGE.  The host waits for that copy only
  * after the call's kernels are enqueued, so the check adds no idle time on the
  * GPU; the products of a failing call run with the invalid slots dropped, and

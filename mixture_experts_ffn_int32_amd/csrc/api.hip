@@ -205,8 +205,8 @@ struct Stage {
   }
 };
 
-// Per-thread objects of the id check: a pinned host word and an event that
-// marks the word's arrival.
+// Per-thread objects of the id check: a pinned (coherent, device-visible) host
+// word that the routing kernel writes, and an event recorded after the routing.
 struct IdCheck {
   int32_t* word = nullptr;
   hipEvent_t ev = nullptr;
@@ -214,7 +214,7 @@ struct IdCheck {
 IdCheck* id_check() {
   thread_local IdCheck c;
   if (!c.word) {
-    if (hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) c.word = nullptr;
+    if (hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocCoherent) != hipSuccess) c.word = nullptr;
   }
   if (c.word && !c.ev) {
     if (hipEventCreateWithFlags(&c.ev, hipEventDisableTiming) != hipSuccess) c.ev = nullptr;
@@ -222,31 +222,29 @@ IdCheck* id_check() {
   return (c.word && c.ev) ? &c : nullptr;
 }
 
-// Enqueue the routing; with validate_ids also enqueue the 4-byte copy of the
-// error word to pinned host memory and an event after it.  The caller waits
-// with finish_id_check (after enqueueing its products, so the GPU never idles
-// while the host waits).
+// Enqueue the routing; with validate_ids the routing also stores its error flag
+// into the pinned host word, and an event is recorded after it.  The caller
+// waits with finish_id_check (after enqueueing its products, so the GPU never
+// idles while the host waits).
 hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                      int32_t* row_of_slot, int32_t* tok_of_row, int32_t* tiles, int32_t* err, void* scratch,
                      const RouteScratch& rs, bool validate_ids, hipStream_t stream) {
+  IdCheck* c = nullptr;
+  if (validate_ids) {
+    c = id_check();
+    if (!c) return fail(HMM_ERR_HIP, "could not create the id-check word or event");
+    *c->word = 0;
+  }
   hipError_t e;
   {
     Stage stage("route", stream);
     e = hmm::launch_route(ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E, d.small), d.small ? 0 : 1,
                           counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err,
                           at<int32_t>(scratch, rs.blockhist), at<int32_t>(scratch, rs.blockbase),
-                          at<int32_t>(scratch, rs.blockerr), stream);
+                          at<int32_t>(scratch, rs.blockerr), c ? c->word : nullptr, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "routing launch");
-  if (validate_ids) {
-    IdCheck* c = id_check();
-    if (!c) return fail(HMM_ERR_HIP, "could not create the id-check word or event");
-    *c->word = 0;
-    {
-      Stage stage("id_readback", stream);
-      e = hipMemcpyAsync(c->word, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "id-validation read-back");
+  if (c) {
     e = hipEventRecord(c->ev, stream);
     if (e != hipSuccess) return hip_fail(e, "id-validation event");
   }
@@ -456,14 +454,10 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
     if (e != hipSuccess) return hip_fail(e, "input_grad launch");
     {
       Stage stage("combine_dx", st);
-      e = hmm::launch_combine(dxp, row_of_slot, nullptr, d.T, (int)d.K, d.H, (uint16_t*)dx, st);
+      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, (uint16_t*)dx, dwpart, W.dw_cols,
+                                 d_topk_weights, st);
     }
     if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
-    {
-      Stage stage("dw_finalize", st);
-      e = hmm::launch_dw_finalize(dwpart, W.dw_cols, row_of_slot, d.S, d_topk_weights, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "d_topk_weights launch");
   }
   {
     Stage stage("dw2", st);

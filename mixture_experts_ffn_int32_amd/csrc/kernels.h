@@ -11,6 +11,9 @@ constexpr int MAX_EXPERTS = 1024;     // E limit (the dispatch op's moeExpertNum
 constexpr int RT_THREADS = 256;       // routing block size
 constexpr int RT_SLOTS = 1024;        // slots per routing block
 constexpr int RT_SCAN_THREADS = 1024; // the single scan block (>= MAX_EXPERTS)
+constexpr int RT_ONE_THREADS = 1024;  // one-workgroup routing of small problems
+constexpr int RT_ONE_MAX_SLOTS = 8192;
+constexpr int RT_ONE_MAX_EXPERTS = 256;
 
 constexpr int TILE_BIG = 256;         // rows of a big row-grouped product tile
 constexpr int TILE_SMALL = 64;        // rows of a small tile (expert remainders, small experts)
@@ -45,7 +48,7 @@ inline int64_t tile_table_ints(int64_t S, int64_t E, bool small) {
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
-                        hipStream_t stream);
+                        int32_t* host_err, hipStream_t stream);
 
 // grouped products (gemm.hip).  All matrices bf16 (uint16_t storage).
 struct RowGroups {
@@ -84,7 +87,8 @@ int act_grad_dw_cols(int64_t I, bool narrow);
 // pointwise (pointwise.hip)
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
                           int K, int64_t H, uint16_t* out, hipStream_t stream);
-hipError_t launch_dw_finalize(const float* dwpart, int dw_cols, const int32_t* row_of_slot, int64_t S,
-                              float* dw, hipStream_t stream);
+// combine(dX) (unweighted) with d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c] folded in
+hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
+                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
 
 }  // namespace hmm

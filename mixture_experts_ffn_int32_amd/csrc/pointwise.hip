@@ -5,7 +5,8 @@
 //                 out[t] = sum_k w[t,k] * rows[row_of_slot[t*K+k]]   (w = 1 if NULL)
 //                 in float32, k ascending, then one bf16 rounding; no atomics, so
 //                 the result is deterministic.
-//   dw_finalize  d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c], c ascending.
+//   combine(dX) also finalises d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c],
+//                c ascending, in the threads of each token's first K chunks.
 #include "device.h"
 #include "kernels.h"
 
@@ -14,11 +15,15 @@ namespace hmm {
 constexpr int PW_THREADS = 256;
 
 // One thread per 8 consecutive hidden elements of one token (16-byte loads).
+// With dwpart, the thread of chunk k (< K) of a token also finalises slot k of
+// that token: dw[s] = sum_c dwpart[row_of_slot[s]][c], c ascending.
 template <bool WEIGHTED>
 __global__ void __launch_bounds__(PW_THREADS) combine_kernel(const uint16_t* __restrict__ rows,
                                                              const int32_t* __restrict__ row_of_slot,
                                                              const float* __restrict__ tw, int64_t T, int K,
-                                                             int64_t H, uint16_t* __restrict__ out) {
+                                                             int64_t H, uint16_t* __restrict__ out,
+                                                             const float* __restrict__ dwpart, int dw_cols,
+                                                             float* __restrict__ dw) {
   const int64_t chunks_per_row = H >> 3;
   const int64_t total = T * chunks_per_row;
   for (int64_t idx = (int64_t)blockIdx.x * PW_THREADS + threadIdx.x; idx < total;
@@ -37,21 +42,19 @@ __global__ void __launch_bounds__(PW_THREADS) combine_kernel(const uint16_t* __r
       for (int j = 0; j < 8; ++j) acc[j] = WEIGHTED ? __builtin_fmaf(wk, v[j], acc[j]) : acc[j] + v[j];
     }
     *reinterpret_cast<u32x4*>(out + t * H + c * 8) = pack8(acc);
+    if (dwpart) {
+      for (int64_t k = c; k < K; k += chunks_per_row) {
+        const int64_t s = t * K + k;
+        const int r = row_of_slot[s];
+        float a = 0.f;
+        if (r >= 0) {
+          const float* p = dwpart + (int64_t)r * dw_cols;
+          for (int q = 0; q < dw_cols; ++q) a += p[q];
+        }
+        dw[s] = a;
+      }
+    }
   }
-}
-
-__global__ void __launch_bounds__(PW_THREADS) dw_finalize_kernel(const float* __restrict__ dwpart, int dw_cols,
-                                                                 const int32_t* __restrict__ row_of_slot,
-                                                                 int64_t S, float* __restrict__ dw) {
-  const int64_t s = (int64_t)blockIdx.x * PW_THREADS + threadIdx.x;
-  if (s >= S) return;
-  const int r = row_of_slot[s];
-  float acc = 0.f;
-  if (r >= 0) {
-    const float* p = dwpart + (int64_t)r * dw_cols;
-    for (int c = 0; c < dw_cols; ++c) acc += p[c];
-  }
-  dw[s] = acc;
 }
 
 static unsigned grid_for(int64_t work, int64_t cap) {
@@ -64,20 +67,17 @@ hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, cons
                           int K, int64_t H, uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned g = grid_for(T * (H / 8), 1 << 20);
-  if (topk_w)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
-                       K, H, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
-                       K, H, out);
+  hipLaunchKernelGGL(combine_kernel<true>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T, K, H,
+                     out, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_dw_finalize(const float* dwpart, int dw_cols, const int32_t* row_of_slot, int64_t S, float* dw,
-                              hipStream_t stream) {
-  if (S <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dw_finalize_kernel, dim3(grid_for(S, 1 << 30)), dim3(PW_THREADS), 0, stream, dwpart, dw_cols,
-                     row_of_slot, S, dw);
+hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
+                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const unsigned g = grid_for(T * (H / 8), 1 << 20);
+  hipLaunchKernelGGL(combine_kernel<false>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, nullptr, T, K,
+                     H, dx, dwpart, dw_cols, dw);
   return hipGetLastError();
 }
 

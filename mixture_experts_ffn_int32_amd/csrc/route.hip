@@ -4,7 +4,8 @@
 // slots; section 3.1: offsets are built inside the operator; section 6.2:
 // slots are sorted by expert and un-sorted afterwards.)
 //
-// Slot s = t*K + k.  Three kernels, all integer and deterministic:
+// Slot s = t*K + k.  Three kernels, all integer and deterministic (a small
+// problem runs the same steps in one workgroup, route_one):
 //   route_hist     one block per RT_SLOTS slots: LDS histogram -> blockhist[b][e]
 //   route_scan     one block: counts, per-block bases, offsets, tile tables
 //   route_scatter  one block per RT_SLOTS slots: stable rank inside the block
@@ -55,7 +56,8 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ blockbase,
                                                               int32_t* __restrict__ tiles,
-                                                              int32_t* __restrict__ err) {
+                                                              int32_t* __restrict__ err,
+                                                              int32_t* __restrict__ host_err) {
   __shared__ int32_t scan_c[RT_SCAN_THREADS];
   __shared__ int32_t scan_b[RT_SCAN_THREADS];
   __shared__ int32_t scan_s[RT_SCAN_THREADS];
@@ -113,7 +115,10 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
   int bad = 0;
   for (int b = e; b < nblk; b += RT_SCAN_THREADS) bad |= blockerr[b];
   bad = __syncthreads_or(bad);
-  if (e == 0) *err = bad;
+  if (e == 0) {
+    *err = bad;
+    if (host_err) __hip_atomic_store(host_err, bad, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __restrict__ ids, int64_t S, int E,
@@ -173,20 +178,153 @@ __global__ void __launch_bounds__(RT_THREADS) route_scatter(const int32_t* __res
   }
 }
 
+// Small problems (S <= RT_ONE_MAX_SLOTS, E <= RT_ONE_MAX_EXPERTS): the whole
+// routing in one workgroup of RT_ONE_THREADS threads, with the same results as
+// route_hist + route_scan + route_scatter.  Slots are taken in rounds of
+// RT_ONE_THREADS in ascending order; inside a round the rank of a slot among
+// the slots of its expert comes from a wave multisplit and a fixed-order sum
+// over the waves before it.
+__global__ void __launch_bounds__(RT_ONE_THREADS) route_one(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                            int K, int nbits, int max_big, int big_on,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_slot,
+                                                            int32_t* __restrict__ row_of_slot,
+                                                            int32_t* __restrict__ tok_of_row,
+                                                            int32_t* __restrict__ tiles, int32_t* __restrict__ err,
+                                                            int32_t* __restrict__ host_err) {
+  constexpr int NW = RT_ONE_THREADS / 64;
+  __shared__ int32_t hist[RT_ONE_MAX_EXPERTS];
+  __shared__ int32_t running[RT_ONE_MAX_EXPERTS];
+  __shared__ int32_t wcnt[NW][RT_ONE_MAX_EXPERTS];
+  __shared__ int32_t scan_c[RT_ONE_THREADS];
+  __shared__ int32_t scan_b[RT_ONE_THREADS];
+  __shared__ int32_t scan_s[RT_ONE_THREADS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  for (int e = tid; e < E; e += RT_ONE_THREADS) {
+    hist[e] = 0;
+    for (int q = 0; q < NW; ++q) wcnt[q][e] = 0;
+  }
+  __syncthreads();
+  int bad = 0;
+  for (int64_t s = tid; s < S; s += RT_ONE_THREADS) {
+    const int e = ids[s];
+    if (e >= 0 && e < E)
+      atomicAdd(&hist[e], 1);
+    else
+      bad = 1;
+  }
+  bad = __syncthreads_or(bad);
+  // offsets and tile table (the rule of route_scan)
+  const int c = (tid < E) ? hist[tid] : 0;
+  const int rem = big_on ? c % TILE_BIG : c;
+  const int nbig = big_on ? c / TILE_BIG + (rem > TILE_BIG / 2 ? 1 : 0) : 0;
+  const int nsmall = (big_on && rem > TILE_BIG / 2) ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
+  scan_c[tid] = c;
+  scan_b[tid] = (tid < E) ? nbig : 0;
+  scan_s[tid] = (tid < E) ? nsmall : 0;
+  __syncthreads();
+  for (int d = 1; d < RT_ONE_THREADS; d <<= 1) {
+    const int vc = (tid >= d) ? scan_c[tid - d] : 0;
+    const int vb = (tid >= d) ? scan_b[tid - d] : 0;
+    const int vs = (tid >= d) ? scan_s[tid - d] : 0;
+    __syncthreads();
+    scan_c[tid] += vc;
+    scan_b[tid] += vb;
+    scan_s[tid] += vs;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int off = scan_c[tid] - c;
+    const int b0 = scan_b[tid] - nbig;
+    const int s0 = scan_s[tid] - nsmall;
+    counts[tid] = c;
+    offsets[tid] = off;
+    running[tid] = off;
+    for (int i = 0; i < nbig; ++i) {
+      tiles[4 + 2 * (b0 + i)] = tid;
+      tiles[4 + 2 * (b0 + i) + 1] = off + i * TILE_BIG;
+    }
+    int32_t* small = tiles + 4 + 2 * max_big;
+    const int srow = off + nbig * TILE_BIG;
+    for (int i = 0; i < nsmall; ++i) {
+      small[2 * (s0 + i)] = tid;
+      small[2 * (s0 + i) + 1] = srow + i * TILE_SMALL;
+    }
+  }
+  if (tid == RT_ONE_THREADS - 1) {
+    offsets[E] = scan_c[tid];
+    tiles[0] = scan_b[tid];
+    tiles[1] = scan_s[tid];
+    tiles[2] = TILE_BIG;
+    tiles[3] = TILE_SMALL;
+  }
+  if (tid == 0) {
+    *err = bad;
+    if (host_err) __hip_atomic_store(host_err, bad, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+  // stable scatter, one round of RT_ONE_THREADS slots at a time
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rounds = (int)((S + RT_ONE_THREADS - 1) / RT_ONE_THREADS);
+  for (int r = 0; r < rounds; ++r) {
+    const int64_t s = (int64_t)r * RT_ONE_THREADS + tid;
+    int e = -1;
+    bool valid = false;
+    if (s < S) {
+      e = ids[s];
+      valid = (e >= 0 && e < E);
+      if (!valid) row_of_slot[s] = -1;
+    }
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    if (!valid) peers = 0;
+    const int rank = __popcll(peers & lt_mask);
+    const int cnt = __popcll(peers);
+    const int tag = (r + 1) << 16;
+    if (valid && rank == 0) wcnt[w][e] = tag | cnt;
+    __syncthreads();
+    if (valid) {
+      int row = running[e] + rank;
+      for (int q = 0; q < w; ++q) {
+        const int v = wcnt[q][e];
+        if ((v >> 16) == r + 1) row += v & 0xffff;
+      }
+      sorted_slot[row] = (int32_t)s;
+      tok_of_row[row] = (int32_t)(s / K);
+      row_of_slot[s] = row;
+    }
+    __syncthreads();
+    if (valid && rank == 0) atomicAdd(&running[e], cnt);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
-                        hipStream_t stream) {
+                        int32_t* host_err, hipStream_t stream) {
   const int nblk = (int)((S + RT_SLOTS - 1) / RT_SLOTS);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (S <= RT_ONE_MAX_SLOTS && E <= RT_ONE_MAX_EXPERTS) {
+    hipLaunchKernelGGL(route_one, dim3(1), dim3(RT_ONE_THREADS), 0, stream, ids, S, E, K, nbits, max_big, big_on,
+                       counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err, host_err);
+    return hipGetLastError();
+  }
   if (nblk > 0) {
     hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr);
   }
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, max_big,
-                     big_on, counts, offsets, blockbase, tiles, err);
+                     big_on, counts, offsets, blockbase, tiles, err, host_err);
   if (nblk > 0) {
     hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, nbits, offsets,
                        blockbase, K, sorted_slot, row_of_slot, tok_of_row);
