@@ -20,8 +20,10 @@ def bf(t):
     return t.to(torch.bfloat16).to(torch.float32)
 
 
-def f32_pipeline(p):
-    """Independent float32 pipeline: permute by expert, grouped matmuls, bf16 at R1..R9."""
+def f32_pipeline(p, up=None):
+    """Independent float32 pipeline: permute by expert, grouped matmuls, bf16 at R1..R9.
+
+    ``up(X, e)`` replaces the up-projection X . W1[e] (float32 result, before R1)."""
     f = lambda a: torch.tensor(np.asarray(a), dtype=torch.float32)  # noqa: E731
     x, W1, W2, dY = f(p["x"]), f(p["up_proj_weight"]), f(p["down_proj_weight"]), f(p["dY"])
     w = f(p["topk_weights"])
@@ -42,7 +44,7 @@ def f32_pipeline(p):
         tok = slots // K
         ws = w.reshape(-1)[slots][:, None]
         X = x[tok]
-        h = bf(X @ W1[e])
+        h = bf(X @ W1[e] if up is None else up(X, e))
         g, u = h[:, :I], h[:, I:]
         s = torch.sigmoid(g)
         a = bf(g * s * u)
@@ -115,3 +117,49 @@ def test_dev_flags_a_rounding_tie():
     assert g[0, 0] == 1.0 and gd[0, 0] == 2.0 ** -7      # the other neighbour, 1 + 2^-7, is admissible
     assert ud[0, 0] == 0.0                               # u = 1 exactly: no doubt
     assert ad[0, 0] > 0                                  # the doubt on g reaches a
+
+
+def _e4m3_rows(a):
+    """Per-row dynamic E4M3 quantisation with torch's float8 cast: (values, descale), float32 scale math."""
+    amax = a.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, torch.tensor(448.0) / amax, torch.ones_like(amax))
+    q = (a * scale).to(torch.float8_e4m3fn).to(torch.float64)
+    return q, (1.0 / scale).to(torch.float64)
+
+
+def _fp8_instruction_sum(qa, qb, group=8, keep_bits=13):
+    """A model of an FP8 matrix instruction's sum: the products of each group of ``group``
+    consecutive k are truncated toward zero to ``keep_bits`` bits below the group's largest
+    product, summed, and the group sums added into a float32 accumulator."""
+    n, H = qa.shape
+    t = qa[:, :, None] * qb[None, :, :]                          # [n, H, N], exact
+    t = t.reshape(n, H // group, group, -1)
+    m = np.abs(t).max(axis=2, keepdims=True)
+    quantum = np.where(m > 0, np.exp2(np.floor(np.log2(np.where(m > 0, m, 1.0))) - keep_bits), 1.0)
+    gs = (np.trunc(t / quantum) * quantum).sum(axis=2)           # [n, H/group, N]
+    acc = np.zeros((n, t.shape[-1]), np.float32)
+    for j in range(gs.shape[1]):
+        acc = (acc + gs[:, j].astype(np.float32)).astype(np.float32)
+    return acc
+
+
+@pytest.mark.parametrize("T,H,I,E,K,seed", [(128, 256, 64, 4, 2, 3), (96, 512, 64, 3, 3, 4)])
+def test_fp8_instruction_model_within_dev(T, H, I, E, K, seed):
+    """The FP8 variant's R1 deviation covers a matrix instruction that keeps only ~13 bits per group."""
+    p = problem(T, H, I, E, K, seed)
+    p["x"][::7] *= 16.0                                          # outlier rows
+    W1 = torch.tensor(p["up_proj_weight"], dtype=torch.float32)
+    wq, wds = zip(*[_e4m3_rows(W1[e].T) for e in range(E)])     # per-column quantisation
+
+    def up(X, e):
+        xq, xds = _e4m3_rows(X)
+        acc = _fp8_instruction_sum(xq.numpy(), wq[e].T.numpy())
+        return (torch.tensor(acc) * xds.float()) * wds[e].float().reshape(1, -1)
+
+    m = MoEFFN(**p, mode="faithful", gmm1="fp8")
+    y, yd = m.forward_dev()
+    (dx, dw, dW1, dW2), (dxd, dwd, dW1d, dW2d) = m.backward_dev()
+    got = f32_pipeline(p, up)
+    for name, g, r, d in zip(("y", "dx", "dw", "dW1", "dW2"), got, (y, dx, dw, dW1, dW2), (yd, dxd, dwd, dW1d, dW2d)):
+        bad = np.abs(g - r) > d
+        assert not bad.any(), "%s: %d entries beyond dev" % (name, bad.sum())
