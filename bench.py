@@ -7,7 +7,7 @@ synthetic input already resident in HBM, through the C ABI of libhmm.
 
 Prints ONE JSON line on stdout; details go to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8]
 
 Timing: W untimed warm-up steps (the first one's time is reported as
 first_step_ms), then K steps between two synchronisations, timed with HIP
@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -62,8 +63,10 @@ def recorded_traffic(workload, kernel):
 
 
 def stage_work(stage, T, H, I, E, K):
-    """Algorithmic work of one launch of a stage: (bound, amount, unit)."""
+    """Algorithmic work of one launch of a stage: (bound, amount, unit, peak)."""
     S = T * K
+    if stage == "gmm1_fp8_swiglu":
+        return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
     flops = {
         "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
         "gmm2": 2 * S * I * H,          # [S,I] x [I,H]
@@ -73,17 +76,20 @@ def stage_work(stage, T, H, I, E, K):
         "dw1": 4 * S * H * I,           # [H,S] x [S,2I]
     }
     if stage in flops:
-        return "mfma", flops[stage], "TFLOP/s"
+        return "mfma", flops[stage], "TFLOP/s", PEAK_BF16_TFLOPS
     nbytes = {
         # read K gathered rows per token + row index + weight, write one row
         "combine": S * H * 2 + S * 8 + T * H * 2,
         "combine_dx": S * H * 2 + S * 4 + T * H * 2,   # (+ d_topk_weights partials, small)
         # ids read twice, histograms, sorted_slot + row_of_slot written
         "route": S * 4 * 2 + S * 8,
+        # FP8 quantisers: read the bf16 operand once, write its codes and descales
+        "quant_x": T * H * 2 + T * H + T * 4,
+        "quant_w1": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * 4,
     }
     if stage in nbytes:
-        return "hbm", nbytes[stage], "GB/s"
-    return None, 0, None
+        return "hbm", nbytes[stage], "GB/s", PEAK_HBM_GBS
+    return None, 0, None, None
 
 
 class Runner:
@@ -114,7 +120,8 @@ class Runner:
         self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
         flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
-        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, _lib.HMM_BF16, flags, 0)
+        gmm1 = _lib.HMM_FP8_E4M3 if spec.get("gmm1", "bf16") == "fp8" else _lib.HMM_BF16
+        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, gmm1, flags, 0)
         fws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
         _lib.check(self.lib.hmm_forward_sizes(ctypes.byref(self.prob), ctypes.byref(fws), ctypes.byref(sv)))
         _lib.check(self.lib.hmm_backward_sizes(ctypes.byref(self.prob), ctypes.byref(bws)))
@@ -171,7 +178,7 @@ def cpu_baseline(spec, seed, budget_s=12.0):
                  topk_weights=inp["topk_weights"][:tp], up_proj_weight=synth.bits_to_f32(inp["up_proj_weight"]),
                  down_proj_weight=synth.bits_to_f32(inp["down_proj_weight"]), dY=synth.bits_to_f32(inp["dY"][:tp]))
         t0 = time.perf_counter()
-        m = MoEFFN(**d, mode="faithful")
+        m = MoEFFN(**d, mode="faithful", gmm1=spec.get("gmm1", "bf16"))
         m.forward()
         m.backward()
         return time.perf_counter() - t0
@@ -219,10 +226,7 @@ def main():
         log("[bench] copied %d MiB 5 times (reads %d KiB, writes %d KiB per copy)" % (n >> 20, n >> 10, n >> 10))
         return
     spec = dict(synth.WORKLOADS[args.workload])
-    if spec.get("gmm1", "bf16") != "bf16":
-        print("workload %s needs the FP8 up-projection, which this build does not run yet" % args.workload,
-              file=sys.stderr)
-        sys.exit(1)
+    fp8 = spec.get("gmm1", "bf16") == "fp8"
     T, H, I, E, K = (spec[k] for k in "THIEK")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -250,16 +254,17 @@ def main():
     log("[bench] profiled pass %.4f ms/step; %d launches untimed" % (prof_ms / args.steps, dropped))
     S = T * K
     gemm_ms = 0.0
+    gemm_ms_at_peak = 0.0          # time the products would take at their dtype's peak
     rows = []
     for name, (n, tot) in sorted(stages.items(), key=lambda kv: -kv[1][1]):
         avg = tot / max(n, 1)
-        bound, work, unit = stage_work(name, T, H, I, E, K)
+        bound, work, unit, peak = stage_work(name, T, H, I, E, K)
         rate = (work / (avg * 1e-3) / (1e12 if bound == "mfma" else 1e9)) if bound else None
-        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
         if bound == "mfma":
             gemm_ms += tot / args.steps
-        rows.append((name, n, avg, bound, work, rate, unit, (rate / peak) if rate else None))
-        log("[bench]   %-12s launches %4d  avg %9.4f ms  %s" % (
+            gemm_ms_at_peak += work / (peak * 1e12) * 1e3 * n / args.steps
+        rows.append((name, n, avg, bound, work, rate, unit, (rate / peak) if rate else None, peak))
+        log("[bench]   %-16s launches %4d  avg %9.4f ms  %s" % (
             name, n, avg, ("%.1f %s (%.1f%% of peak)" % (rate, unit, 100 * rate / peak)) if rate else ""))
     dom = max((x for x in rows if x[3]), key=lambda x: x[2] * x[1])
     gemm_flops = 18 * S * H * I
@@ -268,7 +273,7 @@ def main():
         "kernel": dom[0],
         "bound": dom[3],
         "achieved": round(dom[5], 3),
-        "peak": PEAK_BF16_TFLOPS if dom[3] == "mfma" else PEAK_HBM_GBS,
+        "peak": dom[8],
         "unit": dom[6],
         "frac": round(dom[7], 5),
         "algorithmic": dom[4],
@@ -293,12 +298,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
                    "routing": spec.get("routing"), "seed": args.seed, "validate_ids": not args.no_validate},
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
-        "gemm_frac_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 5) if gemm_tflops else None,
+        "gemm_frac_peak": round(gemm_ms_at_peak / gemm_ms, 5) if gemm_ms > 0 else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

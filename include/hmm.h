@@ -98,7 +98,9 @@ typedef enum hmm_dtype {
  *   gmm1_dtype  HMM_BF16, or HMM_FP8_E4M3 for the FP8 up-projection: tokens
  *               are quantised per row, the up-projection weight per
  *               (expert, column), both as scale = 448 / max|.| (the per-token
- *               dynamic quantisation of MoeDistributeDispatchV2, case 3).
+ *               dynamic quantisation of MoeDistributeDispatchV2, case 3);
+ *               H must then be a multiple of 128.  Only the up-projection
+ *               changes: the rest of the forward and the backward stay bf16.
  *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward. */
 typedef struct hmm_problem {
   int64_t T, H, I, E, K;
@@ -178,6 +180,25 @@ hmm_status hmm_route_workspace_size(const hmm_problem* p, size_t* workspace_byte
 hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
                      int32_t* sorted_slot, int32_t* row_of_slot, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* FP8 E4M3 quantisation stages of the FP8 up-projection, exported for tests
+ * and tools (hmm_forward runs the same kernels internally).  Per-token dynamic
+ * quantisation as in MoeDistributeDispatchV2 (function description, case 3):
+ * in float32, scale = 448 / max|row| (1 for an all-zero row), the code is the
+ * round-to-nearest-even E4M3 (OCP e4m3fn) cast of value * scale, and the
+ * stored factor is descale = 1 / scale.
+ *   hmm_quant_rows_fp8: x bf16 [T,H] -> xq [T,H] E4M3 bytes, descale [T] f32.
+ *   hmm_quant_cols_fp8: w bf16 [E,H,N] -> wq [E,H,N] E4M3 bytes, descale [E,N]
+ *                       f32, one scale per (expert, column), the maximum taken
+ *                       over H; needs hmm_quant_cols_workspace_size bytes of
+ *                       workspace (column maxima per chunk of 256 rows).
+ * T >= 0, E >= 1; H and N multiples of 8, positive; all arrays below 4 GiB.
+ * Pointers are device pointers, 16-byte aligned, caller-owned; errors as for
+ * every other call, checked before any launch. */
+hmm_status hmm_quant_rows_fp8(const void* x, int64_t T, int64_t H, uint8_t* xq, float* descale, void* stream);
+hmm_status hmm_quant_cols_workspace_size(int64_t E, int64_t H, int64_t N, size_t* workspace_bytes);
+hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* descale,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Names of statuses, and the calling thread's last error text. */
 const char* hmm_status_string(hmm_status s);

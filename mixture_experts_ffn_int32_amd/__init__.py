@@ -7,8 +7,8 @@ on the GPU, with a fused backward, through the C ABI of ``include/hmm.h``
 load the library; the first call does, and raises if it has not been built.
 """
 
-from .moe import (HyperMegaMoEFunction, backward_from_saved, forward_with_saved, hyper_mega_moe, route,  # noqa: F401
-                  saved_views)
+from .moe import (HyperMegaMoEFunction, backward_from_saved, forward_with_saved, hyper_mega_moe,  # noqa: F401
+                  quantize_cols_fp8, quantize_rows_fp8, route, saved_views)
 
 __all__ = ["hyper_mega_moe", "HyperMegaMoEFunction", "route", "forward_with_saved", "backward_from_saved",
-           "saved_views"]
+           "saved_views", "quantize_rows_fp8", "quantize_cols_fp8"]

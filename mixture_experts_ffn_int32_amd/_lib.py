@@ -31,7 +31,8 @@ TILE_FLAGS = {"auto": 0, "large": HMM_FLAG_TILES_LARGE, "narrow": HMM_FLAG_TILES
 EXPORTS = (
     "hmm_forward_sizes", "hmm_saved_layout_of", "hmm_forward", "hmm_backward_sizes", "hmm_backward",
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
-    "hmm_profile_enable", "hmm_profile_read",
+    "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
+    "hmm_quant_cols_fp8",
 )
 
 
@@ -65,6 +66,9 @@ _SIGS = {
     "hmm_backward": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _SZ, _P],
     "hmm_route_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
     "hmm_route": [_PROB, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "hmm_quant_rows_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "hmm_quant_cols_workspace_size": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_SZ)],
+    "hmm_quant_cols_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _SZ, _P],
     "hmm_status_string": [ctypes.c_int],
     "hmm_last_error_message": [],
     "hmm_build_info": [],

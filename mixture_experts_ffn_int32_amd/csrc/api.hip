@@ -36,6 +36,7 @@ inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 struct Dims {
   int64_t T, H, I, E, K, S;
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
+  bool fp8;    // FP8 E4M3 up-projection
 };
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
@@ -67,13 +68,16 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
       if (x > lim) return fail(HMM_ERR_UNSUPPORTED, "an operand array exceeds 4 GiB (%lld bytes)", (long long)x);
   }
   if (p->out_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is not implemented");
-  if (p->gmm1_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "gmm1_dtype HMM_FP8_E4M3 is not implemented");
+  if (p->gmm1_dtype == HMM_FP8_E4M3 && p->H % 128)
+    return fail(HMM_ERR_BAD_SHAPE, "gmm1_dtype HMM_FP8_E4M3 needs H to be a multiple of 128 (got %lld)",
+                (long long)p->H);
   d->T = p->T;
   d->H = p->H;
   d->I = p->I;
   d->E = p->E;
   d->K = p->K;
   d->S = p->T * p->K;
+  d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3;
   d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
@@ -129,15 +133,25 @@ RouteScratch route_scratch(const Dims& d, size_t base) {
   return r;
 }
 
+// Forward scratch: routing scratch, the expert outputs o [S,H] and, for the FP8
+// up-projection, the quantised operands with their descales and the column
+// maxima of the weight quantisation.
 struct FwdWork {
   RouteScratch rs;
-  size_t o, total;
+  size_t o, xq, dsx, wq, dsw, pmax, total;
 };
 FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
   w.rs = route_scratch(d, 0);
   size_t o = w.rs.total;
   w.o = o; o += up(d.S * d.H * 2);
+  if (d.fp8) {
+    w.xq = o;   o += up(d.T * d.H);
+    w.dsx = o;  o += up(d.T * 4);
+    w.wq = o;   o += up(d.E * d.H * 2 * d.I);
+    w.dsw = o;  o += up(d.E * 2 * d.I * 4);
+    w.pmax = o; o += up(hmm::quant_cols_chunks(d.H) * d.E * 2 * d.I * 4);
+  }
   w.total = o;
   return w;
 }
@@ -282,7 +296,8 @@ const char* hmm_status_string(hmm_status s) {
 const char* hmm_last_error_message(void) { return g_last_error.c_str(); }
 
 const char* hmm_build_info(void) {
-  return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16; 256x256x64 and 64x256x64 tiles, grouped rasterisation";
+  return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16 and fp8 e4m3 MFMA 32x32x64; 256x256, 64x256 and 64x64 tiles, "
+         "grouped rasterisation";
 }
 
 hmm_status hmm_forward_sizes(const hmm_problem* p, size_t* workspace_bytes, size_t* saved_bytes) {
@@ -353,6 +368,52 @@ hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* cou
   return finish_id_check(d);
 }
 
+namespace {
+hmm_status quant_dims(int64_t E, int64_t H, int64_t N) {
+  if (E < 1 || H < 8 || N < 8 || H % 8 || N % 8)
+    return fail(HMM_ERR_BAD_SHAPE, "quantisation needs E >= 1 and H, N positive multiples of 8 (E=%lld H=%lld N=%lld)",
+                (long long)E, (long long)H, (long long)N);
+  if (E * H * N > (int64_t)0xFFFFFF00 || E > (int64_t)0x7fffffff)
+    return fail(HMM_ERR_UNSUPPORTED, "quantised array exceeds 4 GiB");
+  return HMM_OK;
+}
+}  // namespace
+
+hmm_status hmm_quant_rows_fp8(const void* x, int64_t T, int64_t H, uint8_t* xq, float* descale, void* stream) {
+  if (T < 0 || T > (int64_t)0x7fffffff) return fail(HMM_ERR_BAD_SHAPE, "T must be in [0, 2^31) (got %lld)", (long long)T);
+  hmm_status s = quant_dims(T > 0 ? T : 1, H, 8);
+  if (s != HMM_OK) return s;
+  const bool ne = T > 0;
+  if ((s = need(x, ne, "x")) || (s = need(xq, ne, "xq")) || (s = need(descale, ne, "descale"))) return s;
+  Stage stage("quant_x", (hipStream_t)stream);
+  const hipError_t e = hmm::launch_quant_rows_fp8((const uint16_t*)x, T, H, xq, descale, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "token quantisation launch");
+}
+
+hmm_status hmm_quant_cols_workspace_size(int64_t E, int64_t H, int64_t N, size_t* workspace_bytes) {
+  hmm_status s = quant_dims(E, H, N);
+  if (s != HMM_OK) return s;
+  if (!workspace_bytes) return fail(HMM_ERR_NULL_POINTER, "size output is NULL");
+  *workspace_bytes = up(hmm::quant_cols_chunks(H) * E * N * 4);
+  return HMM_OK;
+}
+
+hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* descale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need_ws = 0;
+  hmm_status s = hmm_quant_cols_workspace_size(E, H, N, &need_ws);
+  if (s != HMM_OK) return s;
+  if ((s = need(w, true, "w")) || (s = need(wq, true, "wq")) || (s = need(descale, true, "descale")) ||
+      (s = need(workspace, true, "workspace")))
+    return s;
+  if (workspace_bytes < need_ws)
+    return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need_ws);
+  Stage stage("quant_w1", (hipStream_t)stream);
+  const hipError_t e =
+      hmm::launch_quant_cols_fp8((const uint16_t*)w, E, H, N, (float*)workspace, wq, descale, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
+}
+
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
                        const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,
                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -387,10 +448,29 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   uint16_t* aw = at<uint16_t>(saved, L.aw);
   uint16_t* o = at<uint16_t>(workspace, W.o);
   hipError_t e;
-  {
+  if (d.fp8) {
+    uint8_t* xq = at<uint8_t>(workspace, W.xq);
+    uint8_t* wq = at<uint8_t>(workspace, W.wq);
+    float* dsx = at<float>(workspace, W.dsx);
+    float* dsw = at<float>(workspace, W.dsw);
+    {
+      Stage stage("quant_x", st);
+      e = hmm::launch_quant_rows_fp8((const uint16_t*)x, d.T, d.H, xq, dsx, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "token quantisation launch");
+    {
+      Stage stage("quant_w1", st);
+      e = hmm::launch_quant_cols_fp8((const uint16_t*)up_w, d.E, d.H, 2 * d.I, at<float>(workspace, W.pmax), wq, dsw,
+                                     st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
+    {
+      Stage stage("gmm1_fp8_swiglu", st);
+      e = hmm::launch_gmm1_fp8(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
+    }
+  } else {
     Stage stage("gmm1_swiglu", st);
-    e = hmm::launch_gmm1_swiglu(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a,
-                                         aw, st);
+    e = hmm::launch_gmm1_swiglu(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw, st);
   }
   if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
   {

@@ -12,6 +12,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 // bfloat16 <-> float.  The float -> bf16 cast is IEEE round-to-nearest-even
 // (one v_cvt_pk_bf16_f32 on gfx950).

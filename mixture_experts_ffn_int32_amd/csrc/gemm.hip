@@ -41,6 +41,7 @@
 // and workgroup ids are remapped so that the consecutive logical tiles of such
 // a group run on one XCD and share its L2.
 #include "device.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace hmm {
@@ -48,7 +49,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;   // pitch of a K-major LDS tile (elements)
-constexpr int GROUP_M = 8;    // row tiles per rasterisation group
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Cfg {
@@ -69,32 +69,6 @@ typedef Cfg<64, 256, 1, 4> Small;
 typedef Cfg<64, 64, 2, 2> Narrow;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  // nblocks is a multiple of 8; workgroups are dealt to the 8 XCDs round robin
-  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
-}
-
-// logical index -> (row tile r, column tile c) of an R x C grid, walking groups
-// of GROUP_M row tiles column by column (a bijection on [0, R*C))
-__device__ __forceinline__ void raster(int idx, int R, int C, int& r, int& c) {
-  const int per_group = GROUP_M * C;
-  const int g = idx / per_group;
-  const int first = g * GROUP_M;
-  const int gsz = min(GROUP_M, R - first);
-  const int w = idx - g * per_group;
-  r = first + w % gsz;
-  c = w / gsz;
-}
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-// buffer resource over [base, base + bytes); bytes < 2^32
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
 
 // LDS placement of 16-byte chunk c of a tile with R rows (K-major) or R columns (M/N-major)
 template <bool KMAJ, int R>

@@ -1,0 +1,313 @@
+// FP8 (E4M3) up-projection with the SwiGLU epilogue, for the FP8 forward
+// variant: per-token dynamic quantisation of the tokens (MoeDistributeDispatchV2,
+// case 3) and per-(expert, column) quantisation of the up-projection weight
+// feed v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 block scales); the float32
+// accumulator is dequantised with the row and column factors before the bf16
+// rounding of h, then a = silu(g) u and aw = w a as in the bf16 product.
+//
+// Same structure as the bf16 products: the routing's big (256-row) and small
+// (64-row) tile tables, or 64x64 tiles on small problems; LDS double buffered
+// with loads three K steps (of 128 bytes) ahead; grouped rasterisation with the
+// XCD remap.  A (tokens, K-major, gathered) sits in LDS as [row][k] (pitch 144
+// bytes) and is read 32 bytes per lane with two ds_read_b128; B (weights,
+// N-major) sits as [k][n] (pitch BN+32 bytes, so the 8 k rows a 32-lane pass
+// of ds_read_b64_tr_b8 touches fall in distinct banks) and is read with four
+// transposing reads of 8 k each.  Lane l of a 32x32x64 operand holds row/column
+// l % 32 and k = 32 (l / 32) + 0..31.
+#include "device.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace hmm {
+namespace {
+
+constexpr int BKB = 128;   // k per step (bytes = fp8 elements)
+constexpr int LDKB = 144;  // pitch of a K-major LDS tile (bytes)
+
+// SETS: register sets of prefetched global data (2: loads run three K steps
+// ahead of the MFMAs, 1: two steps; the 256x256 tile has no registers for two).
+template <int BM_, int BN_, int WM_, int WN_, int SETS_>
+struct F8Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, SETS = SETS_;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MB = TM / 32, NB = TN / 32;
+  static constexpr int CA = BM * BKB / 16 / NTHR;
+  static constexpr int CB = BN * BKB / 16 / NTHR;
+  static constexpr int LDB = BN + 32;
+  static constexpr int A_BYTES = BM * LDKB, B_BYTES = BKB * LDB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static_assert(CA >= 1 && CB >= 1 && STAGE % 16 == 0, "tile shape");
+};
+typedef F8Cfg<256, 256, 2, 4, 1> Big8;
+typedef F8Cfg<64, 256, 1, 4, 2> Small8;
+typedef F8Cfg<64, 64, 2, 2, 2> Narrow8;
+
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+template <class C>
+__device__ __forceinline__ int acc_row8(int wm, int mb, int r, int lane) {
+  return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+template <class C, bool SMALL>
+struct Gmm1F8 {
+  struct Args {
+    RowGroups g;
+    const uint8_t* xq;   // [T][H] E4M3
+    const float* dsx;    // [T]
+    const uint8_t* wq;   // [E][H][2I] E4M3
+    const float* dsw;    // [E][2I]
+    const float* tw;
+    int64_t T, H, I;
+    uint16_t *h, *a, *aw;
+    int n_ntiles;
+  };
+  const Args* ar;
+  int e, row0, rows, nt, i0, nk;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    const RowGroups& g = A.g;
+    const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+    if (logical >= R * A.n_ntiles) return false;
+    int j;
+    raster(logical, R, A.n_ntiles, j, nt);
+    if (j >= g.tiles[SMALL ? 1 : 0]) return false;
+    const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
+    e = tab[2 * j];
+    row0 = tab[2 * j + 1];
+    rows = min(C::BM, g.offsets[e + 1] - row0);
+    i0 = nt * (C::BN / 2);
+    const int tid = threadIdx.x;
+    ra_ = make_rsrc(A.xq, A.T * A.H);
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int p = row0 + min(c >> 3, rows - 1);
+      aoff[i] = (uint32_t)((int64_t)g.tok_of_row[p] * A.H + (c & 7) * 16);
+    }
+    rb_ = make_rsrc(A.wq + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I);
+    constexpr int CPR = C::BN / 16, HALF = C::BN / 32;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c16 = c % CPR;
+      const int64_t gi = min((int64_t)(i0 + (c16 % HALF) * 16), A.I - 16);  // gate column (clamped)
+      const int64_t col = (c16 < HALF) ? gi : A.I + gi;
+      boff[i] = (uint32_t)(kr * 2 * A.I + col);
+    }
+    nk = (int)(A.H / BKB);
+    return true;
+  }
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BKB);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    const uint32_t so = (uint32_t)(kt * BKB * 2 * ar->I);
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
+  }
+
+  // g, u = bf16(acc * dsx[token] * dsw[column]) staged in LDS, then as the bf16
+  // product's epilogue: 8 columns of one row per thread, 16-byte stores.
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint8_t* smemb) {
+    constexpr int LD = C::BN + 8;
+    static_assert(C::BM * LD * 2 + (2 * C::BM + C::BN) * 4 <= 2 * C::STAGE, "staging must fit");
+    uint16_t* smem = reinterpret_cast<uint16_t*>(smemb);
+    float* wrow = reinterpret_cast<float*>(smemb + C::BM * LD * 2);
+    float* rsc = wrow + C::BM;
+    float* csc = rsc + C::BM;
+    const int tid = threadIdx.x;
+    const int64_t I = ar->I;
+    for (int t = tid; t < C::BM; t += C::NTHR) {
+      const bool v = t < rows;
+      wrow[t] = v ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
+      rsc[t] = v ? ar->dsx[ar->g.tok_of_row[row0 + t]] : 0.f;
+    }
+    for (int t = tid; t < C::BN; t += C::NTHR) {
+      const int64_t gi = i0 + (t % (C::BN / 2));
+      const int64_t col = (t < C::BN / 2) ? gi : I + gi;
+      csc[t] = (gi < I) ? ar->dsw[(int64_t)e * 2 * I + col] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row8<C>(wm, mb, r, lane);
+          const int col = wn * C::TN + nb * 32 + (lane & 31);
+          smem[row * LD + col] = f2bf(acc[mb][nb][r] * rsc[row] * csc[col]);
+        }
+    __syncthreads();
+    constexpr int CPR = C::BN / 16;
+    for (int c = tid; c < C::BM * CPR; c += C::NTHR) {
+      const int row = c / CPR, c8 = c % CPR;
+      const int64_t i = i0 + c8 * 8;
+      if (row >= rows || i >= I) continue;
+      const int64_t p = row0 + row;
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(smem + row * LD + C::BN / 2 + c8 * 8);
+      float g[8], u[8], av[8], aw[8];
+      unpack8(gv, g);
+      unpack8(uv, u);
+      const float w = wrow[row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[j] = round_bf(g[j] * sigmoidf_(g[j]) * u[j]);
+        aw[j] = w * av[j];
+      }
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
+      *reinterpret_cast<u32x4*>(ar->a + p * I + i) = pack8(av);
+      *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
+    }
+  }
+};
+
+template <class C, class P>
+__device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const int c = tid + i * C::NTHR;
+    *reinterpret_cast<u32x4*>(st + (c >> 3) * LDKB + (c & 7) * 16) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + i * C::NTHR;
+    *reinterpret_cast<u32x4*>(st + C::A_BYTES + (c / (C::BN / 16)) * C::LDB + (c % (C::BN / 16)) * 16) = rb[i];
+  }
+}
+
+template <class P>
+__global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P::Args args) {
+  typedef typename P::Cc C;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  P pol;
+  if (!pol.init(args, xcd_remap(blockIdx.x, gridDim.x))) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int nk = pol.nk;
+  f32x16 acc[C::MB][C::NB];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (nk > 0) {
+    constexpr int AHEAD = C::SETS + 1;  // K steps between a load and its MFMAs
+    u32x4 ra0[C::CA], rb0[C::CB], ra1[C::SETS == 2 ? C::CA : 1], rb1[C::SETS == 2 ? C::CB : 1];
+    pol.load_a(0, ra0);
+    pol.load_b(0, rb0);
+    if constexpr (C::SETS == 2) {
+      if (nk > 1) {
+        pol.load_a(1, ra1);
+        pol.load_b(1, rb1);
+      }
+    }
+    store_stage8<C, P>(smem, ra0, rb0);
+    if (nk > AHEAD - 1) {
+      pol.load_a(AHEAD - 1, ra0);
+      pol.load_b(AHEAD - 1, rb0);
+    }
+    __syncthreads();
+    auto step = [&](int kt, auto& nxa, auto& nxb) {
+      if (kt + 1 < nk) store_stage8<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
+      if (kt + AHEAD < nk) {
+        pol.load_a(kt + AHEAD, nxa);
+        pol.load_b(kt + AHEAD, nxb);
+      }
+      const uint8_t* sa = smem + (kt & 1) * C::STAGE;
+      const uint8_t* sb = sa + C::A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < BKB / 64; ++kk) {
+        // B fragments for the whole wave tile, then one A fragment at a time
+        // (keeps the live fragment registers at NB + 1 operands)
+        i32x8 fb[C::NB];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const int i = lane & 15;
+          const int n = wn * C::TN + nb * 32 + 16 * ((lane >> 4) & 1) + 8 * (i & 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = kk * 64 + 32 * (lane >> 5) + 8 * q + (i >> 1);
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + k * C::LDB + n));
+            fb[nb][2 * q] = v[0];
+            fb[nb][2 * q + 1] = v[1];
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+          const uint8_t* p = sa + (wm * C::TM + mb * 32 + (lane & 31)) * LDKB + kk * 64 + 32 * (lane >> 5);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+          const i32x8 fa = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, 127, 0, 127);
+        }
+      }
+      __syncthreads();
+    };
+    if constexpr (C::SETS == 2) {
+      int kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        step(kt, ra1, rb1);
+        step(kt + 1, ra0, rb0);
+      }
+      if (kt < nk) step(kt, ra1, rb1);
+    } else {
+      for (int kt = 0; kt < nk; ++kt) step(kt, ra0, rb0);
+    }
+  }
+  pol.epilogue(acc, wm, wn, lane, smem);
+}
+
+template <class C, bool SMALL>
+struct Gmm1F8K : Gmm1F8<C, SMALL> {
+  typedef C Cc;
+  static constexpr int NTHR_ = C::NTHR;
+};
+
+template <class P>
+hipError_t launch8(const typename P::Args& args, int64_t logical_blocks, hipStream_t stream) {
+  if (logical_blocks <= 0) return hipSuccess;
+  const int64_t g = (logical_blocks + 7) / 8 * 8;
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_fp8_kernel<P>, dim3((unsigned)g), dim3(P::NTHR_), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <class C, bool SMALL>
+hipError_t launch_one(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
+                      const float* tw, int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw,
+                      hipStream_t stream) {
+  typedef Gmm1F8K<C, SMALL> P;
+  const int nnt = (int)((I + C::BN / 2 - 1) / (C::BN / 2));
+  typename P::Args A{g, xq, dsx, wq, dsw, tw, g.T, H, I, h, a, aw, nnt};
+  return launch8<P>(A, (SMALL ? g.max_small : g.max_big) * nnt, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
+                           const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                           uint16_t* aw, hipStream_t stream) {
+  if (g.narrow) return launch_one<Narrow8, true>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
+  hipError_t e = launch_one<Big8, false>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
+  if (e != hipSuccess) return e;
+  return launch_one<Small8, true>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
+}
+
+}  // namespace hmm

@@ -84,6 +84,19 @@ hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t
 // number of d_topk_weights partial columns written by launch_act_grad for a given I
 int act_grad_dw_cols(int64_t I, bool narrow);
 
+// FP8 E4M3 quantisation (quant.hip): per-token rows of x, per-(expert, column)
+// columns of a weight [E][H][N]; descales are 1 / scale in float32.
+hipError_t launch_quant_rows_fp8(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, float* dsx,
+                                 hipStream_t stream);
+int64_t quant_cols_chunks(int64_t H);  // pmax holds quant_cols_chunks(H) * E * N floats
+hipError_t launch_quant_cols_fp8(const uint16_t* w, int64_t E, int64_t H, int64_t N, float* pmax, uint8_t* wq,
+                                 float* dsw, hipStream_t stream);
+// FP8 up-projection + SwiGLU (gemm_fp8.hip): h = bf16((xq[tok] . wq[e]) dsx[tok] dsw[e]), then as
+// launch_gmm1_swiglu.  H must be a multiple of 128.
+hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
+                           const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                           uint16_t* aw, hipStream_t stream);
+
 // pointwise (pointwise.hip)
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
                           int K, int64_t H, uint16_t* out, hipStream_t stream);

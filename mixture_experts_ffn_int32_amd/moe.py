@@ -57,15 +57,24 @@ def _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight):
     return T, H, I, E, topk_ids.shape[1]
 
 
+GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3}
+
+
+def _gmm1_code(gmm1_dtype):
+    if gmm1_dtype not in GMM1_DTYPES:
+        raise ValueError("gmm1_dtype must be one of %s (got %r)" % (sorted(GMM1_DTYPES), gmm1_dtype))
+    return GMM1_DTYPES[gmm1_dtype]
+
+
 def _contig(t, dtype=None):
     if dtype is not None and t.dtype != dtype:
         t = t.to(dtype)
     return t.contiguous()
 
 
-def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags):
+def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16):
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags)
+    prob = _problem(T, H, I, E, K, flags, gmm1_dtype=gmm1)
     ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
     _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
     dev = x.device
@@ -77,9 +86,9 @@ def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags):
     return y, saved
 
 
-def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags):
+def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16):
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags)
+    prob = _problem(T, H, I, E, K, flags, gmm1_dtype=gmm1)
     ws = ctypes.c_size_t()
     _lib.check(lib.hmm_backward_sizes(ctypes.byref(prob), ctypes.byref(ws)))
     dev = x.device
@@ -98,7 +107,7 @@ class HyperMegaMoEFunction(torch.autograd.Function):
     """Forward calls hmm_forward and keeps the saved buffer; backward calls hmm_backward."""
 
     @staticmethod
-    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags):
+    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags, gmm1):
         T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
         x_ = _contig(x)
         ids = _contig(topk_ids, torch.int32)
@@ -106,23 +115,24 @@ class HyperMegaMoEFunction(torch.autograd.Function):
         W1 = _contig(up_proj_weight)
         W2 = _contig(down_proj_weight)
         with torch.cuda.device(x.device):
-            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags)
+            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags, gmm1)
         ctx.save_for_backward(x_, ids, w, W1, W2, saved)
-        ctx.dims = (T, H, I, E, K, flags)
+        ctx.dims = (T, H, I, E, K, flags, gmm1)
         ctx.w_dtype = topk_weights.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
         x_, ids, w, W1, W2, saved = ctx.saved_tensors
-        T, H, I, E, K, flags = ctx.dims
+        T, H, I, E, K, flags, gmm1 = ctx.dims
         dy = _contig(dy, torch.bfloat16)
         with torch.cuda.device(x_.device):
-            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags)
-        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None
+            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1)
+        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None, None
 
 
-def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True):
+def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True,
+                   gmm1_dtype="bf16"):
     """y [T,H] = sum_k topk_weights[t,k] * SwiGLU-FFN_{topk_ids[t,k]}(x[t]), on the GPU.
 
     x bf16 [T,H]; topk_ids int32/int64 [T,K] (0 <= id < E); topk_weights float [T,K];
@@ -130,10 +140,14 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     bf16 [E,I,H].  Differentiable in x, topk_weights and both weights.
     ``validate_ids`` checks the ids on the device before the matrix products
     (one small device-to-host read-back) and raises ValueError if one is out
-    of range.
+    of range.  ``gmm1_dtype="fp8"`` runs the up-projection in FP8 E4M3: each
+    token row and each (expert, column) of up_proj_weight is quantised with a
+    dynamic per-row / per-column scale (H must then be a multiple of 128); the
+    rest of the forward and the whole backward stay bf16.
     """
     flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
-    return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags)
+    return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags,
+                                      _gmm1_code(gmm1_dtype))
 
 
 # ----------------------------------------------------------------------------- stage entry points (tests, tools)
@@ -163,6 +177,37 @@ def route(topk_ids, E, validate_ids=True):
     return out
 
 
+def quantize_rows_fp8(x):
+    """Per-token FP8 E4M3 quantisation of x bf16 [T,H]: (codes uint8 [T,H], descale float32 [T])."""
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [T,H] tensor on a HIP device")
+    x = _contig(x)
+    T, H = x.shape
+    q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    ds = torch.empty(T, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.load().hmm_quant_rows_fp8(_ptr(x), T, H, _ptr(q), _ptr(ds), _stream(x.device)))
+    return q, ds
+
+
+def quantize_cols_fp8(w):
+    """Per-(expert, column) FP8 E4M3 quantisation of w bf16 [E,H,N]: (codes uint8 [E,H,N], descale float32 [E,N])."""
+    if w.device.type != "cuda" or w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("w must be a bf16 [E,H,N] tensor on a HIP device")
+    w = _contig(w)
+    E, H, N = w.shape
+    lib = _lib.load()
+    ws = ctypes.c_size_t()
+    _lib.check(lib.hmm_quant_cols_workspace_size(E, H, N, ctypes.byref(ws)))
+    q = torch.empty((E, H, N), dtype=torch.uint8, device=w.device)
+    ds = torch.empty((E, N), dtype=torch.float32, device=w.device)
+    work = torch.empty(ws.value, dtype=torch.uint8, device=w.device)
+    with torch.cuda.device(w.device):
+        _lib.check(lib.hmm_quant_cols_fp8(_ptr(w), E, H, N, _ptr(q), _ptr(ds), _ptr(work), ws.value,
+                                          _stream(w.device)))
+    return q, ds
+
+
 def saved_views(saved, T, H, I, E, K, tiles="auto"):
     """Typed views of the arrays a forward recorded in its saved buffer."""
     lib = _lib.load()
@@ -189,7 +234,7 @@ def saved_views(saved, T, H, I, E, K, tiles="auto"):
 
 
 def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True,
-                       tiles="auto"):
+                       tiles="auto", gmm1_dtype="bf16"):
     """Forward without autograd; returns (y, saved buffer) for stage-level checks.
 
     ``tiles`` forces the tiling of the grouped products ("auto", "large" or
@@ -199,13 +244,16 @@ def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weig
     flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | _lib.TILE_FLAGS[tiles]
     with torch.cuda.device(x.device):
         return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
-                            _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags)
+                            _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags,
+                            _gmm1_code(gmm1_dtype))
 
 
-def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto"):
+def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto",
+                        gmm1_dtype="bf16"):
     """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights)."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     with torch.cuda.device(x.device):
         return _backward_raw(_contig(dy, torch.bfloat16), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
-                             _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles])
+                             _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles],
+                             _gmm1_code(gmm1_dtype))

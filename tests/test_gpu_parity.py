@@ -18,13 +18,14 @@ from oracle.routing import route as oracle_route
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(g, tiles="auto"):
+def run_gpu(g, tiles="auto", gmm1="bf16"):
     import torch
     from mixture_experts_ffn_int32_amd import backward_from_saved, forward_with_saved
     y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
-                                  g["down_proj_weight"], tiles=tiles)
+                                  g["down_proj_weight"], tiles=tiles, gmm1_dtype=gmm1)
     dx, dW1, dW2, dw = backward_from_saved(g["dY"], g["x"], g["topk_ids"], g["topk_weights"],
-                                           g["up_proj_weight"], g["down_proj_weight"], saved, tiles=tiles)
+                                           g["up_proj_weight"], g["down_proj_weight"], saved, tiles=tiles,
+                                           gmm1_dtype=gmm1)
     torch.cuda.synchronize()
     return y, saved, dx, dW1, dW2, dw
 
@@ -165,16 +166,17 @@ def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):
     import torch
     spec = synth.WORKLOADS[name]
     T, H, I, E, K = (spec[k] for k in "THIEK")
+    gmm1 = spec.get("gmm1", "bf16")
     inp = synth.make_inputs(spec, seed=0)
     announce("full-size sampled parity %s" % name)
     g = gpu_inputs(inp, "cuda")
-    y, saved, dx, dW1, dW2, dw = run_gpu(g)
+    y, saved, dx, dW1, dW2, dw = run_gpu(g, gmm1=gmm1)
     from mixture_experts_ffn_int32_amd import saved_views
     v = saved_views(saved, T, H, I, E, K)
     ref_route = oracle_route(inp["topk_ids"], E)
     for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
         assert np.array_equal(v[k].cpu().numpy(), ref_route[k]), k
-    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful", gmm1=gmm1)
     rng = np.random.default_rng(1)
     toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_tok, replace=False)]))
     ti = torch.from_numpy(toks).cuda()
@@ -223,3 +225,9 @@ def test_full_size_skewed_sampled():
 @pytest.mark.slow
 def test_full_size_hotspot_sampled():
     _sample_full("hotspot", n_tok=4)
+
+
+@pytest.mark.slow
+def test_full_size_fp8_sampled():
+    """FP8 up-projection workload (T=16384, H=4096, I=1536, E=64, K=6)."""
+    _sample_full("fp8", n_tok=4)
