@@ -75,6 +75,8 @@ def stage_work(stage, T, H, I, E, K):
         "dw2": 2 * S * I * H,           # [I,S] x [S,H]
         "dw1": 4 * S * H * I,           # [H,S] x [S,2I]
     }
+    flops["act_grad+dw2"] = flops["act_grad"] + flops["dw2"]      # two products in one launch
+    flops["input_grad+dw1"] = flops["input_grad"] + flops["dw1"]
     if stage in flops:
         return "mfma", flops[stage], "TFLOP/s", PEAK_BF16_TFLOPS
     nbytes = {

@@ -21,8 +21,9 @@
  * ---------------------------------------
  * - Pointers named as tensors are DEVICE pointers (HBM of the current HIP
  *   device); all are caller-owned and caller-allocated.  The library never
- *   allocates device memory.  Its only state is, per host thread, one pinned
- *   host word and event for the id check, and the optional stage-timing events.
+ *   allocates device memory.  Its only state is, per host thread and device,
+ *   one pinned host word and event for the id check, and the optional
+ *   stage-timing events.
  * - All tensors are dense, row-major (last index fastest), with no padding.
  *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
  *   be 16-byte aligned.

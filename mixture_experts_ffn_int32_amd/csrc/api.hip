@@ -219,21 +219,31 @@ struct Stage {
   }
 };
 
-// Per-thread objects of the id check: a pinned (coherent, device-visible) host
-// word that the routing kernel writes, and an event recorded after the routing.
-struct IdCheck {
+// Per-thread, per-device objects of the id check: a pinned (coherent,
+// device-visible) host word that the routing kernel writes, and an event recorded
+// after the routing.  Created on first use with that device current.
+constexpr int MAX_DEVICES = 64;
+struct DevState {
+  bool ready = false;
   int32_t* word = nullptr;
-  hipEvent_t ev = nullptr;
+  hipEvent_t id_ev = nullptr;
 };
-IdCheck* id_check() {
-  thread_local IdCheck c;
-  if (!c.word) {
-    if (hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocCoherent) != hipSuccess) c.word = nullptr;
+DevState* dev_state() {
+  thread_local DevState st[MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  DevState& c = st[dev];
+  if (c.ready) return &c;
+  bool ok = hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocCoherent) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c.id_ev, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {  // release whatever was made; the next call tries again
+    if (c.word) (void)hipHostFree(c.word);
+    if (c.id_ev) (void)hipEventDestroy(c.id_ev);
+    c = DevState{};
+    return nullptr;
   }
-  if (c.word && !c.ev) {
-    if (hipEventCreateWithFlags(&c.ev, hipEventDisableTiming) != hipSuccess) c.ev = nullptr;
-  }
-  return (c.word && c.ev) ? &c : nullptr;
+  c.ready = true;
+  return &c;
 }
 
 // Enqueue the routing; with validate_ids the routing also stores its error flag
@@ -243,10 +253,10 @@ IdCheck* id_check() {
 hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                      int32_t* row_of_slot, int32_t* tok_of_row, int32_t* tiles, int32_t* err, void* scratch,
                      const RouteScratch& rs, bool validate_ids, hipStream_t stream) {
-  IdCheck* c = nullptr;
+  DevState* c = nullptr;
   if (validate_ids) {
-    c = id_check();
-    if (!c) return fail(HMM_ERR_HIP, "could not create the id-check word or event");
+    c = dev_state();
+    if (!c) return fail(HMM_ERR_HIP, "could not create the per-device id-check word or event");
     *c->word = 0;
   }
   hipError_t e;
@@ -259,16 +269,16 @@ hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t
   }
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   if (c) {
-    e = hipEventRecord(c->ev, stream);
+    e = hipEventRecord(c->id_ev, stream);
     if (e != hipSuccess) return hip_fail(e, "id-validation event");
   }
   return HMM_OK;
 }
 
 hmm_status finish_id_check(const Dims& d) {
-  IdCheck* c = id_check();
+  DevState* c = dev_state();
   if (!c) return fail(HMM_ERR_HIP, "id-check state missing");
-  hipError_t e = hipEventSynchronize(c->ev);
+  hipError_t e = hipEventSynchronize(c->id_ev);
   if (e != hipSuccess) return hip_fail(e, "id-validation wait");
   if (*c->word) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
   return HMM_OK;
@@ -520,11 +530,34 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   uint16_t* dxp = at<uint16_t>(workspace, W.dxp);
   float* dwpart = at<float>(workspace, W.dwpart);
   hipError_t e;
+  if (ne && d.small) {
+    // small problems: each product fills only part of the chip, so the independent
+    // ones share a launch (RFC 2.2: W2Grad alongside act_grad, W1Grad alongside the
+    // rest of the dX chain)
+    {
+      Stage stage("act_grad+dw2", st);
+      e = hmm::launch_act_grad_dw2_narrow(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, aw,
+                                          d.E, d.H, d.I, dh, dwpart, W.dw_cols, (uint16_t*)d_down_w, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "act_grad + W2Grad launch");
+    {
+      Stage stage("input_grad+dw1", st);
+      e = hmm::launch_input_grad_dw1_narrow(g, dh, (const uint16_t*)up_w, (const uint16_t*)x, d.E, d.H, d.I, dxp,
+                                            (uint16_t*)d_up_w, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "input_grad + W1Grad launch");
+    {
+      Stage stage("combine_dx", st);
+      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, (uint16_t*)dx, dwpart, W.dw_cols,
+                                 d_topk_weights, st);
+    }
+    return e == hipSuccess ? HMM_OK : hip_fail(e, "combine(dX) launch");
+  }
   if (ne) {
     {
       Stage stage("act_grad", st);
-      e = hmm::launch_act_grad(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh, dwpart,
-                             W.dw_cols, st);
+      e = hmm::launch_act_grad(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh,
+                               dwpart, W.dw_cols, st);
     }
     if (e != hipSuccess) return hip_fail(e, "act_grad launch");
     {

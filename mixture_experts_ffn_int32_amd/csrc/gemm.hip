@@ -115,12 +115,12 @@ __device__ __forceinline__ void store_stage(uint16_t* st, const u32x4 (&ra)[C::C
     *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
 }
 
+// The main loop of every bf16 product, for workgroup ``bid`` of ``nblocks``.
 template <class P>
-__global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::Args args) {
+__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, int nblocks, uint16_t* smem) {
   typedef typename P::C C;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
   P pol;
-  if (!pol.init(args, xcd_remap(blockIdx.x, gridDim.x))) return;
+  if (!pol.init(args, P::RAW_INDEX ? bid : xcd_remap(bid, nblocks))) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -190,6 +190,27 @@ __global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::A
   pol.epilogue(acc, wm, wn, lane, smem);
 }
 
+template <class P>
+__global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::Args args) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * P::C::STAGE];
+  gemm_body<P>(args, blockIdx.x, gridDim.x, smem);
+}
+
+// Two independent products in one launch (small problems, where each fills only
+// part of the chip): workgroups [0, n1) run P1, the others P2.  n1 is a multiple
+// of 8, so both parts keep their workgroup-to-XCD mapping.
+template <class P1, class P2>
+__global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_pair_kernel(const typename P1::Args a1, int n1,
+                                                                   const typename P2::Args a2) {
+  static_assert(P1::C::NTHR == P2::C::NTHR, "one workgroup size");
+  constexpr int S1 = 2 * P1::C::STAGE, S2 = 2 * P2::C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[S1 > S2 ? S1 : S2];
+  if ((int)blockIdx.x < n1)
+    gemm_body<P1>(a1, blockIdx.x, n1, smem);
+  else
+    gemm_body<P2>(a2, blockIdx.x - n1, gridDim.x - n1, smem);
+}
+
 // Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
 // [BM][BN] tile and written out as 16-byte row chunks (rows < valid_rows,
 // columns < ncols), so every global store is a full, coalesced vector.
@@ -228,6 +249,7 @@ struct PlainCols {
 template <class Cc, bool SMALL>
 struct RowTile {
   typedef Cc C;
+  static constexpr bool RAW_INDEX = false;  // init takes the XCD-remapped logical index
   int e, row0, rows, n0, nk, nt;
   __device__ __forceinline__ void index(int) {}  // K-major rows are fixed for the whole tile
   __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
@@ -575,6 +597,7 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 template <class Cc, bool GATHER_A, bool GATHER_B>
 struct Dw : PlainCols<Cc> {
   typedef Cc C;
+  static constexpr bool RAW_INDEX = true;  // init maps the workgroup index to XCDs itself
   using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
   struct Args {
@@ -598,11 +621,10 @@ struct Dw : PlainCols<Cc> {
   // (workgroups b with b % 8 == x) walks the experts in order and takes tiles
   // [x * per, (x + 1) * per) of each, per = ceil(mt * nt / 8); inside a slice the
   // tiles are rasterised in groups of GROUP_M row tiles.
-  __device__ __forceinline__ bool init(const Args& A, int) {
+  __device__ __forceinline__ bool init(const Args& A, int b) {
     ar = &A;
     const int per_e = A.mt * A.nt;
     const int per = (per_e + 7) / 8;
-    const int b = blockIdx.x;
     const int j = b >> 3;
     e = j / per;
     if (e >= A.E) return false;
@@ -666,6 +688,17 @@ hipError_t launch(const typename P::Args& args, int64_t logical_blocks, hipStrea
   const int64_t g = round8(logical_blocks);
   if (g > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_kernel<P>, dim3((unsigned)g), dim3(P::C::NTHR), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <class P1, class P2>
+hipError_t launch_pair(const typename P1::Args& a1, int64_t blocks1, const typename P2::Args& a2, int64_t blocks2,
+                       hipStream_t stream) {
+  if (blocks1 <= 0) return launch<P2>(a2, blocks2, stream);
+  if (blocks2 <= 0) return launch<P1>(a1, blocks1, stream);
+  const int64_t g1 = round8(blocks1), g = g1 + round8(blocks2);
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_pair_kernel<P1, P2>), dim3((unsigned)g), dim3(P1::C::NTHR), 0, stream, a1, (int)g1, a2);
   return hipGetLastError();
 }
 
@@ -751,6 +784,45 @@ hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t
                       hipStream_t stream) {
   if (narrow) return launch_dw<Narrow, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
   return launch_dw<Big, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
+}
+
+namespace {
+template <class C, bool GA, bool GB>
+typename Dw<C, GA, GB>::Args dw_args(const int32_t* offsets, const int32_t* tok_of_row, int64_t E, const uint16_t* A_,
+                                     const uint16_t* B_, int64_t a_rows, int64_t b_rows, int64_t M, int64_t N,
+                                     uint16_t* out) {
+  return typename Dw<C, GA, GB>::Args{offsets, tok_of_row, E, A_, B_, a_rows, b_rows, M, N, out,
+                                      (int)((M + C::BM - 1) / C::BM), (int)((N + C::BN - 1) / C::BN)};
+}
+template <class A>
+int64_t dw_blocks(const A& a) { return a.E * 8 * ((a.mt * a.nt + 7) / 8); }
+}  // namespace
+
+hipError_t launch_act_grad_dw2_narrow(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
+                                      const uint16_t* h, const uint16_t* a, const uint16_t* aw, int64_t E, int64_t H,
+                                      int64_t I, uint16_t* dh, float* dwpart, int dw_cols, uint16_t* dw2,
+                                      hipStream_t stream) {
+  typedef ActGrad<Narrow, true> P1;
+  typedef Dw<Narrow, false, true> P2;
+  const int nnt = (int)((I + Narrow::BN - 1) / Narrow::BN);
+  typename P1::Args a1;
+  a1.g = g; a1.dy = dy; a1.w2 = w2; a1.tw = topk_w; a1.h = h; a1.a = a; a1.T = g.T; a1.H = H; a1.I = I; a1.dh = dh;
+  a1.dwpart = dwpart; a1.dw_cols = dw_cols; a1.n_ntiles = nnt;
+  const typename P2::Args a2 = dw_args<Narrow, false, true>(g.offsets, g.tok_of_row, E, aw, dy, g.S, g.T, I, H, dw2);
+  return launch_pair<P1, P2>(a1, g.max_small * nnt, a2, dw_blocks(a2), stream);
+}
+
+hipError_t launch_input_grad_dw1_narrow(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, const uint16_t* x,
+                                        int64_t E, int64_t H, int64_t I, uint16_t* dxp, uint16_t* dw1,
+                                        hipStream_t stream) {
+  typedef InputGrad<Narrow, true> P1;
+  typedef Dw<Narrow, true, false> P2;
+  const int nnt = (int)((H + Narrow::BN - 1) / Narrow::BN);
+  typename P1::Args a1;
+  a1.g = g; a1.dh = dh; a1.w1 = w1; a1.S = g.S; a1.H = H; a1.I = I; a1.dxp = dxp; a1.n_ntiles = nnt;
+  const typename P2::Args a2 =
+      dw_args<Narrow, true, false>(g.offsets, g.tok_of_row, E, x, dh, g.T, g.S, H, 2 * I, dw1);
+  return launch_pair<P1, P2>(a1, g.max_small * nnt, a2, dw_blocks(a2), stream);
 }
 
 }  // namespace hmm

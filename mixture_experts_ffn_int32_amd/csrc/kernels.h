@@ -81,6 +81,15 @@ hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t
 hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
                       const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, bool narrow,
                       hipStream_t stream);
+// Small problems (narrow tiles): two independent products in one launch each,
+// act_grad with W2Grad, then input_grad with W1Grad (the same products as above).
+hipError_t launch_act_grad_dw2_narrow(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
+                                      const uint16_t* h, const uint16_t* a, const uint16_t* aw, int64_t E, int64_t H,
+                                      int64_t I, uint16_t* dh, float* dwpart, int dw_cols, uint16_t* dw2,
+                                      hipStream_t stream);
+hipError_t launch_input_grad_dw1_narrow(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, const uint16_t* x,
+                                        int64_t E, int64_t H, int64_t I, uint16_t* dxp, uint16_t* dw1,
+                                        hipStream_t stream);
 // number of d_topk_weights partial columns written by launch_act_grad for a given I
 int act_grad_dw_cols(int64_t I, bool narrow);
 
