@@ -95,7 +95,12 @@ typedef enum hmm_dtype {
  *   E  experts held by this device, 1 <= E <= 1024
  *   K  experts per token, 1 <= K <= 16  (the dispatch op's top-k bound)
  *   T*K must stay below 2^31.
- *   out_dtype   HMM_BF16 (y and dx in bf16).  HMM_F32 is reserved (UNSUPPORTED).
+ *   out_dtype   HMM_BF16: y, dy, dx, d_up_proj_weight and d_down_proj_weight
+ *               are bf16.  HMM_F32 (accuracy mode, RFC 7.1's 1e-3 agreement with
+ *               an unrounded computation): those five are float32, and every
+ *               intermediate is kept in float32 or as a bf16 pair hi + lo
+ *               (hi = bf16(v), lo = bf16(v - hi)); about twice the MFMA work.
+ *               Needs gmm1_dtype HMM_BF16.
  *   gmm1_dtype  HMM_BF16, or HMM_FP8_E4M3 for the FP8 up-projection: tokens
  *               are quantised per row, the up-projection weight per
  *               (expert, column), both as scale = 448 / max|.| (the per-token
@@ -123,6 +128,8 @@ typedef struct hmm_problem {
  *   h[S,2I] bf16         up-projection output per permuted row ([gate | up])
  *   a[S,I] bf16          SwiGLU output per permuted row
  *   aw[S,I] bf16         topk weight * a, the W2-gradient operand
+ *                        (out_dtype HMM_F32: h is float32 [S,2I]; a and aw are
+ *                        bf16 [S,2I] holding hi in columns [0,I), lo in [I,2I))
  *   id_error int32       1 if an id was out of range on the recording call */
 typedef struct hmm_saved_layout {
   size_t counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, h, a, aw, id_error, total;
@@ -140,7 +147,7 @@ hmm_status hmm_saved_layout_of(const hmm_problem* p, hmm_saved_layout* out);
  *   topk_weights  float32 [T,K]    routing weights
  *   up_w          bf16 [E,H,2I]    up_proj_weight; columns [0,I) gate, [I,2I) up
  *   down_w        bf16 [E,I,H]     down_proj_weight
- *   y             bf16 [T,H]       output (overwritten)
+ *   y             bf16 [T,H]       output (overwritten; float32 with HMM_F32)
  *   saved         forward_sizes' saved_bytes; filled for the backward, must
  *                 stay untouched until the matching backward has run
  *   workspace     forward_sizes' workspace_bytes of scratch (free after the
@@ -157,7 +164,7 @@ hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes);
 
 /* Backward (RFC section 2.2: Dispatch(dY) -> act_grad (dY . W2^T) -> SwiGLUGrad
  * -> input_grad GMM -> Combine(dX); W2Grad and W1Grad GMMs; d_topk_weights).
- *   dy              bf16 [T,H]       gradient of y
+ *   dy              bf16 [T,H]       gradient of y (float32 with HMM_F32)
  *   x, topk_ids, topk_weights, up_w, down_w   the forward's inputs (topk_ids
  *                   is only shape-checked: the routing recorded in ``saved``
  *                   is used)
@@ -165,6 +172,7 @@ hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes);
  *   dx              bf16 [T,H]       overwritten
  *   d_up_w          bf16 [E,H,2I]    overwritten (experts without tokens: zeros)
  *   d_down_w        bf16 [E,I,H]     overwritten (experts without tokens: zeros)
+ *                   (dx, d_up_w and d_down_w are float32 with HMM_F32)
  *   d_topk_weights  float32 [T,K]    overwritten (0 for dropped slots) */
 hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
                         const float* topk_weights, const void* up_w, const void* down_w,

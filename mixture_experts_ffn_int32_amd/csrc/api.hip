@@ -37,6 +37,7 @@ struct Dims {
   int64_t T, H, I, E, K, S;
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
   bool fp8;    // FP8 E4M3 up-projection
+  bool f32;    // float32 outputs (accuracy mode)
 };
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
@@ -62,12 +63,14 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16 or HMM_FP8_E4M3 (got %d)", p->gmm1_dtype);
   {
     // every array a product reads through a buffer resource must stay below 4 GiB
-    const int64_t S = p->T * p->K, lim = (int64_t)0xFFFFFF00;
-    const int64_t ext[] = {p->T * p->H * 2, S * 2 * p->I * 2, S * p->H * 2, p->H * 2 * p->I * 2};
+    // (the float32-output mode reads [hi | lo] operands of twice the width)
+    const int64_t S = p->T * p->K, lim = (int64_t)0xFFFFFF00, w = (p->out_dtype == HMM_F32) ? 2 : 1;
+    const int64_t ext[] = {p->T * p->H * 2 * w, S * 2 * p->I * 2 * w, S * p->H * 2 * w, p->H * 2 * p->I * 2};
     for (int64_t x : ext)
       if (x > lim) return fail(HMM_ERR_UNSUPPORTED, "an operand array exceeds 4 GiB (%lld bytes)", (long long)x);
   }
-  if (p->out_dtype != HMM_BF16) return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is not implemented");
+  if (p->out_dtype == HMM_F32 && p->gmm1_dtype != HMM_BF16)
+    return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is implemented with gmm1_dtype HMM_BF16 only");
   if (p->gmm1_dtype == HMM_FP8_E4M3 && p->H % 128)
     return fail(HMM_ERR_BAD_SHAPE, "gmm1_dtype HMM_FP8_E4M3 needs H to be a multiple of 128 (got %lld)",
                 (long long)p->H);
@@ -78,6 +81,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->K = p->K;
   d->S = p->T * p->K;
   d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3;
+  d->f32 = p->out_dtype == HMM_F32;
   d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
@@ -110,9 +114,11 @@ hmm_saved_layout saved_layout(const Dims& d) {
   L.row_of_slot = o;   o += up(d.S * 4);
   L.tok_of_row = o;    o += up(d.S * 4);
   L.tiles = o;         o += up(tile_ints(d) * 4);
-  L.h = o;             o += up(d.S * 2 * d.I * 2);
-  L.a = o;             o += up(d.S * d.I * 2);
-  L.aw = o;            o += up(d.S * d.I * 2);
+  // float32-output mode: h float32, a and aw as bf16 [hi | lo] pairs (twice as wide)
+  const int64_t hb = d.f32 ? 4 : 2, ab = d.f32 ? 4 : 2;
+  L.h = o;             o += up(d.S * 2 * d.I * hb);
+  L.a = o;             o += up(d.S * d.I * ab);
+  L.aw = o;            o += up(d.S * d.I * ab);
   L.id_error = o;      o += up(4);
   L.total = o;
   return L;
@@ -144,7 +150,7 @@ FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
   w.rs = route_scratch(d, 0);
   size_t o = w.rs.total;
-  w.o = o; o += up(d.S * d.H * 2);
+  w.o = o; o += up(d.S * d.H * (d.f32 ? 4 : 2));
   if (d.fp8) {
     w.xq = o;   o += up(d.T * d.H);
     w.dsx = o;  o += up(d.T * 4);
@@ -156,16 +162,22 @@ FwdWork fwd_work(const Dims& d) {
   return w;
 }
 
+// Backward scratch: dH, dXp, the d_topk_weights partials and, in the float32-output
+// mode, dY as a bf16 [hi | lo] pair (dH is then a pair too and dXp float32).
 struct BwdWork {
-  size_t dh, dxp, dwpart, total;
+  size_t dy2, dh, dxp, dwpart, total;
   int dw_cols;
 };
 BwdWork bwd_work(const Dims& d) {
   BwdWork w{};
-  w.dw_cols = hmm::act_grad_dw_cols(d.I, d.small);
+  w.dw_cols = d.f32 ? hmm::act_grad_f32_dw_cols(d.I) : hmm::act_grad_dw_cols(d.I, d.small);
+  const int64_t wide = d.f32 ? 2 : 1;
   size_t o = 0;
-  w.dh = o;     o += up(d.S * 2 * d.I * 2);
-  w.dxp = o;    o += up(d.S * d.H * 2);
+  if (d.f32) {
+    w.dy2 = o;  o += up(d.T * 2 * d.H * 2);
+  }
+  w.dh = o;     o += up(d.S * 2 * d.I * 2 * wide);
+  w.dxp = o;    o += up(d.S * d.H * (d.f32 ? 4 : 2));
   w.dwpart = o; o += up(d.S * w.dw_cols * 4);
   w.total = o;
   return w;
@@ -458,6 +470,27 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   uint16_t* aw = at<uint16_t>(saved, L.aw);
   uint16_t* o = at<uint16_t>(workspace, W.o);
   hipError_t e;
+  if (d.f32) {
+    float* h32 = at<float>(saved, L.h);
+    float* o32 = at<float>(workspace, W.o);
+    {
+      Stage stage("gmm1_swiglu", st);
+      e = hmm::launch_gmm1_f32(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h32, a, aw, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+    {
+      Stage stage("gmm2", st);
+      e = hmm::launch_gmm2_f32(g, a, (const uint16_t*)down_w, d.H, d.I, o32, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+    {
+      Stage stage("combine", st);
+      e = hmm::launch_combine_f32(o32, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, (float*)y,
+                                  st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return validate_ids ? finish_id_check(d) : HMM_OK;
+  }
   if (d.fp8) {
     uint8_t* xq = at<uint8_t>(workspace, W.xq);
     uint8_t* wq = at<uint8_t>(workspace, W.wq);
@@ -530,6 +563,46 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   uint16_t* dxp = at<uint16_t>(workspace, W.dxp);
   float* dwpart = at<float>(workspace, W.dwpart);
   hipError_t e;
+  if (d.f32) {
+    uint16_t* dy2 = at<uint16_t>(workspace, W.dy2);
+    float* dxp32 = at<float>(workspace, W.dxp);
+    const float* h32 = at<float>(saved, L.h);
+    if (ne) {
+      {
+        Stage stage("split_dy", st);
+        e = hmm::launch_split_rows((const float*)dy, d.T, d.H, dy2, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "dY split launch");
+      {
+        Stage stage("act_grad", st);
+        e = hmm::launch_act_grad_f32(g, dy2, (const uint16_t*)down_w, topk_weights, h32, a, d.H, d.I, dh, dwpart,
+                                     W.dw_cols, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+      {
+        Stage stage("input_grad", st);
+        e = hmm::launch_input_grad_f32(g, dh, (const uint16_t*)up_w, d.H, d.I, dxp32, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+      {
+        Stage stage("combine_dx", st);
+        e = hmm::launch_combine_dx_f32(dxp32, row_of_slot, d.T, (int)d.K, d.H, (float*)dx, dwpart, W.dw_cols,
+                                       d_topk_weights, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
+    }
+    {
+      Stage stage("dw2", st);
+      e = hmm::launch_dw2_f32(offsets, tok_of_row, d.T, d.S, d.E, aw, dy2, d.H, d.I, (float*)d_down_w, d.small, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+    {
+      Stage stage("dw1", st);
+      e = hmm::launch_dw1_f32(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (float*)d_up_w,
+                              d.small, st);
+    }
+    return e == hipSuccess ? HMM_OK : hip_fail(e, "W1Grad launch");
+  }
   if (ne && d.small) {
     // small problems: each product fills only part of the chip, so the independent
     // ones share a launch (RFC 2.2: W2Grad alongside act_grad, W1Grad alongside the

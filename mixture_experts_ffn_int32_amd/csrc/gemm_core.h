@@ -1,0 +1,305 @@
+// The main loop shared by the row-grouped and weight-gradient bf16 products:
+// tile shapes, LDS layouts and fragment reads, the software pipeline, the LDS
+// staged epilogue, the row-tile base and the launch helpers.  Every kernel file
+// that includes it gets its own instantiations (anonymous namespace).
+#pragma once
+
+#include "device.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace hmm {
+namespace {
+
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;   // pitch of a K-major LDS tile (elements)
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int MB = TM / 32, NB = TN / 32;  // 32x32 accumulator blocks per wave
+  static constexpr int CA = BM * BK / 8 / NTHR;     // 16-byte chunks of A per thread per K step
+  static constexpr int CB = BN * BK / 8 / NTHR;
+  static constexpr int LDA_MN = BM + 32, LDB_MN = BN + 32;
+  static constexpr int A_ELEMS = (BM * LDK > BK * LDA_MN) ? BM * LDK : BK * LDA_MN;
+  static constexpr int B_ELEMS = (BN * LDK > BK * LDB_MN) ? BN * LDK : BK * LDB_MN;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static_assert(CA >= 1 && CB >= 1 && MB >= 1 && NB >= 1, "tile too small for the workgroup");
+};
+typedef Cfg<256, 256, 2, 4> Big;
+typedef Cfg<64, 256, 1, 4> Small;
+typedef Cfg<64, 64, 2, 2> Narrow;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// LDS placement of 16-byte chunk c of a tile with R rows (K-major) or R columns (M/N-major)
+template <bool KMAJ, int R>
+__device__ __forceinline__ int lds_chunk_off(int c) {
+  if constexpr (KMAJ) return (c >> 3) * LDK + (c & 7) * 8;               // [R rows][64 k]
+  else return (c / (R / 8)) * (R + 32) + (c % (R / 8)) * 8;              // [64 k][R cols]
+}
+
+// MFMA operand fragment (8 bf16 along k) of a 32-row block starting at row0
+template <bool KMAJ, int R>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row0, int kk, int lane) {
+  if constexpr (KMAJ) {
+    const uint16_t* p = tile + (row0 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    constexpr int LD = R + 32;
+    const int k = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int m = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint16_t* p0 = tile + k * LD + m;
+    const uint16_t* p1 = p0 + 4 * LD;
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+}
+
+// Row (within the tile) of accumulator element r of block mb of wave row wm
+template <class C>
+__device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
+  return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+template <class C, class P>
+__device__ __forceinline__ void store_stage(uint16_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i)
+    *reinterpret_cast<u32x4*>(st + lds_chunk_off<P::A_KMAJ, C::BM>(tid + i * C::NTHR)) = ra[i];
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i)
+    *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
+}
+
+// The main loop of every bf16 product, for workgroup ``bid`` of ``nblocks``.
+template <class P>
+__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, int nblocks, uint16_t* smem) {
+  typedef typename P::C C;
+  P pol;
+  if (!pol.init(args, P::RAW_INDEX ? bid : xcd_remap(bid, nblocks))) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int nk = pol.nk;
+
+  f32x16 acc[C::MB][C::NB];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (nk > 0) {
+    u32x4 ra0[C::CA], rb0[C::CB], ra1[C::CA], rb1[C::CB];
+    pol.index(0);
+    pol.load_a(0, ra0);
+    pol.load_b(0, rb0);
+    if (nk > 1) {
+      pol.index(1);
+      pol.load_a(1, ra1);
+      pol.load_b(1, rb1);
+    }
+    store_stage<C, P>(smem, ra0, rb0);
+    if (nk > 2) {
+      pol.index(2);
+      pol.load_a(2, ra0);
+      pol.load_b(2, rb0);
+    }
+    if (nk > 3) pol.index(3);
+    __syncthreads();
+    // one K step: park step kt+1 (in set `nx`) in the other LDS buffer, refill
+    // that set with step kt+3, fetch the indices of step kt+4, then multiply step kt
+    auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB]) {
+      if (kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
+      if (kt + 3 < nk) {
+        pol.load_a(kt + 3, nxa);
+        pol.load_b(kt + 3, nxb);
+      }
+      if (kt + 4 < nk) pol.index(kt + 4);
+      const uint16_t* sa = smem + (kt & 1) * C::STAGE;
+      const uint16_t* sb = sa + C::A_ELEMS;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 fa[C::MB], fb[C::NB];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<P::A_KMAJ, C::BM>(sa, wm * C::TM + mb * 32, kk, lane);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<P::B_KMAJ, C::BN>(sb, P::ncol0(wn, nb), kk, lane);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+      }
+      __syncthreads();
+    };
+    // register set 1 holds odd steps, set 0 even steps
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, ra1, rb1);
+      step(kt + 1, ra0, rb0);
+    }
+    if (kt < nk) step(kt, ra1, rb1);
+  }
+  pol.epilogue(acc, wm, wn, lane, smem);
+}
+
+template <class P>
+__global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::Args args) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * P::C::STAGE];
+  gemm_body<P>(args, blockIdx.x, gridDim.x, smem);
+}
+
+// Two independent products in one launch (small problems, where each fills only
+// part of the chip): workgroups [0, n1) run P1, the others P2.  n1 is a multiple
+// of 8, so both parts keep their workgroup-to-XCD mapping.
+template <class P1, class P2>
+__global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_pair_kernel(const typename P1::Args a1, int n1,
+                                                                   const typename P2::Args a2) {
+  static_assert(P1::C::NTHR == P2::C::NTHR, "one workgroup size");
+  constexpr int S1 = 2 * P1::C::STAGE, S2 = 2 * P2::C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[S1 > S2 ? S1 : S2];
+  if ((int)blockIdx.x < n1)
+    gemm_body<P1>(a1, blockIdx.x, n1, smem);
+  else
+    gemm_body<P2>(a2, blockIdx.x - n1, gridDim.x - n1, smem);
+}
+
+// Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
+// [BM][BN] tile and written out as 16-byte row chunks (rows < valid_rows,
+// columns < ncols), so every global store is a full, coalesced vector.
+template <class C, class P>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem,
+                                           uint16_t* out, int64_t ld, int64_t row_base, int valid_rows,
+                                           int64_t col_base, int64_t ncols) {
+  constexpr int LD = C::BN + 8;
+  static_assert(C::BM * LD <= 2 * C::STAGE, "staging tile must fit in the LDS buffers");
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        smem[acc_row<C>(wm, mb, r, lane) * LD + P::ncol0(wn, nb) + (lane & 31)] = f2bf(acc[mb][nb][r]);
+  __syncthreads();
+  constexpr int CPR = C::BN / 8;
+  for (int c = threadIdx.x; c < C::BM * CPR; c += C::NTHR) {
+    const int row = c / CPR, c8 = c % CPR;
+    const int64_t col = col_base + c8 * 8;
+    if (row < valid_rows && col < ncols)
+      *reinterpret_cast<u32x4*>(out + (row_base + row) * ld + col) =
+          *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+  }
+}
+
+// Column base (within the tile) of accumulator block nb of wave column wn
+template <class C>
+struct PlainCols {
+  __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
+};
+
+// ------------------------------------------------------------- row-grouped base
+// Tile j of one of the routing's tables: expert e, permuted rows [row0, row0 + rows).
+template <class Cc, bool SMALL>
+struct RowTile {
+  typedef Cc C;
+  static constexpr bool RAW_INDEX = false;  // init takes the XCD-remapped logical index
+  int e, row0, rows, n0, nk, nt;
+  __device__ __forceinline__ void index(int) {}  // K-major rows are fixed for the whole tile
+  __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
+    const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+    if (logical >= R * n_ntiles) return false;
+    int j;
+    raster(logical, R, n_ntiles, j, nt);
+    if (j >= g.tiles[SMALL ? 1 : 0]) return false;
+    const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
+    e = tab[2 * j];
+    row0 = tab[2 * j + 1];
+    rows = min(C::BM, g.offsets[e + 1] - row0);
+    n0 = nt * C::BN;
+    return true;
+  }
+  // K-major A rows of this tile: byte offset of chunk i (the tile's rows past the
+  // expert's end repeat its last row; their results are not stored)
+  template <bool GATHER>
+  __device__ __forceinline__ void a_rows(const RowGroups& g, int64_t ld, uint32_t (&off)[C::CA]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int p = row0 + min(c >> 3, rows - 1);
+      const int64_t row = GATHER ? (int64_t)g.tok_of_row[p] : (int64_t)p;
+      off[i] = (uint32_t)((row * ld + (c & 7) * 8) * 2);
+    }
+  }
+  // K-major B rows n0 + r (clamped to N - 1), offsets within the expert's slice
+  __device__ __forceinline__ void b_rows(int64_t ld, int64_t N, uint32_t (&off)[C::CB]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int64_t n = min((int64_t)(n0 + (c >> 3)), N - 1);
+      off[i] = (uint32_t)((n * ld + (c & 7) * 8) * 2);
+    }
+  }
+};
+
+inline int64_t round8(int64_t n) { return (n + 7) / 8 * 8; }
+
+template <class P>
+hipError_t launch(const typename P::Args& args, int64_t logical_blocks, hipStream_t stream) {
+  if (logical_blocks <= 0) return hipSuccess;
+  const int64_t g = round8(logical_blocks);
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_kernel<P>, dim3((unsigned)g), dim3(P::C::NTHR), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <class P1, class P2>
+hipError_t launch_pair(const typename P1::Args& a1, int64_t blocks1, const typename P2::Args& a2, int64_t blocks2,
+                       hipStream_t stream) {
+  if (blocks1 <= 0) return launch<P2>(a2, blocks2, stream);
+  if (blocks2 <= 0) return launch<P1>(a1, blocks1, stream);
+  const int64_t g1 = round8(blocks1), g = g1 + round8(blocks2);
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_pair_kernel<P1, P2>), dim3((unsigned)g), dim3(P1::C::NTHR), 0, stream, a1, (int)g1, a2);
+  return hipGetLastError();
+}
+
+// big-tile launch, then small-tile launch, of a row-grouped product (n_ntiles
+// is a function of the tile width); in narrow mode one launch of 64x64 tiles
+template <template <class, bool> class P, class NarrowC, class ArgsFill, class NTiles>
+hipError_t launch_rows_c(const RowGroups& g, NTiles n_ntiles, ArgsFill fill, hipStream_t stream) {
+  if (g.narrow) {
+    typedef P<NarrowC, true> PN;
+    typename PN::Args an;
+    fill(an, n_ntiles(NarrowC::BN));
+    return launch<PN>(an, g.max_small * n_ntiles(NarrowC::BN), stream);
+  }
+  typedef P<Big, false> PB;
+  typedef P<Small, true> PS;
+  typename PB::Args ab;
+  fill(ab, n_ntiles(Big::BN));
+  hipError_t e = launch<PB>(ab, g.max_big * n_ntiles(Big::BN), stream);
+  if (e != hipSuccess) return e;
+  typename PS::Args as;
+  fill(as, n_ntiles(Small::BN));
+  return launch<PS>(as, g.max_small * n_ntiles(Small::BN), stream);
+}
+template <template <class, bool> class P, class ArgsFill, class NTiles>
+hipError_t launch_rows(const RowGroups& g, NTiles n_ntiles, ArgsFill fill, hipStream_t stream) {
+  return launch_rows_c<P, Narrow>(g, n_ntiles, fill, stream);
+}
+
+}  // namespace
+}  // namespace hmm

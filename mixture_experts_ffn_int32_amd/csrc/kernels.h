@@ -113,4 +113,29 @@ hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, cons
 hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
                              uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
 
+// float32-output (accuracy) mode (gemm_f32.hip, pointwise.hip).  Operands that are
+// not exact bf16 inputs are bf16 [hi | lo] pairs of twice the width; see gemm_f32.hip.
+hipError_t launch_gmm1_f32(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w, int64_t H,
+                           int64_t I, float* h, uint16_t* a2, uint16_t* aw2, hipStream_t stream);
+hipError_t launch_gmm2_f32(const RowGroups& g, const uint16_t* a2, const uint16_t* w2, int64_t H, int64_t I, float* o,
+                           hipStream_t stream);
+hipError_t launch_act_grad_f32(const RowGroups& g, const uint16_t* dy2, const uint16_t* w2, const float* topk_w,
+                               const float* h, const uint16_t* a2, int64_t H, int64_t I, uint16_t* dh2, float* dwpart,
+                               int dw_cols, hipStream_t stream);
+hipError_t launch_input_grad_f32(const RowGroups& g, const uint16_t* dh2, const uint16_t* w1, int64_t H, int64_t I,
+                                 float* dxp, hipStream_t stream);
+hipError_t launch_dw1_f32(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                          const uint16_t* x, const uint16_t* dh2, int64_t H, int64_t I, float* dw1, bool narrow,
+                          hipStream_t stream);
+hipError_t launch_dw2_f32(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                          const uint16_t* aw2, const uint16_t* dy2, int64_t H, int64_t I, float* dw2, bool narrow,
+                          hipStream_t stream);
+int act_grad_f32_dw_cols(int64_t I);  // partial columns (32-column blocks) of launch_act_grad_f32
+hipError_t launch_combine_f32(const float* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
+                              int64_t H, float* out, hipStream_t stream);
+hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, float* dx,
+                                 const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
+// x float32 [n][H] -> bf16 [n][2H] = [hi | lo]
+hipError_t launch_split_rows(const float* x, int64_t n, int64_t H, uint16_t* out, hipStream_t stream);
+
 }  // namespace hmm

@@ -14,14 +14,31 @@ namespace hmm {
 
 constexpr int PW_THREADS = 256;
 
+// 8 consecutive elements of a row: bf16 (one 16-byte load / store) or float32 (two)
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) { unpack8(*reinterpret_cast<const u32x4*>(p), v); }
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = a[j];
+    v[4 + j] = b[j];
+  }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) { *reinterpret_cast<u32x4*>(p) = pack8(v); }
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = (f32x4){v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = (f32x4){v[4], v[5], v[6], v[7]};
+}
+
 // One thread per 8 consecutive hidden elements of one token (16-byte loads).
 // With dwpart, the thread of chunk k (< K) of a token also finalises slot k of
-// that token: dw[s] = sum_c dwpart[row_of_slot[s]][c], c ascending.
-template <bool WEIGHTED>
-__global__ void __launch_bounds__(PW_THREADS) combine_kernel(const uint16_t* __restrict__ rows,
+// that token: dw[s] = sum_c dwpart[row_of_slot[s]][c], c ascending.  T is bf16
+// (the default) or float32 (the accuracy mode) for both the rows and the output.
+template <bool WEIGHTED, class T_>
+__global__ void __launch_bounds__(PW_THREADS) combine_kernel(const T_* __restrict__ rows,
                                                              const int32_t* __restrict__ row_of_slot,
                                                              const float* __restrict__ tw, int64_t T, int K,
-                                                             int64_t H, uint16_t* __restrict__ out,
+                                                             int64_t H, T_* __restrict__ out,
                                                              const float* __restrict__ dwpart, int dw_cols,
                                                              float* __restrict__ dw) {
   const int64_t chunks_per_row = H >> 3;
@@ -37,11 +54,11 @@ __global__ void __launch_bounds__(PW_THREADS) combine_kernel(const uint16_t* __r
       if (r < 0) continue;
       const float wk = WEIGHTED ? tw[s] : 1.f;
       float v[8];
-      unpack8(*reinterpret_cast<const u32x4*>(rows + (int64_t)r * H + c * 8), v);
+      load8(rows + (int64_t)r * H + c * 8, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = WEIGHTED ? __builtin_fmaf(wk, v[j], acc[j]) : acc[j] + v[j];
     }
-    *reinterpret_cast<u32x4*>(out + t * H + c * 8) = pack8(acc);
+    store8(out + t * H + c * 8, acc);
     if (dwpart) {
       for (int64_t k = c; k < K; k += chunks_per_row) {
         const int64_t s = t * K + k;
@@ -63,21 +80,66 @@ static unsigned grid_for(int64_t work, int64_t cap) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
-hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
-                          int K, int64_t H, uint16_t* out, hipStream_t stream) {
+template <class T_>
+hipError_t combine_t(const T_* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K, int64_t H,
+                     T_* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned g = grid_for(T * (H / 8), 1 << 20);
-  hipLaunchKernelGGL(combine_kernel<true>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T, K, H,
-                     out, nullptr, 0, nullptr);
+  hipLaunchKernelGGL((combine_kernel<true, T_>), dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
+                     K, H, out, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
-                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
+template <class T_>
+hipError_t combine_dx_t(const T_* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, T_* dx,
+                        const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned g = grid_for(T * (H / 8), 1 << 20);
-  hipLaunchKernelGGL(combine_kernel<false>, dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, nullptr, T, K,
-                     H, dx, dwpart, dw_cols, dw);
+  hipLaunchKernelGGL((combine_kernel<false, T_>), dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, nullptr,
+                     T, K, H, dx, dwpart, dw_cols, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
+                          int64_t H, uint16_t* out, hipStream_t stream) {
+  return combine_t(rows, row_of_slot, topk_w, T, K, H, out, stream);
+}
+hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
+                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
+  return combine_dx_t(rows, row_of_slot, T, K, H, dx, dwpart, dw_cols, dw, stream);
+}
+hipError_t launch_combine_f32(const float* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
+                              int64_t H, float* out, hipStream_t stream) {
+  return combine_t(rows, row_of_slot, topk_w, T, K, H, out, stream);
+}
+hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, float* dx,
+                                 const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
+  return combine_dx_t(rows, row_of_slot, T, K, H, dx, dwpart, dw_cols, dw, stream);
+}
+
+// x float32 [n][H] -> out bf16 [n][2H]: [hi | lo] with hi = bf16(v), lo = bf16(v - hi)
+__global__ void __launch_bounds__(PW_THREADS) split_rows_kernel(const float* __restrict__ x, int64_t n, int64_t H,
+                                                                uint16_t* __restrict__ out) {
+  const int64_t cpr = H >> 3, total = n * cpr;
+  for (int64_t idx = (int64_t)blockIdx.x * PW_THREADS + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * PW_THREADS) {
+    const int64_t t = idx / cpr, c = idx - t * cpr;
+    float v[8], hi[8], lo[8];
+    load8(x + t * H + c * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hi[j] = round_bf(v[j]);
+      lo[j] = v[j] - hi[j];
+    }
+    store8(out + t * 2 * H + c * 8, hi);
+    store8(out + t * 2 * H + H + c * 8, lo);
+  }
+}
+
+hipError_t launch_split_rows(const float* x, int64_t n, int64_t H, uint16_t* out, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const unsigned g = grid_for(n * (H / 8), 1 << 20);
+  hipLaunchKernelGGL(split_rows_kernel, dim3(g), dim3(PW_THREADS), 0, stream, x, n, H, out);
   return hipGetLastError();
 }
 

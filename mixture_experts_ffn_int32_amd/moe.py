@@ -66,19 +66,32 @@ def _gmm1_code(gmm1_dtype):
     return GMM1_DTYPES[gmm1_dtype]
 
 
+OUT_DTYPES = {"bf16": _lib.HMM_BF16, "f32": _lib.HMM_F32}
+
+
+def _out_code(out_dtype):
+    """'bf16' / torch.bfloat16 (default) or 'f32' / torch.float32 (the accuracy mode)."""
+    if out_dtype in (torch.bfloat16, "bf16"):
+        return _lib.HMM_BF16
+    if out_dtype in (torch.float32, "f32"):
+        return _lib.HMM_F32
+    raise ValueError("out_dtype must be torch.bfloat16 or torch.float32 (got %r)" % (out_dtype,))
+
+
 def _contig(t, dtype=None):
     if dtype is not None and t.dtype != dtype:
         t = t.to(dtype)
     return t.contiguous()
 
 
-def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16):
+def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16):
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags, gmm1_dtype=gmm1)
+    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1)
     ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
     _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
     dev = x.device
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    odt = torch.float32 if out == _lib.HMM_F32 else torch.bfloat16
+    y = torch.empty((T, H), dtype=odt, device=dev)
     saved = torch.empty(sv.value, dtype=torch.uint8, device=dev)
     work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
     _lib.check(lib.hmm_forward(ctypes.byref(prob), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2), _ptr(y),
@@ -86,15 +99,16 @@ def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16):
     return y, saved
 
 
-def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16):
+def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16):
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags, gmm1_dtype=gmm1)
+    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1)
     ws = ctypes.c_size_t()
     _lib.check(lib.hmm_backward_sizes(ctypes.byref(prob), ctypes.byref(ws)))
     dev = x.device
-    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    dW1 = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=dev)
-    dW2 = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+    odt = torch.float32 if out == _lib.HMM_F32 else torch.bfloat16
+    dx = torch.empty((T, H), dtype=odt, device=dev)
+    dW1 = torch.empty((E, H, 2 * I), dtype=odt, device=dev)
+    dW2 = torch.empty((E, I, H), dtype=odt, device=dev)
     dw = torch.empty((T, K), dtype=torch.float32, device=dev)
     work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
     _lib.check(lib.hmm_backward(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2),
@@ -107,7 +121,7 @@ class HyperMegaMoEFunction(torch.autograd.Function):
     """Forward calls hmm_forward and keeps the saved buffer; backward calls hmm_backward."""
 
     @staticmethod
-    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags, gmm1):
+    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags, gmm1, out):
         T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
         x_ = _contig(x)
         ids = _contig(topk_ids, torch.int32)
@@ -115,24 +129,24 @@ class HyperMegaMoEFunction(torch.autograd.Function):
         W1 = _contig(up_proj_weight)
         W2 = _contig(down_proj_weight)
         with torch.cuda.device(x.device):
-            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags, gmm1)
+            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags, gmm1, out)
         ctx.save_for_backward(x_, ids, w, W1, W2, saved)
-        ctx.dims = (T, H, I, E, K, flags, gmm1)
+        ctx.dims = (T, H, I, E, K, flags, gmm1, out)
         ctx.w_dtype = topk_weights.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
         x_, ids, w, W1, W2, saved = ctx.saved_tensors
-        T, H, I, E, K, flags, gmm1 = ctx.dims
-        dy = _contig(dy, torch.bfloat16)
+        T, H, I, E, K, flags, gmm1, out = ctx.dims
+        dy = _contig(dy, torch.float32 if out == _lib.HMM_F32 else torch.bfloat16)
         with torch.cuda.device(x_.device):
-            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1)
-        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None, None
+            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1, out)
+        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None, None, None
 
 
 def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True,
-                   gmm1_dtype="bf16"):
+                   gmm1_dtype="bf16", out_dtype=torch.bfloat16):
     """y [T,H] = sum_k topk_weights[t,k] * SwiGLU-FFN_{topk_ids[t,k]}(x[t]), on the GPU.
 
     x bf16 [T,H]; topk_ids int32/int64 [T,K] (0 <= id < E); topk_weights float [T,K];
@@ -143,11 +157,16 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     of range.  ``gmm1_dtype="fp8"`` runs the up-projection in FP8 E4M3: each
     token row and each (expert, column) of up_proj_weight is quantised with a
     dynamic per-row / per-column scale (H must then be a multiple of 128); the
-    rest of the forward and the whole backward stay bf16.
+    rest of the forward and the whole backward stay bf16.  ``out_dtype=torch.float32``
+    is the accuracy mode: y (and dx and the weight gradients of the raw backward)
+    are float32 and every intermediate is kept to about 16 significant bits
+    (bf16 hi + lo pairs), for agreement with an unrounded computation to 1e-3;
+    it costs about twice the MFMA work.  Under autograd, gradients are cast to
+    the dtype of their inputs (bf16 weights get bf16 gradients).
     """
     flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
     return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags,
-                                      _gmm1_code(gmm1_dtype))
+                                      _gmm1_code(gmm1_dtype), _out_code(out_dtype))
 
 
 # ----------------------------------------------------------------------------- stage entry points (tests, tools)
@@ -208,13 +227,18 @@ def quantize_cols_fp8(w):
     return q, ds
 
 
-def saved_views(saved, T, H, I, E, K, tiles="auto"):
-    """Typed views of the arrays a forward recorded in its saved buffer."""
+def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16"):
+    """Typed views of the arrays a forward recorded in its saved buffer.
+
+    In the float32-output mode h is float32 [S, 2I] and a, aw are bf16 [S, 2I]
+    pairs (hi in the first I columns, lo in the last I)."""
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles])
+    out = _out_code(out_dtype)
+    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles], out_dtype=out)
     L = _lib.SavedLayout()
     _lib.check(lib.hmm_saved_layout_of(ctypes.byref(prob), ctypes.byref(L)))
     S = T * K
+    f32 = out == _lib.HMM_F32
 
     def view(off, n, dtype, shape):
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
@@ -226,15 +250,15 @@ def saved_views(saved, T, H, I, E, K, tiles="auto"):
         "sorted_slot": view(L.sorted_slot, S, torch.int32, (S,)),
         "row_of_slot": view(L.row_of_slot, S, torch.int32, (S,)),
         "tok_of_row": view(L.tok_of_row, S, torch.int32, (S,)),
-        "h": view(L.h, S * 2 * I, torch.bfloat16, (S, 2 * I)),
-        "a": view(L.a, S * I, torch.bfloat16, (S, I)),
-        "aw": view(L.aw, S * I, torch.bfloat16, (S, I)),
+        "h": view(L.h, S * 2 * I, torch.float32 if f32 else torch.bfloat16, (S, 2 * I)),
+        "a": view(L.a, S * I * (2 if f32 else 1), torch.bfloat16, (S, 2 * I if f32 else I)),
+        "aw": view(L.aw, S * I * (2 if f32 else 1), torch.bfloat16, (S, 2 * I if f32 else I)),
         "id_error": view(L.id_error, 1, torch.int32, (1,)),
     }
 
 
 def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True,
-                       tiles="auto", gmm1_dtype="bf16"):
+                       tiles="auto", gmm1_dtype="bf16", out_dtype="bf16"):
     """Forward without autograd; returns (y, saved buffer) for stage-level checks.
 
     ``tiles`` forces the tiling of the grouped products ("auto", "large" or
@@ -245,15 +269,19 @@ def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weig
     with torch.cuda.device(x.device):
         return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
                             _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags,
-                            _gmm1_code(gmm1_dtype))
+                            _gmm1_code(gmm1_dtype), _out_code(out_dtype))
 
 
 def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto",
-                        gmm1_dtype="bf16"):
-    """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights)."""
+                        gmm1_dtype="bf16", out_dtype="bf16"):
+    """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights).
+
+    With out_dtype float32, dy is taken in float32 and dx, dW1, dW2 are float32."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    out = _out_code(out_dtype)
+    dyt = torch.float32 if out == _lib.HMM_F32 else torch.bfloat16
     with torch.cuda.device(x.device):
-        return _backward_raw(_contig(dy, torch.bfloat16), _contig(x), _contig(topk_ids, torch.int32),
+        return _backward_raw(_contig(dy, dyt), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
                              _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles],
-                             _gmm1_code(gmm1_dtype))
+                             _gmm1_code(gmm1_dtype), out)

@@ -53,7 +53,8 @@ def _prob(**kw):
     (dict(K=17), _lib.HMM_ERR_BAD_SHAPE), (dict(E=0), _lib.HMM_ERR_BAD_SHAPE), (dict(E=1025), _lib.HMM_ERR_BAD_SHAPE),
     (dict(T=-1), _lib.HMM_ERR_BAD_SHAPE), (dict(T=1 << 28, K=16), _lib.HMM_ERR_BAD_SHAPE),
     (dict(out_dtype=7), _lib.HMM_ERR_BAD_DTYPE), (dict(gmm1_dtype=9), _lib.HMM_ERR_BAD_DTYPE),
-    (dict(out_dtype=_lib.HMM_F32), _lib.HMM_ERR_UNSUPPORTED), (dict(flags=8), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(out_dtype=_lib.HMM_F32, gmm1_dtype=_lib.HMM_FP8_E4M3), _lib.HMM_ERR_UNSUPPORTED),
+    (dict(gmm1_dtype=_lib.HMM_FP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=8), _lib.HMM_ERR_BAD_SHAPE),
     (dict(reserved=1), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=6), _lib.HMM_ERR_BAD_SHAPE),
 ])
 def test_sizes_reject_bad_problems(lib, kw, status):
@@ -99,3 +100,22 @@ def test_profile_read_without_launches(lib):
     assert lib.hmm_profile_read(buf, 8, ctypes.byref(n), ctypes.byref(dropped)) == 0
     assert n.value == 0 and dropped.value == 0
     lib.hmm_profile_enable(0)
+
+
+def test_f32_mode_sizes(lib):
+    """The accuracy mode keeps h in float32 and a, aw as [hi | lo] pairs; its workspaces grow to match."""
+    sizes = {}
+    for out in (_lib.HMM_BF16, _lib.HMM_F32):
+        p = _prob(out_dtype=out)
+        ws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.hmm_forward_sizes(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(sv)) == 0
+        assert lib.hmm_backward_sizes(ctypes.byref(p), ctypes.byref(bws)) == 0
+        L = _lib.SavedLayout()
+        assert lib.hmm_saved_layout_of(ctypes.byref(p), ctypes.byref(L)) == 0
+        sizes[out] = (ws.value, sv.value, bws.value, L)
+    S, H, I, T = 2048, 512, 128, 1024
+    L = sizes[_lib.HMM_F32][3]
+    assert L.a - L.h >= S * 2 * I * 4 and L.aw - L.a >= S * 2 * I * 2 and L.id_error - L.aw >= S * 2 * I * 2
+    assert sizes[_lib.HMM_F32][0] >= S * H * 4                       # o in float32
+    assert sizes[_lib.HMM_F32][2] >= T * 2 * H * 2 + S * 4 * I * 2 + S * H * 4
+    assert all(sizes[_lib.HMM_F32][i] > sizes[_lib.HMM_BF16][i] for i in range(3))
