@@ -62,9 +62,13 @@ def recorded_traffic(workload, kernel):
     return None if ent is None else int(round(ent["bytes"]))
 
 
-def stage_work(stage, T, H, I, E, K):
-    """Algorithmic work of one launch of a stage: (bound, amount, unit, peak)."""
+def stage_work(stage, T, H, I, E, K, f32=False):
+    """Algorithmic work of one launch of a stage: (bound, amount, unit, peak).
+
+    The float32-output mode counts the same algorithmic flops (its hi/lo operand
+    pairs make the MFMAs do about 1.9x that work) and float32 rows in the combines."""
     S = T * K
+    eb = 4 if f32 else 2
     if stage == "gmm1_fp8_swiglu":
         return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
     flops = {
@@ -81,8 +85,9 @@ def stage_work(stage, T, H, I, E, K):
         return "mfma", flops[stage], "TFLOP/s", PEAK_BF16_TFLOPS
     nbytes = {
         # read K gathered rows per token + row index + weight, write one row
-        "combine": S * H * 2 + S * 8 + T * H * 2,
-        "combine_dx": S * H * 2 + S * 4 + T * H * 2,   # (+ d_topk_weights partials, small)
+        "combine": S * H * eb + S * 8 + T * H * eb,
+        "combine_dx": S * H * eb + S * 4 + T * H * eb,   # (+ d_topk_weights partials, small)
+        "split_dy": T * H * 4 + T * H * 4,              # float32 dY -> bf16 hi | lo
         # ids read twice, histograms, sorted_slot + row_of_slot written
         "route": S * 4 * 2 + S * 8,
         # FP8 quantisers: read the bf16 operand once, write its codes and descales
@@ -97,7 +102,7 @@ def stage_work(stage, T, H, I, E, K):
 class Runner:
     """Preallocated buffers and raw C-ABI calls for one workload."""
 
-    def __init__(self, spec, seed, device, validate_ids=True):
+    def __init__(self, spec, seed, device, validate_ids=True, out_dtype="bf16"):
         import torch
         from mixture_experts_ffn_int32_amd import _lib, synth
         self.torch = torch
@@ -123,18 +128,22 @@ class Runner:
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
         flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
         gmm1 = _lib.HMM_FP8_E4M3 if spec.get("gmm1", "bf16") == "fp8" else _lib.HMM_BF16
-        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, gmm1, flags, 0)
+        f32 = out_dtype == "f32"
+        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_F32 if f32 else _lib.HMM_BF16, gmm1, flags, 0)
         fws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
         _lib.check(self.lib.hmm_forward_sizes(ctypes.byref(self.prob), ctypes.byref(fws), ctypes.byref(sv)))
         _lib.check(self.lib.hmm_backward_sizes(ctypes.byref(self.prob), ctypes.byref(bws)))
         u8 = torch.uint8
-        self.y = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        odt = torch.float32 if f32 else torch.bfloat16
+        if f32:
+            self.dy = self.dy.float()
+        self.y = torch.empty((T, H), dtype=odt, device=device)
         self.saved = torch.empty(sv.value, dtype=u8, device=device)
         self.fwork = torch.empty(fws.value, dtype=u8, device=device)
         self.bwork = torch.empty(bws.value, dtype=u8, device=device)
-        self.dx = torch.empty((T, H), dtype=torch.bfloat16, device=device)
-        self.dW1 = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=device)
-        self.dW2 = torch.empty((E, I, H), dtype=torch.bfloat16, device=device)
+        self.dx = torch.empty((T, H), dtype=odt, device=device)
+        self.dW1 = torch.empty((E, H, 2 * I), dtype=odt, device=device)
+        self.dW2 = torch.empty((E, I, H), dtype=odt, device=device)
         self.dw = torch.empty((T, K), dtype=torch.float32, device=device)
         self.sizes = (fws.value, sv.value, bws.value)
         self.stream = torch.cuda.current_stream(device)
@@ -203,6 +212,8 @@ def main():
     ap.add_argument("--workload", default="sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-validate", action="store_true", help="skip the id check's device-to-host read-back")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="f32: the float32-output accuracy mode (hi/lo operand pairs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -232,7 +243,7 @@ def main():
     T, H, I, E, K = (spec[k] for k in "THIEK")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate)
+    r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate, out_dtype=args.out_dtype)
     log("[bench] workload %s T=%d H=%d I=%d E=%d K=%d; workspace fwd %.1f MB, saved %.1f MB, bwd %.1f MB"
         % (args.workload, T, H, I, E, K, r.sizes[0] / 1e6, r.sizes[1] / 1e6, r.sizes[2] / 1e6))
 
@@ -260,7 +271,7 @@ def main():
     rows = []
     for name, (n, tot) in sorted(stages.items(), key=lambda kv: -kv[1][1]):
         avg = tot / max(n, 1)
-        bound, work, unit, peak = stage_work(name, T, H, I, E, K)
+        bound, work, unit, peak = stage_work(name, T, H, I, E, K, args.out_dtype == "f32")
         rate = (work / (avg * 1e-3) / (1e12 if bound == "mfma" else 1e9)) if bound else None
         if bound == "mfma":
             gemm_ms += tot / args.steps
@@ -300,10 +311,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp8" if fp8 else "bf16",
+        "dtype": "bf16+fp8" if fp8 else ("bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
-                   "routing": spec.get("routing"), "seed": args.seed, "validate_ids": not args.no_validate},
+                   "routing": spec.get("routing"), "seed": args.seed, "validate_ids": not args.no_validate,
+                   "out_dtype": args.out_dtype},
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
         "gemm_frac_peak": round(gemm_ms_at_peak / gemm_ms, 5) if gemm_ms > 0 else None,
         "roofline": roofline,

@@ -170,7 +170,7 @@ struct BwdWork {
 };
 BwdWork bwd_work(const Dims& d) {
   BwdWork w{};
-  w.dw_cols = d.f32 ? hmm::act_grad_f32_dw_cols(d.I) : hmm::act_grad_dw_cols(d.I, d.small);
+  w.dw_cols = d.f32 ? hmm::act_grad_f32_dw_cols(d.I, d.small) : hmm::act_grad_dw_cols(d.I, d.small);
   const int64_t wide = d.f32 ? 2 : 1;
   size_t o = 0;
   if (d.f32) {

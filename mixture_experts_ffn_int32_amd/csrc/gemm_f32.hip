@@ -196,10 +196,13 @@ struct Gmm2F32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
 };
 
 // ------------------------------------------------------------- act_grad + SwiGLUGrad
-// G = dY[tok] . W2[e]^T over K = 2H ([dY_hi | dY_lo]); epilogue in float32 from h
-// (float32) and a = a_hi + a_lo; dH stored as [dg_hi | du_hi | dg_lo | du_lo];
-// sum_i G a reduced over each 32-column block in a fixed order (lane butterfly):
-// one partial per (row, 32-column block).
+// G = dY[tok] . W2[e]^T over K = 2H ([dY_hi | dY_lo]).  Epilogue as in the bf16
+// product: one wave column of G at a time is staged in LDS (float32), then each
+// thread takes 8 consecutive columns of one row, reads g, u (float32) and
+// a = a_hi + a_lo as 16-byte vectors, writes dH = [dg_hi | du_hi | dg_lo | du_lo]
+// as 16-byte vectors and adds its share of sum_i G a; the row sums are reduced in a
+// fixed order (8-lane butterfly, then wave columns in order): one partial per
+// (row, N tile).
 template <class Cc, bool SMALL>
 struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   typedef RowTile<Cc, SMALL> B_;
@@ -243,43 +246,82 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
-    const float* wrow = stage_weights<C>(ar->g, ar->tw, row0, rows, smem);
+    constexpr int LDF = C::TN + 4;
+    constexpr int CPR = C::TN / 8;
+    constexpr int PER = C::BM * CPR / C::NTHR;
+    static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
+    static_assert((C::BM * LDF + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    float* gst = reinterpret_cast<float*>(smem);
+    float* wrow = gst + C::BM * LDF;
+    const int tid = threadIdx.x;
+    for (int t = tid; t < C::BM; t += C::NTHR) wrow[t] = (t < rows) ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
     const int64_t I = ar->I;
+    float part[PER];
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int k = 0; k < PER; ++k) part[k] = 0.f;
+    for (int q = 0; q < C::WN; ++q) {
+      if (wn == q) {
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int64_t blk0 = n0 + ncol0(wn, nb);   // first column of this 32-column block
+        for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(wm, mb, r, lane);
-          const int64_t i = blk0 + (lane & 31);
-          float s = 0.f;
-          if (row < rows && i < I) {
-            const int64_t p = row0 + row;
-            const float G = acc[mb][nb][r];
-            const float g = ar->h[p * 2 * I + i], u = ar->h[p * 2 * I + I + i];
-            const float a = bf2f(ar->a2[p * 2 * I + i]) + bf2f(ar->a2[p * 2 * I + I + i]);
-            s = G * a;
-            const float dA = wrow[row] * G;
-            const float sg = sigmoidf_(g);
-            const float dg = dA * u * sg * (1.f + g * (1.f - sg));
-            const float du = dA * g * sg;
-            uint16_t hi, lo;
-            split_bf(dg, hi, lo);
-            ar->dh2[p * 4 * I + i] = hi;
-            ar->dh2[p * 4 * I + 2 * I + i] = lo;
-            split_bf(du, hi, lo);
-            ar->dh2[p * 4 * I + I + i] = hi;
-            ar->dh2[p * 4 * I + 3 * I + i] = lo;
-          }
-          // the 32 columns of this row sit in 32 consecutive lanes: fixed-order butterfly
+          for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-          for (int d = 16; d >= 1; d >>= 1) s += __shfl_xor(s, d);
-          if ((lane & 31) == 0 && row < rows && blk0 < I)
-            ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + blk0 / 32] = s;
-        }
+            for (int r = 0; r < 16; ++r)
+              gst[acc_row<C>(wm, mb, r, lane) * LDF + nb * 32 + (lane & 31)] = acc[mb][nb][r];
       }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int c = tid + k * C::NTHR;
+        const int row = c / CPR, c8 = c % CPR;
+        const int64_t i = n0 + q * C::TN + c8 * 8;
+        float s = 0.f;
+        if (row < rows && i < I) {
+          const int64_t p = row0 + row;
+          float g[8], u[8], ah[8], al[8], dg[8], du[8];
+          const f32x4* hp = reinterpret_cast<const f32x4*>(ar->h + p * 2 * I + i);
+          const f32x4* up = reinterpret_cast<const f32x4*>(ar->h + p * 2 * I + I + i);
+          const f32x4 g0 = hp[0], g1 = hp[1], u0 = up[0], u1 = up[1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            g[j] = g0[j]; g[4 + j] = g1[j];
+            u[j] = u0[j]; u[4 + j] = u1[j];
+          }
+          unpack8(*reinterpret_cast<const u32x4*>(ar->a2 + p * 2 * I + i), ah);
+          unpack8(*reinterpret_cast<const u32x4*>(ar->a2 + p * 2 * I + I + i), al);
+          const float w = wrow[row];
+          const float* G = gst + row * LDF + c8 * 8;
+          float dgh[8], dgl[8], duh[8], dul[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            s += G[j] * (ah[j] + al[j]);
+            const float dA = w * G[j];
+            const float sg = sigmoidf_(g[j]);
+            dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
+            du[j] = dA * g[j] * sg;
+            dgh[j] = round_bf(dg[j]);
+            dgl[j] = dg[j] - dgh[j];
+            duh[j] = round_bf(du[j]);
+            dul[j] = du[j] - duh[j];
+          }
+          uint16_t* d = ar->dh2 + p * 4 * I + i;
+          *reinterpret_cast<u32x4*>(d) = pack8(dgh);
+          *reinterpret_cast<u32x4*>(d + I) = pack8(duh);
+          *reinterpret_cast<u32x4*>(d + 2 * I) = pack8(dgl);
+          *reinterpret_cast<u32x4*>(d + 3 * I) = pack8(dul);
+        }
+#pragma unroll
+        for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+        part[k] += s;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = tid + k * C::NTHR;
+      const int row = c / CPR;
+      if (c % CPR == 0 && row < rows) ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
+    }
   }
 };
 
@@ -431,7 +473,10 @@ hipError_t launch_dw_f32(const int32_t* offsets, const int32_t* tok_of_row, int6
 
 }  // namespace
 
-int act_grad_f32_dw_cols(int64_t I) { return (int)((I + 31) / 32); }
+int act_grad_f32_dw_cols(int64_t I, bool narrow) {
+  const int64_t bn = narrow ? NarrowF::BN : Big::BN;  // Big and Small share BN
+  return (int)((I + bn - 1) / bn);
+}
 
 hipError_t launch_gmm1_f32(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w, int64_t H,
                            int64_t I, float* h, uint16_t* a2, uint16_t* aw2, hipStream_t stream) {

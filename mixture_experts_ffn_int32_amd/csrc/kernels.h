@@ -130,7 +130,7 @@ hipError_t launch_dw1_f32(const int32_t* offsets, const int32_t* tok_of_row, int
 hipError_t launch_dw2_f32(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
                           const uint16_t* aw2, const uint16_t* dy2, int64_t H, int64_t I, float* dw2, bool narrow,
                           hipStream_t stream);
-int act_grad_f32_dw_cols(int64_t I);  // partial columns (32-column blocks) of launch_act_grad_f32
+int act_grad_f32_dw_cols(int64_t I, bool narrow);  // d_topk_weights partial columns of launch_act_grad_f32
 hipError_t launch_combine_f32(const float* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
                               int64_t H, float* out, hipStream_t stream);
 hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, float* dx,
