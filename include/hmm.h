@@ -88,6 +88,15 @@ typedef enum hmm_dtype {
 #define HMM_FLAG_TILES_LARGE 2u
 #define HMM_FLAG_TILES_NARROW 4u
 
+/* Run the forward of a small problem (narrow tiling, S <= 8192, E <= 256, bf16
+ * outputs and bf16 up-projection) as ONE persistent launch: routing, both
+ * products and the combine, with tile-ready counters between them (RFC 6.1).
+ * The results are identical to the kernel sequence.  On MI355X it is slower
+ * today (every array one tile writes for another has to go through the
+ * device-wide coherence point, because the eight XCDs have separate L2s), so it
+ * is opt-in; ignored where it does not apply. */
+#define HMM_FLAG_FUSED_FORWARD 8u
+
 /* Problem description.
  *   T  tokens (>= 0; T = 0 is a no-op that still writes zero weight gradients)
  *   H  hidden size, multiple of 64, 64 <= H <= 65536

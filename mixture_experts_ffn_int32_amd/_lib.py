@@ -25,6 +25,7 @@ HMM_BF16, HMM_F32, HMM_FP8_E4M3 = 0, 1, 2
 HMM_FLAG_VALIDATE_IDS = 1
 HMM_FLAG_TILES_LARGE = 2
 HMM_FLAG_TILES_NARROW = 4
+HMM_FLAG_FUSED_FORWARD = 8
 TILE_FLAGS = {"auto": 0, "large": HMM_FLAG_TILES_LARGE, "narrow": HMM_FLAG_TILES_NARROW}
 
 # every symbol include/hmm.h declares

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libhmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["route.hip", "gemm.hip", "gemm_f32.hip", "gemm_fp8.hip", "quant.hip", "pointwise.hip", "api.hip"]
+SOURCES = ["route.hip", "gemm.hip", "gemm_f32.hip", "gemm_fp8.hip", "quant.hip", "pointwise.hip", "fused.hip", "api.hip"]
 
 
 def hipcc():

@@ -2,6 +2,10 @@
 // the forward and backward calls declared in include/hmm.h.
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -38,6 +42,7 @@ struct Dims {
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
   bool fp8;    // FP8 E4M3 up-projection
   bool f32;    // float32 outputs (accuracy mode)
+  bool fused;  // small problem whose forward runs as one fused launch (fused.hip)
 };
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
@@ -53,7 +58,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_SHAPE, "I must be a multiple of 64 in [64, 65536] (got %lld)", (long long)p->I);
   if (p->T > (int64_t)0x7fffffff / p->K)
     return fail(HMM_ERR_BAD_SHAPE, "T*K must stay below 2^31 (T=%lld, K=%lld)", (long long)p->T, (long long)p->K);
-  if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW))
+  if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW | HMM_FLAG_FUSED_FORWARD))
     return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
   if ((p->flags & HMM_FLAG_TILES_LARGE) && (p->flags & HMM_FLAG_TILES_NARROW))
     return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
@@ -85,6 +90,8 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
+  d->fused = d->small && !d->fp8 && !d->f32 && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
+             d->E <= hmm::RT_ONE_MAX_EXPERTS && (p->flags & HMM_FLAG_FUSED_FORWARD);
   return HMM_OK;
 }
 
@@ -144,7 +151,7 @@ RouteScratch route_scratch(const Dims& d, size_t base) {
 // maxima of the weight quantisation.
 struct FwdWork {
   RouteScratch rs;
-  size_t o, xq, dsx, wq, dsw, pmax, total;
+  size_t o, xq, dsx, wq, dsw, pmax, sync, total;
 };
 FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
@@ -157,6 +164,9 @@ FwdWork fwd_work(const Dims& d) {
     w.wq = o;   o += up(d.E * d.H * 2 * d.I);
     w.dsw = o;  o += up(d.E * 2 * d.I * 4);
     w.pmax = o; o += up(hmm::quant_cols_chunks(d.H) * d.E * 2 * d.I * 4);
+  }
+  if (d.fused) {
+    w.sync = o; o += up(hmm::fused_forward_sync_words(d.S, d.E) * 4);  // tile-ready counters
   }
   w.total = o;
   return w;
@@ -235,10 +245,12 @@ struct Stage {
 // device-visible) host word that the routing kernel writes, and an event recorded
 // after the routing.  Created on first use with that device current.
 constexpr int MAX_DEVICES = 64;
+constexpr int32_t ID_PENDING = -1;  // the id-check word before the routing has written it
 struct DevState {
   bool ready = false;
   int32_t* word = nullptr;
   hipEvent_t id_ev = nullptr;
+  int cus = 0;  // compute units (the fused kernel's workgroup count: all resident)
 };
 DevState* dev_state() {
   thread_local DevState st[MAX_DEVICES];
@@ -248,6 +260,7 @@ DevState* dev_state() {
   if (c.ready) return &c;
   bool ok = hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocCoherent) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&c.id_ev, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c.cus > 0;
   if (!ok) {  // release whatever was made; the next call tries again
     if (c.word) (void)hipHostFree(c.word);
     if (c.id_ev) (void)hipEventDestroy(c.id_ev);
@@ -269,7 +282,7 @@ hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t
   if (validate_ids) {
     c = dev_state();
     if (!c) return fail(HMM_ERR_HIP, "could not create the per-device id-check word or event");
-    *c->word = 0;
+    *c->word = ID_PENDING;
   }
   hipError_t e;
   {
@@ -287,13 +300,38 @@ hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t
   return HMM_OK;
 }
 
+// The routing stores 0 or 1 into the host word as soon as the ids are checked
+// (the word holds ID_PENDING until then); the host polls it, and falls back on
+// the event recorded after the launch that contains the routing.
 hmm_status finish_id_check(const Dims& d) {
   DevState* c = dev_state();
   if (!c) return fail(HMM_ERR_HIP, "id-check state missing");
-  hipError_t e = hipEventSynchronize(c->id_ev);
-  if (e != hipSuccess) return hip_fail(e, "id-validation wait");
-  if (*c->word) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
+  volatile int32_t* w = c->word;
+  int32_t v = *w;
+  for (uint32_t spin = 0; v == ID_PENDING; ++spin) {
+    if ((spin & 1023) == 1023) {
+      const hipError_t q = hipEventQuery(c->id_ev);
+      if (q == hipSuccess) {
+        v = *w;
+        if (v == ID_PENDING) return fail(HMM_ERR_HIP, "the routing did not report its id check");
+        break;
+      }
+      if (q != hipErrorNotReady) return hip_fail(q, "id-validation wait");
+    }
+    v = *w;
+  }
+  if (v) return fail(HMM_ERR_EXPERT_ID_OUT_OF_RANGE, "topk_ids holds a value outside [0, E=%lld)", (long long)d.E);
   return HMM_OK;
+}
+
+// A per-call value for the fused kernel's flag word: distinct for 2^32 calls of
+// this process and unlikely to be left in a workspace by anything else.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  static const uint32_t salt =
+      (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ ((uint32_t)getpid() * 2654435761u);
+  const uint32_t e = salt + counter.fetch_add(1) * 2654435761u;
+  return e ? e : 1u;
 }
 
 }  // namespace
@@ -459,6 +497,29 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   int32_t* tiles = at<int32_t>(saved, L.tiles);
   int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
   const bool validate_ids = (p->flags & HMM_FLAG_VALIDATE_IDS) != 0;
+  if (d.fused) {
+    // small problem: routing, both products and the combine in one launch
+    DevState* c = dev_state();
+    if (!c) return fail(HMM_ERR_HIP, "could not create the per-device id-check word or event");
+    if (validate_ids) *c->word = ID_PENDING;
+    hipError_t e;
+    {
+      Stage stage("fused_forward", st);
+      e = hmm::launch_fused_forward(topk_ids, d.T, d.H, d.I, (int)d.E, (int)d.K, (const uint16_t*)x,
+                                    (const uint16_t*)up_w, (const uint16_t*)down_w, topk_weights, (uint16_t*)y,
+                                    at<int32_t>(saved, L.counts), offsets, sorted_slot,
+                                    at<int32_t>(saved, L.row_of_slot), tok_of_row, tiles,
+                                    at<int32_t>(saved, L.id_error), validate_ids ? c->word : nullptr,
+                                    at<uint16_t>(saved, L.h), at<uint16_t>(saved, L.a), at<uint16_t>(saved, L.aw),
+                                    at<uint16_t>(workspace, W.o), at<uint32_t>(workspace, W.sync), next_epoch(),
+                                    c->cus, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+    if (!validate_ids) return HMM_OK;
+    e = hipEventRecord(c->id_ev, st);
+    if (e != hipSuccess) return hip_fail(e, "id-validation event");
+    return finish_id_check(d);
+  }
   s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
                 tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, st);
   if (s != HMM_OK) return s;

@@ -1,0 +1,413 @@
+// Policies of the bf16 products (what A and B are, how their tiles are
+// addressed, what the epilogue does), for gemm_core.h's main loop: the
+// row-grouped up-projection + SwiGLU, down-projection, act_grad + SwiGLUGrad and
+// input_grad, and the two weight gradients.  Included by the launchers
+// (gemm.hip) and by the fused small-problem kernels (fused.hip).
+#pragma once
+
+#include "gemm_core.h"
+
+namespace hmm {
+namespace {
+
+// ------------------------------------------------------------- gmm1 + SwiGLU
+template <class Cc, bool SMALL>
+struct Gmm1 : RowTile<Cc, SMALL> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::nt;
+  static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  struct Args {
+    RowGroups g;
+    const uint16_t* x;
+    const uint16_t* w1;
+    const float* tw;
+    int64_t T, H, I;
+    uint16_t *h, *a, *aw;
+    int n_ntiles;
+    bool coh = false;  // ``a`` goes to the coherence point (read by another XCD in the same launch)
+  };
+  const Args* ar;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+  int i0;
+  // the B tile holds BN/2 gate columns then the BN/2 matching up columns; the
+  // epilogue pairs them through LDS
+  __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    i0 = nt * (C::BN / 2);
+    ra_ = make_rsrc(A.x, A.T * A.H * 2);
+    this->template a_rows<true>(A.g, A.H, aoff);
+    rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
+    const int tid = threadIdx.x;
+    constexpr int CPR = C::BN / 8, HALF = C::BN / 16;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
+      const int64_t gi = min((int64_t)(i0 + (c8 % HALF) * 8), A.I - 8);   // gate column (clamped)
+      const int64_t col = (c8 < HALF) ? gi : A.I + gi;
+      boff[i] = (uint32_t)((kr * 2 * A.I + col) * 2);
+    }
+    nk = (int)(A.H / BK);
+    return true;
+  }
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    const uint32_t so = (uint32_t)(kt * BK * 2 * ar->I * 2);
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
+  }
+  // g and u (rounded to bf16) are staged in LDS as the [BM][BN] tile (gate
+  // columns first); then each thread takes 8 consecutive columns of one row and
+  // writes h (both halves), a = bf16(silu(g) u) and aw = bf16(w a) as 16-byte chunks.
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    constexpr int LD = C::BN + 8;
+    static_assert(C::BM * LD * 2 + C::BM * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    float* wrow = reinterpret_cast<float*>(smem + C::BM * LD);
+    const int tid = threadIdx.x;
+    for (int t = tid; t < C::BM; t += C::NTHR)
+      wrow[t] = (t < rows) ? ar->tw[get(ar->g.sorted_slot + row0 + t, ar->g.coh)] : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          smem[acc_row<C>(wm, mb, r, lane) * LD + ncol0(wn, nb) + (lane & 31)] = f2bf(acc[mb][nb][r]);
+    __syncthreads();
+    const int64_t I = ar->I;
+    constexpr int CPR = C::BN / 16;  // 8-column chunks of the gate half
+    for (int c = tid; c < C::BM * CPR; c += C::NTHR) {
+      const int row = c / CPR, c8 = c % CPR;
+      const int64_t i = i0 + c8 * 8;
+      if (row >= rows || i >= I) continue;
+      const int64_t p = row0 + row;
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(smem + row * LD + C::BN / 2 + c8 * 8);
+      float g[8], u[8], av[8], aw[8];
+      unpack8(gv, g);
+      unpack8(uv, u);
+      const float w = wrow[row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[j] = round_bf(g[j] * sigmoidf_(g[j]) * u[j]);
+        aw[j] = w * av[j];
+      }
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
+      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
+      put16(ar->a, ar->g.S * I * 2, p * I + i, pack8(av), ar->coh);
+      *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
+    }
+  }
+};
+
+// ------------------------------------------------------------- gmm2
+template <class Cc, bool SMALL>
+struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
+  using PlainCols<Cc>::ncol0;
+  static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  struct Args {
+    RowGroups g;
+    const uint16_t* a;
+    const uint16_t* w2;
+    int64_t S, H, I;
+    uint16_t* o;
+    int n_ntiles;
+    bool coh = false;  // ``o`` goes to the coherence point (read by another XCD in the same launch)
+  };
+  const Args* ar;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.a, A.S * A.I * 2);
+    this->template a_rows<false>(A.g, A.I, aoff);
+    rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
+    const int tid = threadIdx.x;
+    constexpr int CPR = C::BN / 8;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
+      const int64_t col = min((int64_t)(n0 + c8 * 8), A.H - 8);
+      boff[i] = (uint32_t)((kr * A.H + col) * 2);
+    }
+    nk = (int)(A.I / BK);
+    return true;
+  }
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+    if (ar->coh) {  // ``a`` was written in the same launch: read it at the coherence point
+#pragma unroll
+      for (int i = 0; i < C::CA; ++i) r[i] = bload_coh(ra_, aoff[i], kt * BK * 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    }
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+    const uint32_t so = (uint32_t)(kt * BK * ar->H * 2);
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, Gmm2>(acc, wm, wn, lane, smem, ar->o, ar->H, row0, rows, n0, ar->H, ar->coh, ar->S);
+  }
+};
+
+// ------------------------------------------------------------- act_grad + SwiGLUGrad
+template <class Cc, bool SMALL>
+struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0; using B_::nt;
+  using PlainCols<Cc>::ncol0;
+  static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  struct Args {
+    RowGroups g;
+    const uint16_t* dy;
+    const uint16_t* w2;
+    const float* tw;
+    const uint16_t* h;
+    const uint16_t* a;
+    int64_t T, H, I;
+    uint16_t* dh;
+    float* dwpart;
+    int dw_cols;
+    int n_ntiles;
+  };
+  const Args* ar;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.dy, A.T * A.H * 2);
+    this->template a_rows<true>(A.g, A.H, aoff);
+    rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
+    this->b_rows(A.H, A.I, boff);
+    nk = (int)(A.H / BK);
+    return true;
+  }
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
+  }
+  // G stays in float32: one wave column (TN columns) at a time it is staged in
+  // LDS, then each thread takes 8 consecutive columns of one row, reads g, u and
+  // a as 16-byte chunks, writes dH = [dg | du] as 16-byte chunks and adds its
+  // share of sum_i G a.  The row sums are reduced in a fixed order (8-lane
+  // butterfly, then wave columns in order): one partial per (row, N tile).
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
+    constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
+    constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
+    static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
+    static_assert((C::BM * LDF + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    float* gst = reinterpret_cast<float*>(smem);
+    float* wrow = gst + C::BM * LDF;
+    const int tid = threadIdx.x;
+    for (int t = tid; t < C::BM; t += C::NTHR)
+      wrow[t] = (t < rows) ? ar->tw[get(ar->g.sorted_slot + row0 + t, ar->g.coh)] : 0.f;
+    const int64_t I = ar->I;
+    float part[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) part[k] = 0.f;
+    for (int q = 0; q < C::WN; ++q) {
+      if (wn == q) {
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              gst[acc_row<C>(wm, mb, r, lane) * LDF + nb * 32 + (lane & 31)] = acc[mb][nb][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int c = tid + k * C::NTHR;
+        const int row = c / CPR, c8 = c % CPR;
+        const int64_t i = n0 + q * C::TN + c8 * 8;
+        float s = 0.f;
+        if (row < rows && i < I) {
+          const int64_t p = row0 + row;
+          float g[8], u[8], av[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + i), g);
+          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + I + i), u);
+          unpack8(*reinterpret_cast<const u32x4*>(ar->a + p * I + i), av);
+          const float w = wrow[row];
+          const float* G = gst + row * LDF + c8 * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            s += G[j] * av[j];
+            const float dA = w * G[j];
+            const float sg = sigmoidf_(g[j]);
+            dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
+            du[j] = dA * g[j] * sg;
+          }
+          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + i) = pack8(dg);
+          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + I + i) = pack8(du);
+        }
+        // the CPR threads of a row are consecutive lanes: fixed-order butterfly
+#pragma unroll
+        for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+        part[k] += s;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = tid + k * C::NTHR;
+      const int row = c / CPR;
+      if (c % CPR == 0 && row < rows) ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
+    }
+  }
+};
+
+// ------------------------------------------------------------- input_grad
+template <class Cc, bool SMALL>
+struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  typedef RowTile<Cc, SMALL> B_;
+  typedef Cc C;
+  using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
+  using PlainCols<Cc>::ncol0;
+  static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  struct Args {
+    RowGroups g;
+    const uint16_t* dh;
+    const uint16_t* w1;
+    int64_t S, H, I;
+    uint16_t* dxp;
+    int n_ntiles;
+  };
+  const Args* ar;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    ra_ = make_rsrc(A.dh, A.S * 2 * A.I * 2);
+    this->template a_rows<false>(A.g, 2 * A.I, aoff);
+    rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
+    this->b_rows(2 * A.I, A.H, boff);
+    nk = (int)(2 * A.I / BK);
+    return true;
+  }
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, InputGrad>(acc, wm, wn, lane, smem, ar->dxp, ar->H, row0, rows, n0, ar->H);
+  }
+};
+
+// ------------------------------------------------------------- weight gradients
+// C[e][m][n] = sum over the expert's rows p of A[p][m] * B[p][n]; both operands
+// are read along their row (m or n contiguous) and transposed by the LDS read.
+template <class Cc, bool GATHER_A, bool GATHER_B>
+struct Dw : PlainCols<Cc> {
+  typedef Cc C;
+  static constexpr bool RAW_INDEX = true;  // init maps the workgroup index to XCDs itself
+  using PlainCols<Cc>::ncol0;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false;
+  struct Args {
+    const int32_t* offsets;
+    const int32_t* tok_of_row;
+    int64_t E;
+    const uint16_t* A;  // [rows or tokens][M]
+    const uint16_t* B;  // [rows or tokens][N]
+    int64_t a_rows, b_rows;  // rows held by A and B
+    int64_t M, N;
+    uint16_t* Cout;     // [E][M][N]
+    int mt, nt;
+  };
+  const Args* ar;
+  rsrc_t ra_, rb_;
+  int e, m0, n0, nk, p0, p1;
+  // byte offsets of the rows of the next step to be loaded (computed by index())
+  uint32_t rowoff_a[C::CA], rowoff_b[C::CB];
+  // The cost of a tile grows with its expert's row count, so every XCD gets an
+  // equal slice of every expert's tiles (not a contiguous run of experts): XCD x
+  // (workgroups b with b % 8 == x) walks the experts in order and takes tiles
+  // [x * per, (x + 1) * per) of each, per = ceil(mt * nt / 8); inside a slice the
+  // tiles are rasterised in groups of GROUP_M row tiles.
+  __device__ __forceinline__ bool init(const Args& A, int b) {
+    ar = &A;
+    const int per_e = A.mt * A.nt;
+    const int per = (per_e + 7) / 8;
+    const int j = b >> 3;
+    e = j / per;
+    if (e >= A.E) return false;
+    const int t = (b & 7) * per + (j - e * per);
+    if (t >= per_e) return false;
+    int r, c;
+    raster(t, A.mt, A.nt, r, c);
+    m0 = r * C::BM;
+    n0 = c * C::BN;
+    p0 = A.offsets[e];
+    p1 = A.offsets[e + 1];
+    nk = (p1 - p0 + BK - 1) / BK;
+    ra_ = make_rsrc(A.A, A.a_rows * A.M * 2);
+    rb_ = make_rsrc(A.B, A.b_rows * A.N * 2);
+    return true;
+  }
+  // row part of the offsets of step kt: rows p past the expert's end and columns
+  // past the matrix get the resource's end (reads zeros)
+  template <bool GATHER, int R, int CN>
+  __device__ __forceinline__ void rows_of(int64_t nrows, int64_t ld, int64_t c0, int kt, uint32_t (&ro)[CN]) {
+    const int tid = threadIdx.x;
+    constexpr int CPR = R / 8;
+    const uint32_t end = (uint32_t)(nrows * ld * 2);
+#pragma unroll
+    for (int i = 0; i < CN; ++i) {
+      const int c = tid + i * C::NTHR;
+      const int kr = c / CPR, c8 = c % CPR;
+      const int p = p0 + kt * BK + kr;
+      const int64_t col = c0 + c8 * 8;
+      uint32_t off = end;
+      if (p < p1 && col < ld) {
+        const int64_t row = GATHER ? (int64_t)ar->tok_of_row[p] : (int64_t)p;
+        off = (uint32_t)((row * ld + col) * 2);
+      }
+      ro[i] = off;
+    }
+  }
+  __device__ __forceinline__ void index(int kt) {
+    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->M, m0, kt, rowoff_a);
+    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->N, n0, kt, rowoff_b);
+  }
+  __device__ __forceinline__ void load_a(int, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, rowoff_a[i], 0);
+  }
+  __device__ __forceinline__ void load_b(int, u32x4 (&r)[C::CB]) {
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, rowoff_b[i], 0);
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
+    store_tile<C, Dw>(acc, wm, wn, lane, smem, ar->Cout + (int64_t)e * ar->M * ar->N, ar->N, m0,
+                      (int)min((int64_t)C::BM, ar->M - m0), n0, ar->N);
+  }
+};
+
+}  // namespace
+}  // namespace hmm

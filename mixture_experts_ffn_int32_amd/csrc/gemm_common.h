@@ -33,5 +33,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
+// the same at the device-wide coherence point (sc1), for data written earlier in the same launch
+__device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 16));
+}
 
 }  // namespace hmm

@@ -79,12 +79,13 @@ __device__ __forceinline__ void store_stage(uint16_t* st, const u32x4 (&ra)[C::C
     *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
 }
 
-// The main loop of every bf16 product, for workgroup ``bid`` of ``nblocks``.
+// The main loop of every bf16 product for tile ``idx`` (the index the policy's
+// init takes); false if that tile does not exist.  The whole workgroup calls it.
 template <class P>
-__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, int nblocks, uint16_t* smem) {
+__device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx, uint16_t* smem) {
   typedef typename P::C C;
   P pol;
-  if (!pol.init(args, P::RAW_INDEX ? bid : xcd_remap(bid, nblocks))) return;
+  if (!pol.init(args, idx)) return false;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -152,6 +153,13 @@ __device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid,
     if (kt < nk) step(kt, ra1, rb1);
   }
   pol.epilogue(acc, wm, wn, lane, smem);
+  return true;
+}
+
+// ... for workgroup ``bid`` of ``nblocks`` of a launch
+template <class P>
+__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, int nblocks, uint16_t* smem) {
+  (void)gemm_tile<P>(args, P::RAW_INDEX ? bid : xcd_remap(bid, nblocks), smem);
 }
 
 template <class P>
@@ -178,10 +186,27 @@ __global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_pair_kernel(const typenam
 // Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
 // [BM][BN] tile and written out as 16-byte row chunks (rows < valid_rows,
 // columns < ncols), so every global store is a full, coalesced vector.
+// A routing array element; with ``coh`` read at the device-wide coherence point
+// (an agent-scope load, sc1: the array was written in the same launch, maybe on
+// another XCD, and this XCD's L2 may still hold an older copy).
+__device__ __forceinline__ int32_t get(const int32_t* p, bool coh) {
+  return coh ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+}
+
+// A 16-byte store of a result; with ``coh`` it goes to the device-wide coherence
+// point (sc1, as an agent-scope store), for a consumer on another XCD in the same
+// launch.  ``base``/``bytes`` describe the whole output array (below 4 GiB).
+__device__ __forceinline__ void put16(uint16_t* base, int64_t bytes, int64_t elem, u32x4 v, bool coh) {
+  if (coh)
+    __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(base, bytes), (uint32_t)(elem * 2), 0, 16);
+  else
+    *reinterpret_cast<u32x4*>(base + elem) = v;
+}
+
 template <class C, class P>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem,
                                            uint16_t* out, int64_t ld, int64_t row_base, int valid_rows,
-                                           int64_t col_base, int64_t ncols) {
+                                           int64_t col_base, int64_t ncols, bool coh = false, int64_t out_rows = 0) {
   constexpr int LD = C::BN + 8;
   static_assert(C::BM * LD <= 2 * C::STAGE, "staging tile must fit in the LDS buffers");
 #pragma unroll
@@ -197,8 +222,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[C::MB][C::NB], in
     const int row = c / CPR, c8 = c % CPR;
     const int64_t col = col_base + c8 * 8;
     if (row < valid_rows && col < ncols)
-      *reinterpret_cast<u32x4*>(out + (row_base + row) * ld + col) =
-          *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8);
+      put16(out, out_rows * ld * 2, (row_base + row) * ld + col, *reinterpret_cast<const u32x4*>(smem + row * LD + c8 * 8),
+            coh);
   }
 }
 
@@ -221,11 +246,11 @@ struct RowTile {
     if (logical >= R * n_ntiles) return false;
     int j;
     raster(logical, R, n_ntiles, j, nt);
-    if (j >= g.tiles[SMALL ? 1 : 0]) return false;
+    if (j >= get(g.tiles + (SMALL ? 1 : 0), g.coh)) return false;
     const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-    e = tab[2 * j];
-    row0 = tab[2 * j + 1];
-    rows = min(C::BM, g.offsets[e + 1] - row0);
+    e = get(tab + 2 * j, g.coh);
+    row0 = get(tab + 2 * j + 1, g.coh);
+    rows = min(C::BM, get(g.offsets + e + 1, g.coh) - row0);
     n0 = nt * C::BN;
     return true;
   }
@@ -238,7 +263,7 @@ struct RowTile {
     for (int i = 0; i < C::CA; ++i) {
       const int c = tid + i * C::NTHR;
       const int p = row0 + min(c >> 3, rows - 1);
-      const int64_t row = GATHER ? (int64_t)g.tok_of_row[p] : (int64_t)p;
+      const int64_t row = GATHER ? (int64_t)get(g.tok_of_row + p, g.coh) : (int64_t)p;
       off[i] = (uint32_t)((row * ld + (c & 7) * 8) * 2);
     }
   }

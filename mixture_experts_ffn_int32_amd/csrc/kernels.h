@@ -59,6 +59,8 @@ struct RowGroups {
   int64_t max_big, max_small;  // table capacities
   int64_t T, S;                // tokens, routed rows (extents of the buffer resources)
   bool narrow;                 // small-problem mode: 64x64 tiles over the small table only
+  bool coh = false;            // the arrays above were written in the same launch (fused
+                               // kernel): read them at the device-wide coherence point
 };
 
 // h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
@@ -112,6 +114,19 @@ hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, cons
 // combine(dX) (unweighted) with d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c] folded in
 hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
                              uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
+
+// Fused small-problem forward (fused.hip): routing, up-projection + SwiGLU,
+// down-projection and combine in one launch of at most max_groups workgroups
+// (all resident), synchronised through fused_forward_sync_words(S, E) counters
+// in ``sync`` that the call resets itself (epoch: a nonzero per-call value).
+// Needs S <= RT_ONE_MAX_SLOTS, E <= RT_ONE_MAX_EXPERTS and the narrow tiling.
+int64_t fused_forward_sync_words(int64_t S, int64_t E);
+hipError_t launch_fused_forward(const int32_t* ids, int64_t T, int64_t H, int64_t I, int E, int K, const uint16_t* x,
+                                const uint16_t* w1, const uint16_t* w2, const float* topk_w, uint16_t* y,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot,
+                                int32_t* tok_of_row, int32_t* tiles, int32_t* err, int32_t* host_err, uint16_t* h,
+                                uint16_t* a, uint16_t* aw, uint16_t* o, uint32_t* sync, uint32_t epoch, int max_groups,
+                                hipStream_t stream);
 
 // float32-output (accuracy) mode (gemm_f32.hip, pointwise.hip).  Operands that are
 // not exact bf16 inputs are bf16 [hi | lo] pairs of twice the width; see gemm_f32.hip.

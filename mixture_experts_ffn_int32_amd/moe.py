@@ -258,14 +258,18 @@ def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16"):
 
 
 def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True,
-                       tiles="auto", gmm1_dtype="bf16", out_dtype="bf16"):
+                       tiles="auto", gmm1_dtype="bf16", out_dtype="bf16", fused=False):
     """Forward without autograd; returns (y, saved buffer) for stage-level checks.
 
     ``tiles`` forces the tiling of the grouped products ("auto", "large" or
     "narrow"); the matching backward_from_saved call must use the same value.
+    ``fused=True`` runs a small problem's forward as one persistent launch
+    (same results; slower on MI355X today, see include/hmm.h).
     """
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | _lib.TILE_FLAGS[tiles]
+    if fused:
+        flags |= _lib.HMM_FLAG_FUSED_FORWARD
     with torch.cuda.device(x.device):
         return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
                             _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags,

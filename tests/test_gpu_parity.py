@@ -231,3 +231,63 @@ def test_full_size_hotspot_sampled():
 def test_full_size_fp8_sampled():
     """FP8 up-projection workload (T=16384, H=4096, I=1536, E=64, K=6)."""
     _sample_full("fp8", n_tok=4)
+
+
+# ----------------------------------------------------------------------------- fused small-problem forward (opt-in)
+
+FUSED = [
+    ("sample-like", dict(T=1024, H=512, I=128, E=4, K=2, routing="uniform")),
+    ("ragged", dict(T=300, H=256, I=192, E=6, K=3, routing="uniform")),
+    ("k1", dict(T=200, H=128, I=128, E=3, K=1, routing="uniform")),
+    ("zipf-empty", dict(T=411, H=256, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
+    ("max-slots", dict(T=1024, H=128, I=64, E=256, K=8, routing="uniform")),
+]
+
+
+@pytest.mark.parametrize("name,over", FUSED, ids=[f[0] for f in FUSED])
+def test_fused_forward_equals_kernel_sequence(name, over):
+    """The one-launch forward gives bit-identical y and saved arrays to the kernel sequence."""
+    import torch
+    from mixture_experts_ffn_int32_amd import forward_with_saved, saved_views
+    spec = synth.spec_with("tiny", **over)
+    inp = synth.make_inputs(spec, seed=41)
+    announce("fused forward %s %s" % (name, {k: spec[k] for k in "THIEK"}))
+    g = gpu_inputs(inp, "cuda")
+    args = (g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"])
+    y1, s1 = forward_with_saved(*args, tiles="narrow", fused=True)
+    y0, s0 = forward_with_saved(*args, tiles="narrow", fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0)
+    v1 = saved_views(s1, *(spec[k] for k in "THIEK"), tiles="narrow")
+    v0 = saved_views(s0, *(spec[k] for k in "THIEK"), tiles="narrow")
+    for k in v1:
+        assert torch.equal(v1[k], v0[k]), k
+
+
+def test_fused_forward_reuses_its_workspace():
+    """Raw calls on one workspace: counters from the previous call never leak into the next."""
+    import ctypes
+    import torch
+    from mixture_experts_ffn_int32_amd import _lib, forward_with_saved
+    spec = synth.spec_with("tiny", T=512, H=256, I=128, E=8, K=2, routing="uniform")
+    T, H, I, E, K = (spec[k] for k in "THIEK")
+    lib = _lib.load()
+    prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, _lib.HMM_BF16,
+                        _lib.HMM_FLAG_VALIDATE_IDS | _lib.HMM_FLAG_FUSED_FORWARD | _lib.HMM_FLAG_TILES_NARROW, 0)
+    ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
+    work = torch.full((ws.value,), 0xA5, dtype=torch.uint8, device="cuda")   # garbage counters at the start
+    saved = torch.empty(sv.value, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for seed in (50, 51, 52):
+        g = gpu_inputs(synth.make_inputs(spec, seed=seed), "cuda")
+        announce("fused forward, reused workspace, seed %d" % seed)
+        _lib.check(lib.hmm_forward(ctypes.byref(prob), P(g["x"]), P(g["topk_ids"]), P(g["topk_weights"]),
+                                   P(g["up_proj_weight"]), P(g["down_proj_weight"]), P(y), P(saved), sv.value,
+                                   P(work), ws.value, stream))
+        ref, _ = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
+                                    g["down_proj_weight"], tiles="narrow", fused=False)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
