@@ -114,7 +114,7 @@ class MoEFFN:
     """
 
     def __init__(self, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
-                 dY=None, mode="faithful", gmm1="bf16"):
+                 dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None):
         if mode not in ("pure", "faithful"):
             raise ValueError(mode)
         if gmm1 not in ("bf16", "fp8"):
@@ -137,6 +137,19 @@ class MoEFFN:
             raise ValueError("weights must be [E,H,2I] and [E,I,H]")
         check_ids(self.ids, self.E)
         self._w1, self._w2, self._w1q = {}, {}, {}
+        # Shared expert (RFC 6.1: an optional shared expert whose GMM1, SwiGLU and GMM2
+        # run with the routed experts and whose output joins at the Combine).  Reading:
+        # every token goes through it with weight 1; its output is added after the K
+        # routed terms of the combine sum (and its dX after the K routed dXp terms).
+        # It is evaluated as a one-expert, K = 1 problem of its own (bf16 products).
+        self.shared = None
+        if shared_up_proj_weight is not None:
+            ws1 = np.asarray(shared_up_proj_weight)
+            ws2 = np.asarray(shared_down_proj_weight)
+            if ws1.ndim != 2 or ws1.shape[0] != self.H or ws2.shape != (ws1.shape[1] // 2, self.H):
+                raise ValueError("shared weights must be [H, 2Is] and [Is, H]")
+            self.shared = MoEFFN(self.x, np.zeros((self.T, 1), np.int64), np.ones((self.T, 1), np.float32),
+                                 ws1[None], ws2[None], dY=self.dY, mode=mode)
 
     # -- helpers ---------------------------------------------------------------
     def _round(self, v, d):
@@ -236,6 +249,8 @@ class MoEFFN:
         toks = np.arange(self.T) if tokens is None else np.asarray(tokens)
         y = np.zeros((toks.size, self.H))
         yd = np.zeros((toks.size, self.H))
+        if self.shared is not None:  # shared output o_s (R3 of the shared problem; its R4 of one term is exact)
+            ys, ysd = self.shared.forward_dev(toks, out_dtype)
         for j, t in enumerate(toks):
             acc = np.zeros(self.H)
             accd = np.zeros(self.H)
@@ -247,8 +262,11 @@ class MoEFFN:
                 acc = acc + self.w[t, k] * o[0]
                 accd = accd + abs(self.w[t, k]) * od[0]
                 sq = sq + (self.w[t, k] * o[0]) ** 2
+            nterm = self.K
+            if self.shared is not None:
+                acc, accd, sq, nterm = acc + ys[j], accd + ysd[j], sq + ys[j] ** 2, self.K + 1
             if out_dtype == "bf16":
-                y[j], yd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, self.K))      # R4
+                y[j], yd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, nterm))      # R4
             else:
                 y[j], yd[j] = acc, accd
         return y, yd
@@ -283,6 +301,8 @@ class MoEFFN:
         dxd = np.zeros((toks.size, self.H))
         dw = np.zeros((toks.size, self.K))
         dwd = np.zeros((toks.size, self.K))
+        if self.shared is not None:  # the shared dX rows (R6 of the shared problem)
+            (dxs, _), (dxsd, _) = self.shared.backward_tokens_dev(toks, out_dtype)
         for j, t in enumerate(toks):
             acc = np.zeros(self.H)
             accd = np.zeros(self.H)
@@ -302,8 +322,11 @@ class MoEFFN:
                 acc = acc + xp[0]
                 accd = accd + xpd[0]
                 sq = sq + xp[0] ** 2
+            nterm = self.K
+            if self.shared is not None:
+                acc, accd, sq, nterm = acc + dxs[j], accd + dxsd[j], sq + dxs[j] ** 2, self.K + 1
             if out_dtype == "bf16":
-                dx[j], dxd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, self.K))     # R7
+                dx[j], dxd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, nterm))     # R7
             else:
                 dx[j], dxd[j] = acc, accd
         return (dx, dw), (dxd, dwd)
@@ -367,3 +390,13 @@ class MoEFFN:
     def backward(self, out_dtype="bf16"):
         """Full backward: dx [T,H], d_topk_weights [T,K], dW1 [E,H,2I], dW2 [E,I,H]."""
         return self.backward_dev(out_dtype)[0]
+
+    # -- shared expert -----------------------------------------------------------
+    def shared_weight_grads_dev(self, icols=None, out_dtype="bf16"):
+        """Gradients of the shared weights, as weight_grads_expert_dev of its one-expert problem."""
+        return self.shared.weight_grads_expert_dev(0, icols, out_dtype)
+
+    def shared_backward_dev(self, out_dtype="bf16"):
+        """((d_shared_up [H,2Is], d_shared_down [Is,H]), their devs)."""
+        (g, u, r), (gd, ud, rd) = self.shared_weight_grads_dev(None, out_dtype)
+        return (np.concatenate([g, u], 1), r), (np.concatenate([gd, ud], 1), rd)
