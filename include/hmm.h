@@ -89,7 +89,7 @@ typedef enum hmm_dtype {
 #define HMM_FLAG_TILES_NARROW 4u
 
 /* Run the forward of a small problem (narrow tiling, S <= 8192, E <= 256, bf16
- * outputs and bf16 up-projection) as ONE persistent launch: routing, both
+ * outputs, bf16 up-projection, no shared expert) as ONE persistent launch: routing, both
  * products and the combine, with tile-ready counters between them (RFC 6.1).
  * The results are identical to the kernel sequence.  On MI355X it is slower
  * today (every array one tile writes for another has to go through the
@@ -116,13 +116,16 @@ typedef enum hmm_dtype {
  *               dynamic quantisation of MoeDistributeDispatchV2, case 3);
  *               H must then be a multiple of 128.  Only the up-projection
  *               changes: the rest of the forward and the backward stay bf16.
- *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward. */
+ *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward.
+ *   shared_I    0, or the intermediate size Is of a shared expert (a multiple of
+ *               64 in [64, 65536]): then the calls are hmm_forward_shared and
+ *               hmm_backward_shared, which take its weights. */
 typedef struct hmm_problem {
   int64_t T, H, I, E, K;
   int32_t out_dtype;
   int32_t gmm1_dtype;
   uint32_t flags;
-  uint32_t reserved; /* must be 0 */
+  uint32_t shared_I;
 } hmm_problem;
 
 /* Byte offsets of the arrays a forward call records in ``saved`` (for tests
@@ -139,9 +142,20 @@ typedef struct hmm_problem {
  *   aw[S,I] bf16         topk weight * a, the W2-gradient operand
  *                        (out_dtype HMM_F32: h is float32 [S,2I]; a and aw are
  *                        bf16 [S,2I] holding hi in columns [0,I), lo in [I,2I))
- *   id_error int32       1 if an id was out of range on the recording call */
+ *   id_error int32       1 if an id was out of range on the recording call
+ * With a shared expert (shared_I = Is > 0; all of these are empty without one):
+ *   shared_offsets[2] int32  {0, T}: one group holding every token
+ *   shared_idx[T] int32      0 .. T-1 (the group's rows are the tokens in order)
+ *   shared_ones[T] float32   1.0, the shared expert's combine weight
+ *   shared_tiles             int32 tile table of that group
+ *   shared_h[T,2Is] bf16     the shared up-projection output ([gate | up])
+ *   shared_a[T,Is] bf16      the shared SwiGLU output
+ *                            (HMM_F32: shared_h float32 [T,2Is], shared_a bf16
+ *                            [T,2Is] as hi | lo) */
 typedef struct hmm_saved_layout {
-  size_t counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, h, a, aw, id_error, total;
+  size_t counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, h, a, aw, id_error;
+  size_t shared_offsets, shared_idx, shared_ones, shared_tiles, shared_h, shared_a;
+  size_t total;
 } hmm_saved_layout;
 
 /* Sizes of the forward's workspace and saved buffers for ``p`` (bytes). */
@@ -162,11 +176,30 @@ hmm_status hmm_saved_layout_of(const hmm_problem* p, hmm_saved_layout* out);
  *   workspace     forward_sizes' workspace_bytes of scratch (free after the
  *                 call has executed on the stream)
  * On HMM_ERR_EXPERT_ID_OUT_OF_RANGE (with HMM_FLAG_VALIDATE_IDS) the contents
- * of y and saved are unspecified. */
+ * of y and saved are unspecified.  Needs p->shared_I == 0 (else
+ * HMM_ERR_BAD_SHAPE: use hmm_forward_shared). */
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids,
                        const float* topk_weights, const void* up_w, const void* down_w, void* y,
                        void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Forward with a shared expert (RFC section 6.1: a shared expert fused into the
+ * same pipeline, its output merged at the Combine).  Every token also goes
+ * through one dense SwiGLU FFN of intermediate size Is = p->shared_I:
+ *   [gs|us] = x[t] . shared_up_w;  as = silu(gs) * us;  os = as . shared_down_w;
+ *   y[t] = sum_k topk_weights[t,k] * o_k  +  os,
+ * the shared term added last, in the same float32 sum, before the one rounding
+ * of y.  Its products run on the same kernels as the routed experts' (as one
+ * more group of all T tokens; bf16 also when gmm1_dtype is FP8).
+ *   shared_up_w    bf16 [H,2Is]   columns [0,Is) gate, [Is,2Is) up
+ *   shared_down_w  bf16 [Is,H]
+ * The other arguments are those of hmm_forward; the sizes come from
+ * hmm_forward_sizes of the same problem.  With p->shared_I == 0 this is
+ * hmm_forward (the shared pointers are ignored). */
+hmm_status hmm_forward_shared(const hmm_problem* p, const void* x, const int32_t* topk_ids,
+                              const float* topk_weights, const void* up_w, const void* down_w,
+                              const void* shared_up_w, const void* shared_down_w, void* y, void* saved,
+                              size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Size of the backward's workspace (bytes). */
 hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes);
@@ -182,11 +215,26 @@ hmm_status hmm_backward_sizes(const hmm_problem* p, size_t* workspace_bytes);
  *   d_up_w          bf16 [E,H,2I]    overwritten (experts without tokens: zeros)
  *   d_down_w        bf16 [E,I,H]     overwritten (experts without tokens: zeros)
  *                   (dx, d_up_w and d_down_w are float32 with HMM_F32)
- *   d_topk_weights  float32 [T,K]    overwritten (0 for dropped slots) */
+ *   d_topk_weights  float32 [T,K]    overwritten (0 for dropped slots)
+ * Needs p->shared_I == 0 (else HMM_ERR_BAD_SHAPE: use hmm_backward_shared). */
 hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
                         const float* topk_weights, const void* up_w, const void* down_w,
                         const void* saved, size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w,
                         float* d_topk_weights, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward with a shared expert: hmm_backward's outputs, plus
+ *   d_shared_up_w    bf16 [H,2Is]   overwritten (zeros for T = 0)
+ *   d_shared_down_w  bf16 [Is,H]    overwritten
+ *                    (float32 with HMM_F32)
+ * and dx then also holds the shared expert's term (added after the K routed
+ * terms, in the same float32 sum).  ``saved`` is the buffer filled by the
+ * matching hmm_forward_shared.  With p->shared_I == 0 this is hmm_backward. */
+hmm_status hmm_backward_shared(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
+                               const float* topk_weights, const void* up_w, const void* down_w,
+                               const void* shared_up_w, const void* shared_down_w, const void* saved,
+                               size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w, void* d_shared_up_w,
+                               void* d_shared_down_w, float* d_topk_weights, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Routing alone (RFC section 4.1 top-k expand; 3.1 offset construction; 6.2
  * sort by expert): writes counts[E], offsets[E+1], sorted_slot[S] and

@@ -33,20 +33,20 @@ EXPORTS = (
     "hmm_forward_sizes", "hmm_saved_layout_of", "hmm_forward", "hmm_backward_sizes", "hmm_backward",
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
     "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
-    "hmm_quant_cols_fp8",
+    "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared",
 )
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("out_dtype", ctypes.c_int32), ("gmm1_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("shared_I", ctypes.c_uint32)]
 
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("counts", "offsets", "sorted_slot", "row_of_slot", "tok_of_row", "tiles", "h", "a", "aw", "id_error",
-                 "total")]
+                 "shared_offsets", "shared_idx", "shared_ones", "shared_tiles", "shared_h", "shared_a", "total")]
 
 
 class StageTime(ctypes.Structure):
@@ -65,6 +65,8 @@ _SIGS = {
     "hmm_forward": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P],
     "hmm_backward_sizes": [_PROB, ctypes.POINTER(_SZ)],
     "hmm_backward": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _SZ, _P],
+    "hmm_forward_shared": [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P],
+    "hmm_backward_shared": [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "hmm_route_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
     "hmm_route": [_PROB, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "hmm_quant_rows_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],

@@ -39,6 +39,8 @@ inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
   int64_t T, H, I, E, K, S;
+  int64_t Is;  // shared expert's intermediate size (0: none)
+  bool shared;
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
   bool fp8;    // FP8 E4M3 up-projection
   bool f32;    // float32 outputs (accuracy mode)
@@ -47,7 +49,8 @@ struct Dims {
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
   if (!p) return fail(HMM_ERR_NULL_POINTER, "problem is NULL");
-  if (p->reserved != 0) return fail(HMM_ERR_BAD_SHAPE, "hmm_problem.reserved must be 0");
+  if (p->shared_I != 0 && (p->shared_I < 64 || p->shared_I > 65536 || p->shared_I % 64))
+    return fail(HMM_ERR_BAD_SHAPE, "shared_I must be 0 or a multiple of 64 in [64, 65536] (got %u)", p->shared_I);
   if (p->T < 0) return fail(HMM_ERR_BAD_SHAPE, "T must be >= 0 (got %lld)", (long long)p->T);
   if (p->K < 1 || p->K > 16) return fail(HMM_ERR_BAD_SHAPE, "K must be in [1, 16] (got %lld)", (long long)p->K);
   if (p->E < 1 || p->E > hmm::MAX_EXPERTS)
@@ -70,7 +73,9 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     // every array a product reads through a buffer resource must stay below 4 GiB
     // (the float32-output mode reads [hi | lo] operands of twice the width)
     const int64_t S = p->T * p->K, lim = (int64_t)0xFFFFFF00, w = (p->out_dtype == HMM_F32) ? 2 : 1;
-    const int64_t ext[] = {p->T * p->H * 2 * w, S * 2 * p->I * 2 * w, S * p->H * 2 * w, p->H * 2 * p->I * 2};
+    const int64_t Is = p->shared_I;
+    const int64_t ext[] = {p->T * p->H * 2 * w, S * 2 * p->I * 2 * w, S * p->H * 2 * w, p->H * 2 * p->I * 2,
+                           p->T * 2 * Is * 2 * w, p->H * 2 * Is * 2};
     for (int64_t x : ext)
       if (x > lim) return fail(HMM_ERR_UNSUPPORTED, "an operand array exceeds 4 GiB (%lld bytes)", (long long)x);
   }
@@ -85,12 +90,14 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->E = p->E;
   d->K = p->K;
   d->S = p->T * p->K;
+  d->Is = p->shared_I;
+  d->shared = p->shared_I != 0;
   d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3;
   d->f32 = p->out_dtype == HMM_F32;
   d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
-  d->fused = d->small && !d->fp8 && !d->f32 && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
+  d->fused = d->small && !d->fp8 && !d->f32 && !d->shared && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
              d->E <= hmm::RT_ONE_MAX_EXPERTS && (p->flags & HMM_FLAG_FUSED_FORWARD);
   return HMM_OK;
 }
@@ -111,6 +118,14 @@ hmm::RowGroups row_groups(const Dims& d, const int32_t* tiles, const int32_t* of
   return hmm::RowGroups{tiles, offsets, sorted_slot, tok_of_row, hmm::max_big_tiles(d.S, d.E, d.small),
                         hmm::max_small_tiles(d.S, d.E, d.small), d.T, d.S, d.small};
 }
+// The shared expert as a grouped problem of its own: one expert, all T tokens
+// in token order (idx is both its sorted_slot and its tok_of_row), the same
+// tiling mode as the routed experts.
+int64_t shared_tile_ints(const Dims& d) { return hmm::tile_table_ints(d.T, 1, d.small); }
+hmm::RowGroups shared_groups(const Dims& d, const int32_t* tiles, const int32_t* offsets, const int32_t* idx) {
+  return hmm::RowGroups{tiles, offsets, idx, idx, hmm::max_big_tiles(d.T, 1, d.small),
+                        hmm::max_small_tiles(d.T, 1, d.small), d.T, d.T, d.small};
+}
 
 hmm_saved_layout saved_layout(const Dims& d) {
   hmm_saved_layout L{};
@@ -127,6 +142,14 @@ hmm_saved_layout saved_layout(const Dims& d) {
   L.a = o;             o += up(d.S * d.I * ab);
   L.aw = o;            o += up(d.S * d.I * ab);
   L.id_error = o;      o += up(4);
+  // shared expert (all zero-sized without one)
+  const int64_t Ts = d.shared ? d.T : 0;
+  L.shared_offsets = o; o += d.shared ? up(2 * 4) : 0;
+  L.shared_idx = o;     o += up(Ts * 4);
+  L.shared_ones = o;    o += up(Ts * 4);
+  L.shared_tiles = o;   o += d.shared ? up(shared_tile_ints(d) * 4) : 0;
+  L.shared_h = o;       o += up(Ts * 2 * d.Is * hb);
+  L.shared_a = o;       o += up(Ts * d.Is * ab);
   L.total = o;
   return L;
 }
@@ -151,13 +174,16 @@ RouteScratch route_scratch(const Dims& d, size_t base) {
 // maxima of the weight quantisation.
 struct FwdWork {
   RouteScratch rs;
-  size_t o, xq, dsx, wq, dsw, pmax, sync, total;
+  size_t o, os, xq, dsx, wq, dsw, pmax, sync, total;
 };
 FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
   w.rs = route_scratch(d, 0);
   size_t o = w.rs.total;
   w.o = o; o += up(d.S * d.H * (d.f32 ? 4 : 2));
+  if (d.shared) {
+    w.os = o; o += up(d.T * d.H * (d.f32 ? 4 : 2));  // the shared expert's output rows
+  }
   if (d.fp8) {
     w.xq = o;   o += up(d.T * d.H);
     w.dsx = o;  o += up(d.T * 4);
@@ -175,7 +201,7 @@ FwdWork fwd_work(const Dims& d) {
 // Backward scratch: dH, dXp, the d_topk_weights partials and, in the float32-output
 // mode, dY as a bf16 [hi | lo] pair (dH is then a pair too and dXp float32).
 struct BwdWork {
-  size_t dy2, dh, dxp, dwpart, total;
+  size_t dy2, dh, dxp, dwpart, dhs, dxs, total;
   int dw_cols;
 };
 BwdWork bwd_work(const Dims& d) {
@@ -189,6 +215,10 @@ BwdWork bwd_work(const Dims& d) {
   w.dh = o;     o += up(d.S * 2 * d.I * 2 * wide);
   w.dxp = o;    o += up(d.S * d.H * (d.f32 ? 4 : 2));
   w.dwpart = o; o += up(d.S * w.dw_cols * 4);
+  if (d.shared) {  // the shared expert's dH and dX rows
+    w.dhs = o;  o += up(d.T * 2 * d.Is * 2 * wide);
+    w.dxs = o;  o += up(d.T * d.H * (d.f32 ? 4 : 2));
+  }
   w.total = o;
   return w;
 }
@@ -474,16 +504,23 @@ hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, ui
   return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
 }
 
-hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
-                       const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  hmm_status s = validate(p, &d);
-  if (s != HMM_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// The forward of hmm_forward and hmm_forward_shared (up_s / down_s: the shared
+// expert's weights, used when d.shared).
+hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* up_w, const void* down_w, const void* up_s,
+                        const void* down_s, void* y, void* saved, size_t saved_bytes, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  hmm_status s;
   const bool ne = d.S > 0;
   if ((s = need(x, ne, "x")) || (s = need(topk_ids, ne, "topk_ids")) || (s = need(topk_weights, ne, "topk_weights")) ||
       (s = need(up_w, true, "up_proj_weight")) || (s = need(down_w, true, "down_proj_weight")) ||
-      (s = need(y, ne, "y")) || (s = need(saved, true, "saved")) || (s = need(workspace, true, "workspace")))
+      (s = need(up_s, d.shared, "shared_up_proj_weight")) ||
+      (s = need(down_s, d.shared, "shared_down_proj_weight")) || (s = need(y, ne, "y")) ||
+      (s = need(saved, true, "saved")) || (s = need(workspace, true, "workspace")))
     return s;
   const hmm_saved_layout L = saved_layout(d);
   const FwdWork W = fwd_work(d);
@@ -523,35 +560,68 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
   s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
                 tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, st);
   if (s != HMM_OK) return s;
+  hipError_t e;
+  hmm::RowGroups gs{};
+  if (d.shared) {
+    // the shared expert's tables (also for T = 0: the backward's weight gradients read them)
+    int32_t* s_idx = at<int32_t>(saved, L.shared_idx);
+    {
+      Stage stage("shared_tables", st);
+      e = hmm::launch_shared_tables(d.T, (int)hmm::max_big_tiles(d.T, 1, d.small), d.small ? 0 : 1,
+                                    at<int32_t>(saved, L.shared_offsets), s_idx, at<float>(saved, L.shared_ones),
+                                    at<int32_t>(saved, L.shared_tiles), st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared-expert tables launch");
+    gs = shared_groups(d, at<int32_t>(saved, L.shared_tiles), at<int32_t>(saved, L.shared_offsets), s_idx);
+  }
   if (!ne) return validate_ids ? finish_id_check(d) : HMM_OK;
 
   hmm::RowGroups g = row_groups(d, tiles, offsets, sorted_slot, tok_of_row);
-  uint16_t* h = at<uint16_t>(saved, L.h);
-  uint16_t* a = at<uint16_t>(saved, L.a);
-  uint16_t* aw = at<uint16_t>(saved, L.aw);
-  uint16_t* o = at<uint16_t>(workspace, W.o);
-  hipError_t e;
+  const float* ones = at<float>(saved, L.shared_ones);
   if (d.f32) {
     float* h32 = at<float>(saved, L.h);
     float* o32 = at<float>(workspace, W.o);
+    uint16_t* a2 = at<uint16_t>(saved, L.a);
     {
       Stage stage("gmm1_swiglu", st);
-      e = hmm::launch_gmm1_f32(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h32, a, aw, st);
+      e = hmm::launch_gmm1_f32(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h32, a2,
+                               at<uint16_t>(saved, L.aw), st);
     }
     if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+    if (d.shared) {
+      Stage stage("shared_gmm1", st);
+      e = hmm::launch_gmm1_f32(gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is,
+                               at<float>(saved, L.shared_h), at<uint16_t>(saved, L.shared_a), nullptr, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared gmm1 launch");
     {
       Stage stage("gmm2", st);
-      e = hmm::launch_gmm2_f32(g, a, (const uint16_t*)down_w, d.H, d.I, o32, st);
+      e = hmm::launch_gmm2_f32(g, a2, (const uint16_t*)down_w, d.H, d.I, o32, st);
     }
     if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+    if (d.shared) {
+      Stage stage("shared_gmm2", st);
+      e = hmm::launch_gmm2_f32(gs, at<uint16_t>(saved, L.shared_a), (const uint16_t*)down_s, d.H, d.Is,
+                               at<float>(workspace, W.os), st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared gmm2 launch");
     {
       Stage stage("combine", st);
-      e = hmm::launch_combine_f32(o32, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, (float*)y,
-                                  st);
+      e = hmm::launch_combine_f32(o32, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H,
+                                  d.shared ? at<float>(workspace, W.os) : nullptr, (float*)y, st);
     }
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return validate_ids ? finish_id_check(d) : HMM_OK;
   }
+  uint16_t* h = at<uint16_t>(saved, L.h);
+  uint16_t* a = at<uint16_t>(saved, L.a);
+  uint16_t* aw = at<uint16_t>(saved, L.aw);
+  uint16_t* o = at<uint16_t>(workspace, W.o);
+  uint16_t* hs = at<uint16_t>(saved, L.shared_h);
+  uint16_t* as = at<uint16_t>(saved, L.shared_a);
+  uint16_t* os = d.shared ? at<uint16_t>(workspace, W.os) : nullptr;
+  // narrow tiling: the routed and the shared products share their launches
+  const bool pair = d.shared && d.small;
   if (d.fp8) {
     uint8_t* xq = at<uint8_t>(workspace, W.xq);
     uint8_t* wq = at<uint8_t>(workspace, W.wq);
@@ -572,37 +642,60 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
       Stage stage("gmm1_fp8_swiglu", st);
       e = hmm::launch_gmm1_fp8(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
     }
+  } else if (pair) {
+    Stage stage("gmm1_swiglu+shared", st);
+    e = hmm::launch_gmm1_swiglu_with_shared(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h,
+                                            a, aw, gs, (const uint16_t*)up_s, ones, d.Is, hs, as, st);
   } else {
     Stage stage("gmm1_swiglu", st);
     e = hmm::launch_gmm1_swiglu(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw, st);
   }
   if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
-  {
+  if (d.shared && (d.fp8 || !pair)) {
+    // the shared expert's up-projection is bf16 also when the routed one is FP8
+    Stage stage("shared_gmm1", st);
+    e = hmm::launch_gmm1_swiglu(gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "shared gmm1 launch");
+  }
+  if (pair) {
+    Stage stage("gmm2+shared", st);
+    e = hmm::launch_gmm2_with_shared(g, a, (const uint16_t*)down_w, d.H, d.I, o, gs, as, (const uint16_t*)down_s, d.Is,
+                                     os, st);
+  } else {
     Stage stage("gmm2", st);
     e = hmm::launch_gmm2(g, a, (const uint16_t*)down_w, d.H, d.I, o, st);
   }
   if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+  if (d.shared && !pair) {
+    Stage stage("shared_gmm2", st);
+    e = hmm::launch_gmm2(gs, as, (const uint16_t*)down_s, d.H, d.Is, os, st);
+    if (e != hipSuccess) return hip_fail(e, "shared gmm2 launch");
+  }
   {
     Stage stage("combine", st);
-    e = hmm::launch_combine(o, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, (uint16_t*)y, st);
+    e = hmm::launch_combine(o, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, os, (uint16_t*)y,
+                            st);
   }
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return validate_ids ? finish_id_check(d) : HMM_OK;
 }
 
-hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
-                        const float* topk_weights, const void* up_w, const void* down_w, const void* saved,
-                        size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w, float* d_topk_weights,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  hmm_status s = validate(p, &d);
-  if (s != HMM_OK) return s;
+// The backward of hmm_backward and hmm_backward_shared.
+hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int32_t* topk_ids,
+                         const float* topk_weights, const void* up_w, const void* down_w, const void* up_s,
+                         const void* down_s, const void* saved, size_t saved_bytes, void* dx, void* d_up_w,
+                         void* d_down_w, void* d_up_s, void* d_down_s, float* d_topk_weights, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  hmm_status s;
   const bool ne = d.S > 0;
   if ((s = need(dy, ne, "dy")) || (s = need(x, ne, "x")) || (s = need(topk_ids, ne, "topk_ids")) ||
       (s = need(topk_weights, ne, "topk_weights")) || (s = need(up_w, true, "up_proj_weight")) ||
-      (s = need(down_w, true, "down_proj_weight")) || (s = need(saved, true, "saved")) ||
+      (s = need(down_w, true, "down_proj_weight")) || (s = need(up_s, d.shared, "shared_up_proj_weight")) ||
+      (s = need(down_s, d.shared, "shared_down_proj_weight")) || (s = need(saved, true, "saved")) ||
       (s = need(dx, ne, "dx")) || (s = need(d_up_w, true, "d_up_proj_weight")) ||
-      (s = need(d_down_w, true, "d_down_proj_weight")) || (s = need(d_topk_weights, ne, "d_topk_weights")))
+      (s = need(d_down_w, true, "d_down_proj_weight")) || (s = need(d_up_s, d.shared, "d_shared_up_proj_weight")) ||
+      (s = need(d_down_s, d.shared, "d_shared_down_proj_weight")) ||
+      (s = need(d_topk_weights, ne, "d_topk_weights")))
     return s;
   const hmm_saved_layout L = saved_layout(d);
   const BwdWork W = bwd_work(d);
@@ -617,16 +710,25 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
   const int32_t* row_of_slot = at<int32_t>(saved, L.row_of_slot);
   const int32_t* tok_of_row = at<int32_t>(saved, L.tok_of_row);
   hmm::RowGroups g = row_groups(d, at<int32_t>(saved, L.tiles), offsets, sorted_slot, tok_of_row);
+  // the shared expert: one group of all tokens (tables recorded by the forward)
+  const int32_t* s_offsets = at<int32_t>(saved, L.shared_offsets);
+  const int32_t* s_idx = at<int32_t>(saved, L.shared_idx);
+  const float* ones = at<float>(saved, L.shared_ones);
+  const hmm::RowGroups gs = d.shared ? shared_groups(d, at<int32_t>(saved, L.shared_tiles), s_offsets, s_idx)
+                                     : hmm::RowGroups{};
   const uint16_t* h = at<uint16_t>(saved, L.h);
   const uint16_t* a = at<uint16_t>(saved, L.a);
   const uint16_t* aw = at<uint16_t>(saved, L.aw);
+  const uint16_t* as = at<uint16_t>(saved, L.shared_a);
   uint16_t* dh = at<uint16_t>(workspace, W.dh);
   uint16_t* dxp = at<uint16_t>(workspace, W.dxp);
+  uint16_t* dhs = d.shared ? at<uint16_t>(workspace, W.dhs) : nullptr;
   float* dwpart = at<float>(workspace, W.dwpart);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   if (d.f32) {
     uint16_t* dy2 = at<uint16_t>(workspace, W.dy2);
     float* dxp32 = at<float>(workspace, W.dxp);
+    float* dxs32 = d.shared ? at<float>(workspace, W.dxs) : nullptr;
     const float* h32 = at<float>(saved, L.h);
     if (ne) {
       {
@@ -640,14 +742,25 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
                                      W.dw_cols, st);
       }
       if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+      if (d.shared) {
+        Stage stage("shared_act_grad", st);
+        e = hmm::launch_act_grad_f32(gs, dy2, (const uint16_t*)down_s, ones, at<float>(saved, L.shared_h), as, d.H,
+                                     d.Is, dhs, nullptr, 0, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "shared act_grad launch");
       {
         Stage stage("input_grad", st);
         e = hmm::launch_input_grad_f32(g, dh, (const uint16_t*)up_w, d.H, d.I, dxp32, st);
       }
       if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+      if (d.shared) {
+        Stage stage("shared_input_grad", st);
+        e = hmm::launch_input_grad_f32(gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs32, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "shared input_grad launch");
       {
         Stage stage("combine_dx", st);
-        e = hmm::launch_combine_dx_f32(dxp32, row_of_slot, d.T, (int)d.K, d.H, (float*)dx, dwpart, W.dw_cols,
+        e = hmm::launch_combine_dx_f32(dxp32, row_of_slot, d.T, (int)d.K, d.H, dxs32, (float*)dx, dwpart, W.dw_cols,
                                        d_topk_weights, st);
       }
       if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
@@ -657,13 +770,25 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
       e = hmm::launch_dw2_f32(offsets, tok_of_row, d.T, d.S, d.E, aw, dy2, d.H, d.I, (float*)d_down_w, d.small, st);
     }
     if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+    if (d.shared) {
+      Stage stage("shared_dw2", st);
+      e = hmm::launch_dw2_f32(s_offsets, s_idx, d.T, d.T, 1, as, dy2, d.H, d.Is, (float*)d_down_s, d.small, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared W2Grad launch");
     {
       Stage stage("dw1", st);
       e = hmm::launch_dw1_f32(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (float*)d_up_w,
                               d.small, st);
     }
-    return e == hipSuccess ? HMM_OK : hip_fail(e, "W1Grad launch");
+    if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
+    if (d.shared) {
+      Stage stage("shared_dw1", st);
+      e = hmm::launch_dw1_f32(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (float*)d_up_s,
+                              d.small, st);
+    }
+    return e == hipSuccess ? HMM_OK : hip_fail(e, "shared W1Grad launch");
   }
+  uint16_t* dxs = d.shared ? at<uint16_t>(workspace, W.dxs) : nullptr;
   if (ne && d.small) {
     // small problems: each product fills only part of the chip, so the independent
     // ones share a launch (RFC 2.2: W2Grad alongside act_grad, W1Grad alongside the
@@ -674,15 +799,28 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
                                           d.E, d.H, d.I, dh, dwpart, W.dw_cols, (uint16_t*)d_down_w, st);
     }
     if (e != hipSuccess) return hip_fail(e, "act_grad + W2Grad launch");
+    if (d.shared) {
+      Stage stage("shared_act_grad+dw2", st);
+      e = hmm::launch_act_grad_dw2_narrow(gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones,
+                                          at<uint16_t>(saved, L.shared_h), as, as, 1, d.H, d.Is, dhs, nullptr, 0,
+                                          (uint16_t*)d_down_s, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared act_grad + W2Grad launch");
     {
       Stage stage("input_grad+dw1", st);
       e = hmm::launch_input_grad_dw1_narrow(g, dh, (const uint16_t*)up_w, (const uint16_t*)x, d.E, d.H, d.I, dxp,
                                             (uint16_t*)d_up_w, st);
     }
     if (e != hipSuccess) return hip_fail(e, "input_grad + W1Grad launch");
+    if (d.shared) {
+      Stage stage("shared_input_grad+dw1", st);
+      e = hmm::launch_input_grad_dw1_narrow(gs, dhs, (const uint16_t*)up_s, (const uint16_t*)x, 1, d.H, d.Is, dxs,
+                                            (uint16_t*)d_up_s, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared input_grad + W1Grad launch");
     {
       Stage stage("combine_dx", st);
-      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, (uint16_t*)dx, dwpart, W.dw_cols,
+      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
                                  d_topk_weights, st);
     }
     return e == hipSuccess ? HMM_OK : hip_fail(e, "combine(dX) launch");
@@ -694,14 +832,25 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
                                dwpart, W.dw_cols, st);
     }
     if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+    if (d.shared) {
+      Stage stage("shared_act_grad", st);
+      e = hmm::launch_act_grad(gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones, at<uint16_t>(saved, L.shared_h),
+                               as, d.H, d.Is, dhs, nullptr, 0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared act_grad launch");
     {
       Stage stage("input_grad", st);
       e = hmm::launch_input_grad(g, dh, (const uint16_t*)up_w, d.H, d.I, dxp, st);
     }
     if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+    if (d.shared) {
+      Stage stage("shared_input_grad", st);
+      e = hmm::launch_input_grad(gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared input_grad launch");
     {
       Stage stage("combine_dx", st);
-      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, (uint16_t*)dx, dwpart, W.dw_cols,
+      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
                                  d_topk_weights, st);
     }
     if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
@@ -712,13 +861,76 @@ hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, con
                         d.small, st);
   }
   if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+  if (d.shared) {
+    Stage stage("shared_dw2", st);
+    e = hmm::launch_dw2(s_offsets, s_idx, d.T, d.T, 1, as, (const uint16_t*)dy, d.H, d.Is, (uint16_t*)d_down_s,
+                        d.small, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "shared W2Grad launch");
   {
     Stage stage("dw1", st);
     e = hmm::launch_dw1(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w,
                         d.small, st);
   }
   if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
-  return HMM_OK;
+  if (d.shared) {
+    Stage stage("shared_dw1", st);
+    e = hmm::launch_dw1(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (uint16_t*)d_up_s, d.small,
+                        st);
+  }
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "shared W1Grad launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                       const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (d.shared) return fail(HMM_ERR_BAD_SHAPE, "shared_I != 0: call hmm_forward_shared with the shared weights");
+  return forward_impl(p, d, x, topk_ids, topk_weights, up_w, down_w, nullptr, nullptr, y, saved, saved_bytes,
+                      workspace, workspace_bytes, stream);
+}
+
+hmm_status hmm_forward_shared(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                              const void* up_w, const void* down_w, const void* shared_up_w,
+                              const void* shared_down_w, void* y, void* saved, size_t saved_bytes, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  return forward_impl(p, d, x, topk_ids, topk_weights, up_w, down_w, shared_up_w, shared_down_w, y, saved,
+                      saved_bytes, workspace, workspace_bytes, stream);
+}
+
+hmm_status hmm_backward(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* up_w, const void* down_w, const void* saved,
+                        size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w, float* d_topk_weights,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (d.shared) return fail(HMM_ERR_BAD_SHAPE, "shared_I != 0: call hmm_backward_shared with the shared weights");
+  return backward_impl(d, dy, x, topk_ids, topk_weights, up_w, down_w, nullptr, nullptr, saved, saved_bytes, dx,
+                       d_up_w, d_down_w, nullptr, nullptr, d_topk_weights, workspace, workspace_bytes, stream);
+}
+
+hmm_status hmm_backward_shared(const hmm_problem* p, const void* dy, const void* x, const int32_t* topk_ids,
+                               const float* topk_weights, const void* up_w, const void* down_w,
+                               const void* shared_up_w, const void* shared_down_w, const void* saved,
+                               size_t saved_bytes, void* dx, void* d_up_w, void* d_down_w, void* d_shared_up_w,
+                               void* d_shared_down_w, float* d_topk_weights, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  return backward_impl(d, dy, x, topk_ids, topk_weights, up_w, down_w, shared_up_w, shared_down_w, saved, saved_bytes,
+                       dx, d_up_w, d_down_w, d_shared_up_w, d_shared_down_w, d_topk_weights, workspace,
+                       workspace_bytes, stream);
 }
 
 hmm_status hmm_profile_enable(int32_t on) {

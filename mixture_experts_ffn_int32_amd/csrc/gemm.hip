@@ -43,9 +43,6 @@
 #include "gemm_bf16.h"
 
 namespace hmm {
-namespace {
-
-}  // namespace
 
 int act_grad_dw_cols(int64_t I, bool narrow) {
   const int64_t bn = narrow ? Narrow::BN : Big::BN;  // Big and Small share BN
@@ -66,6 +63,32 @@ hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2
   return launch_rows<Gmm2>(g, [&](int bn) { return (int)((H + bn - 1) / bn); }, [&](auto& A, int nnt) {
     A.g = g; A.a = a; A.w2 = w2; A.S = g.S; A.H = H; A.I = I; A.o = o; A.n_ntiles = nnt;
   }, stream);
+}
+
+// Narrow tiling: a routed product and the shared expert's share one launch.
+hipError_t launch_gmm1_swiglu_with_shared(const RowGroups& g, const uint16_t* x, const uint16_t* w1,
+                                          const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                                          uint16_t* aw, const RowGroups& gs, const uint16_t* w1s, const float* ones,
+                                          int64_t Is, uint16_t* hs, uint16_t* as, hipStream_t stream) {
+  typedef Gmm1<Narrow, true> P;
+  constexpr int HALF = Narrow::BN / 2;
+  typename P::Args a1, a2;
+  a1.g = g; a1.x = x; a1.w1 = w1; a1.tw = topk_w; a1.T = g.T; a1.H = H; a1.I = I; a1.h = h; a1.a = a; a1.aw = aw;
+  a1.n_ntiles = (int)((I + HALF - 1) / HALF);
+  a2.g = gs; a2.x = x; a2.w1 = w1s; a2.tw = ones; a2.T = gs.T; a2.H = H; a2.I = Is; a2.h = hs; a2.a = as;
+  a2.aw = nullptr; a2.n_ntiles = (int)((Is + HALF - 1) / HALF);
+  return launch_pair<P, P>(a1, g.max_small * a1.n_ntiles, a2, gs.max_small * a2.n_ntiles, stream);
+}
+
+hipError_t launch_gmm2_with_shared(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
+                                   uint16_t* o, const RowGroups& gs, const uint16_t* as, const uint16_t* w2s,
+                                   int64_t Is, uint16_t* os, hipStream_t stream) {
+  typedef Gmm2<Narrow, true> P;
+  typename P::Args a1, a2;
+  const int nnt = (int)((H + Narrow::BN - 1) / Narrow::BN);
+  a1.g = g; a1.a = a; a1.w2 = w2; a1.S = g.S; a1.H = H; a1.I = I; a1.o = o; a1.n_ntiles = nnt;
+  a2.g = gs; a2.a = as; a2.w2 = w2s; a2.S = gs.S; a2.H = H; a2.I = Is; a2.o = os; a2.n_ntiles = nnt;
+  return launch_pair<P, P>(a1, g.max_small * nnt, a2, gs.max_small * nnt, stream);
 }
 
 hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,

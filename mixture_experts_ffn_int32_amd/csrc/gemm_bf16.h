@@ -23,7 +23,7 @@ struct Gmm1 : RowTile<Cc, SMALL> {
     const uint16_t* w1;
     const float* tw;
     int64_t T, H, I;
-    uint16_t *h, *a, *aw;
+    uint16_t *h, *a, *aw;  // aw may be NULL (not stored)
     int n_ntiles;
     bool coh = false;  // ``a`` goes to the coherence point (read by another XCD in the same launch)
   };
@@ -102,7 +102,7 @@ struct Gmm1 : RowTile<Cc, SMALL> {
       *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
       *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
       put16(ar->a, ar->g.S * I * 2, p * I + i, pack8(av), ar->coh);
-      *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
+      if (ar->aw) *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
     }
   }
 };
@@ -181,7 +181,7 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     const uint16_t* a;
     int64_t T, H, I;
     uint16_t* dh;
-    float* dwpart;
+    float* dwpart;  // may be NULL (the sums are not stored)
     int dw_cols;
     int n_ntiles;
   };
@@ -273,7 +273,8 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     for (int k = 0; k < PER; ++k) {
       const int c = tid + k * C::NTHR;
       const int row = c / CPR;
-      if (c % CPR == 0 && row < rows) ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
+      if (ar->dwpart && c % CPR == 0 && row < rows)
+        ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
     }
   }
 };

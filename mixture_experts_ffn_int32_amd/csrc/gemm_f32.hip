@@ -75,7 +75,7 @@ struct Gmm1F32 : RowTile<Cc, SMALL> {
     int64_t T, H, I;
     float* h;       // [S][2I]
     uint16_t* a2;   // [S][2I]: a_hi | a_lo
-    uint16_t* aw2;  // [S][2I]: aw_hi | aw_lo
+    uint16_t* aw2;  // [S][2I]: aw_hi | aw_lo (may be NULL: not stored)
     int n_ntiles;
   };
   const Args* ar;
@@ -137,9 +137,11 @@ struct Gmm1F32 : RowTile<Cc, SMALL> {
           split_bf(a, hi, lo);
           ar->a2[p * 2 * I + i] = hi;
           ar->a2[p * 2 * I + I + i] = lo;
-          split_bf(aw, hi, lo);
-          ar->aw2[p * 2 * I + i] = hi;
-          ar->aw2[p * 2 * I + I + i] = lo;
+          if (ar->aw2) {
+            split_bf(aw, hi, lo);
+            ar->aw2[p * 2 * I + i] = hi;
+            ar->aw2[p * 2 * I + I + i] = lo;
+          }
         }
   }
 };
@@ -219,7 +221,7 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     const uint16_t* a2;   // [S][2I]
     int64_t T, H, I;
     uint16_t* dh2;        // [S][4I]
-    float* dwpart;        // [S][dw_cols]
+    float* dwpart;        // [S][dw_cols] (may be NULL: not stored)
     int dw_cols;
     int n_ntiles;
   };
@@ -320,7 +322,8 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     for (int k = 0; k < PER; ++k) {
       const int c = tid + k * C::NTHR;
       const int row = c / CPR;
-      if (c % CPR == 0 && row < rows) ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
+      if (ar->dwpart && c % CPR == 0 && row < rows)
+        ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
     }
   }
 };

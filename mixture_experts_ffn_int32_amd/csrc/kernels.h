@@ -50,6 +50,12 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
                         int32_t* host_err, hipStream_t stream);
 
+// The shared expert's routing tables (route.hip): one expert holding all T
+// tokens in token order: offsets[2] = {0, T}, idx[T] = 0..T-1 (its sorted_slot
+// and tok_of_row), ones[T] = 1.0 (its weights), tiles (tile_table_ints(T, 1, !big_on)).
+hipError_t launch_shared_tables(int64_t T, int max_big, int big_on, int32_t* offsets, int32_t* idx, float* ones,
+                                int32_t* tiles, hipStream_t stream);
+
 // grouped products (gemm.hip).  All matrices bf16 (uint16_t storage).
 struct RowGroups {
   const int32_t* tiles;        // tile table written by route_scan (layout in route.hip)
@@ -63,13 +69,23 @@ struct RowGroups {
                                // kernel): read them at the device-wide coherence point
 };
 
-// h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
+// h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU;
+// aw may be NULL)
 hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
                               int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream);
 // o = a . W2[e]                                                (forward down-projection)
 hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
                        uint16_t* o, hipStream_t stream);
-// G = dY[tok] . W2[e]^T; dH = SwiGLUGrad(w G); dwpart = partial sums of G a
+// Narrow tiling: the routed product and the shared expert's (groups gs, width Is,
+// weight 1, no aw) in one launch each.
+hipError_t launch_gmm1_swiglu_with_shared(const RowGroups& g, const uint16_t* x, const uint16_t* w1,
+                                          const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                                          uint16_t* aw, const RowGroups& gs, const uint16_t* w1s, const float* ones,
+                                          int64_t Is, uint16_t* hs, uint16_t* as, hipStream_t stream);
+hipError_t launch_gmm2_with_shared(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
+                                   uint16_t* o, const RowGroups& gs, const uint16_t* as, const uint16_t* w2s,
+                                   int64_t Is, uint16_t* os, hipStream_t stream);
+// G = dY[tok] . W2[e]^T; dH = SwiGLUGrad(w G); dwpart = partial sums of G a (dwpart may be NULL)
 hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
                            const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
                            float* dwpart, int dw_cols, hipStream_t stream);
@@ -108,12 +124,14 @@ hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* d
                            const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
                            uint16_t* aw, hipStream_t stream);
 
-// pointwise (pointwise.hip)
+// pointwise (pointwise.hip).  ``extra`` [T][H] (may be NULL): the shared expert's rows,
+// added with weight 1 after the K routed terms.
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,
-                          int K, int64_t H, uint16_t* out, hipStream_t stream);
+                          int K, int64_t H, const uint16_t* extra, uint16_t* out, hipStream_t stream);
 // combine(dX) (unweighted) with d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c] folded in
 hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
-                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
+                             const uint16_t* extra, uint16_t* dx, const float* dwpart, int dw_cols, float* dw,
+                             hipStream_t stream);
 
 // Fused small-problem forward (fused.hip): routing, up-projection + SwiGLU,
 // down-projection and combine in one launch of at most max_groups workgroups
@@ -147,9 +165,10 @@ hipError_t launch_dw2_f32(const int32_t* offsets, const int32_t* tok_of_row, int
                           hipStream_t stream);
 int act_grad_f32_dw_cols(int64_t I, bool narrow);  // d_topk_weights partial columns of launch_act_grad_f32
 hipError_t launch_combine_f32(const float* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
-                              int64_t H, float* out, hipStream_t stream);
-hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, float* dx,
-                                 const float* dwpart, int dw_cols, float* dw, hipStream_t stream);
+                              int64_t H, const float* extra, float* out, hipStream_t stream);
+hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
+                                 const float* extra, float* dx, const float* dwpart, int dw_cols, float* dw,
+                                 hipStream_t stream);
 // x float32 [n][H] -> bf16 [n][2H] = [hi | lo]
 hipError_t launch_split_rows(const float* x, int64_t n, int64_t H, uint16_t* out, hipStream_t stream);
 

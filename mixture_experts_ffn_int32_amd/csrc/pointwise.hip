@@ -3,8 +3,9 @@
 //                 their token and are summed with the top-k weights; section 2.2
 //                 Combine(dX): the same gather without weights)
 //                 out[t] = sum_k w[t,k] * rows[row_of_slot[t*K+k]]   (w = 1 if NULL)
-//                 in float32, k ascending, then one bf16 rounding; no atomics, so
-//                 the result is deterministic.
+//                          (+ extra[t], the shared expert's row, when given)
+//                 in float32, k ascending, the extra term last, then one bf16
+//                 rounding; no atomics, so the result is deterministic.
 //   combine(dX) also finalises d_topk_weights[s] = sum_c dwpart[row_of_slot[s]][c],
 //                c ascending, in the threads of each token's first K chunks.
 #include "device.h"
@@ -67,7 +68,8 @@ template <bool WEIGHTED, class T_>
 __global__ void __launch_bounds__(PW_THREADS) combine_kernel(const T_* __restrict__ rows,
                                                              const int32_t* __restrict__ row_of_slot,
                                                              const float* __restrict__ tw, int64_t T, int K,
-                                                             int64_t H, T_* __restrict__ out,
+                                                             int64_t H, const T_* __restrict__ extra,
+                                                             T_* __restrict__ out,
                                                              const float* __restrict__ dwpart, int dw_cols,
                                                              float* __restrict__ dw) {
   const int64_t chunks_per_row = H >> 3;
@@ -108,6 +110,12 @@ __global__ void __launch_bounds__(PW_THREADS) combine_kernel(const T_* __restric
         }
       }
     }
+    if (extra) {  // the shared expert's row of this token, weight 1, after the K routed terms
+      float v[8];
+      unraw(load8_nt(extra + t * H + c * 8), extra, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += v[j];
+    }
     store8_nt(out + t * H + c * 8, acc);
     if (dwpart) {
       for (int64_t k = c; k < K; k += chunks_per_row) {
@@ -132,39 +140,41 @@ static unsigned grid_for(int64_t work, int64_t cap) {
 
 template <class T_>
 hipError_t combine_t(const T_* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K, int64_t H,
-                     T_* out, hipStream_t stream) {
+                     const T_* extra, T_* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned g = grid_for(T * (H / 8), 1 << 20);
   hipLaunchKernelGGL((combine_kernel<true, T_>), dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, topk_w, T,
-                     K, H, out, nullptr, 0, nullptr);
+                     K, H, extra, out, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
 template <class T_>
-hipError_t combine_dx_t(const T_* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, T_* dx,
-                        const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
+hipError_t combine_dx_t(const T_* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, const T_* extra,
+                        T_* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned g = grid_for(T * (H / 8), 1 << 20);
   hipLaunchKernelGGL((combine_kernel<false, T_>), dim3(g), dim3(PW_THREADS), 0, stream, rows, row_of_slot, nullptr,
-                     T, K, H, dx, dwpart, dw_cols, dw);
+                     T, K, H, extra, dx, dwpart, dw_cols, dw);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
-                          int64_t H, uint16_t* out, hipStream_t stream) {
-  return combine_t(rows, row_of_slot, topk_w, T, K, H, out, stream);
+                          int64_t H, const uint16_t* extra, uint16_t* out, hipStream_t stream) {
+  return combine_t(rows, row_of_slot, topk_w, T, K, H, extra, out, stream);
 }
 hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
-                             uint16_t* dx, const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
-  return combine_dx_t(rows, row_of_slot, T, K, H, dx, dwpart, dw_cols, dw, stream);
+                             const uint16_t* extra, uint16_t* dx, const float* dwpart, int dw_cols, float* dw,
+                             hipStream_t stream) {
+  return combine_dx_t(rows, row_of_slot, T, K, H, extra, dx, dwpart, dw_cols, dw, stream);
 }
 hipError_t launch_combine_f32(const float* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T, int K,
-                              int64_t H, float* out, hipStream_t stream) {
-  return combine_t(rows, row_of_slot, topk_w, T, K, H, out, stream);
+                              int64_t H, const float* extra, float* out, hipStream_t stream) {
+  return combine_t(rows, row_of_slot, topk_w, T, K, H, extra, out, stream);
 }
-hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H, float* dx,
-                                 const float* dwpart, int dw_cols, float* dw, hipStream_t stream) {
-  return combine_dx_t(rows, row_of_slot, T, K, H, dx, dwpart, dw_cols, dw, stream);
+hipError_t launch_combine_dx_f32(const float* rows, const int32_t* row_of_slot, int64_t T, int K, int64_t H,
+                                 const float* extra, float* dx, const float* dwpart, int dw_cols, float* dw,
+                                 hipStream_t stream) {
+  return combine_dx_t(rows, row_of_slot, T, K, H, extra, dx, dwpart, dw_cols, dw, stream);
 }
 
 // x float32 [n][H] -> out bf16 [n][2H]: [hi | lo] with hi = bf16(v), lo = bf16(v - hi)

@@ -194,7 +194,52 @@ __global__ void __launch_bounds__(RT_ONE_THREADS) route_one(const int32_t* __res
                               tok_of_row, tiles, err, host_err);
 }
 
+// The shared expert's tables (RFC section 6.1: the shared expert runs through
+// the same grouped products as one more group): one expert that holds every
+// token, in token order.  offsets = {0, T}; idx[p] = p, which is both the slot
+// and the token of row p; ones[p] = 1, its combine weight; and the tile table
+// of one expert with T rows under route_scan's rule.
+__global__ void __launch_bounds__(RT_THREADS) shared_tables(int64_t T, int max_big, int big_on,
+                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ idx,
+                                                            float* __restrict__ ones, int32_t* __restrict__ tiles) {
+  const int64_t i = (int64_t)blockIdx.x * RT_THREADS + threadIdx.x;
+  const int64_t rem = big_on ? T % TILE_BIG : T;
+  const bool big_tail = big_on && rem > TILE_BIG / 2;
+  const int64_t nbig = big_on ? T / TILE_BIG + (big_tail ? 1 : 0) : 0;
+  const int64_t nsmall = big_tail ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
+  if (i < T) {
+    idx[i] = (int32_t)i;
+    ones[i] = 1.f;
+  }
+  if (i < nbig) {
+    tiles[4 + 2 * i] = 0;
+    tiles[4 + 2 * i + 1] = (int32_t)(i * TILE_BIG);
+  }
+  if (i < nsmall) {
+    int32_t* small = tiles + 4 + 2 * (int64_t)max_big;
+    small[2 * i] = 0;
+    small[2 * i + 1] = (int32_t)(nbig * TILE_BIG + i * TILE_SMALL);
+  }
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = (int32_t)T;
+    tiles[0] = (int32_t)nbig;
+    tiles[1] = (int32_t)nsmall;
+    tiles[2] = TILE_BIG;
+    tiles[3] = TILE_SMALL;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_shared_tables(int64_t T, int max_big, int big_on, int32_t* offsets, int32_t* idx, float* ones,
+                                int32_t* tiles, hipStream_t stream) {
+  // every table entry index is below max(T, 1): #big and #small are at most T
+  const int64_t nb = (T + RT_THREADS - 1) / RT_THREADS;
+  hipLaunchKernelGGL(shared_tables, dim3((unsigned)(nb < 1 ? 1 : nb)), dim3(RT_THREADS), 0, stream, T, max_big,
+                     big_on, offsets, idx, ones, tiles);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,

@@ -6,7 +6,8 @@ the C ABI of include/hmm.h; torch supplies device memory and the current HIP
 stream.  (HyperMegaMoE RFC section 3.1: the public call takes exactly x,
 topk_ids, topk_weights, up_proj_weight and down_proj_weight and returns y;
 section 3.2: the backward returns one gradient per public argument, None for
-topk_ids; section 3.3: offsets, tiling and buffers are internal.)
+topk_ids; section 3.3: offsets, tiling and buffers are internal.)  The
+optional shared expert (section 6.1) is a keyword-only pair of weights.
 """
 
 import ctypes
@@ -16,8 +17,9 @@ import torch
 from . import _lib
 
 
-def _problem(T, H, I, E, K, flags=_lib.HMM_FLAG_VALIDATE_IDS, out_dtype=_lib.HMM_BF16, gmm1_dtype=_lib.HMM_BF16):
-    return _lib.Problem(int(T), int(H), int(I), int(E), int(K), out_dtype, gmm1_dtype, flags, 0)
+def _problem(T, H, I, E, K, flags=_lib.HMM_FLAG_VALIDATE_IDS, out_dtype=_lib.HMM_BF16, gmm1_dtype=_lib.HMM_BF16,
+             shared_I=0):
+    return _lib.Problem(int(T), int(H), int(I), int(E), int(K), out_dtype, gmm1_dtype, flags, int(shared_I))
 
 
 def _ptr(t):
@@ -57,6 +59,30 @@ def _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight):
     return T, H, I, E, topk_ids.shape[1]
 
 
+def _check_shared(x, shared_up_proj_weight, shared_down_proj_weight):
+    """Shared-expert weights: both or neither; bf16 [H,2Is] and [Is,H] on x's device.  Returns Is (0: none)."""
+    if shared_up_proj_weight is None and shared_down_proj_weight is None:
+        return 0
+    if shared_up_proj_weight is None or shared_down_proj_weight is None:
+        raise ValueError("shared_up_proj_weight and shared_down_proj_weight go together")
+    for name, t in (("shared_up_proj_weight", shared_up_proj_weight),
+                    ("shared_down_proj_weight", shared_down_proj_weight)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device != x.device:
+            raise ValueError("%s is on %s, x on %s" % (name, t.device, x.device))
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16" % name)
+    H = x.shape[1]
+    if shared_up_proj_weight.dim() != 2 or shared_down_proj_weight.dim() != 2:
+        raise ValueError("expected shared_up_proj_weight [H,2Is] and shared_down_proj_weight [Is,H]")
+    Is = shared_down_proj_weight.shape[0]
+    if tuple(shared_up_proj_weight.shape) != (H, 2 * Is) or tuple(shared_down_proj_weight.shape) != (Is, H):
+        raise ValueError("shared_up_proj_weight must be [H,2Is] and shared_down_proj_weight [Is,H] (got %s, %s, H=%d)"
+                         % (tuple(shared_up_proj_weight.shape), tuple(shared_down_proj_weight.shape), H))
+    return Is
+
+
 GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3}
 
 
@@ -84,9 +110,10 @@ def _contig(t, dtype=None):
     return t.contiguous()
 
 
-def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16):
+def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16, Ws1=None, Ws2=None):
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1)
+    Is = 0 if Ws2 is None else Ws2.shape[0]
+    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1, shared_I=Is)
     ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
     _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
     dev = x.device
@@ -94,14 +121,22 @@ def _forward_raw(x, ids, w, W1, W2, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, ou
     y = torch.empty((T, H), dtype=odt, device=dev)
     saved = torch.empty(sv.value, dtype=torch.uint8, device=dev)
     work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
-    _lib.check(lib.hmm_forward(ctypes.byref(prob), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2), _ptr(y),
-                               _ptr(saved), sv.value, _ptr(work), ws.value, _stream(dev)))
+    if Is:
+        _lib.check(lib.hmm_forward_shared(ctypes.byref(prob), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2),
+                                          _ptr(Ws1), _ptr(Ws2), _ptr(y), _ptr(saved), sv.value, _ptr(work), ws.value,
+                                          _stream(dev)))
+    else:
+        _lib.check(lib.hmm_forward(ctypes.byref(prob), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2), _ptr(y),
+                                   _ptr(saved), sv.value, _ptr(work), ws.value, _stream(dev)))
     return y, saved
 
 
-def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16):
+def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.HMM_BF16, out=_lib.HMM_BF16,
+                  Ws1=None, Ws2=None):
+    """(dx, dW1, dW2, d_topk_weights), and (dWs1, dWs2) after them with a shared expert."""
     lib = _lib.load()
-    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1)
+    Is = 0 if Ws2 is None else Ws2.shape[0]
+    prob = _problem(T, H, I, E, K, flags, out_dtype=out, gmm1_dtype=gmm1, shared_I=Is)
     ws = ctypes.c_size_t()
     _lib.check(lib.hmm_backward_sizes(ctypes.byref(prob), ctypes.byref(ws)))
     dev = x.device
@@ -111,6 +146,14 @@ def _backward_raw(dy, x, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1=_lib.
     dW2 = torch.empty((E, I, H), dtype=odt, device=dev)
     dw = torch.empty((T, K), dtype=torch.float32, device=dev)
     work = torch.empty(ws.value, dtype=torch.uint8, device=dev)
+    if Is:
+        dWs1 = torch.empty((H, 2 * Is), dtype=odt, device=dev)
+        dWs2 = torch.empty((Is, H), dtype=odt, device=dev)
+        _lib.check(lib.hmm_backward_shared(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1),
+                                           _ptr(W2), _ptr(Ws1), _ptr(Ws2), _ptr(saved), saved.numel(), _ptr(dx),
+                                           _ptr(dW1), _ptr(dW2), _ptr(dWs1), _ptr(dWs2), _ptr(dw), _ptr(work),
+                                           ws.value, _stream(dev)))
+        return dx, dW1, dW2, dw, dWs1, dWs2
     _lib.check(lib.hmm_backward(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(ids), _ptr(w), _ptr(W1), _ptr(W2),
                                 _ptr(saved), saved.numel(), _ptr(dx), _ptr(dW1), _ptr(dW2), _ptr(dw),
                                 _ptr(work), ws.value, _stream(dev)))
@@ -121,32 +164,39 @@ class HyperMegaMoEFunction(torch.autograd.Function):
     """Forward calls hmm_forward and keeps the saved buffer; backward calls hmm_backward."""
 
     @staticmethod
-    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags, gmm1, out):
+    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags, gmm1, out,
+                shared_up_proj_weight=None, shared_down_proj_weight=None):
         T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+        Is = _check_shared(x, shared_up_proj_weight, shared_down_proj_weight)
         x_ = _contig(x)
         ids = _contig(topk_ids, torch.int32)
         w = _contig(topk_weights, torch.float32)
         W1 = _contig(up_proj_weight)
         W2 = _contig(down_proj_weight)
+        Ws1 = _contig(shared_up_proj_weight) if Is else None
+        Ws2 = _contig(shared_down_proj_weight) if Is else None
         with torch.cuda.device(x.device):
-            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags, gmm1, out)
-        ctx.save_for_backward(x_, ids, w, W1, W2, saved)
+            y, saved = _forward_raw(x_, ids, w, W1, W2, T, H, I, E, K, flags, gmm1, out, Ws1, Ws2)
+        ctx.save_for_backward(x_, ids, w, W1, W2, saved, Ws1, Ws2)
         ctx.dims = (T, H, I, E, K, flags, gmm1, out)
         ctx.w_dtype = topk_weights.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x_, ids, w, W1, W2, saved = ctx.saved_tensors
+        x_, ids, w, W1, W2, saved, Ws1, Ws2 = ctx.saved_tensors
         T, H, I, E, K, flags, gmm1, out = ctx.dims
         dy = _contig(dy, torch.float32 if out == _lib.HMM_F32 else torch.bfloat16)
         with torch.cuda.device(x_.device):
-            dx, dW1, dW2, dw = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1, out)
-        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None, None, None
+            g = _backward_raw(dy, x_, ids, w, W1, W2, saved, T, H, I, E, K, flags, gmm1, out, Ws1, Ws2)
+        dx, dW1, dW2, dw = g[:4]
+        dWs1, dWs2 = g[4:] if Ws1 is not None else (None, None)
+        return dx, None, dw.to(ctx.w_dtype), dW1, dW2, None, None, None, dWs1, dWs2
 
 
 def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True,
-                   gmm1_dtype="bf16", out_dtype=torch.bfloat16):
+                   gmm1_dtype="bf16", out_dtype=torch.bfloat16, shared_up_proj_weight=None,
+                   shared_down_proj_weight=None):
     """y [T,H] = sum_k topk_weights[t,k] * SwiGLU-FFN_{topk_ids[t,k]}(x[t]), on the GPU.
 
     x bf16 [T,H]; topk_ids int32/int64 [T,K] (0 <= id < E); topk_weights float [T,K];
@@ -163,10 +213,15 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     (bf16 hi + lo pairs), for agreement with an unrounded computation to 1e-3;
     it costs about twice the MFMA work.  Under autograd, gradients are cast to
     the dtype of their inputs (bf16 weights get bf16 gradients).
+    ``shared_up_proj_weight`` bf16 [H,2Is] and ``shared_down_proj_weight`` bf16
+    [Is,H] add a shared expert: every token also goes through that SwiGLU FFN,
+    and its output is added to y with weight 1 (after the routed terms); both
+    get gradients.  Its up-projection stays bf16 under ``gmm1_dtype="fp8"``.
     """
     flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
     return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags,
-                                      _gmm1_code(gmm1_dtype), _out_code(out_dtype))
+                                      _gmm1_code(gmm1_dtype), _out_code(out_dtype), shared_up_proj_weight,
+                                      shared_down_proj_weight)
 
 
 # ----------------------------------------------------------------------------- stage entry points (tests, tools)
@@ -227,14 +282,15 @@ def quantize_cols_fp8(w):
     return q, ds
 
 
-def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16"):
+def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16", shared_I=0):
     """Typed views of the arrays a forward recorded in its saved buffer.
 
     In the float32-output mode h is float32 [S, 2I] and a, aw are bf16 [S, 2I]
-    pairs (hi in the first I columns, lo in the last I)."""
+    pairs (hi in the first I columns, lo in the last I).  With a shared expert
+    (shared_I = Is > 0) also shared_h [T, 2Is] and shared_a [T, Is] (same rules)."""
     lib = _lib.load()
     out = _out_code(out_dtype)
-    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles], out_dtype=out)
+    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles], out_dtype=out, shared_I=shared_I)
     L = _lib.SavedLayout()
     _lib.check(lib.hmm_saved_layout_of(ctypes.byref(prob), ctypes.byref(L)))
     S = T * K
@@ -244,7 +300,7 @@ def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16"):
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
         return saved[off:off + nbytes].view(dtype).view(shape)
 
-    return {
+    views = {
         "counts": view(L.counts, E, torch.int32, (E,)),
         "offsets": view(L.offsets, E + 1, torch.int32, (E + 1,)),
         "sorted_slot": view(L.sorted_slot, S, torch.int32, (S,)),
@@ -255,10 +311,21 @@ def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16"):
         "aw": view(L.aw, S * I * (2 if f32 else 1), torch.bfloat16, (S, 2 * I if f32 else I)),
         "id_error": view(L.id_error, 1, torch.int32, (1,)),
     }
+    if shared_I:
+        Is = shared_I
+        views.update({
+            "shared_offsets": view(L.shared_offsets, 2, torch.int32, (2,)),
+            "shared_idx": view(L.shared_idx, T, torch.int32, (T,)),
+            "shared_ones": view(L.shared_ones, T, torch.float32, (T,)),
+            "shared_h": view(L.shared_h, T * 2 * Is, torch.float32 if f32 else torch.bfloat16, (T, 2 * Is)),
+            "shared_a": view(L.shared_a, T * Is * (2 if f32 else 1), torch.bfloat16, (T, 2 * Is if f32 else Is)),
+        })
+    return views
 
 
 def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, validate_ids=True,
-                       tiles="auto", gmm1_dtype="bf16", out_dtype="bf16", fused=False):
+                       tiles="auto", gmm1_dtype="bf16", out_dtype="bf16", fused=False, shared_up_proj_weight=None,
+                       shared_down_proj_weight=None):
     """Forward without autograd; returns (y, saved buffer) for stage-level checks.
 
     ``tiles`` forces the tiling of the grouped products ("auto", "large" or
@@ -267,25 +334,32 @@ def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weig
     (same results; slower on MI355X today, see include/hmm.h).
     """
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    Is = _check_shared(x, shared_up_proj_weight, shared_down_proj_weight)
     flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | _lib.TILE_FLAGS[tiles]
     if fused:
         flags |= _lib.HMM_FLAG_FUSED_FORWARD
     with torch.cuda.device(x.device):
         return _forward_raw(_contig(x), _contig(topk_ids, torch.int32), _contig(topk_weights, torch.float32),
                             _contig(up_proj_weight), _contig(down_proj_weight), T, H, I, E, K, flags,
-                            _gmm1_code(gmm1_dtype), _out_code(out_dtype))
+                            _gmm1_code(gmm1_dtype), _out_code(out_dtype),
+                            _contig(shared_up_proj_weight) if Is else None,
+                            _contig(shared_down_proj_weight) if Is else None)
 
 
 def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto",
-                        gmm1_dtype="bf16", out_dtype="bf16"):
-    """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights).
+                        gmm1_dtype="bf16", out_dtype="bf16", shared_up_proj_weight=None,
+                        shared_down_proj_weight=None):
+    """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights),
+    then (d_shared_up_proj_weight, d_shared_down_proj_weight) with a shared expert.
 
-    With out_dtype float32, dy is taken in float32 and dx, dW1, dW2 are float32."""
+    With out_dtype float32, dy is taken in float32 and dx and the weight gradients are float32."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    Is = _check_shared(x, shared_up_proj_weight, shared_down_proj_weight)
     out = _out_code(out_dtype)
     dyt = torch.float32 if out == _lib.HMM_F32 else torch.bfloat16
     with torch.cuda.device(x.device):
         return _backward_raw(_contig(dy, dyt), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
                              _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles],
-                             _gmm1_code(gmm1_dtype), out)
+                             _gmm1_code(gmm1_dtype), out, _contig(shared_up_proj_weight) if Is else None,
+                             _contig(shared_down_proj_weight) if Is else None)

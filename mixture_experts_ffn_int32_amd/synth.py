@@ -11,7 +11,10 @@ Recipe (every workload):
 * up_proj_weight [E,H,2I] ~ N(0, 1/H), down_proj_weight [E,I,H] ~ N(0, 1/I)
   (variance 1/fan_in; fan_in is the contracted dimension);
 * topk_weights = softmax over K of N(0, 1) logits, float32;
-* the K ids of a token are kept in the order they were drawn.
+* the K ids of a token are kept in the order they were drawn;
+* with ``shared_I`` = Is > 0 in the spec, a shared expert: shared_up_proj_weight
+  [H,2Is] ~ N(0, 1/H) and shared_down_proj_weight [Is,H] ~ N(0, 1/Is), from
+  streams of their own (the other tensors do not change).
 
 Routing structures:
 * ``uniform``: K distinct experts per token, uniformly (the first K entries of
@@ -139,7 +142,8 @@ def make_inputs(spec, seed=0, with_dy=True):
     """All inputs of one problem; bf16 tensors as uint16 bit arrays.
 
     Returns dict(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
-    dY, info).
+    dY, info), plus shared_up_proj_weight and shared_down_proj_weight when the
+    spec has shared_I > 0.
     """
     T, H, I, E = spec["T"], spec["H"], spec["I"], spec["E"]
     ss = np.random.SeedSequence([seed, 0])
@@ -161,6 +165,11 @@ def make_inputs(spec, seed=0, with_dy=True):
     }
     if with_dy:
         out["dY"] = _bf16_normal(r_dy, (T, H), 1.0)
+    Is = spec.get("shared_I", 0)
+    if Is:
+        r_s1, r_s2 = [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence([seed, 2]).spawn(2)]
+        out["shared_up_proj_weight"] = _bf16_normal(r_s1, (H, 2 * Is), 1.0 / math.sqrt(H))
+        out["shared_down_proj_weight"] = _bf16_normal(r_s2, (Is, H), 1.0 / math.sqrt(Is))
     return out
 
 

@@ -58,6 +58,9 @@ def gpu_inputs(inp, device):
     }
     if "dY" in inp:
         out["dY"] = bf16_tensor(inp["dY"], device)
+    for k in ("shared_up_proj_weight", "shared_down_proj_weight"):
+        if k in inp:
+            out[k] = bf16_tensor(inp[k], device)
     return out
 
 
@@ -72,4 +75,7 @@ def oracle_inputs(inp):
     }
     if "dY" in inp:
         d["dY"] = synth.bits_to_f32(inp["dY"])
+    for k in ("shared_up_proj_weight", "shared_down_proj_weight"):
+        if k in inp:
+            d[k] = synth.bits_to_f32(inp[k])
     return d

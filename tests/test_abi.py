@@ -43,7 +43,7 @@ def test_status_strings(lib):
 
 def _prob(**kw):
     d = dict(T=1024, H=512, I=128, E=4, K=2, out_dtype=_lib.HMM_BF16, gmm1_dtype=_lib.HMM_BF16,
-             flags=_lib.HMM_FLAG_VALIDATE_IDS, reserved=0)
+             flags=_lib.HMM_FLAG_VALIDATE_IDS, shared_I=0)
     d.update(kw)
     return _lib.Problem(**d)
 
@@ -55,7 +55,8 @@ def _prob(**kw):
     (dict(out_dtype=7), _lib.HMM_ERR_BAD_DTYPE), (dict(gmm1_dtype=9), _lib.HMM_ERR_BAD_DTYPE),
     (dict(out_dtype=_lib.HMM_F32, gmm1_dtype=_lib.HMM_FP8_E4M3), _lib.HMM_ERR_UNSUPPORTED),
     (dict(gmm1_dtype=_lib.HMM_FP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=16), _lib.HMM_ERR_BAD_SHAPE),
-    (dict(reserved=1), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=6), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(shared_I=1), _lib.HMM_ERR_BAD_SHAPE), (dict(shared_I=32), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(shared_I=65600), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=6), _lib.HMM_ERR_BAD_SHAPE),
 ])
 def test_sizes_reject_bad_problems(lib, kw, status):
     ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
@@ -119,3 +120,41 @@ def test_f32_mode_sizes(lib):
     assert sizes[_lib.HMM_F32][0] >= S * H * 4                       # o in float32
     assert sizes[_lib.HMM_F32][2] >= T * 2 * H * 2 + S * 4 * I * 2 + S * H * 4
     assert all(sizes[_lib.HMM_F32][i] > sizes[_lib.HMM_BF16][i] for i in range(3))
+
+
+def test_shared_expert_sizes_and_entry_points(lib):
+    """A shared expert (shared_I = Is) adds its tables, h_s and a_s to ``saved`` and its
+    output / dH / dX rows to the workspaces; the plain entry points refuse such a problem."""
+    T, H, I, Is = 1024, 512, 128, 192
+    base, shr = _prob(), _prob(shared_I=Is)
+    got = {}
+    for name, p in (("base", base), ("shared", shr)):
+        ws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.hmm_forward_sizes(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(sv)) == 0
+        assert lib.hmm_backward_sizes(ctypes.byref(p), ctypes.byref(bws)) == 0
+        L = _lib.SavedLayout()
+        assert lib.hmm_saved_layout_of(ctypes.byref(p), ctypes.byref(L)) == 0
+        got[name] = (ws.value, sv.value, bws.value, L)
+    Lb, Ls = got["base"][3], got["shared"][3]
+    assert Lb.shared_h == Lb.shared_a == Lb.total                      # empty without a shared expert
+    offs = [Ls.id_error, Ls.shared_offsets, Ls.shared_idx, Ls.shared_ones, Ls.shared_tiles, Ls.shared_h,
+            Ls.shared_a, Ls.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert Ls.shared_ones - Ls.shared_idx >= T * 4 and Ls.shared_a - Ls.shared_h >= T * 2 * Is * 2
+    assert Ls.total - Ls.shared_a >= T * Is * 2
+    assert got["shared"][0] - got["base"][0] >= T * H * 2                     # shared output rows
+    assert got["shared"][2] - got["base"][2] >= T * 2 * Is * 2 + T * H * 2      # shared dH and dX rows
+    z = ctypes.c_void_p(0)
+    ok = ctypes.c_void_p(0x1000)              # never dereferenced: every check fails first
+    assert lib.hmm_forward(ctypes.byref(shr), ok, ok, ok, ok, ok, ok, ok, 1 << 40, ok, 1 << 40, z) == \
+        _lib.HMM_ERR_BAD_SHAPE
+    assert lib.hmm_backward(ctypes.byref(shr), ok, ok, ok, ok, ok, ok, ok, 1 << 40, ok, ok, ok, ok, ok, 1 << 40,
+                            z) == _lib.HMM_ERR_BAD_SHAPE
+    # the shared weights are required with shared_I > 0, ignored without
+    assert lib.hmm_forward_shared(ctypes.byref(shr), ok, ok, ok, ok, ok, z, z, ok, ok, 1 << 40, ok, 1 << 40, z) == \
+        _lib.HMM_ERR_NULL_POINTER
+    assert b"shared_up_proj_weight" in lib.hmm_last_error_message()
+    assert lib.hmm_backward_shared(ctypes.byref(shr), ok, ok, ok, ok, ok, ok, ok, ok, ok, 1 << 40, ok, ok, ok, z, z,
+                                   ok, ok, 1 << 40, z) == _lib.HMM_ERR_NULL_POINTER
+    assert lib.hmm_forward_shared(ctypes.byref(base), ok, ok, ok, ok, ok, z, z, ok, ok, 16, ok, 16, z) == \
+        _lib.HMM_ERR_WORKSPACE_TOO_SMALL

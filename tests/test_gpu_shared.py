@@ -1,0 +1,168 @@
+"""The shared expert (RFC 6.1) on the GPU against the oracle.
+
+Every token also goes through one dense SwiGLU FFN of intermediate size Is; its
+output joins the routed terms at the combine with weight 1 (its dX likewise).
+bf16 outputs are compared with the FAITHFUL oracle element by element (+ its
+admissible deviation) in both tilings, including Is != I, K = 1, a hot expert
+and T = 0; the float32-output mode with the PURE oracle at 1e-3; FP8 runs the
+routed up-projection in FP8 and the shared one in bf16, as the oracle does.
+"""
+
+import numpy as np
+import pytest
+
+from _util import announce, assert_close, gpu_inputs, oracle_inputs, to_f64
+from mixture_experts_ffn_int32_amd import synth
+from oracle.moe_ffn import MoEFFN
+
+pytestmark = pytest.mark.gpu
+
+
+def run_shared(g, tiles="auto", gmm1="bf16", out="bf16", dy=None):
+    import torch
+    from mixture_experts_ffn_int32_amd import backward_from_saved, forward_with_saved
+    sw = dict(shared_up_proj_weight=g["shared_up_proj_weight"], shared_down_proj_weight=g["shared_down_proj_weight"])
+    y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
+                                  g["down_proj_weight"], tiles=tiles, gmm1_dtype=gmm1, out_dtype=out, **sw)
+    res = backward_from_saved(g["dY"] if dy is None else dy, g["x"], g["topk_ids"], g["topk_weights"],
+                              g["up_proj_weight"], g["down_proj_weight"], saved, tiles=tiles, gmm1_dtype=gmm1,
+                              out_dtype=out, **sw)
+    torch.cuda.synchronize()
+    assert len(res) == 6
+    return (y, saved) + tuple(res)
+
+
+def check_all(name, o, got, out="bf16", tol=None):
+    y, _, dx, dW1, dW2, dw, dWs1, dWs2 = got
+    kw = {} if tol is None else dict(rtol=tol, atol=tol)
+    ry, ryd = o.forward_dev(out_dtype=out)
+    (rdx, rdw, rdW1, rdW2), (ddx, ddw, ddW1, ddW2) = o.backward_dev(out_dtype=out)
+    (rs1, rs2), (ds1, ds2) = o.shared_backward_dev(out_dtype=out)
+    if tol is not None:  # PURE oracle: no admissible deviation
+        ryd = ddx = ddw = ddW1 = ddW2 = ds1 = ds2 = 0.0
+    assert_close(to_f64(y), ry, name + " y", ryd, **kw)
+    assert_close(to_f64(dx), rdx, name + " dx", ddx, **kw)
+    assert_close(to_f64(dw), rdw, name + " d_topk_weights", ddw, **kw)
+    assert_close(to_f64(dW1), rdW1, name + " d_up_proj_weight", ddW1, **kw)
+    assert_close(to_f64(dW2), rdW2, name + " d_down_proj_weight", ddW2, **kw)
+    assert_close(to_f64(dWs1), rs1, name + " d_shared_up_proj_weight", ds1, **kw)
+    assert_close(to_f64(dWs2), rs2, name + " d_shared_down_proj_weight", ds2, **kw)
+
+
+CASES = [
+    ("tiny", dict(shared_I=64)),
+    ("ragged", dict(T=300, H=256, I=192, E=6, K=3, routing="uniform", shared_I=128)),
+    ("hot_wide", dict(T=257, H=192, I=128, E=5, K=2, routing="hot", shared_I=320)),
+    ("k1", dict(T=200, H=128, I=128, E=3, K=1, routing="uniform", shared_I=64)),
+    ("zipf", dict(T=411, H=256, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5, shared_I=256)),
+]
+
+
+@pytest.mark.parametrize("tiles", ["large", "narrow"])
+@pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
+def test_shared_expert_parity(name, over, tiles):
+    spec = synth.spec_with("tiny", **over)
+    inp = synth.make_inputs(spec, seed=41)
+    announce("shared expert %s %s Is=%d tiles=%s" % (name, {k: spec[k] for k in "THIEK"}, spec["shared_I"], tiles))
+    g = gpu_inputs(inp, "cuda")
+    got = run_shared(g, tiles)
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    check_all(name, o, got)
+
+
+@pytest.mark.parametrize("tiles", ["large", "narrow"])
+def test_shared_expert_intermediates_and_tables(tiles):
+    from mixture_experts_ffn_int32_amd import saved_views
+    spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3, shared_I=128)
+    inp = synth.make_inputs(spec, seed=42)
+    announce("shared intermediates tiles=%s" % tiles)
+    g = gpu_inputs(inp, "cuda")
+    _, saved, *_ = run_shared(g, tiles)
+    T, Is = spec["T"], spec["shared_I"]
+    v = saved_views(saved, *(spec[k] for k in "THIEK"), tiles=tiles, shared_I=Is)
+    assert v["shared_offsets"].cpu().tolist() == [0, T]
+    assert np.array_equal(v["shared_idx"].cpu().numpy(), np.arange(T))
+    assert np.array_equal(v["shared_ones"].cpu().numpy(), np.ones(T, np.float32))
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    (h, a, _), (hd, ad, _) = o.shared.slot_intermediates_dev(np.arange(T))
+    assert_close(to_f64(v["shared_h"]), h, "shared h", hd)
+    assert_close(to_f64(v["shared_a"]), a, "shared a", ad)
+
+
+def test_shared_expert_t0_and_determinism():
+    import torch
+    spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3, shared_I=128)
+    g = gpu_inputs(synth.make_inputs(spec, seed=43), "cuda")
+    announce("shared determinism")
+    r1 = run_shared(g)
+    r2 = run_shared(g)
+    for i in (0, 2, 3, 4, 5, 6, 7):
+        assert torch.equal(r1[i], r2[i]), i
+    announce("shared T=0")
+    g0 = gpu_inputs(synth.make_inputs(synth.spec_with(spec, T=0), seed=43), "cuda")
+    for tiles in ("large", "narrow"):
+        y, _, dx, dW1, dW2, dw, dWs1, dWs2 = run_shared(g0, tiles)
+        assert y.shape == (0, 256) and dx.shape == (0, 256)
+        for t in (dW1, dW2, dWs1, dWs2):
+            assert not t.float().abs().sum().item()
+
+
+def test_shared_expert_fp8_routed():
+    """FP8 routed up-projection; the shared expert's stays bf16 (as in the oracle)."""
+    spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3, gmm1="fp8", shared_I=128)
+    inp = synth.make_inputs(spec, seed=44)
+    announce("shared + fp8")
+    g = gpu_inputs(inp, "cuda")
+    for tiles in ("large", "narrow"):
+        got = run_shared(g, tiles, gmm1="fp8")
+        o = MoEFFN(**oracle_inputs(inp), mode="faithful", gmm1="fp8")
+        check_all("fp8 " + tiles, o, got)
+
+
+@pytest.mark.parametrize("tiles", ["large", "narrow"])
+def test_shared_expert_f32_mode(tiles):
+    import torch
+    spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3, shared_I=128)
+    inp = synth.make_inputs(spec, seed=45)
+    announce("shared f32 mode tiles=%s" % tiles)
+    g = gpu_inputs(inp, "cuda")
+    rng = np.random.default_rng(7)
+    d = synth.bits_to_f32(inp["dY"])
+    dy = (d * (1.0 + 1e-3 * rng.standard_normal(d.shape))).astype(np.float32)
+    got = run_shared(g, tiles, out="f32", dy=torch.from_numpy(dy).cuda())
+    assert all(t.dtype == torch.float32 for t in (got[0], got[2], got[3], got[4], got[6], got[7]))
+    oi = oracle_inputs(inp)
+    oi["dY"] = dy
+    o = MoEFFN(**oi, mode="pure")
+    check_all("f32 " + tiles, o, got, out="f32", tol=1e-3)
+
+
+def test_shared_expert_autograd():
+    import torch
+    from mixture_experts_ffn_int32_amd import hyper_mega_moe
+    spec = synth.spec_with("tiny", T=96, H=128, I=64, E=4, K=2, shared_I=128)
+    g = gpu_inputs(synth.make_inputs(spec, seed=46), "cuda")
+    announce("shared autograd")
+    leaves = {k: g[k].clone().requires_grad_(True) for k in
+              ("x", "topk_weights", "up_proj_weight", "down_proj_weight", "shared_up_proj_weight",
+               "shared_down_proj_weight")}
+    y = hyper_mega_moe(leaves["x"], g["topk_ids"], leaves["topk_weights"], leaves["up_proj_weight"],
+                       leaves["down_proj_weight"], shared_up_proj_weight=leaves["shared_up_proj_weight"],
+                       shared_down_proj_weight=leaves["shared_down_proj_weight"])
+    y.backward(g["dY"])
+    y_raw, _, dx, dW1, dW2, dw, dWs1, dWs2 = run_shared(g)
+    assert torch.equal(y, y_raw) and torch.equal(leaves["x"].grad, dx)
+    assert torch.equal(leaves["up_proj_weight"].grad, dW1) and torch.equal(leaves["down_proj_weight"].grad, dW2)
+    assert torch.equal(leaves["topk_weights"].grad, dw)
+    assert torch.equal(leaves["shared_up_proj_weight"].grad, dWs1)
+    assert torch.equal(leaves["shared_down_proj_weight"].grad, dWs2)
+    # without the shared weights the routed result is unchanged by their presence elsewhere
+    y0 = hyper_mega_moe(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"])
+    assert not torch.equal(y0, y_raw)
+    with pytest.raises(ValueError):
+        hyper_mega_moe(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"],
+                       shared_up_proj_weight=g["shared_up_proj_weight"])
+    with pytest.raises(ValueError):
+        hyper_mega_moe(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"],
+                       shared_up_proj_weight=g["shared_up_proj_weight"][:, :64].contiguous(),
+                       shared_down_proj_weight=g["shared_down_proj_weight"])
