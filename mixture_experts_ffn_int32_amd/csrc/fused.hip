@@ -36,7 +36,7 @@ namespace hmm {
 namespace {
 
 typedef Gmm1<Narrow, true> FG1;
-typedef Gmm2<Narrow, true> FG2;
+typedef Gmm2<Narrow, true, true> FG2;
 constexpr int FT = Narrow::NTHR;
 constexpr uint32_t SPIN_CAP = 1u << 20;  // polls (an L2 round trip and s_sleep each): about a second
 

@@ -108,7 +108,9 @@ struct Gmm1 : RowTile<Cc, SMALL> {
 };
 
 // ------------------------------------------------------------- gmm2
-template <class Cc, bool SMALL>
+// COH_A: ``a`` was written in the same launch (the fused forward): read it at
+// the coherence point.  A template parameter, so the main loop has no branch.
+template <class Cc, bool SMALL, bool COH_A = false>
 struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   typedef RowTile<Cc, SMALL> B_;
   typedef Cc C;
@@ -146,7 +148,7 @@ struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
-    if (ar->coh) {  // ``a`` was written in the same launch: read it at the coherence point
+    if constexpr (COH_A) {
 #pragma unroll
       for (int i = 0; i < C::CA; ++i) r[i] = bload_coh(ra_, aoff[i], kt * BK * 2);
     } else {
@@ -346,6 +348,10 @@ struct Dw : PlainCols<Cc> {
   int e, m0, n0, nk, p0, p1;
   // byte offsets of the rows of the next step to be loaded (computed by index())
   uint32_t rowoff_a[C::CA], rowoff_b[C::CB];
+  // row indices of a step of the gathered operand(s), as fetched
+  struct Raw {
+    int32_t a[GATHER_A ? C::CA : 1], b[GATHER_B ? C::CB : 1];
+  };
   // The cost of a tile grows with its expert's row count, so every XCD gets an
   // equal slice of every expert's tiles (not a contiguous run of experts): XCD x
   // (workgroups b with b % 8 == x) walks the experts in order and takes tiles
@@ -371,10 +377,27 @@ struct Dw : PlainCols<Cc> {
     rb_ = make_rsrc(A.B, A.b_rows * A.N * 2);
     return true;
   }
+  // Loads of the token index of every row this thread will read in step kt
+  // (rows past the expert's end load its last row's index, unused).
+  template <int R, int CN>
+  __device__ __forceinline__ void fetch_rows(int kt, int32_t (&raw)[CN]) {
+    const int tid = threadIdx.x;
+    constexpr int CPR = R / 8;
+#pragma unroll
+    for (int i = 0; i < CN; ++i) {
+      const int p = min(p0 + kt * BK + (tid + i * C::NTHR) / CPR, p1 - 1);
+      raw[i] = ar->tok_of_row[p];
+    }
+  }
+  __device__ __forceinline__ void fetch(int kt, Raw& r) {
+    if constexpr (GATHER_A) fetch_rows<C::BM>(kt, r.a);
+    if constexpr (GATHER_B) fetch_rows<C::BN>(kt, r.b);
+  }
   // row part of the offsets of step kt: rows p past the expert's end and columns
   // past the matrix get the resource's end (reads zeros)
-  template <bool GATHER, int R, int CN>
-  __device__ __forceinline__ void rows_of(int64_t nrows, int64_t ld, int64_t c0, int kt, uint32_t (&ro)[CN]) {
+  template <bool GATHER, int R, int CN, int CR>
+  __device__ __forceinline__ void rows_of(int64_t nrows, int64_t ld, int64_t c0, int kt, const int32_t (&raw)[CR],
+                                          uint32_t (&ro)[CN]) {
     const int tid = threadIdx.x;
     constexpr int CPR = R / 8;
     const uint32_t end = (uint32_t)(nrows * ld * 2);
@@ -383,18 +406,15 @@ struct Dw : PlainCols<Cc> {
       const int c = tid + i * C::NTHR;
       const int kr = c / CPR, c8 = c % CPR;
       const int p = p0 + kt * BK + kr;
-      const int64_t col = c0 + c8 * 8;
-      uint32_t off = end;
-      if (p < p1 && col < ld) {
-        const int64_t row = GATHER ? (int64_t)ar->tok_of_row[p] : (int64_t)p;
-        off = (uint32_t)((row * ld + col) * 2);
-      }
-      ro[i] = off;
+      const uint32_t col = (uint32_t)c0 + c8 * 8;  // every offset fits 32 bits (resources < 4 GiB)
+      uint32_t row = (uint32_t)p;
+      if constexpr (GATHER) row = (uint32_t)raw[i];
+      ro[i] = (p < p1 && col < (uint32_t)ld) ? (row * (uint32_t)ld + col) * 2u : end;
     }
   }
-  __device__ __forceinline__ void index(int kt) {
-    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->M, m0, kt, rowoff_a);
-    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->N, n0, kt, rowoff_b);
+  __device__ __forceinline__ void index(int kt, const Raw& r) {
+    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->M, m0, kt, r.a, rowoff_a);
+    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->N, n0, kt, r.b, rowoff_b);
   }
   __device__ __forceinline__ void load_a(int, u32x4 (&r)[C::CA]) {
 #pragma unroll

@@ -101,32 +101,44 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (nk > 0) {
+    // Gathered operands take two phases per K step: fetch(k) issues the loads of
+    // step k's row indices into the Raw set, index(k) turns them into offsets one
+    // step later, so in the steady state no index load is waited for right after
+    // it is issued (the memory counter is in order: such a wait would drain the
+    // data loads issued before it too).  Inside the loop every load and LDS store
+    // is unconditional (the last steps run in a tail after it): with a load under
+    // a condition, the wait before the LDS stores at the top of the loop would
+    // have to assume it was skipped and drain every load in flight.
     u32x4 ra0[C::CA], rb0[C::CB], ra1[C::CA], rb1[C::CB];
-    pol.index(0);
+    typename P::Raw rw;
+    const auto kc = [nk](int k) { return k < nk ? k : nk - 1; };
+    pol.fetch(0, rw);
+    pol.index(0, rw);
     pol.load_a(0, ra0);
     pol.load_b(0, rb0);
-    if (nk > 1) {
-      pol.index(1);
-      pol.load_a(1, ra1);
-      pol.load_b(1, rb1);
-    }
+    pol.fetch(kc(1), rw);
+    pol.index(kc(1), rw);
+    pol.load_a(kc(1), ra1);
+    pol.load_b(kc(1), rb1);
     store_stage<C, P>(smem, ra0, rb0);
-    if (nk > 2) {
-      pol.index(2);
-      pol.load_a(2, ra0);
-      pol.load_b(2, rb0);
-    }
-    if (nk > 3) pol.index(3);
+    pol.fetch(kc(2), rw);
+    pol.index(kc(2), rw);
+    pol.load_a(kc(2), ra0);
+    pol.load_b(kc(2), rb0);
+    pol.fetch(kc(3), rw);
     __syncthreads();
-    // one K step: park step kt+1 (in set `nx`) in the other LDS buffer, refill
-    // that set with step kt+3, fetch the indices of step kt+4, then multiply step kt
-    auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB]) {
-      if (kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
-      if (kt + 3 < nk) {
+    // one K step: park step kt+1 (in set `nx`) in the other LDS buffer, turn the
+    // indices of step kt+3 (fetched one step ago) into offsets, fetch the indices
+    // of step kt+4, refill `nx` with step kt+3, then multiply step kt.  ``full``:
+    // all of those steps exist (the loop), else each is checked (the tail).
+    auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB], bool full) {
+      if (full || kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
+      if (full || kt + 3 < nk) {
+        pol.index(kt + 3, rw);
+        pol.fetch(kc(kt + 4), rw);
         pol.load_a(kt + 3, nxa);
         pol.load_b(kt + 3, nxb);
       }
-      if (kt + 4 < nk) pol.index(kt + 4);
       const uint16_t* sa = smem + (kt & 1) * C::STAGE;
       const uint16_t* sb = sa + C::A_ELEMS;
 #pragma unroll
@@ -144,13 +156,17 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
       }
       __syncthreads();
     };
-    // register set 1 holds odd steps, set 0 even steps
+    // register set 1 holds odd steps, set 0 even steps; the loop runs while both
+    // of its steps have a step 3 ahead, the tail (at most 4 steps) after it
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, ra1, rb1);
-      step(kt + 1, ra0, rb0);
+    for (; kt + 4 < nk; kt += 2) {
+      step(kt, ra1, rb1, true);
+      step(kt + 1, ra0, rb0, true);
     }
-    if (kt < nk) step(kt, ra1, rb1);
+    if (kt < nk) step(kt, ra1, rb1, false);
+    if (kt + 1 < nk) step(kt + 1, ra0, rb0, false);
+    if (kt + 2 < nk) step(kt + 2, ra1, rb1, false);
+    if (kt + 3 < nk) step(kt + 3, ra0, rb0, false);
   }
   pol.epilogue(acc, wm, wn, lane, smem);
   return true;
@@ -240,7 +256,9 @@ struct RowTile {
   typedef Cc C;
   static constexpr bool RAW_INDEX = false;  // init takes the XCD-remapped logical index
   int e, row0, rows, n0, nk, nt;
-  __device__ __forceinline__ void index(int) {}  // K-major rows are fixed for the whole tile
+  struct Raw {};  // K-major rows are fixed for the whole tile: no per-step indices
+  __device__ __forceinline__ void fetch(int, Raw&) {}
+  __device__ __forceinline__ void index(int, Raw&) {}
   __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
     const int R = SMALL ? (int)g.max_small : (int)g.max_big;
     if (logical >= R * n_ntiles) return false;

@@ -425,9 +425,28 @@ struct DwF32 : PlainCols<Cc> {
     rb_ = make_rsrc(A.B, A.b_rows * A.ldb * 2);
     return true;
   }
-  template <bool GATHER, int R, int CN>
+  // row indices of a step of the gathered operand, as fetched (see gemm_tile)
+  struct Raw {
+    int32_t a[GATHER_A ? C::CA : 1], b[GATHER_B ? C::CB : 1];
+  };
+  template <int R, int CN>
+  __device__ __forceinline__ void fetch_rows(int kk, int32_t (&raw)[CN]) {
+    const int tid = threadIdx.x;
+    constexpr int CPR = R / 8;
+#pragma unroll
+    for (int i = 0; i < CN; ++i) {
+      const int p = min(p0 + kk * BK + (tid + i * C::NTHR) / CPR, p1 - 1);
+      raw[i] = ar->tok_of_row[p];
+    }
+  }
+  __device__ __forceinline__ void fetch(int kt, Raw& r) {
+    const int kk = kt % nk1;
+    if constexpr (GATHER_A) fetch_rows<C::BM>(kk, r.a);
+    if constexpr (GATHER_B) fetch_rows<C::BN>(kk, r.b);
+  }
+  template <bool GATHER, int R, int CN, int CR>
   __device__ __forceinline__ void rows_of(int64_t nrows, int64_t ld, int64_t width, int64_t shift, int64_t c0, int kk,
-                                          uint32_t (&ro)[CN]) {
+                                          const int32_t (&raw)[CR], uint32_t (&ro)[CN]) {
     const int tid = threadIdx.x;
     constexpr int CPR = R / 8;
     const uint32_t end = (uint32_t)(nrows * ld * 2);
@@ -436,19 +455,16 @@ struct DwF32 : PlainCols<Cc> {
       const int c = tid + i * C::NTHR;
       const int kr = c / CPR, c8 = c % CPR;
       const int p = p0 + kk * BK + kr;
-      const int64_t col = c0 + c8 * 8;
-      uint32_t off = end;
-      if (p < p1 && col < width) {
-        const int64_t row = GATHER ? (int64_t)ar->tok_of_row[p] : (int64_t)p;
-        off = (uint32_t)((row * ld + shift + col) * 2);
-      }
-      ro[i] = off;
+      const uint32_t col = (uint32_t)c0 + c8 * 8;  // every offset fits 32 bits (resources < 4 GiB)
+      uint32_t row = (uint32_t)p;
+      if constexpr (GATHER) row = (uint32_t)raw[i];
+      ro[i] = (p < p1 && col < (uint32_t)width) ? (row * (uint32_t)ld + (uint32_t)shift + col) * 2u : end;
     }
   }
-  __device__ __forceinline__ void index(int kt) {
+  __device__ __forceinline__ void index(int kt, const Raw& r) {
     const int q = kt / nk1, kk = kt - q * nk1;
-    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->lda, ar->M, qa(q) * ar->a_shift, m0, kk, rowoff_a);
-    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->ldb, ar->N, qb(q) * ar->b_shift, n0, kk, rowoff_b);
+    rows_of<GATHER_A, C::BM, C::CA>(ar->a_rows, ar->lda, ar->M, qa(q) * ar->a_shift, m0, kk, r.a, rowoff_a);
+    rows_of<GATHER_B, C::BN, C::CB>(ar->b_rows, ar->ldb, ar->N, qb(q) * ar->b_shift, n0, kk, r.b, rowoff_b);
   }
   __device__ __forceinline__ void load_a(int, u32x4 (&r)[C::CA]) {
 #pragma unroll

@@ -206,24 +206,24 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
 
   if (nk > 0) {
     constexpr int AHEAD = C::SETS + 1;  // K steps between a load and its MFMAs
+    // Inside the loops every load and LDS store is unconditional (the last steps
+    // run in a tail), so the waits at the top of the loop can count on the loads
+    // issued after the ones they wait for (see gemm_core.h).
+    const auto kc = [nk](int k) { return k < nk ? k : nk - 1; };
     u32x4 ra0[C::CA], rb0[C::CB], ra1[C::SETS == 2 ? C::CA : 1], rb1[C::SETS == 2 ? C::CB : 1];
     pol.load_a(0, ra0);
     pol.load_b(0, rb0);
     if constexpr (C::SETS == 2) {
-      if (nk > 1) {
-        pol.load_a(1, ra1);
-        pol.load_b(1, rb1);
-      }
+      pol.load_a(kc(1), ra1);
+      pol.load_b(kc(1), rb1);
     }
     store_stage8<C, P>(smem, ra0, rb0);
-    if (nk > AHEAD - 1) {
-      pol.load_a(AHEAD - 1, ra0);
-      pol.load_b(AHEAD - 1, rb0);
-    }
+    pol.load_a(kc(AHEAD - 1), ra0);
+    pol.load_b(kc(AHEAD - 1), rb0);
     __syncthreads();
-    auto step = [&](int kt, auto& nxa, auto& nxb) {
-      if (kt + 1 < nk) store_stage8<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
-      if (kt + AHEAD < nk) {
+    auto step = [&](int kt, auto& nxa, auto& nxb, bool full) {
+      if (full || kt + 1 < nk) store_stage8<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
+      if (full || kt + AHEAD < nk) {
         pol.load_a(kt + AHEAD, nxa);
         pol.load_b(kt + AHEAD, nxb);
       }
@@ -262,13 +262,18 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
     };
     if constexpr (C::SETS == 2) {
       int kt = 0;
-      for (; kt + 1 < nk; kt += 2) {
-        step(kt, ra1, rb1);
-        step(kt + 1, ra0, rb0);
+      for (; kt + AHEAD + 1 < nk; kt += 2) {
+        step(kt, ra1, rb1, true);
+        step(kt + 1, ra0, rb0, true);
       }
-      if (kt < nk) step(kt, ra1, rb1);
+      if (kt < nk) step(kt, ra1, rb1, false);
+      if (kt + 1 < nk) step(kt + 1, ra0, rb0, false);
+      if (kt + 2 < nk) step(kt + 2, ra1, rb1, false);
+      if (kt + 3 < nk) step(kt + 3, ra0, rb0, false);
     } else {
-      for (int kt = 0; kt < nk; ++kt) step(kt, ra0, rb0);
+      int kt = 0;
+      for (; kt + AHEAD < nk; ++kt) step(kt, ra0, rb0, true);
+      for (; kt < nk; ++kt) step(kt, ra0, rb0, false);
     }
   }
   pol.epilogue(acc, wm, wn, lane, smem);
