@@ -62,11 +62,12 @@ def recorded_traffic(workload, kernel):
     return None if ent is None else int(round(ent["bytes"]))
 
 
-def stage_work(stage, T, H, I, E, K, f32=False):
+def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
     """Algorithmic work of one launch of a stage: (bound, amount, unit, peak).
 
     The float32-output mode counts the same algorithmic flops (its hi/lo operand
-    pairs make the MFMAs do about 1.9x that work) and float32 rows in the combines."""
+    pairs make the MFMAs do about 1.9x that work) and float32 rows in the combines.
+    Is > 0: a shared expert of that width (one more group of all T rows)."""
     S = T * K
     eb = 4 if f32 else 2
     if stage == "gmm1_fp8_swiglu":
@@ -81,12 +82,19 @@ def stage_work(stage, T, H, I, E, K, f32=False):
     }
     flops["act_grad+dw2"] = flops["act_grad"] + flops["dw2"]      # two products in one launch
     flops["input_grad+dw1"] = flops["input_grad"] + flops["dw1"]
+    # a shared expert: the same products over T rows of width Is, in the routed launches ("<stage>+shared")
+    shared = {k: v * T * Is // (S * I) for k, v in flops.items()}
+    for k, v in shared.items():
+        flops[k + "+shared"] = flops[k] + v
+        flops["shared_" + k] = v                      # its own launches (float32-output mode)
+    flops["shared_gmm1"] = shared["gmm1_swiglu"]
     if stage in flops:
         return "mfma", flops[stage], "TFLOP/s", PEAK_BF16_TFLOPS
     nbytes = {
         # read K gathered rows per token + row index + weight, write one row
-        "combine": S * H * eb + S * 8 + T * H * eb,
-        "combine_dx": S * H * eb + S * 4 + T * H * eb,   # (+ d_topk_weights partials, small)
+        "combine": S * H * eb + S * 8 + T * H * eb + (T * H * eb if Is else 0),   # (+ shared rows)
+        "combine_dx": S * H * eb + S * 4 + T * H * eb + (T * H * eb if Is else 0),  # (+ d_topk_weights partials)
+        "shared_tables": T * 12,
         "split_dy": T * H * 4 + T * H * 4,              # float32 dY -> bf16 hi | lo
         # ids read twice, histograms, sorted_slot + row_of_slot written
         "route": S * 4 * 2 + S * 8,
@@ -129,7 +137,8 @@ class Runner:
         flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
         gmm1 = _lib.HMM_FP8_E4M3 if spec.get("gmm1", "bf16") == "fp8" else _lib.HMM_BF16
         f32 = out_dtype == "f32"
-        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_F32 if f32 else _lib.HMM_BF16, gmm1, flags, 0)
+        Is = spec.get("shared_I", 0)
+        self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_F32 if f32 else _lib.HMM_BF16, gmm1, flags, Is)
         fws, sv, bws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
         _lib.check(self.lib.hmm_forward_sizes(ctypes.byref(self.prob), ctypes.byref(fws), ctypes.byref(sv)))
         _lib.check(self.lib.hmm_backward_sizes(ctypes.byref(self.prob), ctypes.byref(bws)))
@@ -148,15 +157,30 @@ class Runner:
         self.sizes = (fws.value, sv.value, bws.value)
         self.stream = torch.cuda.current_stream(device)
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-        self.fargs = (ctypes.byref(self.prob), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2), P(self.y),
-                      P(self.saved), sv.value, P(self.fwork), fws.value, ctypes.c_void_p(self.stream.cuda_stream))
-        self.bargs = (ctypes.byref(self.prob), P(self.dy), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2),
-                      P(self.saved), sv.value, P(self.dx), P(self.dW1), P(self.dW2), P(self.dw), P(self.bwork),
-                      bws.value, ctypes.c_void_p(self.stream.cuda_stream))
+        st = ctypes.c_void_p(self.stream.cuda_stream)
+        self.shared = bool(Is)
+        if self.shared:  # the shared-expert entry points, with its weights and their gradients
+            self.Ws1 = bf(inp["shared_up_proj_weight"])
+            self.Ws2 = bf(inp["shared_down_proj_weight"])
+            self.dWs1 = torch.empty((H, 2 * Is), dtype=odt, device=device)
+            self.dWs2 = torch.empty((Is, H), dtype=odt, device=device)
+            self.fargs = (ctypes.byref(self.prob), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2),
+                          P(self.Ws1), P(self.Ws2), P(self.y), P(self.saved), sv.value, P(self.fwork), fws.value, st)
+            self.bargs = (ctypes.byref(self.prob), P(self.dy), P(self.x), P(self.ids), P(self.w), P(self.W1),
+                          P(self.W2), P(self.Ws1), P(self.Ws2), P(self.saved), sv.value, P(self.dx), P(self.dW1),
+                          P(self.dW2), P(self.dWs1), P(self.dWs2), P(self.dw), P(self.bwork), bws.value, st)
+            self.fwd, self.bwd = self.lib.hmm_forward_shared, self.lib.hmm_backward_shared
+        else:
+            self.fargs = (ctypes.byref(self.prob), P(self.x), P(self.ids), P(self.w), P(self.W1), P(self.W2),
+                          P(self.y), P(self.saved), sv.value, P(self.fwork), fws.value, st)
+            self.bargs = (ctypes.byref(self.prob), P(self.dy), P(self.x), P(self.ids), P(self.w), P(self.W1),
+                          P(self.W2), P(self.saved), sv.value, P(self.dx), P(self.dW1), P(self.dW2), P(self.dw),
+                          P(self.bwork), bws.value, st)
+            self.fwd, self.bwd = self.lib.hmm_forward, self.lib.hmm_backward
 
     def step(self):
-        self._lib.check(self.lib.hmm_forward(*self.fargs))
-        self._lib.check(self.lib.hmm_backward(*self.bargs))
+        self._lib.check(self.fwd(*self.fargs))
+        self._lib.check(self.bwd(*self.bargs))
 
     def timed(self, n):
         torch = self.torch
@@ -188,10 +212,15 @@ def cpu_baseline(spec, seed, budget_s=12.0):
         d = dict(x=synth.bits_to_f32(inp["x"][:tp]), topk_ids=inp["topk_ids"][:tp],
                  topk_weights=inp["topk_weights"][:tp], up_proj_weight=synth.bits_to_f32(inp["up_proj_weight"]),
                  down_proj_weight=synth.bits_to_f32(inp["down_proj_weight"]), dY=synth.bits_to_f32(inp["dY"][:tp]))
+        for k in ("shared_up_proj_weight", "shared_down_proj_weight"):
+            if k in inp:
+                d[k] = synth.bits_to_f32(inp[k])
         t0 = time.perf_counter()
         m = MoEFFN(**d, mode="faithful", gmm1=spec.get("gmm1", "bf16"))
         m.forward()
         m.backward()
+        if m.shared is not None:
+            m.shared_backward_dev()
         return time.perf_counter() - t0
 
     tp = min(T, 8)
@@ -214,6 +243,8 @@ def main():
     ap.add_argument("--no-validate", action="store_true", help="skip the id check's device-to-host read-back")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"],
                     help="f32: the float32-output accuracy mode (hi/lo operand pairs)")
+    ap.add_argument("--shared-I", type=int, default=0, metavar="IS",
+                    help="add a shared expert of intermediate size IS (every token, weight 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -239,13 +270,16 @@ def main():
         log("[bench] copied %d MiB 5 times (reads %d KiB, writes %d KiB per copy)" % (n >> 20, n >> 10, n >> 10))
         return
     spec = dict(synth.WORKLOADS[args.workload])
+    if args.shared_I:
+        spec["shared_I"] = args.shared_I
+    Is = spec.get("shared_I", 0)
     fp8 = spec.get("gmm1", "bf16") == "fp8"
     T, H, I, E, K = (spec[k] for k in "THIEK")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate, out_dtype=args.out_dtype)
-    log("[bench] workload %s T=%d H=%d I=%d E=%d K=%d; workspace fwd %.1f MB, saved %.1f MB, bwd %.1f MB"
-        % (args.workload, T, H, I, E, K, r.sizes[0] / 1e6, r.sizes[1] / 1e6, r.sizes[2] / 1e6))
+    log("[bench] workload %s T=%d H=%d I=%d E=%d K=%d shared_I=%d; workspace fwd %.1f MB, saved %.1f MB, bwd %.1f MB"
+        % (args.workload, T, H, I, E, K, Is, r.sizes[0] / 1e6, r.sizes[1] / 1e6, r.sizes[2] / 1e6))
 
     first_ms = r.timed(1)
     for _ in range(max(0, args.warmup - 1)):
@@ -271,7 +305,7 @@ def main():
     rows = []
     for name, (n, tot) in sorted(stages.items(), key=lambda kv: -kv[1][1]):
         avg = tot / max(n, 1)
-        bound, work, unit, peak = stage_work(name, T, H, I, E, K, args.out_dtype == "f32")
+        bound, work, unit, peak = stage_work(name, T, H, I, E, K, args.out_dtype == "f32", Is)
         rate = (work / (avg * 1e-3) / (1e12 if bound == "mfma" else 1e9)) if bound else None
         if bound == "mfma":
             gemm_ms += tot / args.steps
@@ -280,7 +314,7 @@ def main():
         log("[bench]   %-16s launches %4d  avg %9.4f ms  %s" % (
             name, n, avg, ("%.1f %s (%.1f%% of peak)" % (rate, unit, 100 * rate / peak)) if rate else ""))
     dom = max((x for x in rows if x[3]), key=lambda x: x[2] * x[1])
-    gemm_flops = 18 * S * H * I
+    gemm_flops = 18 * S * H * I + 18 * T * H * Is
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
     roofline = {
         "kernel": dom[0],
@@ -314,7 +348,8 @@ def main():
         "dtype": "bf16+fp8" if fp8 else ("bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
-                   "routing": spec.get("routing"), "seed": args.seed, "validate_ids": not args.no_validate,
+                   "routing": spec.get("routing"), "shared_I": Is, "seed": args.seed,
+                   "validate_ids": not args.no_validate,
                    "out_dtype": args.out_dtype},
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
         "gemm_frac_peak": round(gemm_ms_at_peak / gemm_ms, 5) if gemm_ms > 0 else None,

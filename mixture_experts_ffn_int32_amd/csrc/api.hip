@@ -307,7 +307,8 @@ DevState* dev_state() {
 // idles while the host waits).
 hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                      int32_t* row_of_slot, int32_t* tok_of_row, int32_t* tiles, int32_t* err, void* scratch,
-                     const RouteScratch& rs, bool validate_ids, hipStream_t stream) {
+                     const RouteScratch& rs, bool validate_ids, const hmm::SharedTables& shared,
+                     hipStream_t stream) {
   DevState* c = nullptr;
   if (validate_ids) {
     c = dev_state();
@@ -320,7 +321,7 @@ hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t
     e = hmm::launch_route(ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E, d.small), d.small ? 0 : 1,
                           counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err,
                           at<int32_t>(scratch, rs.blockhist), at<int32_t>(scratch, rs.blockbase),
-                          at<int32_t>(scratch, rs.blockerr), c ? c->word : nullptr, stream);
+                          at<int32_t>(scratch, rs.blockerr), c ? c->word : nullptr, shared, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   if (c) {
@@ -452,7 +453,7 @@ hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* cou
   int32_t* err = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4));
   int32_t* tok = at<int32_t>(workspace, rs.total + up(tile_ints(d) * 4) + up(4));
   const bool v = (p->flags & HMM_FLAG_VALIDATE_IDS) != 0;
-  s = run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tok, tiles, err, workspace, rs, v,
+  s = run_route(d, topk_ids, counts, offsets, sorted_slot, row_of_slot, tok, tiles, err, workspace, rs, v, {},
                 (hipStream_t)stream);
   if (s != HMM_OK || !v) return s;
   return finish_id_check(d);
@@ -557,23 +558,19 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
     if (e != hipSuccess) return hip_fail(e, "id-validation event");
     return finish_id_check(d);
   }
+  // the routing launch also writes the shared expert's tables (also for T = 0:
+  // the backward's weight gradients read them)
+  hmm::SharedTables sh{};
+  if (d.shared)
+    sh = hmm::SharedTables{d.T, (int)hmm::max_big_tiles(d.T, 1, d.small), d.small ? 0 : 1,
+                           at<int32_t>(saved, L.shared_offsets), at<int32_t>(saved, L.shared_idx),
+                           at<float>(saved, L.shared_ones), at<int32_t>(saved, L.shared_tiles)};
   s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
-                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, st);
+                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, sh, st);
   if (s != HMM_OK) return s;
   hipError_t e;
-  hmm::RowGroups gs{};
-  if (d.shared) {
-    // the shared expert's tables (also for T = 0: the backward's weight gradients read them)
-    int32_t* s_idx = at<int32_t>(saved, L.shared_idx);
-    {
-      Stage stage("shared_tables", st);
-      e = hmm::launch_shared_tables(d.T, (int)hmm::max_big_tiles(d.T, 1, d.small), d.small ? 0 : 1,
-                                    at<int32_t>(saved, L.shared_offsets), s_idx, at<float>(saved, L.shared_ones),
-                                    at<int32_t>(saved, L.shared_tiles), st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared-expert tables launch");
-    gs = shared_groups(d, at<int32_t>(saved, L.shared_tiles), at<int32_t>(saved, L.shared_offsets), s_idx);
-  }
+  const hmm::RowGroups gs =
+      d.shared ? shared_groups(d, sh.tiles, sh.offsets, sh.idx) : hmm::RowGroups{};
   if (!ne) return validate_ids ? finish_id_check(d) : HMM_OK;
 
   hmm::RowGroups g = row_groups(d, tiles, offsets, sorted_slot, tok_of_row);
@@ -620,8 +617,7 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
   uint16_t* hs = at<uint16_t>(saved, L.shared_h);
   uint16_t* as = at<uint16_t>(saved, L.shared_a);
   uint16_t* os = d.shared ? at<uint16_t>(workspace, W.os) : nullptr;
-  // narrow tiling: the routed and the shared products share their launches
-  const bool pair = d.shared && d.small;
+  const int nj = d.shared ? 2 : 1;  // jobs per product launch: routed experts, then the shared expert
   if (d.fp8) {
     uint8_t* xq = at<uint8_t>(workspace, W.xq);
     uint8_t* wq = at<uint8_t>(workspace, W.wq);
@@ -642,35 +638,28 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
       Stage stage("gmm1_fp8_swiglu", st);
       e = hmm::launch_gmm1_fp8(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
     }
-  } else if (pair) {
-    Stage stage("gmm1_swiglu+shared", st);
-    e = hmm::launch_gmm1_swiglu_with_shared(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h,
-                                            a, aw, gs, (const uint16_t*)up_s, ones, d.Is, hs, as, st);
-  } else {
-    Stage stage("gmm1_swiglu", st);
-    e = hmm::launch_gmm1_swiglu(g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
-  if (d.shared && (d.fp8 || !pair)) {
-    // the shared expert's up-projection is bf16 also when the routed one is FP8
-    Stage stage("shared_gmm1", st);
-    e = hmm::launch_gmm1_swiglu(gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+    if (d.shared) {
+      // the shared expert's up-projection stays bf16
+      const hmm::Gmm1Job js{gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr};
+      Stage stage("shared_gmm1", st);
+      e = hmm::launch_gmm1_swiglu(&js, 1, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "shared gmm1 launch");
-  }
-  if (pair) {
-    Stage stage("gmm2+shared", st);
-    e = hmm::launch_gmm2_with_shared(g, a, (const uint16_t*)down_w, d.H, d.I, o, gs, as, (const uint16_t*)down_s, d.Is,
-                                     os, st);
   } else {
-    Stage stage("gmm2", st);
-    e = hmm::launch_gmm2(g, a, (const uint16_t*)down_w, d.H, d.I, o, st);
+    const hmm::Gmm1Job jobs[2] = {{g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw},
+                                  {gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr}};
+    Stage stage(d.shared ? "gmm1_swiglu+shared" : "gmm1_swiglu", st);
+    e = hmm::launch_gmm1_swiglu(jobs, nj, st);
+    if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  }
+  {
+    const hmm::Gmm2Job jobs[2] = {{g, a, (const uint16_t*)down_w, d.H, d.I, o},
+                                  {gs, as, (const uint16_t*)down_s, d.H, d.Is, os}};
+    Stage stage(d.shared ? "gmm2+shared" : "gmm2", st);
+    e = hmm::launch_gmm2(jobs, nj, st);
   }
   if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
-  if (d.shared && !pair) {
-    Stage stage("shared_gmm2", st);
-    e = hmm::launch_gmm2(gs, as, (const uint16_t*)down_s, d.H, d.Is, os, st);
-    if (e != hipSuccess) return hip_fail(e, "shared gmm2 launch");
-  }
   {
     Stage stage("combine", st);
     e = hmm::launch_combine(o, at<int32_t>(saved, L.row_of_slot), topk_weights, d.T, (int)d.K, d.H, os, (uint16_t*)y,
@@ -789,35 +778,34 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
     return e == hipSuccess ? HMM_OK : hip_fail(e, "shared W1Grad launch");
   }
   uint16_t* dxs = d.shared ? at<uint16_t>(workspace, W.dxs) : nullptr;
+  // jobs per product launch: the routed experts, then the shared expert
+  const int nj = d.shared ? 2 : 1;
+  const hmm::ActGradJob ag[2] = {
+      {g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh, dwpart, W.dw_cols},
+      {gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones, at<uint16_t>(saved, L.shared_h), as, d.H, d.Is, dhs,
+       nullptr, 0}};
+  const hmm::InputGradJob ig[2] = {{g, dh, (const uint16_t*)up_w, d.H, d.I, dxp},
+                                   {gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs}};
+  const hmm::DwJob dw2[2] = {
+      hmm::dw2_job(offsets, tok_of_row, d.T, d.S, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w),
+      hmm::dw2_job(s_offsets, s_idx, d.T, d.T, 1, as, (const uint16_t*)dy, d.H, d.Is, (uint16_t*)d_down_s)};
+  const hmm::DwJob dw1[2] = {
+      hmm::dw1_job(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w),
+      hmm::dw1_job(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (uint16_t*)d_up_s)};
   if (ne && d.small) {
     // small problems: each product fills only part of the chip, so the independent
     // ones share a launch (RFC 2.2: W2Grad alongside act_grad, W1Grad alongside the
-    // rest of the dX chain)
+    // rest of the dX chain), the shared expert's with them
     {
-      Stage stage("act_grad+dw2", st);
-      e = hmm::launch_act_grad_dw2_narrow(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, aw,
-                                          d.E, d.H, d.I, dh, dwpart, W.dw_cols, (uint16_t*)d_down_w, st);
+      Stage stage(d.shared ? "act_grad+dw2+shared" : "act_grad+dw2", st);
+      e = hmm::launch_act_grad_dw2_narrow(ag, dw2, nj, st);
     }
     if (e != hipSuccess) return hip_fail(e, "act_grad + W2Grad launch");
-    if (d.shared) {
-      Stage stage("shared_act_grad+dw2", st);
-      e = hmm::launch_act_grad_dw2_narrow(gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones,
-                                          at<uint16_t>(saved, L.shared_h), as, as, 1, d.H, d.Is, dhs, nullptr, 0,
-                                          (uint16_t*)d_down_s, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared act_grad + W2Grad launch");
     {
-      Stage stage("input_grad+dw1", st);
-      e = hmm::launch_input_grad_dw1_narrow(g, dh, (const uint16_t*)up_w, (const uint16_t*)x, d.E, d.H, d.I, dxp,
-                                            (uint16_t*)d_up_w, st);
+      Stage stage(d.shared ? "input_grad+dw1+shared" : "input_grad+dw1", st);
+      e = hmm::launch_input_grad_dw1_narrow(ig, dw1, nj, st);
     }
     if (e != hipSuccess) return hip_fail(e, "input_grad + W1Grad launch");
-    if (d.shared) {
-      Stage stage("shared_input_grad+dw1", st);
-      e = hmm::launch_input_grad_dw1_narrow(gs, dhs, (const uint16_t*)up_s, (const uint16_t*)x, 1, d.H, d.Is, dxs,
-                                            (uint16_t*)d_up_s, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared input_grad + W1Grad launch");
     {
       Stage stage("combine_dx", st);
       e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
@@ -827,27 +815,15 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
   }
   if (ne) {
     {
-      Stage stage("act_grad", st);
-      e = hmm::launch_act_grad(g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh,
-                               dwpart, W.dw_cols, st);
+      Stage stage(d.shared ? "act_grad+shared" : "act_grad", st);
+      e = hmm::launch_act_grad(ag, nj, st);
     }
     if (e != hipSuccess) return hip_fail(e, "act_grad launch");
-    if (d.shared) {
-      Stage stage("shared_act_grad", st);
-      e = hmm::launch_act_grad(gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones, at<uint16_t>(saved, L.shared_h),
-                               as, d.H, d.Is, dhs, nullptr, 0, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared act_grad launch");
     {
-      Stage stage("input_grad", st);
-      e = hmm::launch_input_grad(g, dh, (const uint16_t*)up_w, d.H, d.I, dxp, st);
+      Stage stage(d.shared ? "input_grad+shared" : "input_grad", st);
+      e = hmm::launch_input_grad(ig, nj, st);
     }
     if (e != hipSuccess) return hip_fail(e, "input_grad launch");
-    if (d.shared) {
-      Stage stage("shared_input_grad", st);
-      e = hmm::launch_input_grad(gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared input_grad launch");
     {
       Stage stage("combine_dx", st);
       e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
@@ -856,29 +832,15 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
     if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
   }
   {
-    Stage stage("dw2", st);
-    e = hmm::launch_dw2(offsets, tok_of_row, d.T, d.S, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w,
-                        d.small, st);
+    Stage stage(d.shared ? "dw2+shared" : "dw2", st);
+    e = hmm::launch_dw2(dw2, nj, d.small, st);
   }
   if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
-  if (d.shared) {
-    Stage stage("shared_dw2", st);
-    e = hmm::launch_dw2(s_offsets, s_idx, d.T, d.T, 1, as, (const uint16_t*)dy, d.H, d.Is, (uint16_t*)d_down_s,
-                        d.small, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "shared W2Grad launch");
   {
-    Stage stage("dw1", st);
-    e = hmm::launch_dw1(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w,
-                        d.small, st);
+    Stage stage(d.shared ? "dw1+shared" : "dw1", st);
+    e = hmm::launch_dw1(dw1, nj, d.small, st);
   }
-  if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
-  if (d.shared) {
-    Stage stage("shared_dw1", st);
-    e = hmm::launch_dw1(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (uint16_t*)d_up_s, d.small,
-                        st);
-  }
-  return e == hipSuccess ? HMM_OK : hip_fail(e, "shared W1Grad launch");
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "W1Grad launch");
 }
 
 }  // namespace

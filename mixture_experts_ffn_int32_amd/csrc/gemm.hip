@@ -49,125 +49,119 @@ int act_grad_dw_cols(int64_t I, bool narrow) {
   return (int)((I + bn - 1) / bn);
 }
 
-hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
-                              int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  // BN/2 gate columns (and their up columns) per N tile
-  return launch_rows<Gmm1>(g, [&](int bn) { return (int)((I + bn / 2 - 1) / (bn / 2)); }, [&](auto& A, int nnt) {
-    A.g = g; A.x = x; A.w1 = w1; A.tw = topk_w; A.T = g.T; A.H = H; A.I = I; A.h = h; A.a = a; A.aw = aw;
-    A.n_ntiles = nnt;
-  }, stream);
-}
-
-hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
-                       uint16_t* o, hipStream_t stream) {
-  return launch_rows<Gmm2>(g, [&](int bn) { return (int)((H + bn - 1) / bn); }, [&](auto& A, int nnt) {
-    A.g = g; A.a = a; A.w2 = w2; A.S = g.S; A.H = H; A.I = I; A.o = o; A.n_ntiles = nnt;
-  }, stream);
-}
-
-// Narrow tiling: a routed product and the shared expert's share one launch.
-hipError_t launch_gmm1_swiglu_with_shared(const RowGroups& g, const uint16_t* x, const uint16_t* w1,
-                                          const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
-                                          uint16_t* aw, const RowGroups& gs, const uint16_t* w1s, const float* ones,
-                                          int64_t Is, uint16_t* hs, uint16_t* as, hipStream_t stream) {
-  typedef Gmm1<Narrow, true> P;
-  constexpr int HALF = Narrow::BN / 2;
-  typename P::Args a1, a2;
-  a1.g = g; a1.x = x; a1.w1 = w1; a1.tw = topk_w; a1.T = g.T; a1.H = H; a1.I = I; a1.h = h; a1.a = a; a1.aw = aw;
-  a1.n_ntiles = (int)((I + HALF - 1) / HALF);
-  a2.g = gs; a2.x = x; a2.w1 = w1s; a2.tw = ones; a2.T = gs.T; a2.H = H; a2.I = Is; a2.h = hs; a2.a = as;
-  a2.aw = nullptr; a2.n_ntiles = (int)((Is + HALF - 1) / HALF);
-  return launch_pair<P, P>(a1, g.max_small * a1.n_ntiles, a2, gs.max_small * a2.n_ntiles, stream);
-}
-
-hipError_t launch_gmm2_with_shared(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
-                                   uint16_t* o, const RowGroups& gs, const uint16_t* as, const uint16_t* w2s,
-                                   int64_t Is, uint16_t* os, hipStream_t stream) {
-  typedef Gmm2<Narrow, true> P;
-  typename P::Args a1, a2;
-  const int nnt = (int)((H + Narrow::BN - 1) / Narrow::BN);
-  a1.g = g; a1.a = a; a1.w2 = w2; a1.S = g.S; a1.H = H; a1.I = I; a1.o = o; a1.n_ntiles = nnt;
-  a2.g = gs; a2.a = as; a2.w2 = w2s; a2.S = gs.S; a2.H = H; a2.I = Is; a2.o = os; a2.n_ntiles = nnt;
-  return launch_pair<P, P>(a1, g.max_small * nnt, a2, gs.max_small * nnt, stream);
-}
-
-hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
-                           const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
-                           float* dwpart, int dw_cols, hipStream_t stream) {
-  return launch_rows<ActGrad>(g, [&](int bn) { return (int)((I + bn - 1) / bn); }, [&](auto& A, int nnt) {
-    A.g = g; A.dy = dy; A.w2 = w2; A.tw = topk_w; A.h = h; A.a = a; A.T = g.T; A.H = H; A.I = I; A.dh = dh;
-    A.dwpart = dwpart; A.dw_cols = dw_cols; A.n_ntiles = nnt;
-  }, stream);
-}
-
-hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
-                             uint16_t* dxp, hipStream_t stream) {
-  return launch_rows<InputGrad>(g, [&](int bn) { return (int)((H + bn - 1) / bn); }, [&](auto& A, int nnt) {
-    A.g = g; A.dh = dh; A.w1 = w1; A.S = g.S; A.H = H; A.I = I; A.dxp = dxp; A.n_ntiles = nnt;
-  }, stream);
-}
-
-template <class C, bool GA, bool GB>
-hipError_t launch_dw(const int32_t* offsets, const int32_t* tok_of_row, int64_t E, const uint16_t* A_,
-                     const uint16_t* B_, int64_t a_rows, int64_t b_rows, int64_t M, int64_t N, uint16_t* out,
-                     hipStream_t stream) {
-  typedef Dw<C, GA, GB> P;
-  typename P::Args A{offsets, tok_of_row, E, A_, B_, a_rows, b_rows, M, N, out,
-                     (int)((M + C::BM - 1) / C::BM), (int)((N + C::BN - 1) / C::BN)};
-  return launch<P>(A, E * 8 * ((A.mt * A.nt + 7) / 8), stream);
-}
-
-hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, bool narrow,
-                      hipStream_t stream) {
-  if (narrow) return launch_dw<Narrow, true, false>(offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, stream);
-  return launch_dw<Big, true, false>(offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1, stream);
-}
-
-hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, bool narrow,
-                      hipStream_t stream) {
-  if (narrow) return launch_dw<Narrow, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
-  return launch_dw<Big, false, true>(offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2, stream);
-}
-
 namespace {
+// per-job policy arguments
+template <class A>
+void fill_gmm1(A& a, const Gmm1Job& j, int nnt) {
+  a.g = j.g; a.x = j.x; a.w1 = j.w1; a.tw = j.tw; a.T = j.g.T; a.H = j.H; a.I = j.I; a.h = j.h; a.a = j.a;
+  a.aw = j.aw; a.n_ntiles = nnt;
+}
+template <class A>
+void fill_gmm2(A& a, const Gmm2Job& j, int nnt) {
+  a.g = j.g; a.a = j.a; a.w2 = j.w2; a.S = j.g.S; a.H = j.H; a.I = j.I; a.o = j.o; a.n_ntiles = nnt;
+}
+template <class A>
+void fill_act_grad(A& a, const ActGradJob& j, int nnt) {
+  a.g = j.g; a.dy = j.dy; a.w2 = j.w2; a.tw = j.tw; a.h = j.h; a.a = j.a; a.T = j.g.T; a.H = j.H; a.I = j.I;
+  a.dh = j.dh; a.dwpart = j.dwpart; a.dw_cols = j.dw_cols; a.n_ntiles = nnt;
+}
+template <class A>
+void fill_input_grad(A& a, const InputGradJob& j, int nnt) {
+  a.g = j.g; a.dh = j.dh; a.w1 = j.w1; a.S = j.g.S; a.H = j.H; a.I = j.I; a.dxp = j.dxp; a.n_ntiles = nnt;
+}
 template <class C, bool GA, bool GB>
-typename Dw<C, GA, GB>::Args dw_args(const int32_t* offsets, const int32_t* tok_of_row, int64_t E, const uint16_t* A_,
-                                     const uint16_t* B_, int64_t a_rows, int64_t b_rows, int64_t M, int64_t N,
-                                     uint16_t* out) {
-  return typename Dw<C, GA, GB>::Args{offsets, tok_of_row, E, A_, B_, a_rows, b_rows, M, N, out,
-                                      (int)((M + C::BM - 1) / C::BM), (int)((N + C::BN - 1) / C::BN)};
+typename Dw<C, GA, GB>::Args dw_args(const DwJob& j) {
+  return typename Dw<C, GA, GB>::Args{j.offsets, j.tok_of_row, j.E, j.A, j.B, j.a_rows, j.b_rows, j.M, j.N, j.out,
+                                      (int)((j.M + C::BM - 1) / C::BM), (int)((j.N + C::BN - 1) / C::BN)};
 }
 template <class A>
 int64_t dw_blocks(const A& a) { return a.E * 8 * ((a.mt * a.nt + 7) / 8); }
+
+int ntiles_half(int64_t n, int bn) { return (int)((n + bn / 2 - 1) / (bn / 2)); }  // BN/2 gate (+ up) columns
+int ntiles_full(int64_t n, int bn) { return (int)((n + bn - 1) / bn); }
+
+// Narrow tiles: the jobs share one launch.  Big tiles: one launch each (the
+// paired big-tile kernel runs out of registers, and a big-tile launch of a
+// weight gradient already holds many tiles).
+template <class C, bool GA, bool GB>
+hipError_t launch_dw_jobs(const DwJob* j, int n, hipStream_t stream) {
+  typedef Dw<C, GA, GB> P;
+  const typename P::Args a0 = dw_args<C, GA, GB>(j[0]);
+  if (n == 1) return launch<P>(a0, dw_blocks(a0), stream);
+  const typename P::Args a1 = dw_args<C, GA, GB>(j[1]);
+  if constexpr (C::BM == Big::BM) {
+    const hipError_t e = launch<P>(a0, dw_blocks(a0), stream);
+    return e != hipSuccess ? e : launch<P>(a1, dw_blocks(a1), stream);
+  } else {
+    return launch_pair<P, P>(a0, dw_blocks(a0), a1, dw_blocks(a1), stream);
+  }
+}
 }  // namespace
 
-hipError_t launch_act_grad_dw2_narrow(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
-                                      const uint16_t* h, const uint16_t* a, const uint16_t* aw, int64_t E, int64_t H,
-                                      int64_t I, uint16_t* dh, float* dwpart, int dw_cols, uint16_t* dw2,
-                                      hipStream_t stream) {
-  typedef ActGrad<Narrow, true> P1;
-  typedef Dw<Narrow, false, true> P2;
-  const int nnt = (int)((I + Narrow::BN - 1) / Narrow::BN);
-  typename P1::Args a1;
-  a1.g = g; a1.dy = dy; a1.w2 = w2; a1.tw = topk_w; a1.h = h; a1.a = a; a1.T = g.T; a1.H = H; a1.I = I; a1.dh = dh;
-  a1.dwpart = dwpart; a1.dw_cols = dw_cols; a1.n_ntiles = nnt;
-  const typename P2::Args a2 = dw_args<Narrow, false, true>(g.offsets, g.tok_of_row, E, aw, dy, g.S, g.T, I, H, dw2);
-  return launch_pair<P1, P2>(a1, g.max_small * nnt, a2, dw_blocks(a2), stream);
+hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream) {
+  return launch_rows_jobs<Gmm1, Narrow>(jobs, n, [](const Gmm1Job& j, int bn) { return ntiles_half(j.I, bn); },
+                                        [](auto& a, const Gmm1Job& j, int nnt) { fill_gmm1(a, j, nnt); }, stream);
 }
 
-hipError_t launch_input_grad_dw1_narrow(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, const uint16_t* x,
-                                        int64_t E, int64_t H, int64_t I, uint16_t* dxp, uint16_t* dw1,
-                                        hipStream_t stream) {
+hipError_t launch_gmm2(const Gmm2Job* jobs, int n, hipStream_t stream) {
+  return launch_rows_jobs<Gmm2, Narrow>(jobs, n, [](const Gmm2Job& j, int bn) { return ntiles_full(j.H, bn); },
+                                        [](auto& a, const Gmm2Job& j, int nnt) { fill_gmm2(a, j, nnt); }, stream);
+}
+
+hipError_t launch_act_grad(const ActGradJob* jobs, int n, hipStream_t stream) {
+  return launch_rows_jobs<ActGrad, Narrow>(jobs, n, [](const ActGradJob& j, int bn) { return ntiles_full(j.I, bn); },
+                                           [](auto& a, const ActGradJob& j, int nnt) { fill_act_grad(a, j, nnt); },
+                                           stream);
+}
+
+hipError_t launch_input_grad(const InputGradJob* jobs, int n, hipStream_t stream) {
+  return launch_rows_jobs<InputGrad, Narrow>(
+      jobs, n, [](const InputGradJob& j, int bn) { return ntiles_full(j.H, bn); },
+      [](auto& a, const InputGradJob& j, int nnt) { fill_input_grad(a, j, nnt); }, stream);
+}
+
+hipError_t launch_dw1(const DwJob* jobs, int n, bool narrow, hipStream_t stream) {
+  return narrow ? launch_dw_jobs<Narrow, true, false>(jobs, n, stream)
+                : launch_dw_jobs<Big, true, false>(jobs, n, stream);
+}
+
+hipError_t launch_dw2(const DwJob* jobs, int n, bool narrow, hipStream_t stream) {
+  return narrow ? launch_dw_jobs<Narrow, false, true>(jobs, n, stream)
+                : launch_dw_jobs<Big, false, true>(jobs, n, stream);
+}
+
+hipError_t launch_act_grad_dw2_narrow(const ActGradJob* ag, const DwJob* dw2, int n, hipStream_t stream) {
+  typedef ActGrad<Narrow, true> P1;
+  typedef Dw<Narrow, false, true> P2;
+  typename P1::Args a[2];
+  typename P2::Args d[2];
+  int64_t ba[2] = {0, 0}, bd[2] = {0, 0};
+  for (int q = 0; q < n; ++q) {
+    const int nnt = ntiles_full(ag[q].I, Narrow::BN);
+    fill_act_grad(a[q], ag[q], nnt);
+    ba[q] = ag[q].g.max_small * nnt;
+    d[q] = dw_args<Narrow, false, true>(dw2[q]);
+    bd[q] = dw_blocks(d[q]);
+  }
+  if (n == 1) return launch_pair<P1, P2>(a[0], ba[0], d[0], bd[0], stream);
+  return launch_quad<P1, P2, P1, P2>(a[0], ba[0], d[0], bd[0], a[1], ba[1], d[1], bd[1], stream);
+}
+
+hipError_t launch_input_grad_dw1_narrow(const InputGradJob* ig, const DwJob* dw1, int n, hipStream_t stream) {
   typedef InputGrad<Narrow, true> P1;
   typedef Dw<Narrow, true, false> P2;
-  const int nnt = (int)((H + Narrow::BN - 1) / Narrow::BN);
-  typename P1::Args a1;
-  a1.g = g; a1.dh = dh; a1.w1 = w1; a1.S = g.S; a1.H = H; a1.I = I; a1.dxp = dxp; a1.n_ntiles = nnt;
-  const typename P2::Args a2 =
-      dw_args<Narrow, true, false>(g.offsets, g.tok_of_row, E, x, dh, g.T, g.S, H, 2 * I, dw1);
-  return launch_pair<P1, P2>(a1, g.max_small * nnt, a2, dw_blocks(a2), stream);
+  typename P1::Args a[2];
+  typename P2::Args d[2];
+  int64_t ba[2] = {0, 0}, bd[2] = {0, 0};
+  for (int q = 0; q < n; ++q) {
+    const int nnt = ntiles_full(ig[q].H, Narrow::BN);
+    fill_input_grad(a[q], ig[q], nnt);
+    ba[q] = ig[q].g.max_small * nnt;
+    d[q] = dw_args<Narrow, true, false>(dw1[q]);
+    bd[q] = dw_blocks(d[q]);
+  }
+  if (n == 1) return launch_pair<P1, P2>(a[0], ba[0], d[0], bd[0], stream);
+  return launch_quad<P1, P2, P1, P2>(a[0], ba[0], d[0], bd[0], a[1], ba[1], d[1], bd[1], stream);
 }
 
 }  // namespace hmm

@@ -199,6 +199,30 @@ __global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_pair_kernel(const typenam
     gemm_body<P2>(a2, blockIdx.x - n1, gridDim.x - n1, smem);
 }
 
+// Four independent products in one launch (small problems with a shared
+// expert): workgroups [s1, s2) run P2, [s2, s3) P3, [s3, end) P4, the first s1
+// P1; every start is a multiple of 8.
+template <class P1, class P2, class P3, class P4>
+__global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_quad_kernel(const typename P1::Args a1, int s1,
+                                                                   const typename P2::Args a2, int s2,
+                                                                   const typename P3::Args a3, int s3,
+                                                                   const typename P4::Args a4) {
+  static_assert(P1::C::NTHR == P2::C::NTHR && P1::C::NTHR == P3::C::NTHR && P1::C::NTHR == P4::C::NTHR,
+                "one workgroup size");
+  constexpr int S1 = 2 * P1::C::STAGE, S2 = 2 * P2::C::STAGE, S3 = 2 * P3::C::STAGE, S4 = 2 * P4::C::STAGE;
+  constexpr int S12 = S1 > S2 ? S1 : S2, S34 = S3 > S4 ? S3 : S4;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[S12 > S34 ? S12 : S34];
+  const int b = blockIdx.x;
+  if (b < s1)
+    gemm_body<P1>(a1, b, s1, smem);
+  else if (b < s2)
+    gemm_body<P2>(a2, b - s1, s2 - s1, smem);
+  else if (b < s3)
+    gemm_body<P3>(a3, b - s2, s3 - s2, smem);
+  else
+    gemm_body<P4>(a4, b - s3, gridDim.x - s3, smem);
+}
+
 // Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
 // [BM][BN] tile and written out as 16-byte row chunks (rows < valid_rows,
 // columns < ncols), so every global store is a full, coalesced vector.
@@ -298,6 +322,10 @@ struct RowTile {
 };
 
 inline int64_t round8(int64_t n) { return (n + 7) / 8 * 8; }
+template <class T>
+struct TypeTag {
+  typedef T type;
+};
 
 template <class P>
 hipError_t launch(const typename P::Args& args, int64_t logical_blocks, hipStream_t stream) {
@@ -319,6 +347,41 @@ hipError_t launch_pair(const typename P1::Args& a1, int64_t blocks1, const typen
   return hipGetLastError();
 }
 
+template <class P1, class P2, class P3, class P4>
+hipError_t launch_quad(const typename P1::Args& a1, int64_t b1, const typename P2::Args& a2, int64_t b2,
+                       const typename P3::Args& a3, int64_t b3, const typename P4::Args& a4, int64_t b4,
+                       hipStream_t stream) {
+  const int64_t s1 = round8(b1), s2 = s1 + round8(b2), s3 = s2 + round8(b3), g = s3 + round8(b4);
+  if (g <= 0) return hipSuccess;
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_quad_kernel<P1, P2, P3, P4>), dim3((unsigned)g), dim3(P1::C::NTHR), 0, stream, a1, (int)s1,
+                     a2, (int)s2, a3, (int)s3, a4);
+  return hipGetLastError();
+}
+
+// A row-grouped product over n <= 2 jobs (the routed experts and the shared
+// expert), which share every launch: big tiles, then small tiles; in narrow mode
+// one launch of 64x64 tiles.  ntiles(job, BN) gives a job's N-tile count and
+// fill(args, job, nnt) its policy arguments.
+template <template <class, bool> class P, class NarrowC, class Job, class NTiles, class Fill>
+hipError_t launch_rows_jobs(const Job* j, int n, NTiles ntiles, Fill fill, hipStream_t stream) {
+  auto run = [&](auto tag, bool big) -> hipError_t {
+    typedef typename decltype(tag)::type PP;
+    typename PP::Args a[2];
+    int64_t blocks[2] = {0, 0};
+    for (int q = 0; q < n; ++q) {
+      const int nnt = ntiles(j[q], PP::C::BN);
+      fill(a[q], j[q], nnt);
+      blocks[q] = (big ? j[q].g.max_big : j[q].g.max_small) * nnt;
+    }
+    return n == 1 ? launch<PP>(a[0], blocks[0], stream) : launch_pair<PP, PP>(a[0], blocks[0], a[1], blocks[1], stream);
+  };
+  if (j[0].g.narrow) return run(TypeTag<P<NarrowC, true>>{}, false);
+  const hipError_t e = run(TypeTag<P<Big, false>>{}, true);
+  if (e != hipSuccess) return e;
+  return run(TypeTag<P<Small, true>>{}, false);
+}
+
 // big-tile launch, then small-tile launch, of a row-grouped product (n_ntiles
 // is a function of the tile width); in narrow mode one launch of 64x64 tiles
 template <template <class, bool> class P, class NarrowC, class ArgsFill, class NTiles>
@@ -338,10 +401,6 @@ hipError_t launch_rows_c(const RowGroups& g, NTiles n_ntiles, ArgsFill fill, hip
   typename PS::Args as;
   fill(as, n_ntiles(Small::BN));
   return launch<PS>(as, g.max_small * n_ntiles(Small::BN), stream);
-}
-template <template <class, bool> class P, class ArgsFill, class NTiles>
-hipError_t launch_rows(const RowGroups& g, NTiles n_ntiles, ArgsFill fill, hipStream_t stream) {
-  return launch_rows_c<P, Narrow>(g, n_ntiles, fill, stream);
 }
 
 }  // namespace

@@ -44,17 +44,24 @@ inline int64_t tile_table_ints(int64_t S, int64_t E, bool small) {
   return 4 + 2 * (max_big_tiles(S, E, small) + max_small_tiles(S, E, small));
 }
 
+// The shared expert's routing tables: one expert holding all T tokens in token
+// order: offsets[2] = {0, T}, idx[T] = 0..T-1 (its sorted_slot and tok_of_row),
+// ones[T] = 1.0 (its weights) and tiles (tile_table_ints(T, 1, !big_on)).  The
+// routing launch writes them too when idx is not NULL.
+struct SharedTables {
+  int64_t T;
+  int max_big, big_on;
+  int32_t* offsets;
+  int32_t* idx;
+  float* ones;
+  int32_t* tiles;
+};
+
 // routing (route.hip)
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
-                        int32_t* host_err, hipStream_t stream);
-
-// The shared expert's routing tables (route.hip): one expert holding all T
-// tokens in token order: offsets[2] = {0, T}, idx[T] = 0..T-1 (its sorted_slot
-// and tok_of_row), ones[T] = 1.0 (its weights), tiles (tile_table_ints(T, 1, !big_on)).
-hipError_t launch_shared_tables(int64_t T, int max_big, int big_on, int32_t* offsets, int32_t* idx, float* ones,
-                                int32_t* tiles, hipStream_t stream);
+                        int32_t* host_err, const SharedTables& shared, hipStream_t stream);
 
 // grouped products (gemm.hip).  All matrices bf16 (uint16_t storage).
 struct RowGroups {
@@ -69,45 +76,78 @@ struct RowGroups {
                                // kernel): read them at the device-wide coherence point
 };
 
-// h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU;
-// aw may be NULL)
-hipError_t launch_gmm1_swiglu(const RowGroups& g, const uint16_t* x, const uint16_t* w1, const float* topk_w,
-                              int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw, hipStream_t stream);
+// Every bf16 product launcher takes n = 1 or 2 jobs: the routed experts and,
+// second, the shared expert (its own groups, width and weights); the jobs share
+// each launch (co-scheduled), and take the tiling mode of the first job.
+//
+// h = x[tok] . W1[e] (gate|up), a = silu(g) u, aw = w a       (forward up-projection + SwiGLU)
+struct Gmm1Job {
+  RowGroups g;
+  const uint16_t* x;
+  const uint16_t* w1;
+  const float* tw;
+  int64_t H, I;
+  uint16_t *h, *a, *aw;  // aw may be NULL (not stored)
+};
+hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream);
 // o = a . W2[e]                                                (forward down-projection)
-hipError_t launch_gmm2(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
-                       uint16_t* o, hipStream_t stream);
-// Narrow tiling: the routed product and the shared expert's (groups gs, width Is,
-// weight 1, no aw) in one launch each.
-hipError_t launch_gmm1_swiglu_with_shared(const RowGroups& g, const uint16_t* x, const uint16_t* w1,
-                                          const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
-                                          uint16_t* aw, const RowGroups& gs, const uint16_t* w1s, const float* ones,
-                                          int64_t Is, uint16_t* hs, uint16_t* as, hipStream_t stream);
-hipError_t launch_gmm2_with_shared(const RowGroups& g, const uint16_t* a, const uint16_t* w2, int64_t H, int64_t I,
-                                   uint16_t* o, const RowGroups& gs, const uint16_t* as, const uint16_t* w2s,
-                                   int64_t Is, uint16_t* os, hipStream_t stream);
-// G = dY[tok] . W2[e]^T; dH = SwiGLUGrad(w G); dwpart = partial sums of G a (dwpart may be NULL)
-hipError_t launch_act_grad(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
-                           const uint16_t* h, const uint16_t* a, int64_t H, int64_t I, uint16_t* dh,
-                           float* dwpart, int dw_cols, hipStream_t stream);
+struct Gmm2Job {
+  RowGroups g;
+  const uint16_t* a;
+  const uint16_t* w2;
+  int64_t H, I;
+  uint16_t* o;
+};
+hipError_t launch_gmm2(const Gmm2Job* jobs, int n, hipStream_t stream);
+// G = dY[tok] . W2[e]^T; dH = SwiGLUGrad(w G); dwpart = partial sums of G a
+struct ActGradJob {
+  RowGroups g;
+  const uint16_t* dy;
+  const uint16_t* w2;
+  const float* tw;
+  const uint16_t *h, *a;
+  int64_t H, I;
+  uint16_t* dh;
+  float* dwpart;  // may be NULL (not stored)
+  int dw_cols;
+};
+hipError_t launch_act_grad(const ActGradJob* jobs, int n, hipStream_t stream);
 // dXp = dH . W1[e]^T
-hipError_t launch_input_grad(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, int64_t H, int64_t I,
-                             uint16_t* dxp, hipStream_t stream);
-// dW1[e] = sum_p x[tok(p)]^T dH[p];  dW2[e] = sum_p aw[p]^T dY[tok(p)]
-hipError_t launch_dw1(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1, bool narrow,
-                      hipStream_t stream);
-hipError_t launch_dw2(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
-                      const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2, bool narrow,
-                      hipStream_t stream);
-// Small problems (narrow tiles): two independent products in one launch each,
-// act_grad with W2Grad, then input_grad with W1Grad (the same products as above).
-hipError_t launch_act_grad_dw2_narrow(const RowGroups& g, const uint16_t* dy, const uint16_t* w2, const float* topk_w,
-                                      const uint16_t* h, const uint16_t* a, const uint16_t* aw, int64_t E, int64_t H,
-                                      int64_t I, uint16_t* dh, float* dwpart, int dw_cols, uint16_t* dw2,
-                                      hipStream_t stream);
-hipError_t launch_input_grad_dw1_narrow(const RowGroups& g, const uint16_t* dh, const uint16_t* w1, const uint16_t* x,
-                                        int64_t E, int64_t H, int64_t I, uint16_t* dxp, uint16_t* dw1,
-                                        hipStream_t stream);
+struct InputGradJob {
+  RowGroups g;
+  const uint16_t* dh;
+  const uint16_t* w1;
+  int64_t H, I;
+  uint16_t* dxp;
+};
+hipError_t launch_input_grad(const InputGradJob* jobs, int n, hipStream_t stream);
+// Weight gradients C[e] = sum over the expert's rows p of A[p]^T B[p]:
+//   dW1[e] = sum_p x[tok(p)]^T dH[p]   (dw1_job; A gathered through tok_of_row)
+//   dW2[e] = sum_p aw[p]^T dY[tok(p)]  (dw2_job; B gathered)
+struct DwJob {
+  const int32_t* offsets;     // [E+1]
+  const int32_t* tok_of_row;  // [S]
+  int64_t E;
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t a_rows, b_rows, M, N;
+  uint16_t* out;              // [E][M][N]
+};
+inline DwJob dw1_job(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                     const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1) {
+  return DwJob{offsets, tok_of_row, E, x, dh, T, S, H, 2 * I, dw1};
+}
+inline DwJob dw2_job(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
+                     const uint16_t* aw, const uint16_t* dy, int64_t H, int64_t I, uint16_t* dw2) {
+  return DwJob{offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2};
+}
+hipError_t launch_dw1(const DwJob* jobs, int n, bool narrow, hipStream_t stream);
+hipError_t launch_dw2(const DwJob* jobs, int n, bool narrow, hipStream_t stream);
+// Small problems (narrow tiles): the independent products share a launch,
+// act_grad with W2Grad, then input_grad with W1Grad (the same products as above;
+// with a shared expert, its two products join each launch).
+hipError_t launch_act_grad_dw2_narrow(const ActGradJob* ag, const DwJob* dw2, int n, hipStream_t stream);
+hipError_t launch_input_grad_dw1_narrow(const InputGradJob* ig, const DwJob* dw1, int n, hipStream_t stream);
 // number of d_topk_weights partial columns written by launch_act_grad for a given I
 int act_grad_dw_cols(int64_t I, bool narrow);
 

@@ -18,9 +18,47 @@
 
 namespace hmm {
 
+// The shared expert's tables (RFC section 6.1: the shared expert runs through
+// the same grouped products as one more group), written by the routing launch
+// alongside the routed tables: one expert that holds every token, in token
+// order, with the tile table of one expert with T rows under route_scan's rule.
+__device__ __forceinline__ void shared_counts(const SharedTables& st, int64_t& nbig, int64_t& nsmall) {
+  const int64_t rem = st.big_on ? st.T % TILE_BIG : st.T;
+  const bool big_tail = st.big_on && rem > TILE_BIG / 2;
+  nbig = st.big_on ? st.T / TILE_BIG + (big_tail ? 1 : 0) : 0;
+  nsmall = big_tail ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
+}
+// entry i of the row arrays and tile lists (i < T; #big and #small are at most T)
+__device__ __forceinline__ void shared_entry(const SharedTables& st, int64_t i) {
+  int64_t nbig, nsmall;
+  shared_counts(st, nbig, nsmall);
+  if (i >= st.T) return;
+  st.idx[i] = (int32_t)i;
+  st.ones[i] = 1.f;
+  if (i < nbig) {
+    st.tiles[4 + 2 * i] = 0;
+    st.tiles[4 + 2 * i + 1] = (int32_t)(i * TILE_BIG);
+  }
+  if (i < nsmall) {
+    int32_t* small = st.tiles + 4 + 2 * (int64_t)st.max_big;
+    small[2 * i] = 0;
+    small[2 * i + 1] = (int32_t)(nbig * TILE_BIG + i * TILE_SMALL);
+  }
+}
+__device__ __forceinline__ void shared_header(const SharedTables& st) {
+  int64_t nbig, nsmall;
+  shared_counts(st, nbig, nsmall);
+  st.offsets[0] = 0;
+  st.offsets[1] = (int32_t)st.T;
+  st.tiles[0] = (int32_t)nbig;
+  st.tiles[1] = (int32_t)nsmall;
+  st.tiles[2] = TILE_BIG;
+  st.tiles[3] = TILE_SMALL;
+}
+
 __global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restrict__ ids, int64_t S, int E,
                                                          int32_t* __restrict__ blockhist,
-                                                         int32_t* __restrict__ blockerr) {
+                                                         int32_t* __restrict__ blockerr, const SharedTables st) {
   __shared__ int32_t hist[MAX_EXPERTS];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += RT_THREADS) hist[e] = 0;
@@ -41,6 +79,9 @@ __global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restri
   bad = __syncthreads_or(bad);
   for (int e = tid; e < E; e += RT_THREADS) blockhist[(int64_t)blockIdx.x * E + e] = hist[e];
   if (tid == 0) blockerr[blockIdx.x] = bad;
+  // the shared expert's entries of this block's range (T <= S: the blocks cover them)
+  if (st.idx)
+    for (int r = 0; r < RT_SLOTS / RT_THREADS; ++r) shared_entry(st, base + r * RT_THREADS + tid);
 }
 
 // One block of RT_SCAN_THREADS threads (>= E).  Besides counts and offsets it
@@ -58,11 +99,13 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
                                                               int32_t* __restrict__ blockbase,
                                                               int32_t* __restrict__ tiles,
                                                               int32_t* __restrict__ err,
-                                                              int32_t* __restrict__ host_err) {
+                                                              int32_t* __restrict__ host_err,
+                                                              const SharedTables st) {
   __shared__ int32_t scan_c[RT_SCAN_THREADS];
   __shared__ int32_t scan_b[RT_SCAN_THREADS];
   __shared__ int32_t scan_s[RT_SCAN_THREADS];
   const int e = threadIdx.x;
+  if (st.idx && e == 0) shared_header(st);
   int c = 0;
   if (e < E) {
     for (int b = 0; b < nblk; ++b) {
@@ -188,76 +231,35 @@ __global__ void __launch_bounds__(RT_ONE_THREADS) route_one(const int32_t* __res
                                                             int32_t* __restrict__ row_of_slot,
                                                             int32_t* __restrict__ tok_of_row,
                                                             int32_t* __restrict__ tiles, int32_t* __restrict__ err,
-                                                            int32_t* __restrict__ host_err) {
+                                                            int32_t* __restrict__ host_err, const SharedTables st) {
   __shared__ RouteLds<RT_ONE_THREADS> lds;
+  if (st.idx) {  // the shared expert's tables first: their stores overlap the routing
+    if (threadIdx.x == 0) shared_header(st);
+    for (int64_t i = threadIdx.x; i < st.T; i += RT_ONE_THREADS) shared_entry(st, i);
+  }
   route_block<RT_ONE_THREADS>(lds, ids, S, E, K, nbits, max_big, big_on, counts, offsets, sorted_slot, row_of_slot,
                               tok_of_row, tiles, err, host_err);
 }
 
-// The shared expert's tables (RFC section 6.1: the shared expert runs through
-// the same grouped products as one more group): one expert that holds every
-// token, in token order.  offsets = {0, T}; idx[p] = p, which is both the slot
-// and the token of row p; ones[p] = 1, its combine weight; and the tile table
-// of one expert with T rows under route_scan's rule.
-__global__ void __launch_bounds__(RT_THREADS) shared_tables(int64_t T, int max_big, int big_on,
-                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ idx,
-                                                            float* __restrict__ ones, int32_t* __restrict__ tiles) {
-  const int64_t i = (int64_t)blockIdx.x * RT_THREADS + threadIdx.x;
-  const int64_t rem = big_on ? T % TILE_BIG : T;
-  const bool big_tail = big_on && rem > TILE_BIG / 2;
-  const int64_t nbig = big_on ? T / TILE_BIG + (big_tail ? 1 : 0) : 0;
-  const int64_t nsmall = big_tail ? 0 : (rem + TILE_SMALL - 1) / TILE_SMALL;
-  if (i < T) {
-    idx[i] = (int32_t)i;
-    ones[i] = 1.f;
-  }
-  if (i < nbig) {
-    tiles[4 + 2 * i] = 0;
-    tiles[4 + 2 * i + 1] = (int32_t)(i * TILE_BIG);
-  }
-  if (i < nsmall) {
-    int32_t* small = tiles + 4 + 2 * (int64_t)max_big;
-    small[2 * i] = 0;
-    small[2 * i + 1] = (int32_t)(nbig * TILE_BIG + i * TILE_SMALL);
-  }
-  if (i == 0) {
-    offsets[0] = 0;
-    offsets[1] = (int32_t)T;
-    tiles[0] = (int32_t)nbig;
-    tiles[1] = (int32_t)nsmall;
-    tiles[2] = TILE_BIG;
-    tiles[3] = TILE_SMALL;
-  }
-}
-
 // ---------------------------------------------------------------- launchers
-
-hipError_t launch_shared_tables(int64_t T, int max_big, int big_on, int32_t* offsets, int32_t* idx, float* ones,
-                                int32_t* tiles, hipStream_t stream) {
-  // every table entry index is below max(T, 1): #big and #small are at most T
-  const int64_t nb = (T + RT_THREADS - 1) / RT_THREADS;
-  hipLaunchKernelGGL(shared_tables, dim3((unsigned)(nb < 1 ? 1 : nb)), dim3(RT_THREADS), 0, stream, T, max_big,
-                     big_on, offsets, idx, ones, tiles);
-  return hipGetLastError();
-}
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
                         int32_t* tiles, int32_t* err, int32_t* blockhist, int32_t* blockbase, int32_t* blockerr,
-                        int32_t* host_err, hipStream_t stream) {
+                        int32_t* host_err, const SharedTables& st, hipStream_t stream) {
   const int nblk = (int)((S + RT_SLOTS - 1) / RT_SLOTS);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   if (S <= RT_ONE_MAX_SLOTS && E <= RT_ONE_MAX_EXPERTS) {
     hipLaunchKernelGGL(route_one, dim3(1), dim3(RT_ONE_THREADS), 0, stream, ids, S, E, K, nbits, max_big, big_on,
-                       counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err, host_err);
+                       counts, offsets, sorted_slot, row_of_slot, tok_of_row, tiles, err, host_err, st);
     return hipGetLastError();
   }
   if (nblk > 0) {
-    hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr);
+    hipLaunchKernelGGL(route_hist, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, blockhist, blockerr, st);
   }
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, blockhist, blockerr, nblk, E, max_big,
-                     big_on, counts, offsets, blockbase, tiles, err, host_err);
+                     big_on, counts, offsets, blockbase, tiles, err, host_err, st);
   if (nblk > 0) {
     hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(RT_THREADS), 0, stream, ids, S, E, nbits, offsets,
                        blockbase, K, sorted_slot, row_of_slot, tok_of_row);
