@@ -180,8 +180,10 @@ def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):
     rng = np.random.default_rng(1)
     toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_tok, replace=False)]))
     ti = torch.from_numpy(toks).cuda()
+    announce("oracle forward of %d tokens" % toks.size)
     ry, ryd = o.forward_dev(toks)
     assert_close(to_f64(y[ti]), ry, name + " y", ryd)
+    announce("oracle backward of %d tokens" % toks.size)
     (rdx, rdw), (ddx, ddw) = o.backward_tokens_dev(toks)
     assert_close(to_f64(dx[ti]), rdx, name + " dx", ddx)
     assert_close(to_f64(dw[ti]), rdw, name + " d_topk_weights", ddw)
@@ -191,6 +193,7 @@ def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):
     experts |= set(np.flatnonzero(counts == 0)[:1].tolist())
     icols = np.unique([min(I - 1, int(f * I)) for f in icols_frac] + [int(rng.integers(I))])
     for e in sorted(experts):
+        announce("oracle weight gradients of expert %d (%d rows)" % (e, counts[e]))
         (gcol, ucol, drow), (gd, ud, rd) = o.weight_grads_expert_dev(e, icols)
         assert_close(to_f64(dW1[e][:, icols]), gcol, "%s dW1[%d] gate cols" % (name, e), gd)
         assert_close(to_f64(dW1[e][:, icols + I]), ucol, "%s dW1[%d] up cols" % (name, e), ud)

@@ -166,3 +166,35 @@ def test_shared_expert_autograd():
         hyper_mega_moe(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"],
                        shared_up_proj_weight=g["shared_up_proj_weight"][:, :64].contiguous(),
                        shared_down_proj_weight=g["shared_down_proj_weight"])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,Is", [("skewed", 768), ("hotspot", 2048)])
+def test_full_size_shared_sampled(name, Is):
+    """Full-size workloads with a shared expert, in the launch configuration bench.py
+    times (--shared-I), on sampled tokens and sampled weight-gradient columns."""
+    import torch
+    spec = synth.spec_with(name, shared_I=Is)
+    T, H, I, E, K = (spec[k] for k in "THIEK")
+    inp = synth.make_inputs(spec, seed=0)
+    announce("full-size sampled shared parity %s Is=%d" % (name, Is))
+    g = gpu_inputs(inp, "cuda")
+    y, saved, dx, dW1, dW2, dw, dWs1, dWs2 = run_shared(g)
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    rng = np.random.default_rng(2)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 5, replace=False)]))
+    ti = torch.from_numpy(toks).cuda()
+    announce("oracle forward of %d tokens" % toks.size)
+    ry, ryd = o.forward_dev(toks)
+    assert_close(to_f64(y[ti]), ry, name + " y", ryd)
+    announce("oracle backward of %d tokens" % toks.size)
+    (rdx, rdw), (ddx, ddw) = o.backward_tokens_dev(toks)
+    assert_close(to_f64(dx[ti]), rdx, name + " dx", ddx)
+    assert_close(to_f64(dw[ti]), rdw, name + " d_topk_weights", ddw)
+    announce("oracle shared weight gradients")
+    icols = np.unique([0, Is - 1, int(rng.integers(Is))])
+    (gcol, ucol, drow), (gd, ud, rd) = o.shared_weight_grads_dev(icols)
+    assert_close(to_f64(dWs1[:, icols]), gcol, name + " d_shared_up gate cols", gd)
+    assert_close(to_f64(dWs1[:, icols + Is]), ucol, name + " d_shared_up up cols", ud)
+    assert_close(to_f64(dWs2[icols]), drow, name + " d_shared_down rows", rd)
+    # the routed weight gradients at this size are checked by the routed sampled tests
