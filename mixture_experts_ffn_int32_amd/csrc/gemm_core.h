@@ -127,22 +127,25 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
     pol.load_b(kc(2), rb0);
     pol.fetch(kc(3), rw);
     __syncthreads();
-    // one K step: park step kt+1 (in set `nx`) in the other LDS buffer, turn the
-    // indices of step kt+3 (fetched one step ago) into offsets, fetch the indices
-    // of step kt+4, refill `nx` with step kt+3, then multiply step kt.  ``full``:
-    // all of those steps exist (the loop), else each is checked (the tail).
+    // one K step: turn the indices of step kt+3 (fetched one step ago) into
+    // offsets and fetch those of step kt+4; multiply step kt, and after each of
+    // its four 16-deep slices park a quarter of step kt+1 (register set `nx`) in
+    // the other LDS buffer (so the stores are spread over the MFMAs instead of one
+    // burst that the fragment reads of every wave would queue behind); then
+    // refill `nx` with step kt+3.  ``full``: all of those steps exist (the loop),
+    // else each is checked (the tail).
     auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB], bool full) {
-      if (full || kt + 1 < nk) store_stage<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
-      if (full || kt + 3 < nk) {
+      const bool st_ok = full || kt + 1 < nk, ld_ok = full || kt + 3 < nk;
+      if (ld_ok) {
         pol.index(kt + 3, rw);
         pol.fetch(kc(kt + 4), rw);
-        pol.load_a(kt + 3, nxa);
-        pol.load_b(kt + 3, nxb);
       }
+      uint16_t* dst = smem + ((kt + 1) & 1) * C::STAGE;
       const uint16_t* sa = smem + (kt & 1) * C::STAGE;
       const uint16_t* sb = sa + C::A_ELEMS;
+      constexpr int NKK = BK / 16;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kk = 0; kk < NKK; ++kk) {
         bf16x8 fa[C::MB], fb[C::NB];
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<P::A_KMAJ, C::BM>(sa, wm * C::TM + mb * 32, kk, lane);
@@ -153,6 +156,19 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+        if (st_ok) {
+          const int t = threadIdx.x;
+#pragma unroll
+          for (int i = kk; i < C::CA; i += NKK)
+            *reinterpret_cast<u32x4*>(dst + lds_chunk_off<P::A_KMAJ, C::BM>(t + i * C::NTHR)) = nxa[i];
+#pragma unroll
+          for (int i = kk; i < C::CB; i += NKK)
+            *reinterpret_cast<u32x4*>(dst + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(t + i * C::NTHR)) = nxb[i];
+        }
+      }
+      if (ld_ok) {
+        pol.load_a(kt + 3, nxa);
+        pol.load_b(kt + 3, nxb);
       }
       __syncthreads();
     };
