@@ -171,15 +171,16 @@ struct Gmm1F8 {
 };
 
 template <class C, class P>
-__device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB]) {
+__device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB],
+                                             int part = 0, int nparts = 1) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < C::CA; ++i) {
+  for (int i = part; i < C::CA; i += nparts) {
     const int c = tid + i * C::NTHR;
     *reinterpret_cast<u32x4*>(st + (c >> 3) * LDKB + (c & 7) * 16) = ra[i];
   }
 #pragma unroll
-  for (int i = 0; i < C::CB; ++i) {
+  for (int i = part; i < C::CB; i += nparts) {
     const int c = tid + i * C::NTHR;
     *reinterpret_cast<u32x4*>(st + C::A_BYTES + (c / (C::BN / 16)) * C::LDB + (c % (C::BN / 16)) * 16) = rb[i];
   }
@@ -221,11 +222,20 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
     pol.load_a(kc(AHEAD - 1), ra0);
     pol.load_b(kc(AHEAD - 1), rb0);
     __syncthreads();
+    // With two register sets the next stage's LDS stores are spread over the
+    // MFMA slices of the step (see gemm_core.h) and the loads follow the last
+    // slice.  With one (the 256x256 tile) that would keep the set live across the
+    // MFMAs and spill: there the stores come first and the loads right after.
+    constexpr bool SPREAD = C::SETS == 2;
     auto step = [&](int kt, auto& nxa, auto& nxb, bool full) {
-      if (full || kt + 1 < nk) store_stage8<C, P>(smem + ((kt + 1) & 1) * C::STAGE, nxa, nxb);
-      if (full || kt + AHEAD < nk) {
-        pol.load_a(kt + AHEAD, nxa);
-        pol.load_b(kt + AHEAD, nxb);
+      const bool st_ok = full || kt + 1 < nk;
+      uint8_t* dst = smem + ((kt + 1) & 1) * C::STAGE;
+      if constexpr (!SPREAD) {
+        if (st_ok) store_stage8<C, P>(dst, nxa, nxb);
+        if (full || kt + AHEAD < nk) {
+          pol.load_a(kt + AHEAD, nxa);
+          pol.load_b(kt + AHEAD, nxb);
+        }
       }
       const uint8_t* sa = smem + (kt & 1) * C::STAGE;
       const uint8_t* sb = sa + C::A_BYTES;
@@ -257,6 +267,11 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
           for (int nb = 0; nb < C::NB; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, 127, 0, 127);
         }
+        if (SPREAD && st_ok) store_stage8<C, P>(dst, nxa, nxb, kk, BKB / 64);
+      }
+      if (SPREAD && (full || kt + AHEAD < nk)) {
+        pol.load_a(kt + AHEAD, nxa);
+        pol.load_b(kt + AHEAD, nxb);
       }
       __syncthreads();
     };
