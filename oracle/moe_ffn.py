@@ -83,12 +83,18 @@ C_F8 * 2^-24 * sqrt(sum of squared products) (in the accumulator's units),
 with C_F8 = 2^14; measured errors of such an instruction on random E4M3 data
 stay below 3300 * 2^-24 * sqrt(sum of squares), and below 1400 for Gaussian
 data (a margin of about 5 over the worst case seen).
+
+The MX variant (``gmm1="mx"``) quantises tokens and weights in blocks of 32
+along the hidden dimension with a power-of-two scale per block (see
+``quant``); the up-projection sums the dequantised products exactly, and the
+same instruction-accumulation bound applies to them (the block scales are
+powers of two, so they add no rounding of their own).
 """
 
 import numpy as np
 
 from .numerics import round_bf16, sigmoid, silu
-from .quant import quantize_columns, quantize_rows
+from .quant import quantize_columns, quantize_columns_mx, quantize_rows, quantize_rows_mx
 from .routing import check_ids
 
 U32 = 2.0 ** -24     # unit roundoff of float32
@@ -117,7 +123,7 @@ class MoEFFN:
                  dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None):
         if mode not in ("pure", "faithful"):
             raise ValueError(mode)
-        if gmm1 not in ("bf16", "fp8"):
+        if gmm1 not in ("bf16", "fp8", "mx"):
             raise ValueError(gmm1)
         self.x = np.asarray(x)
         self.ids = np.asarray(topk_ids, dtype=np.int64)
@@ -173,7 +179,10 @@ class MoEFFN:
 
     def _W1q(self, e):
         if e not in self._w1q:
-            self._w1q[e] = quantize_columns(self.W1[e])  # (q, scale, descale)
+            if self.gmm1 == "mx":   # (q, e): dequantised value q * 2^e, blocks of 32 rows
+                self._w1q[e] = quantize_columns_mx(self.W1[e])
+            else:                   # (q, scale, descale)
+                self._w1q[e] = quantize_columns(self.W1[e])
         return self._w1q[e]
 
     def slots_of_expert(self, e):
@@ -193,6 +202,14 @@ class MoEFFN:
             h = (q @ wqc) * scale
             sq = (q * q) @ (wqc * wqc)
             eps = (acc_eps(sq, self.H) + C_F8 * U32 * np.sqrt(sq)) * scale + 2 * C_EL * U32 * np.abs(h)
+        elif self.gmm1 == "mx":
+            q, ex = quantize_rows_mx(xrows)
+            wq, ew = self._W1q(e)
+            xd = q * np.repeat(np.exp2(ex), 32, axis=-1)           # dequantised tokens, exact
+            wd = (wq * np.repeat(np.exp2(ew), 32, axis=0))[:, cols]  # dequantised weight columns, exact
+            h = xd @ wd
+            sq = (xd * xd) @ (wd * wd)
+            eps = acc_eps(sq, self.H) + C_F8 * U32 * np.sqrt(sq)
         else:
             W = self._W1(e)[:, cols]
             h = xr @ W

@@ -51,3 +51,64 @@ def quantize_columns(w):
     q = round_e4m3(prod.astype(np.float64))
     descale = (np.float32(1.0) / scale).astype(np.float32)
     return q, scale, descale
+
+
+# ----------------------------------------------------------------------------- MX
+# MoeDistributeDispatchV2, case 5 (quantMode 4, "mx"): the shared exponent of a
+# block is floor(log2(max)) - emax, where emax is the exponent of the target
+# type's largest normal value (E4M3: 448 = 1.75 * 2^8, emax = 8); the block's
+# scale is 2^sharedExp and the codes are the FP8 cast of X / scale.
+# Readings (the page leaves them open):
+# * the block is 32 consecutive elements along the contraction dimension (the
+#   OCP MX block size; the page gives none), and "max(x)" is max |x| of the block;
+# * the cast saturates at +-448 (X / scale reaches up to 2^9 - ulp, above the
+#   largest E4M3 value), rounding to nearest even below that;
+# * the exponent is stored as E8M0 (its range is 2^-127 .. 2^127; exponents
+#   outside are clamped); an all-zero block gets the smallest, 2^-127;
+# * the factor that travels with the codes is the scale itself (X ~ code *
+#   2^sharedExp); the page's "1.0/dynamicScales" is case 3's convention, where
+#   the scale multiplies X.
+# The up-projection weight gets the same rule per (expert, column, block of 32
+# rows along the hidden dimension).
+
+MX_BLOCK = 32
+E4M3_EMAX = 8
+
+
+def mx_exponent(absmax):
+    """Shared block exponent floor(log2(absmax)) - 8, clamped to [-127, 127] (-127 for 0)."""
+    a = np.asarray(absmax, dtype=np.float64)
+    _, ex = np.frexp(a)                       # a = m * 2^ex with 0.5 <= m < 1: floor(log2 a) = ex - 1
+    e = ex.astype(np.int64) - 1 - E4M3_EMAX
+    e = np.where(a > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_rows_mx(x):
+    """MX quantisation of ``x`` [..., H] in blocks of 32 along H.
+
+    Returns (q, e): q the E4M3 values [..., H] (float64), e the block exponents
+    [..., H / 32] (int64); the dequantised value is q * 2^e.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    H = x.shape[-1]
+    if H % MX_BLOCK:
+        raise ValueError("H must be a multiple of %d" % MX_BLOCK)
+    xb = x.reshape(x.shape[:-1] + (H // MX_BLOCK, MX_BLOCK))
+    e = mx_exponent(np.max(np.abs(xb), axis=-1))
+    q = round_e4m3(xb / np.exp2(e)[..., None].astype(np.float64))
+    return q.reshape(x.shape), e
+
+
+def quantize_columns_mx(w):
+    """MX quantisation of a weight ``w`` [H, N] in blocks of 32 rows per column.
+
+    Returns (q [H, N], e [H / 32, N])."""
+    w = np.asarray(w, dtype=np.float64)
+    H, N = w.shape
+    if H % MX_BLOCK:
+        raise ValueError("H must be a multiple of %d" % MX_BLOCK)
+    wb = w.reshape(H // MX_BLOCK, MX_BLOCK, N)
+    e = mx_exponent(np.max(np.abs(wb), axis=1))
+    q = round_e4m3(wb / np.exp2(e)[:, None, :].astype(np.float64))
+    return q.reshape(H, N), e

@@ -80,3 +80,122 @@ def test_fp8_up_projection_error_is_bounded():
         h16 = m16.up(e, x)
         bound = (2 * 2.0 ** -4 + 2.0 ** -8) * (np.abs(x) @ np.abs(W1[e]))
         assert np.all(np.abs(h8 - h16) <= bound)
+
+
+# ----------------------------------------------------------------------------- MX (Dispatch case 5)
+from oracle.quant import mx_exponent, quantize_columns_mx, quantize_rows_mx  # noqa: E402
+
+
+def test_mx_closed_forms():
+    """Block exponent floor(log2 max|x|) - 8 (E4M3's emax), codes X / 2^e, saturating at 448."""
+    x = np.zeros((1, 8 * 32))
+    x[0, 0:32] = 0.25                      # max 2^-2: e = -10, every code 256
+    x[0, 32] = 1.5 * 2.0 ** 5              # max 1.5 * 2^5: e = -3, code 384 exactly
+    x[0, 33] = -2.0 ** 5                   # same block: code -256
+    x[0, 64] = 1.875 * 2.0 ** 3            # max 1.875 * 2^3: e = -5, 480 saturates to 448
+    x[0, 96] = 1.75 * 2.0 ** -3            # 1.75 * 256 = 448: representable, no saturation
+    # block 4 stays zero: e = -127, codes 0
+    x[0, 160] = 2.0 ** -140                # e clamped to -127; 2^-13 rounds to code 0
+    x[0, 192] = 2.0 ** 130                 # e = 122, code 256
+    x[0, 193] = 2.0 ** 120                 # 2^120 / 2^122 = 0.25: an exact E4M3 value
+    x[0, 224] = 3.0                        # max 3: e = -7, 3 / 2^-7 = 384
+    x[0, 225] = 3.0 * 2.0 ** -12           # 384 * 2^-12 = 0.09375 = 0.75 * 2^-3: exact
+    x[0, 226] = 3.0 * 2.0 ** -19           # 384 * 2^-19 = 0.000732...: below 2^-10 -> rounds to 0
+    q, e = quantize_rows_mx(x)
+    assert e.tolist() == [[-10, -3, -5, -11, -127, -127, 122, -7]]
+    assert np.all(q[0, 0:32] == 256)
+    assert q[0, 32] == 384 and q[0, 33] == -256 and np.all(q[0, 34:64] == 0)
+    assert q[0, 64] == 448 and q[0, 96] == 448
+    assert np.all(q[0, 128:192] == 0)
+    assert q[0, 192] == 256 and q[0, 193] == 0.25
+    assert q[0, 224] == 384 and q[0, 225] == 0.09375 and q[0, 226] == 0
+    assert mx_exponent(0.0) == -127 and mx_exponent(2.0 ** 200) == 127 and mx_exponent(511.0) == 0
+
+
+def test_mx_rows_match_torch_cast():
+    """Codes equal torch's float8_e4m3fn cast of the block-scaled values clamped to +-448,
+    with the exponent from torch.frexp; blocks span many magnitudes."""
+    rng = np.random.default_rng(5)
+    x = round_bf16(rng.standard_normal((16, 256)) * np.exp2(rng.integers(-30, 30, (16, 256 // 32))).repeat(32, 1))
+    q, e = quantize_rows_mx(x)
+    tx = torch.from_numpy(x).reshape(16, 8, 32)
+    _, ex = torch.frexp(tx.abs().amax(dim=2))
+    te = torch.clamp(ex.to(torch.int64) - 9, -127, 127)
+    assert np.array_equal(e, te.numpy())
+    scaled = tx / torch.exp2(te.to(torch.float64))[..., None]
+    tq = torch.clamp(scaled, -448, 448).to(torch.float8_e4m3fn).to(torch.float64).reshape(16, 256)
+    assert np.array_equal(q, tq.numpy())
+    # dequantisation error: half an E4M3 step at the element's binade, or the
+    # saturation at 448 * 2^e (block maxima up to 512 * 2^e), plus half the
+    # smallest subnormal step of the block
+    deq = q * np.exp2(e).repeat(32, 1)
+    s = np.exp2(e).repeat(32, 1)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), np.abs(x) - 448 * s) + s * 2.0 ** -10
+    assert np.all(np.abs(deq - x) <= bound)
+    assert np.any(np.abs(x) > 448 * s)      # saturation occurs in this data
+
+
+def test_mx_columns_are_row_blocks_per_column():
+    rng = np.random.default_rng(6)
+    w = round_bf16(rng.standard_normal((96, 10)) * np.exp2(rng.integers(-8, 8, (3, 1, 10))).repeat(32, 0).reshape(96, 10))
+    q, e = quantize_columns_mx(w)
+    qt, et = quantize_rows_mx(w.T)          # the same rule, transposed
+    assert np.array_equal(q, qt.T) and np.array_equal(e, et.T)
+    assert e.shape == (3, 10)
+
+
+def test_mx_up_projection_exact_when_blocks_are_representable():
+    """x = code * 2^e per block, with the block's largest |code| in [256, 448], quantises back
+    exactly; likewise W1 per (32-row block, column).  Then the MX up-projection equals
+    the bf16 one exactly (pure mode), so a misplaced block exponent would show."""
+    rng = np.random.default_rng(7)
+    T, H, I, E, K = 5, 64, 8, 2, 2
+    codes = np.array([c for c in np.arange(0, 449, 0.125) if np.array_equal(
+        np.asarray([c]), np.asarray([float(torch.tensor(c).to(torch.float8_e4m3fn).to(torch.float64))]))])
+
+    def block_values(shape):
+        return rng.choice(codes, shape) * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+
+    x = block_values((T, H))
+    x[:, 0], x[:, 32] = 320.0, -448.0               # block maxima in [256, 448]
+    ex = rng.integers(-12, 6, (T, H // 32))
+    x = x * np.exp2(ex).repeat(32, 1)
+    W1 = block_values((E, H, 2 * I))
+    W1[:, 0, :], W1[:, 32, :] = 256.0, 416.0
+    ew = rng.integers(-14, 0, (E, H // 32, 2 * I))
+    W1 = W1 * np.exp2(ew).repeat(32, 1)
+    W2 = rng.standard_normal((E, I, H))
+    ids = np.array([[0, 1]] * T)
+    w = np.full((T, K), 0.5, np.float32)
+    mx = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="mx")
+    bf = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="bf16")
+    for e in range(E):
+        assert np.array_equal(mx.up(e, x), bf.up(e, x))
+    q, e_ = quantize_rows_mx(x)
+    assert np.array_equal(e_, ex) and np.array_equal(q * np.exp2(e_).repeat(32, 1), x)
+    for e in range(E):
+        qw, e_ = quantize_columns_mx(W1[e])
+        assert np.array_equal(e_, ew[e]) and np.array_equal(qw * np.exp2(e_).repeat(32, 0), W1[e])
+
+
+def test_mx_up_projection_error_is_bounded():
+    """Generic data: every dequantised element is within max(2^-4 |v|, |v| - 448 2^e) + 2^(e-10) of v."""
+    rng = np.random.default_rng(8)
+    T, H, I, E, K = 8, 64, 16, 3, 2
+    x = round_bf16(rng.standard_normal((T, H)) * np.exp2(rng.integers(-4, 4, (T, 2))).repeat(32, 1))
+    W1 = round_bf16(rng.standard_normal((E, H, 2 * I)) / 8)
+    W2 = round_bf16(rng.standard_normal((E, I, H)) / 4)
+    ids = np.array([rng.choice(E, K, replace=False) for _ in range(T)])
+    w = np.full((T, K), 0.5, np.float32)
+    mmx = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="mx")
+    m16 = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="bf16")
+    def dev(v, s):
+        return np.maximum(2.0 ** -4 * np.abs(v), np.abs(v) - 448 * s) + s * 2.0 ** -10
+
+    _, ex = quantize_rows_mx(x)
+    dx = dev(x, np.exp2(ex).repeat(32, 1))
+    for e in range(E):
+        _, ew = quantize_columns_mx(W1[e])
+        dw = dev(W1[e], np.exp2(ew).repeat(32, 0))
+        bound = dx @ (np.abs(W1[e]) + dw) + np.abs(x) @ dw
+        assert np.all(np.abs(mmx.up(e, x) - m16.up(e, x)) <= bound)
