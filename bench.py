@@ -7,7 +7,7 @@ synthetic input already resident in HBM, through the C ABI of libhmm.
 
 Prints ONE JSON line on stdout; details go to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8|mx]
 
 Timing: W untimed warm-up steps (the first one's time is reported as
 first_step_ms), then K steps between two synchronisations, timed with HIP
@@ -70,7 +70,7 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
     Is > 0: a shared expert of that width (one more group of all T rows)."""
     S = T * K
     eb = 4 if f32 else 2
-    if stage == "gmm1_fp8_swiglu":
+    if stage in ("gmm1_fp8_swiglu", "gmm1_mx_swiglu"):
         return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
     flops = {
         "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
@@ -101,6 +101,9 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
         # FP8 quantisers: read the bf16 operand once, write its codes and descales
         "quant_x": T * H * 2 + T * H + T * 4,
         "quant_w1": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * 4,
+        # MX quantisers: the bf16 operand once, its codes and one exponent byte per 32 elements
+        "quant_x_mx": T * H * 2 + T * H + T * H // 32,
+        "quant_w1_mx": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * H // 32,
     }
     if stage in nbytes:
         return "hbm", nbytes[stage], "GB/s", PEAK_HBM_GBS
@@ -135,7 +138,7 @@ class Runner:
         self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
         flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
-        gmm1 = _lib.HMM_FP8_E4M3 if spec.get("gmm1", "bf16") == "fp8" else _lib.HMM_BF16
+        gmm1 = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3}[spec.get("gmm1", "bf16")]
         f32 = out_dtype == "f32"
         Is = spec.get("shared_I", 0)
         self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_F32 if f32 else _lib.HMM_BF16, gmm1, flags, Is)
@@ -273,7 +276,7 @@ def main():
     if args.shared_I:
         spec["shared_I"] = args.shared_I
     Is = spec.get("shared_I", 0)
-    fp8 = spec.get("gmm1", "bf16") == "fp8"
+    gmm1_kind = spec.get("gmm1", "bf16")
     T, H, I, E, K = (spec[k] for k in "THIEK")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -345,7 +348,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp8" if fp8 else ("bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
+        "dtype": {"fp8": "bf16+fp8", "mx": "bf16+mxfp8"}.get(
+            gmm1_kind, "bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
                    "routing": spec.get("routing"), "shared_I": Is, "seed": args.seed,

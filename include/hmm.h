@@ -67,7 +67,8 @@ typedef enum hmm_status {
 typedef enum hmm_dtype {
   HMM_BF16 = 0,
   HMM_F32 = 1,
-  HMM_FP8_E4M3 = 2
+  HMM_FP8_E4M3 = 2,    /* E4M3 with one float32 scale per token row / weight column */
+  HMM_MXFP8_E4M3 = 3   /* E4M3 with one E8M0 exponent per 32 elements along H (MX) */
 } hmm_dtype;
 
 /* Check topk_ids: the routing kernel raises a flag for an id outside [0, E)
@@ -116,6 +117,11 @@ typedef enum hmm_dtype {
  *               dynamic quantisation of MoeDistributeDispatchV2, case 3);
  *               H must then be a multiple of 128.  Only the up-projection
  *               changes: the rest of the forward and the backward stay bf16.
+ *               HMM_MXFP8_E4M3: the MX quantisation of MoeDistributeDispatchV2
+ *               (case 5) instead: blocks of 32 along H, one power-of-two scale
+ *               per block (tokens per row, the weight per (expert, column)), see
+ *               hmm_quant_rows_mx; the block exponents feed the scaled FP8
+ *               matrix instruction directly.  H a multiple of 128.
  *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward.
  *   shared_I    0, or the intermediate size Is of a shared expert (a multiple of
  *               64 in [64, 65536]): then the calls are hmm_forward_shared and
@@ -265,6 +271,20 @@ hmm_status hmm_quant_rows_fp8(const void* x, int64_t T, int64_t H, uint8_t* xq, 
 hmm_status hmm_quant_cols_workspace_size(int64_t E, int64_t H, int64_t N, size_t* workspace_bytes);
 hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* descale,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* MX quantisation stages (MoeDistributeDispatchV2 case 5, quantMode 4), exported
+ * for tests and tools (hmm_forward runs the same kernels with HMM_MXFP8_E4M3).
+ * Per block of 32 consecutive elements along H: e = floor(log2 max|v|) - 8 (8 is
+ * the exponent of E4M3's largest value, 448), clamped to [-127, 127] (-127 for an
+ * all-zero block); code = round-to-nearest-even E4M3 of v * 2^-e saturated at
+ * +-448; the block's E8M0 byte is e + 127, and v ~ code * 2^e.
+ *   hmm_quant_rows_mx: x bf16 [T,H] -> xq [T,H] E4M3 bytes, xs [T,H/32] E8M0 bytes.
+ *   hmm_quant_cols_mx: w bf16 [E,H,N] -> wq [E,H,N] E4M3 bytes, ws [E,N,H/32] E8M0
+ *                      bytes (blocks of 32 rows of one column; column-major
+ *                      exponents so a column's blocks are contiguous).
+ * H a multiple of 32, N of 8; arrays below 4 GiB; device pointers, 16-byte aligned. */
+hmm_status hmm_quant_rows_mx(const void* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs, void* stream);
+hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws, void* stream);
 
 /* Names of statuses, and the calling thread's last error text. */
 const char* hmm_status_string(hmm_status s);

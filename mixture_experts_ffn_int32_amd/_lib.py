@@ -21,7 +21,7 @@ HMM_ERR_WORKSPACE_TOO_SMALL = 6
 HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7
 HMM_ERR_HIP = 8
 
-HMM_BF16, HMM_F32, HMM_FP8_E4M3 = 0, 1, 2
+HMM_BF16, HMM_F32, HMM_FP8_E4M3, HMM_MXFP8_E4M3 = 0, 1, 2, 3
 HMM_FLAG_VALIDATE_IDS = 1
 HMM_FLAG_TILES_LARGE = 2
 HMM_FLAG_TILES_NARROW = 4
@@ -33,7 +33,7 @@ EXPORTS = (
     "hmm_forward_sizes", "hmm_saved_layout_of", "hmm_forward", "hmm_backward_sizes", "hmm_backward",
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
     "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
-    "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared",
+    "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared", "hmm_quant_rows_mx", "hmm_quant_cols_mx",
 )
 
 
@@ -72,6 +72,8 @@ _SIGS = {
     "hmm_quant_rows_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_quant_cols_workspace_size": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_SZ)],
     "hmm_quant_cols_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _SZ, _P],
+    "hmm_quant_rows_mx": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "hmm_quant_cols_mx": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_status_string": [ctypes.c_int],
     "hmm_last_error_message": [],
     "hmm_build_info": [],

@@ -42,7 +42,8 @@ struct Dims {
   int64_t Is;  // shared expert's intermediate size (0: none)
   bool shared;
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
-  bool fp8;    // FP8 E4M3 up-projection
+  bool fp8;    // FP8 E4M3 up-projection (per-token scales, or MX block exponents)
+  bool mx;     // ... with MX block exponents
   bool f32;    // float32 outputs (accuracy mode)
   bool fused;  // small problem whose forward runs as one fused launch (fused.hip)
 };
@@ -67,8 +68,9 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
   if (p->out_dtype != HMM_BF16 && p->out_dtype != HMM_F32)
     return fail(HMM_ERR_BAD_DTYPE, "out_dtype must be HMM_BF16 or HMM_F32 (got %d)", p->out_dtype);
-  if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3)
-    return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16 or HMM_FP8_E4M3 (got %d)", p->gmm1_dtype);
+  if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3 && p->gmm1_dtype != HMM_MXFP8_E4M3)
+    return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16, HMM_FP8_E4M3 or HMM_MXFP8_E4M3 (got %d)",
+                p->gmm1_dtype);
   {
     // every array a product reads through a buffer resource must stay below 4 GiB
     // (the float32-output mode reads [hi | lo] operands of twice the width)
@@ -81,9 +83,8 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   }
   if (p->out_dtype == HMM_F32 && p->gmm1_dtype != HMM_BF16)
     return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is implemented with gmm1_dtype HMM_BF16 only");
-  if (p->gmm1_dtype == HMM_FP8_E4M3 && p->H % 128)
-    return fail(HMM_ERR_BAD_SHAPE, "gmm1_dtype HMM_FP8_E4M3 needs H to be a multiple of 128 (got %lld)",
-                (long long)p->H);
+  if (p->gmm1_dtype != HMM_BF16 && p->H % 128)
+    return fail(HMM_ERR_BAD_SHAPE, "an FP8 gmm1_dtype needs H to be a multiple of 128 (got %lld)", (long long)p->H);
   d->T = p->T;
   d->H = p->H;
   d->I = p->I;
@@ -92,7 +93,8 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->S = p->T * p->K;
   d->Is = p->shared_I;
   d->shared = p->shared_I != 0;
-  d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3;
+  d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3 || p->gmm1_dtype == HMM_MXFP8_E4M3;
+  d->mx = p->gmm1_dtype == HMM_MXFP8_E4M3;
   d->f32 = p->out_dtype == HMM_F32;
   d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
@@ -174,7 +176,7 @@ RouteScratch route_scratch(const Dims& d, size_t base) {
 // maxima of the weight quantisation.
 struct FwdWork {
   RouteScratch rs;
-  size_t o, os, xq, dsx, wq, dsw, pmax, sync, total;
+  size_t o, os, xq, dsx, wq, dsw, pmax, xs, ws, sync, total;
 };
 FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
@@ -186,8 +188,13 @@ FwdWork fwd_work(const Dims& d) {
   }
   if (d.fp8) {
     w.xq = o;   o += up(d.T * d.H);
-    w.dsx = o;  o += up(d.T * 4);
     w.wq = o;   o += up(d.E * d.H * 2 * d.I);
+  }
+  if (d.mx) {  // E8M0 block exponents: [T][H/32] and [E][2I][H/32]
+    w.xs = o;   o += up(d.T * (d.H / 32));
+    w.ws = o;   o += up(d.E * 2 * d.I * (d.H / 32));
+  } else if (d.fp8) {
+    w.dsx = o;  o += up(d.T * 4);
     w.dsw = o;  o += up(d.E * 2 * d.I * 4);
     w.pmax = o; o += up(hmm::quant_cols_chunks(d.H) * d.E * 2 * d.I * 4);
   }
@@ -618,7 +625,27 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
   uint16_t* as = at<uint16_t>(saved, L.shared_a);
   uint16_t* os = d.shared ? at<uint16_t>(workspace, W.os) : nullptr;
   const int nj = d.shared ? 2 : 1;  // jobs per product launch: routed experts, then the shared expert
-  if (d.fp8) {
+  if (d.mx) {
+    uint8_t* xq = at<uint8_t>(workspace, W.xq);
+    uint8_t* wq = at<uint8_t>(workspace, W.wq);
+    uint8_t* xs = at<uint8_t>(workspace, W.xs);
+    uint8_t* ws = at<uint8_t>(workspace, W.ws);
+    {
+      Stage stage("quant_x_mx", st);
+      e = hmm::launch_quant_rows_mx((const uint16_t*)x, d.T, d.H, xq, xs, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "token quantisation launch");
+    {
+      Stage stage("quant_w1_mx", st);
+      e = hmm::launch_quant_cols_mx((const uint16_t*)up_w, d.E, d.H, 2 * d.I, wq, ws, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
+    {
+      Stage stage("gmm1_mx_swiglu", st);
+      e = hmm::launch_gmm1_mx(g, xq, xs, wq, ws, topk_weights, d.H, d.I, h, a, aw, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  } else if (d.fp8) {
     uint8_t* xq = at<uint8_t>(workspace, W.xq);
     uint8_t* wq = at<uint8_t>(workspace, W.wq);
     float* dsx = at<float>(workspace, W.dsx);
@@ -639,6 +666,8 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
       e = hmm::launch_gmm1_fp8(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
     }
     if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  }
+  if (d.fp8) {
     if (d.shared) {
       // the shared expert's up-projection stays bf16
       const hmm::Gmm1Job js{gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr};
@@ -846,6 +875,28 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
 }  // namespace
 
 extern "C" {
+
+hmm_status hmm_quant_rows_mx(const void* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs, void* stream) {
+  if (T < 0 || T > (int64_t)0x7fffffff) return fail(HMM_ERR_BAD_SHAPE, "T must be in [0, 2^31) (got %lld)", (long long)T);
+  if (H < 32 || H % 32) return fail(HMM_ERR_BAD_SHAPE, "H must be a positive multiple of 32 (got %lld)", (long long)H);
+  hmm_status s = quant_dims(T > 0 ? T : 1, H, 8);
+  if (s != HMM_OK) return s;
+  const bool ne = T > 0;
+  if ((s = need(x, ne, "x")) || (s = need(xq, ne, "xq")) || (s = need(xs, ne, "xs"))) return s;
+  Stage stage("quant_x_mx", (hipStream_t)stream);
+  const hipError_t e = hmm::launch_quant_rows_mx((const uint16_t*)x, T, H, xq, xs, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "token quantisation launch");
+}
+
+hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws, void* stream) {
+  hmm_status s = quant_dims(E, H, N);
+  if (s != HMM_OK) return s;
+  if (H % 32) return fail(HMM_ERR_BAD_SHAPE, "H must be a multiple of 32 (got %lld)", (long long)H);
+  if ((s = need(w, true, "w")) || (s = need(wq, true, "wq")) || (s = need(ws, true, "ws"))) return s;
+  Stage stage("quant_w1_mx", (hipStream_t)stream);
+  const hipError_t e = hmm::launch_quant_cols_mx((const uint16_t*)w, E, H, N, wq, ws, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
+}
 
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
                        const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,

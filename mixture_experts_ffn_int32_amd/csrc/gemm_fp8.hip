@@ -13,7 +13,19 @@
 // N-major) sits as [k][n] (pitch BN+32 bytes, so the 8 k rows a 32-lane pass
 // of ds_read_b64_tr_b8 touches fall in distinct banks) and is read with four
 // transposing reads of 8 k each.  Lane l of a 32x32x64 operand holds row/column
-// l % 32 and k = 32 (l / 32) + 0..31.
+// l % 32 and, in the instruction's own k order, k = 16 (l / 32) + 0..15 in bytes
+// 0..15 and k = 32 + 16 (l / 32) + 0..15 in bytes 16..31: the instruction's
+// first 32-k scale block is bytes 0..15 of both lane halves (checked on the GPU
+// with one nonzero position at a time).
+//
+// MX variant (MoeDistributeDispatchV2 case 5): tokens and weights carry one
+// E8M0 exponent per 32 elements along the hidden dimension, which is exactly
+// the 32 k values one lane holds in one instruction, so the exponents go to the
+// instruction's per-lane scale operands (lane l scales the instruction's k block
+// l / 32, which is block 2 kk + l / 32 of the step's four: that byte of the
+// step's exponent word of the lane's row or column), and the accumulator needs
+// no dequantisation.  The exponents of a step (one 32-bit word per tile row and
+// per tile column) are staged in LDS behind the operand tiles.
 #include "device.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -50,23 +62,29 @@ __device__ __forceinline__ int acc_row8(int wm, int mb, int r, int lane) {
   return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-template <class C, bool SMALL>
+template <class C, bool SMALL, bool MX = false>
 struct Gmm1F8 {
   struct Args {
     RowGroups g;
     const uint8_t* xq;   // [T][H] E4M3
-    const float* dsx;    // [T]
+    const float* dsx;    // [T] (per-token mode)
     const uint8_t* wq;   // [E][H][2I] E4M3
-    const float* dsw;    // [E][2I]
+    const float* dsw;    // [E][2I] (per-token mode)
     const float* tw;
     int64_t T, H, I;
     uint16_t *h, *a, *aw;
     int n_ntiles;
+    const uint8_t* xs = nullptr;  // [T][H/32] E8M0 (MX mode)
+    const uint8_t* ws = nullptr;  // [E][2I][H/32] E8M0 (MX mode)
   };
+  // MX: one exponent word per tile row and column per step, SCR per thread
+  static constexpr bool MX_ = MX;
+  static constexpr int SCR = MX ? (C::BM + C::BN + C::NTHR - 1) / C::NTHR : 1;
+  static constexpr int SC_BYTES = MX ? (C::BM + C::BN) * 4 : 0;
   const Args* ar;
   int e, row0, rows, nt, i0, nk;
-  rsrc_t ra_, rb_;
-  uint32_t aoff[C::CA], boff[C::CB];
+  rsrc_t ra_, rb_, rsx_, rsw_;
+  uint32_t aoff[C::CA], boff[C::CB], soff[SCR];
 
   __device__ __forceinline__ bool init(const Args& A, int logical) {
     ar = &A;
@@ -100,7 +118,37 @@ struct Gmm1F8 {
       boff[i] = (uint32_t)(kr * 2 * A.I + col);
     }
     nk = (int)(A.H / BKB);
+    if constexpr (MX) {
+      const int64_t nb = A.H / 32;  // exponent bytes per token row / weight column
+      rsx_ = make_rsrc(A.xs, A.T * nb);
+      rsw_ = make_rsrc(A.ws + (int64_t)e * 2 * A.I * nb, 2 * A.I * nb);
+#pragma unroll
+      for (int j = 0; j < SCR; ++j) {
+        const int idx = tid + j * C::NTHR;
+        if (idx < C::BM) {
+          soff[j] = (uint32_t)((int64_t)g.tok_of_row[row0 + min(idx, rows - 1)] * nb);
+        } else {
+          const int n = min(idx - C::BM, C::BN - 1);
+          const int64_t gi = min((int64_t)(i0 + n % (C::BN / 2)), A.I - 1);
+          soff[j] = (uint32_t)(((n < C::BN / 2) ? gi : A.I + gi) * nb);
+        }
+      }
+    }
     return true;
+  }
+  // MX: the exponent words of step kt (four blocks of 32 k) of this thread's rows / columns
+  __device__ __forceinline__ void load_s(int kt, uint32_t (&r)[SCR]) {
+    if constexpr (MX) {
+      const int tid = threadIdx.x;
+#pragma unroll
+      for (int j = 0; j < SCR; ++j) {
+        const int idx = tid + j * C::NTHR;
+        if (idx < C::BM)
+          r[j] = __builtin_amdgcn_raw_buffer_load_b32(rsx_, (int)soff[j], kt * 4, 0);
+        else if (idx < C::BM + C::BN)
+          r[j] = __builtin_amdgcn_raw_buffer_load_b32(rsw_, (int)soff[j], kt * 4, 0);
+      }
+    }
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
@@ -123,15 +171,17 @@ struct Gmm1F8 {
     float* csc = rsc + C::BM;
     const int tid = threadIdx.x;
     const int64_t I = ar->I;
+    // per-token mode: the row and column descales; MX: the instruction applied the
+    // block exponents already
     for (int t = tid; t < C::BM; t += C::NTHR) {
       const bool v = t < rows;
       wrow[t] = v ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
-      rsc[t] = v ? ar->dsx[ar->g.tok_of_row[row0 + t]] : 0.f;
+      rsc[t] = MX ? 1.f : (v ? ar->dsx[ar->g.tok_of_row[row0 + t]] : 0.f);
     }
     for (int t = tid; t < C::BN; t += C::NTHR) {
       const int64_t gi = i0 + (t % (C::BN / 2));
       const int64_t col = (t < C::BN / 2) ? gi : I + gi;
-      csc[t] = (gi < I) ? ar->dsw[(int64_t)e * 2 * I + col] : 0.f;
+      csc[t] = MX ? 1.f : ((gi < I) ? ar->dsw[(int64_t)e * 2 * I + col] : 0.f);
     }
     __syncthreads();
 #pragma unroll
@@ -171,6 +221,18 @@ struct Gmm1F8 {
 };
 
 template <class C, class P>
+__device__ __forceinline__ void store_scales(uint8_t* st, const uint32_t (&rs)[P::SCR]) {
+  if constexpr (P::MX_) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < P::SCR; ++j) {
+      const int idx = tid + j * C::NTHR;
+      if (idx < C::BM + C::BN) reinterpret_cast<uint32_t*>(st + C::STAGE)[idx] = rs[j];
+    }
+  }
+}
+
+template <class C, class P>
 __device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::CA], const u32x4 (&rb)[C::CB],
                                              int part = 0, int nparts = 1) {
   const int tid = threadIdx.x;
@@ -189,7 +251,8 @@ __device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::C
 template <class P>
 __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P::Args args) {
   typedef typename P::Cc C;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  constexpr int ST = C::STAGE + P::SC_BYTES;  // one LDS stage: operand tiles, then the MX exponents
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * ST];
   P pol;
   if (!pol.init(args, xcd_remap(blockIdx.x, gridDim.x))) return;
   const int tid = threadIdx.x;
@@ -212,13 +275,18 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
     // issued after the ones they wait for (see gemm_core.h).
     const auto kc = [nk](int k) { return k < nk ? k : nk - 1; };
     u32x4 ra0[C::CA], rb0[C::CB], ra1[C::SETS == 2 ? C::CA : 1], rb1[C::SETS == 2 ? C::CB : 1];
+    uint32_t rs0[P::SCR], rs1[P::SCR];
+    pol.load_s(0, rs0);
     pol.load_a(0, ra0);
     pol.load_b(0, rb0);
     if constexpr (C::SETS == 2) {
+      pol.load_s(kc(1), rs1);
       pol.load_a(kc(1), ra1);
       pol.load_b(kc(1), rb1);
     }
     store_stage8<C, P>(smem, ra0, rb0);
+    store_scales<C, P>(smem, rs0);
+    pol.load_s(kc(AHEAD - 1), rs0);
     pol.load_a(kc(AHEAD - 1), ra0);
     pol.load_b(kc(AHEAD - 1), rb0);
     __syncthreads();
@@ -227,49 +295,62 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
     // slice.  With one (the 256x256 tile) that would keep the set live across the
     // MFMAs and spill: there the stores come first and the loads right after.
     constexpr bool SPREAD = C::SETS == 2;
-    auto step = [&](int kt, auto& nxa, auto& nxb, bool full) {
+    auto step = [&](int kt, auto& nxa, auto& nxb, auto& nxs, bool full) {
       const bool st_ok = full || kt + 1 < nk;
-      uint8_t* dst = smem + ((kt + 1) & 1) * C::STAGE;
+      uint8_t* dst = smem + ((kt + 1) & 1) * ST;
       if constexpr (!SPREAD) {
-        if (st_ok) store_stage8<C, P>(dst, nxa, nxb);
+        if (st_ok) {
+          store_stage8<C, P>(dst, nxa, nxb);
+          store_scales<C, P>(dst, nxs);
+        }
         if (full || kt + AHEAD < nk) {
+          pol.load_s(kt + AHEAD, nxs);
           pol.load_a(kt + AHEAD, nxa);
           pol.load_b(kt + AHEAD, nxb);
         }
+      } else {
+        if (st_ok) store_scales<C, P>(dst, nxs);
       }
-      const uint8_t* sa = smem + (kt & 1) * C::STAGE;
+      const uint8_t* sa = smem + (kt & 1) * ST;
       const uint8_t* sb = sa + C::A_BYTES;
+      const uint32_t* scl = reinterpret_cast<const uint32_t*>(sa + C::STAGE);
 #pragma unroll
       for (int kk = 0; kk < BKB / 64; ++kk) {
         // B fragments for the whole wave tile, then one A fragment at a time
         // (keeps the live fragment registers at NB + 1 operands)
+        const int sh = 8 * (2 * kk + (lane >> 5));  // this lane's block among the step's four
         i32x8 fb[C::NB];
+        int bsc[C::NB];
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
           const int i = lane & 15;
           const int n = wn * C::TN + nb * 32 + 16 * ((lane >> 4) & 1) + 8 * (i & 1);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int k = kk * 64 + 32 * (lane >> 5) + 8 * q + (i >> 1);
+            const int k = kk * 64 + 32 * (q >> 1) + 16 * (lane >> 5) + 8 * (q & 1) + (i >> 1);
             const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + k * C::LDB + n));
             fb[nb][2 * q] = v[0];
             fb[nb][2 * q + 1] = v[1];
           }
+          bsc[nb] = P::MX_ ? (int)(scl[C::BM + wn * C::TN + nb * 32 + (lane & 31)] >> sh) : 127;
         }
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
-          const uint8_t* p = sa + (wm * C::TM + mb * 32 + (lane & 31)) * LDKB + kk * 64 + 32 * (lane >> 5);
+          const uint8_t* p = sa + (wm * C::TM + mb * 32 + (lane & 31)) * LDKB + kk * 64 + 16 * (lane >> 5);
           const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 32);
           const i32x8 fa = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          const int asc = P::MX_ ? (int)(scl[wm * C::TM + mb * 32 + (lane & 31)] >> sh) : 127;
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, 127, 0, 127);
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, asc, 0,
+                                                                          bsc[nb]);
         }
         if (SPREAD && st_ok) store_stage8<C, P>(dst, nxa, nxb, kk, BKB / 64);
       }
       if (SPREAD && (full || kt + AHEAD < nk)) {
+        pol.load_s(kt + AHEAD, nxs);
         pol.load_a(kt + AHEAD, nxa);
         pol.load_b(kt + AHEAD, nxb);
       }
@@ -278,24 +359,24 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
     if constexpr (C::SETS == 2) {
       int kt = 0;
       for (; kt + AHEAD + 1 < nk; kt += 2) {
-        step(kt, ra1, rb1, true);
-        step(kt + 1, ra0, rb0, true);
+        step(kt, ra1, rb1, rs1, true);
+        step(kt + 1, ra0, rb0, rs0, true);
       }
-      if (kt < nk) step(kt, ra1, rb1, false);
-      if (kt + 1 < nk) step(kt + 1, ra0, rb0, false);
-      if (kt + 2 < nk) step(kt + 2, ra1, rb1, false);
-      if (kt + 3 < nk) step(kt + 3, ra0, rb0, false);
+      if (kt < nk) step(kt, ra1, rb1, rs1, false);
+      if (kt + 1 < nk) step(kt + 1, ra0, rb0, rs0, false);
+      if (kt + 2 < nk) step(kt + 2, ra1, rb1, rs1, false);
+      if (kt + 3 < nk) step(kt + 3, ra0, rb0, rs0, false);
     } else {
       int kt = 0;
-      for (; kt + AHEAD < nk; ++kt) step(kt, ra0, rb0, true);
-      for (; kt < nk; ++kt) step(kt, ra0, rb0, false);
+      for (; kt + AHEAD < nk; ++kt) step(kt, ra0, rb0, rs0, true);
+      for (; kt < nk; ++kt) step(kt, ra0, rb0, rs0, false);
     }
   }
   pol.epilogue(acc, wm, wn, lane, smem);
 }
 
-template <class C, bool SMALL>
-struct Gmm1F8K : Gmm1F8<C, SMALL> {
+template <class C, bool SMALL, bool MX = false>
+struct Gmm1F8K : Gmm1F8<C, SMALL, MX> {
   typedef C Cc;
   static constexpr int NTHR_ = C::NTHR;
 };
@@ -309,14 +390,24 @@ hipError_t launch8(const typename P::Args& args, int64_t logical_blocks, hipStre
   return hipGetLastError();
 }
 
-template <class C, bool SMALL>
+template <class C, bool SMALL, bool MX>
 hipError_t launch_one(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
-                      const float* tw, int64_t H, int64_t I, uint16_t* h, uint16_t* a, uint16_t* aw,
-                      hipStream_t stream) {
-  typedef Gmm1F8K<C, SMALL> P;
+                      const uint8_t* xs, const uint8_t* ws, const float* tw, int64_t H, int64_t I, uint16_t* h,
+                      uint16_t* a, uint16_t* aw, hipStream_t stream) {
+  typedef Gmm1F8K<C, SMALL, MX> P;
   const int nnt = (int)((I + C::BN / 2 - 1) / (C::BN / 2));
-  typename P::Args A{g, xq, dsx, wq, dsw, tw, g.T, H, I, h, a, aw, nnt};
+  typename P::Args A{g, xq, dsx, wq, dsw, tw, g.T, H, I, h, a, aw, nnt, xs, ws};
   return launch8<P>(A, (SMALL ? g.max_small : g.max_big) * nnt, stream);
+}
+
+template <bool MX>
+hipError_t launch_all(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
+                      const uint8_t* xs, const uint8_t* ws, const float* tw, int64_t H, int64_t I, uint16_t* h,
+                      uint16_t* a, uint16_t* aw, hipStream_t stream) {
+  if (g.narrow) return launch_one<Narrow8, true, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+  hipError_t e = launch_one<Big8, false, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+  if (e != hipSuccess) return e;
+  return launch_one<Small8, true, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
 }
 
 }  // namespace
@@ -324,10 +415,13 @@ hipError_t launch_one(const RowGroups& g, const uint8_t* xq, const float* dsx, c
 hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
                            const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
                            uint16_t* aw, hipStream_t stream) {
-  if (g.narrow) return launch_one<Narrow8, true>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
-  hipError_t e = launch_one<Big8, false>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
-  if (e != hipSuccess) return e;
-  return launch_one<Small8, true>(g, xq, dsx, wq, dsw, topk_w, H, I, h, a, aw, stream);
+  return launch_all<false>(g, xq, dsx, wq, dsw, nullptr, nullptr, topk_w, H, I, h, a, aw, stream);
+}
+
+hipError_t launch_gmm1_mx(const RowGroups& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                          uint16_t* aw, hipStream_t stream) {
+  return launch_all<true>(g, xq, nullptr, wq, nullptr, xs, ws, topk_w, H, I, h, a, aw, stream);
 }
 
 }  // namespace hmm

@@ -158,6 +158,18 @@ hipError_t launch_quant_rows_fp8(const uint16_t* x, int64_t T, int64_t H, uint8_
 int64_t quant_cols_chunks(int64_t H);  // pmax holds quant_cols_chunks(H) * E * N floats
 hipError_t launch_quant_cols_fp8(const uint16_t* w, int64_t E, int64_t H, int64_t N, float* pmax, uint8_t* wq,
                                  float* dsw, hipStream_t stream);
+// MX quantisation (quant.hip; MoeDistributeDispatchV2 case 5): blocks of 32
+// along H, one E8M0 exponent byte per block; H a multiple of 32.
+//   x [T][H] -> xq [T][H] E4M3, xs [T][H/32];  w [E][H][N] -> wq, ws [E][N][H/32]
+hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs,
+                                hipStream_t stream);
+hipError_t launch_quant_cols_mx(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws,
+                                hipStream_t stream);
+// MX up-projection + SwiGLU (gemm_fp8.hip): h = bf16(sum_k xq 2^xs . wq 2^ws) by the
+// scaled instruction, then as launch_gmm1_swiglu.  H must be a multiple of 128.
+hipError_t launch_gmm1_mx(const RowGroups& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                          uint16_t* aw, hipStream_t stream);
 // FP8 up-projection + SwiGLU (gemm_fp8.hip): h = bf16((xq[tok] . wq[e]) dsx[tok] dsw[e]), then as
 // launch_gmm1_swiglu.  H must be a multiple of 128.
 hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,

@@ -113,6 +113,109 @@ __global__ void __launch_bounds__(QT) quant_cols_apply(const uint16_t* __restric
   }
 }
 
+// ----------------------------------------------------------------------------- MX
+// MoeDistributeDispatchV2 case 5 (mx): per block of 32 elements along the
+// hidden dimension, shared exponent e = floor(log2 max|x|) - 8 (8: the exponent
+// of E4M3's largest value, 448 = 1.75 * 2^8), clamped to E8M0's [-127, 127],
+// -127 for an all-zero block; codes = round-to-nearest-even E4M3 of x * 2^-e,
+// saturated at +-448 (x * 2^-e reaches up to 2^9).  The exponent is stored as
+// its E8M0 byte e + 127.  floor(log2 m) of a positive float is its unbiased
+// exponent field (a subnormal m gives -127, which the clamp maps like any
+// exponent below -119); x * 2^-e is exact (a power-of-two product whose
+// result is either a normal float or, if subnormal, below E4M3's rounding
+// threshold 2^-10 either way).
+__device__ __forceinline__ int mx_exp(float absmax) {
+  const int field = (int)((__float_as_uint(absmax) >> 23) & 0xff);
+  const int e = absmax > 0.f ? field - 127 - 8 : -127;
+  return min(127, max(-127, e));
+}
+
+// 8 values times 2^-e -> 8 saturated E4M3 bytes
+__device__ __forceinline__ uint2 mx_codes8(const float (&v)[8], int e) {
+  const float s = __builtin_ldexpf(1.f, -e);  // e <= 120 for bf16 data: a normal float
+  float c[8], one[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = fminf(448.f, fmaxf(-448.f, v[j] * s));
+    one[j] = 1.f;
+  }
+  return to_e4m3x8(c, one);
+}
+
+// x [T][H] -> xq [T][H], xs [T][H/32]; four consecutive threads share a block
+__global__ void __launch_bounds__(QT) quant_rows_mx(const uint16_t* __restrict__ x, int64_t chunks, int64_t H,
+                                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  // chunks is a multiple of 4 and QT of 4: the four lanes of a block run the same iterations
+  for (int64_t c = (int64_t)blockIdx.x * QT + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * QT) {
+    float v[8];
+    unpack8(*reinterpret_cast<const u32x4*>(x + c * 8), v);
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int e = mx_exp(m);
+    *reinterpret_cast<uint2*>(xq + c * 8) = mx_codes8(v, e);
+    if ((c & 3) == 0) xs[c >> 2] = (uint8_t)(e + 127);
+  }
+}
+
+// w [E][H][N] -> wq [E][H][N], ws [E][N][H/32]: one thread per (expert, 32-row
+// block, 8 columns); consecutive threads take consecutive column chunks.
+__global__ void __launch_bounds__(QT) quant_cols_mx(const uint16_t* __restrict__ w, int64_t E, int64_t H,
+                                                    int64_t N, uint8_t* __restrict__ wq, uint8_t* __restrict__ ws) {
+  const int64_t n8s = N / 8, hbs = H / 32;
+  const int64_t g = (int64_t)blockIdx.x * QT + threadIdx.x;
+  if (g >= E * hbs * n8s) return;
+  const int64_t e = g / (hbs * n8s);
+  const int64_t rem = g - e * hbs * n8s;
+  const int64_t hb = rem / n8s, n8 = rem - hb * n8s;
+  const uint16_t* base = w + (e * H + hb * 32) * N + n8 * 8;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 32; ++r) {
+    float v[8];
+    unpack8(*reinterpret_cast<const u32x4*>(base + r * N), v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+  }
+  int ex[8];
+  float s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = mx_exp(m[j]);
+    s[j] = __builtin_ldexpf(1.f, -ex[j]);
+    ws[(e * N + n8 * 8 + j) * hbs + hb] = (uint8_t)(ex[j] + 127);
+  }
+  for (int r = 0; r < 32; ++r) {
+    float v[8], one[8];
+    unpack8(*reinterpret_cast<const u32x4*>(base + r * N), v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = fminf(448.f, fmaxf(-448.f, v[j] * s[j]));
+      one[j] = 1.f;
+    }
+    *reinterpret_cast<uint2*>(wq + (e * H + hb * 32 + r) * N + n8 * 8) = to_e4m3x8(v, one);
+  }
+}
+
+hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs,
+                                hipStream_t stream) {
+  const int64_t chunks = T * (H / 8);
+  if (chunks <= 0) return hipSuccess;
+  int64_t blocks = (chunks + QT - 1) / QT;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  hipLaunchKernelGGL(quant_rows_mx, dim3((unsigned)blocks), dim3(QT), 0, stream, x, chunks, H, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols_mx(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws,
+                                hipStream_t stream) {
+  const int64_t work = E * (H / 32) * (N / 8);
+  if (work <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_cols_mx, dim3((unsigned)((work + QT - 1) / QT)), dim3(QT), 0, stream, w, E, H, N, wq, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rows_fp8(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, float* dsx,
                                  hipStream_t stream) {
   if (T <= 0) return hipSuccess;

@@ -83,7 +83,7 @@ def _check_shared(x, shared_up_proj_weight, shared_down_proj_weight):
     return Is
 
 
-GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3}
+GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3}
 
 
 def _gmm1_code(gmm1_dtype):
@@ -207,7 +207,9 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     of range.  ``gmm1_dtype="fp8"`` runs the up-projection in FP8 E4M3: each
     token row and each (expert, column) of up_proj_weight is quantised with a
     dynamic per-row / per-column scale (H must then be a multiple of 128); the
-    rest of the forward and the whole backward stay bf16.  ``out_dtype=torch.float32``
+    rest of the forward and the whole backward stay bf16.  ``gmm1_dtype="mx"``
+    uses MX quantisation instead (one power-of-two scale per 32 elements along
+    H, for tokens and for each weight column).  ``out_dtype=torch.float32``
     is the accuracy mode: y (and dx and the weight gradients of the raw backward)
     are float32 and every intermediate is kept to about 16 significant bits
     (bf16 hi + lo pairs), for agreement with an unrounded computation to 1e-3;
@@ -280,6 +282,33 @@ def quantize_cols_fp8(w):
         _lib.check(lib.hmm_quant_cols_fp8(_ptr(w), E, H, N, _ptr(q), _ptr(ds), _ptr(work), ws.value,
                                           _stream(w.device)))
     return q, ds
+
+
+def quantize_rows_mx(x):
+    """MX quantisation of x bf16 [T,H] (blocks of 32): (codes uint8 [T,H], E8M0 exponents uint8 [T,H/32])."""
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [T,H] tensor on a HIP device")
+    x = _contig(x)
+    T, H = x.shape
+    q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    s = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.load().hmm_quant_rows_mx(_ptr(x), T, H, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def quantize_cols_mx(w):
+    """MX quantisation of w bf16 [E,H,N] in blocks of 32 rows per column:
+    (codes uint8 [E,H,N], E8M0 exponents uint8 [E,N,H/32])."""
+    if w.device.type != "cuda" or w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("w must be a bf16 [E,H,N] tensor on a HIP device")
+    w = _contig(w)
+    E, H, N = w.shape
+    q = torch.empty((E, H, N), dtype=torch.uint8, device=w.device)
+    s = torch.empty((E, N, H // 32), dtype=torch.uint8, device=w.device)
+    with torch.cuda.device(w.device):
+        _lib.check(_lib.load().hmm_quant_cols_mx(_ptr(w), E, H, N, _ptr(q), _ptr(s), _stream(w.device)))
+    return q, s
 
 
 def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16", shared_I=0):

@@ -45,6 +45,9 @@ WORKLOADS = {
     # FP8 up-projection variant with 1% outlier token rows
     "fp8": dict(T=16384, H=4096, I=1536, E=64, K=6, routing="uniform",
                 outlier_frac=0.01, outlier_scale=20.0, gmm1="fp8"),
+    # the same shape with the MX (32-block) quantised up-projection
+    "mx": dict(T=16384, H=4096, I=1536, E=64, K=6, routing="uniform",
+               outlier_frac=0.01, outlier_scale=20.0, gmm1="mx"),
 }
 
 
