@@ -135,6 +135,10 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
     // refill `nx` with step kt+3.  ``full``: all of those steps exist (the loop),
     // else each is checked (the tail).
     auto step = [&](int kt, u32x4 (&nxa)[C::CA], u32x4 (&nxb)[C::CB], bool full) {
+      // the backend's MFMA / LDS interleaving for small GEMM loops, where the
+      // policy asks for it (measured: the bf16 row-grouped products 1-6% faster;
+      // the weight gradients and the float32-mode products spill with it)
+      if constexpr (P::SCHED_HINT) __builtin_amdgcn_iglp_opt(0);
       const bool st_ok = full || kt + 1 < nk, ld_ok = full || kt + 3 < nk;
       if (ld_ok) {
         pol.index(kt + 3, rw);
@@ -295,6 +299,7 @@ template <class Cc, bool SMALL>
 struct RowTile {
   typedef Cc C;
   static constexpr bool RAW_INDEX = false;  // init takes the XCD-remapped logical index
+  static constexpr bool SCHED_HINT = true;  // see gemm_tile
   int e, row0, rows, n0, nk, nt;
   struct Raw {};  // K-major rows are fixed for the whole tile: no per-step indices
   __device__ __forceinline__ void fetch(int, Raw&) {}

@@ -62,6 +62,7 @@ __device__ __forceinline__ float* stage_weights(const RowGroups& g, const float*
 // h = x[tok] . W1[e] kept in float32; a = silu(g) u and aw = w a stored as [hi | lo].
 template <class Cc, bool SMALL>
 struct Gmm1F32 : RowTile<Cc, SMALL> {
+  static constexpr bool SCHED_HINT = false;
   static_assert(Cc::TN % 64 == 0, "every wave needs gate/up block pairs");
   typedef RowTile<Cc, SMALL> B_;
   typedef Cc C;
@@ -149,6 +150,7 @@ struct Gmm1F32 : RowTile<Cc, SMALL> {
 // ------------------------------------------------------------- down-projection
 template <class Cc, bool SMALL>
 struct Gmm2F32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  static constexpr bool SCHED_HINT = false;
   typedef RowTile<Cc, SMALL> B_;
   typedef Cc C;
   using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
@@ -207,6 +209,7 @@ struct Gmm2F32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
 // (row, N tile).
 template <class Cc, bool SMALL>
 struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  static constexpr bool SCHED_HINT = false;
   typedef RowTile<Cc, SMALL> B_;
   typedef Cc C;
   using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
@@ -331,6 +334,7 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
 // ------------------------------------------------------------- input_grad
 template <class Cc, bool SMALL>
 struct InputGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
+  static constexpr bool SCHED_HINT = false;
   typedef RowTile<Cc, SMALL> B_;
   typedef Cc C;
   using B_::e; using B_::row0; using B_::rows; using B_::nk; using B_::n0;
@@ -381,6 +385,7 @@ struct DwF32 : PlainCols<Cc> {
   typedef Cc C;
   using PlainCols<Cc>::ncol0;
   static constexpr bool RAW_INDEX = true;
+  static constexpr bool SCHED_HINT = false;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
   static constexpr int PASSES = MODE == 1 ? 2 : 3;
   static constexpr bool GATHER_A = MODE == 1, GATHER_B = MODE == 2;
