@@ -16,7 +16,8 @@
 // Tile shapes (each wave owns MB x NB accumulator blocks of 32 x 32):
 //   Big   256 x 256 x 64, 8 waves as 2 x 4, 128 x 64 per wave (one workgroup per CU,
 //         two waves per SIMD)
-//   Small  64 x 256 x 64, 4 waves as 1 x 4,  64 x 64 per wave (expert remainders, small experts)
+//   Small  64 x 256 x 64, 8 waves as 2 x 4,  32 x 64 per wave (expert remainders, small experts;
+//          eight waves: one workgroup fits a CU by LDS, and four waves left each SIMD one)
 //   Narrow 64 x  64 x 64, 4 waves as 2 x 2,  32 x 32 per wave (whole problem small: many
 //         workgroups instead of a few big tiles)
 // "rows" products run over the routing's tile tables: each expert's rows are

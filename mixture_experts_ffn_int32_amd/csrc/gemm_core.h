@@ -29,7 +29,7 @@ struct Cfg {
   static_assert(CA >= 1 && CB >= 1 && MB >= 1 && NB >= 1, "tile too small for the workgroup");
 };
 typedef Cfg<256, 256, 2, 4> Big;
-typedef Cfg<64, 256, 1, 4> Small;
+typedef Cfg<64, 256, 2, 4> Small;
 typedef Cfg<64, 64, 2, 2> Narrow;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -386,21 +386,33 @@ hipError_t launch_quad(const typename P1::Args& a1, int64_t b1, const typename P
 // fill(args, job, nnt) its policy arguments.
 template <template <class, bool> class P, class NarrowC, class Job, class NTiles, class Fill>
 hipError_t launch_rows_jobs(const Job* j, int n, NTiles ntiles, Fill fill, hipStream_t stream) {
-  auto run = [&](auto tag, bool big) -> hipError_t {
+  auto args = [&](auto tag, bool big, typename decltype(tag)::type::Args (&a)[2], int64_t (&blocks)[2]) {
     typedef typename decltype(tag)::type PP;
-    typename PP::Args a[2];
-    int64_t blocks[2] = {0, 0};
     for (int q = 0; q < n; ++q) {
       const int nnt = ntiles(j[q], PP::C::BN);
       fill(a[q], j[q], nnt);
       blocks[q] = (big ? j[q].g.max_big : j[q].g.max_small) * nnt;
     }
-    return n == 1 ? launch<PP>(a[0], blocks[0], stream) : launch_pair<PP, PP>(a[0], blocks[0], a[1], blocks[1], stream);
   };
-  if (j[0].g.narrow) return run(TypeTag<P<NarrowC, true>>{}, false);
-  const hipError_t e = run(TypeTag<P<Big, false>>{}, true);
-  if (e != hipSuccess) return e;
-  return run(TypeTag<P<Small, true>>{}, false);
+  if (j[0].g.narrow) {
+    typedef P<NarrowC, true> PN;
+    typename PN::Args a[2];
+    int64_t b[2] = {0, 0};
+    args(TypeTag<PN>{}, false, a, b);
+    return n == 1 ? launch<PN>(a[0], b[0], stream) : launch_pair<PN, PN>(a[0], b[0], a[1], b[1], stream);
+  }
+  // big and small tiles in one launch (both shapes have 8 waves): the small
+  // tiles come last and fill the CUs the big tiles' last round leaves idle
+  typedef P<Big, false> PB;
+  typedef P<Small, true> PS;
+  static_assert(Big::NTHR == Small::NTHR, "one workgroup size");
+  typename PB::Args ab[2];
+  typename PS::Args as[2];
+  int64_t bb[2] = {0, 0}, bs[2] = {0, 0};
+  args(TypeTag<PB>{}, true, ab, bb);
+  args(TypeTag<PS>{}, false, as, bs);
+  if (n == 1) return launch_pair<PB, PS>(ab[0], bb[0], as[0], bs[0], stream);
+  return launch_quad<PB, PB, PS, PS>(ab[0], bb[0], ab[1], bb[1], as[0], bs[0], as[1], bs[1], stream);
 }
 
 // big-tile launch, then small-tile launch, of a row-grouped product (n_ntiles
