@@ -254,7 +254,7 @@ def main():
                     help="only run a plain device copy of MIB MiB, 5 times (scale for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -58,7 +58,7 @@ typedef enum hmm_status {
   HMM_ERR_BAD_SHAPE = 2,             /* T,H,I,E,K inconsistent or out of the supported range */
   HMM_ERR_BAD_DTYPE = 3,             /* unknown or unsupported dtype selection */
   HMM_ERR_MISALIGNED = 4,            /* a device pointer is not 16-byte aligned */
-  HMM_ERR_UNSUPPORTED = 5,           /* valid problem this build does not implement */
+  HMM_ERR_UNSUPPORTED = 5,           /* valid problem the library does not implement */
   HMM_ERR_WORKSPACE_TOO_SMALL = 6,   /* workspace_bytes below the *_sizes figure */
   HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7,/* some topk_ids value is outside [0, E) */
   HMM_ERR_HIP = 8                    /* a HIP runtime call failed */
