@@ -264,7 +264,8 @@ hmm_status hmm_route(const hmm_problem* p, const int32_t* topk_ids, int32_t* cou
  *                       f32, one scale per (expert, column), the maximum taken
  *                       over H; needs hmm_quant_cols_workspace_size bytes of
  *                       workspace (column maxima per chunk of 256 rows).
- * T >= 0, E >= 1; H and N multiples of 8, positive; all arrays below 4 GiB.
+ * T >= 0, E >= 1; H and N multiples of 8, positive, N <= 2^24 (else
+ * HMM_ERR_UNSUPPORTED); all arrays below 4 GiB.
  * Pointers are device pointers, 16-byte aligned, caller-owned; errors as for
  * every other call, checked before any launch. */
 hmm_status hmm_quant_rows_fp8(const void* x, int64_t T, int64_t H, uint8_t* xq, float* descale, void* stream);
@@ -282,7 +283,8 @@ hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, ui
  *   hmm_quant_cols_mx: w bf16 [E,H,N] -> wq [E,H,N] E4M3 bytes, ws [E,N,H/32] E8M0
  *                      bytes (blocks of 32 rows of one column; column-major
  *                      exponents so a column's blocks are contiguous).
- * H a multiple of 32, N of 8; arrays below 4 GiB; device pointers, 16-byte aligned. */
+ * H a multiple of 32, N of 8 and at most 2^24; arrays below 4 GiB; device pointers,
+ * 16-byte aligned. */
 hmm_status hmm_quant_rows_mx(const void* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs, void* stream);
 hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws, void* stream);
 

@@ -473,6 +473,7 @@ hmm_status quant_dims(int64_t E, int64_t H, int64_t N) {
                 (long long)E, (long long)H, (long long)N);
   if (E * H * N > (int64_t)0xFFFFFF00 || E > (int64_t)0x7fffffff)
     return fail(HMM_ERR_UNSUPPORTED, "quantised array exceeds 4 GiB");
+  if (N > ((int64_t)1 << 24)) return fail(HMM_ERR_UNSUPPORTED, "N exceeds 2^24 columns (got %lld)", (long long)N);
   return HMM_OK;
 }
 }  // namespace
