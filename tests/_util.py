@@ -11,9 +11,21 @@ RTOL = 1e-2
 ATOL = 1e-2
 
 
+# pytest's capture manager (set by conftest): announce() writes past the
+# capture, so a long test shows its progress while it runs
+_capman = None
+
+
 def announce(msg):
-    """Name the case before a GPU step, flushed, so a crash log says what ran."""
-    print("[case] %s" % msg, flush=True)
+    """Name the case before a GPU step, flushed, so a crash log says what ran.
+
+    The line goes to the real stdout even while pytest captures output, so a
+    long test prints progress as it goes instead of only after it ends."""
+    if _capman is not None:
+        with _capman.global_and_fixture_disabled():
+            print("[case] %s" % msg, flush=True)
+    else:
+        print("[case] %s" % msg, flush=True)
     sys.stdout.flush()
 
 

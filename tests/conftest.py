@@ -13,6 +13,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds")
+    here = os.path.dirname(os.path.abspath(__file__))
+    if here not in sys.path:
+        sys.path.insert(0, here)
+    import _util
+    _util._capman = config.pluginmanager.getplugin("capturemanager")
 
 
 def pytest_collection_modifyitems(config, items):
