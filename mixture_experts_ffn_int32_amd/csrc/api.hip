@@ -250,8 +250,10 @@ hipEvent_t prof_event() {
   Prof& P = g_prof;
   if (P.used == P.pool.size()) {
     if (P.pool.size() >= PROF_MAX_EVENTS) return nullptr;
+    // timing-only events: no system-scope fence (cache writeback and invalidate)
+    // when recorded, which would add its own cost to every bracketed launch
     hipEvent_t ev;
-    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     P.pool.push_back(ev);
   }
   return P.pool[P.used++];

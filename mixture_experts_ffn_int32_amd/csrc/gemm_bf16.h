@@ -51,15 +51,15 @@ struct Gmm1 : RowTile<Cc, SMALL> {
       const int64_t col = (c8 < HALF) ? gi : A.I + gi;
       boff[i] = (uint32_t)((kr * 2 * A.I + col) * 2);
     }
-    nk = (int)(A.H / BK);
+    nk = (int)(A.H / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(kt * BK * 2 * ar->I * 2);
+    const uint32_t so = (uint32_t)(kt * C::BK * 2 * ar->I * 2);
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -72,7 +72,7 @@ struct Gmm1 : RowTile<Cc, SMALL> {
     float* wrow = reinterpret_cast<float*>(smem + C::BM * LD);
     const int tid = threadIdx.x;
     for (int t = tid; t < C::BM; t += C::NTHR)
-      wrow[t] = (t < rows) ? ar->tw[get(ar->g.sorted_slot + row0 + t, ar->g.coh)] : 0.f;
+      wrow[t] = this->row_weight(ar->tw, ar->g, t);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -144,20 +144,20 @@ struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
       const int64_t col = min((int64_t)(n0 + c8 * 8), A.H - 8);
       boff[i] = (uint32_t)((kr * A.H + col) * 2);
     }
-    nk = (int)(A.I / BK);
+    nk = (int)(A.I / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
     if constexpr (COH_A) {
 #pragma unroll
-      for (int i = 0; i < C::CA; ++i) r[i] = bload_coh(ra_, aoff[i], kt * BK * 2);
+      for (int i = 0; i < C::CA; ++i) r[i] = bload_coh(ra_, aoff[i], kt * C::BK * 2);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+      for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
     }
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(kt * BK * ar->H * 2);
+    const uint32_t so = (uint32_t)(kt * C::BK * ar->H * 2);
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -197,16 +197,16 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     this->template a_rows<true>(A.g, A.H, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
     this->b_rows(A.H, A.I, boff);
-    nk = (int)(A.H / BK);
+    nk = (int)(A.H / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
 #pragma unroll
-    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * C::BK * 2);
   }
   // G stays in float32: one wave column (TN columns) at a time it is staged in
   // LDS, then each thread takes 8 consecutive columns of one row, reads g, u and
@@ -223,7 +223,7 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     float* wrow = gst + C::BM * LDF;
     const int tid = threadIdx.x;
     for (int t = tid; t < C::BM; t += C::NTHR)
-      wrow[t] = (t < rows) ? ar->tw[get(ar->g.sorted_slot + row0 + t, ar->g.coh)] : 0.f;
+      wrow[t] = this->row_weight(ar->tw, ar->g, t);
     const int64_t I = ar->I;
     float part[PER];
 #pragma unroll
@@ -307,16 +307,16 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     this->template a_rows<false>(A.g, 2 * A.I, aoff);
     rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
     this->b_rows(2 * A.I, A.H, boff);
-    nk = (int)(2 * A.I / BK);
+    nk = (int)(2 * A.I / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
 #pragma unroll
-    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BK * 2);
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
     store_tile<C, InputGrad>(acc, wm, wn, lane, smem, ar->dxp, ar->H, row0, rows, n0, ar->H);
@@ -373,7 +373,7 @@ struct Dw : PlainCols<Cc> {
     n0 = c * C::BN;
     p0 = A.offsets[e];
     p1 = A.offsets[e + 1];
-    nk = (p1 - p0 + BK - 1) / BK;
+    nk = (p1 - p0 + C::BK - 1) / C::BK;
     ra_ = make_rsrc(A.A, A.a_rows * A.M * 2);
     rb_ = make_rsrc(A.B, A.b_rows * A.N * 2);
     return true;
@@ -386,7 +386,7 @@ struct Dw : PlainCols<Cc> {
     constexpr int CPR = R / 8;
 #pragma unroll
     for (int i = 0; i < CN; ++i) {
-      const int p = min(p0 + kt * BK + (tid + i * C::NTHR) / CPR, p1 - 1);
+      const int p = min(p0 + kt * C::BK + (tid + i * C::NTHR) / CPR, p1 - 1);
       raw[i] = ar->tok_of_row[p];
     }
   }
@@ -406,7 +406,7 @@ struct Dw : PlainCols<Cc> {
     for (int i = 0; i < CN; ++i) {
       const int c = tid + i * C::NTHR;
       const int kr = c / CPR, c8 = c % CPR;
-      const int p = p0 + kt * BK + kr;
+      const int p = p0 + kt * C::BK + kr;
       const uint32_t col = (uint32_t)c0 + c8 * 8;  // every offset fits 32 bits (resources < 4 GiB)
       uint32_t row = (uint32_t)p;
       if constexpr (GATHER) row = (uint32_t)raw[i];

@@ -11,12 +11,12 @@
 namespace hmm {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;   // pitch of a K-major LDS tile (elements)
-
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BK = BK_;                    // K step
+  static constexpr int LDK = BK + 8;                // pitch of a K-major LDS tile (elements)
+  static constexpr int KCH = BK / 8;                // 16-byte chunks per K-major row
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int MB = TM / 32, NB = TN / 32;  // 32x32 accumulator blocks per wave
@@ -35,17 +35,17 @@ typedef Cfg<64, 64, 2, 2> Narrow;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // LDS placement of 16-byte chunk c of a tile with R rows (K-major) or R columns (M/N-major)
-template <bool KMAJ, int R>
+template <class C, bool KMAJ, int R>
 __device__ __forceinline__ int lds_chunk_off(int c) {
-  if constexpr (KMAJ) return (c >> 3) * LDK + (c & 7) * 8;               // [R rows][64 k]
-  else return (c / (R / 8)) * (R + 32) + (c % (R / 8)) * 8;              // [64 k][R cols]
+  if constexpr (KMAJ) return (int)((unsigned)c / C::KCH) * C::LDK + (int)((unsigned)c % C::KCH) * 8;  // [R rows][BK k]
+  else return (c / (R / 8)) * (R + 32) + (c % (R / 8)) * 8;              // [BK k][R cols]
 }
 
 // MFMA operand fragment (8 bf16 along k) of a 32-row block starting at row0
-template <bool KMAJ, int R>
+template <class C, bool KMAJ, int R>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row0, int kk, int lane) {
   if constexpr (KMAJ) {
-    const uint16_t* p = tile + (row0 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5);
+    const uint16_t* p = tile + (row0 + (lane & 31)) * C::LDK + kk * 16 + 8 * (lane >> 5);
     return *reinterpret_cast<const bf16x8*>(p);
   } else {
     constexpr int LD = R + 32;
@@ -73,10 +73,10 @@ __device__ __forceinline__ void store_stage(uint16_t* st, const u32x4 (&ra)[C::C
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < C::CA; ++i)
-    *reinterpret_cast<u32x4*>(st + lds_chunk_off<P::A_KMAJ, C::BM>(tid + i * C::NTHR)) = ra[i];
+    *reinterpret_cast<u32x4*>(st + lds_chunk_off<C, P::A_KMAJ, C::BM>(tid + i * C::NTHR)) = ra[i];
 #pragma unroll
   for (int i = 0; i < C::CB; ++i)
-    *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
+    *reinterpret_cast<u32x4*>(st + C::A_ELEMS + lds_chunk_off<C, P::B_KMAJ, C::BN>(tid + i * C::NTHR)) = rb[i];
 }
 
 // The main loop of every bf16 product for tile ``idx`` (the index the policy's
@@ -147,14 +147,14 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
       uint16_t* dst = smem + ((kt + 1) & 1) * C::STAGE;
       const uint16_t* sa = smem + (kt & 1) * C::STAGE;
       const uint16_t* sb = sa + C::A_ELEMS;
-      constexpr int NKK = BK / 16;
+      constexpr int NKK = C::BK / 16;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         bf16x8 fa[C::MB], fb[C::NB];
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<P::A_KMAJ, C::BM>(sa, wm * C::TM + mb * 32, kk, lane);
+        for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<C, P::A_KMAJ, C::BM>(sa, wm * C::TM + mb * 32, kk, lane);
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<P::B_KMAJ, C::BN>(sb, P::ncol0(wn, nb), kk, lane);
+        for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<C, P::B_KMAJ, C::BN>(sb, P::ncol0(wn, nb), kk, lane);
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -164,10 +164,10 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
           const int t = threadIdx.x;
 #pragma unroll
           for (int i = kk; i < C::CA; i += NKK)
-            *reinterpret_cast<u32x4*>(dst + lds_chunk_off<P::A_KMAJ, C::BM>(t + i * C::NTHR)) = nxa[i];
+            *reinterpret_cast<u32x4*>(dst + lds_chunk_off<C, P::A_KMAJ, C::BM>(t + i * C::NTHR)) = nxa[i];
 #pragma unroll
           for (int i = kk; i < C::CB; i += NKK)
-            *reinterpret_cast<u32x4*>(dst + C::A_ELEMS + lds_chunk_off<P::B_KMAJ, C::BN>(t + i * C::NTHR)) = nxb[i];
+            *reinterpret_cast<u32x4*>(dst + C::A_ELEMS + lds_chunk_off<C, P::B_KMAJ, C::BN>(t + i * C::NTHR)) = nxb[i];
         }
       }
       if (ld_ok) {
@@ -309,13 +309,34 @@ struct RowTile {
     if (logical >= R * n_ntiles) return false;
     int j;
     raster(logical, R, n_ntiles, j, nt);
-    if (j >= get(g.tiles + (SMALL ? 1 : 0), g.coh)) return false;
+    // the count and the entry are loaded together (entries j < R are in bounds;
+    // one past the count holds stale data and is not used)
     const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-    e = get(tab + 2 * j, g.coh);
+    const int cnt = get(g.tiles + (SMALL ? 1 : 0), g.coh);
+    const int32_t w = get(tab + 2 * j, g.coh);
     row0 = get(tab + 2 * j + 1, g.coh);
-    rows = min(C::BM, get(g.offsets + e + 1, g.coh) - row0);
+    if (j >= cnt) return false;
+    e = tile_expert(w);
+    rows = min(C::BM, tile_rows(w));
     n0 = nt * C::BN;
+    if constexpr (EARLY_SLOT) {
+      const int t = threadIdx.x;
+      slot_own = (t < C::BM && t < rows) ? get(g.sorted_slot + row0 + t, g.coh) : 0;
+    }
     return true;
+  }
+  // Small tiles: thread t < BM loads the routing slot of row t with the tile's
+  // other row indices, so the epilogue's weight load no longer waits for a
+  // dependent index load (a few microseconds of a small problem's launch).
+  static constexpr bool EARLY_SLOT = C::BM <= 64;
+  static_assert(!EARLY_SLOT || C::NTHR >= C::BM, "one thread per row of a small tile");
+  int slot_own;
+  // topk weight of the tile's row t (0 past the expert's rows); on small tiles
+  // only for t == threadIdx.x
+  __device__ __forceinline__ float row_weight(const float* tw, const RowGroups& g, int t) const {
+    if (t >= rows) return 0.f;
+    if constexpr (EARLY_SLOT) return tw[slot_own];
+    else return tw[get(g.sorted_slot + row0 + t, g.coh)];
   }
   // K-major A rows of this tile: byte offset of chunk i (the tile's rows past the
   // expert's end repeat its last row; their results are not stored)
@@ -325,9 +346,9 @@ struct RowTile {
 #pragma unroll
     for (int i = 0; i < C::CA; ++i) {
       const int c = tid + i * C::NTHR;
-      const int p = row0 + min(c >> 3, rows - 1);
+      const int p = row0 + min((int)((unsigned)c / C::KCH), rows - 1);
       const int64_t row = GATHER ? (int64_t)get(g.tok_of_row + p, g.coh) : (int64_t)p;
-      off[i] = (uint32_t)((row * ld + (c & 7) * 8) * 2);
+      off[i] = (uint32_t)((row * ld + (int)((unsigned)c % C::KCH) * 8) * 2);
     }
   }
   // K-major B rows n0 + r (clamped to N - 1), offsets within the expert's slice
@@ -336,8 +357,8 @@ struct RowTile {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) {
       const int c = tid + i * C::NTHR;
-      const int64_t n = min((int64_t)(n0 + (c >> 3)), N - 1);
-      off[i] = (uint32_t)((n * ld + (c & 7) * 8) * 2);
+      const int64_t n = min((int64_t)(n0 + (int)((unsigned)c / C::KCH)), N - 1);
+      off[i] = (uint32_t)((n * ld + (int)((unsigned)c % C::KCH) * 8) * 2);
     }
   }
 };

@@ -104,15 +104,15 @@ struct Gmm1F32 : RowTile<Cc, SMALL> {
       const int64_t col = (b & 1) ? A.I + gi : gi;
       boff[i] = (uint32_t)((kr * 2 * A.I + col) * 2);
     }
-    nk = (int)(A.H / BK);
+    nk = (int)(A.H / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(kt * BK * 2 * ar->I * 2);
+    const uint32_t so = (uint32_t)(kt * C::BK * 2 * ar->I * 2);
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -182,15 +182,15 @@ struct Gmm2F32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
       const int64_t col = min((int64_t)(n0 + c8 * 8), A.H - 8);
       boff[i] = (uint32_t)((kr * A.H + col) * 2);
     }
-    nk = (int)(2 * A.I / BK);
+    nk = (int)(2 * A.I / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(((int64_t)kt * BK % ar->I) * ar->H * 2);  // W2 read once per half of K
+    const uint32_t so = (uint32_t)(((int64_t)kt * C::BK % ar->I) * ar->H * 2);  // W2 read once per half of K
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -238,15 +238,15 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     this->template a_rows<true>(A.g, 2 * A.H, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
     this->b_rows(A.H, A.I, boff);
-    nk = (int)(2 * A.H / BK);
+    nk = (int)(2 * A.H / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(((int64_t)kt * BK % ar->H) * 2);
+    const uint32_t so = (uint32_t)(((int64_t)kt * C::BK % ar->H) * 2);
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -358,15 +358,15 @@ struct InputGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
     this->template a_rows<false>(A.g, 4 * A.I, aoff);
     rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
     this->b_rows(2 * A.I, A.H, boff);
-    nk = (int)(4 * A.I / BK);
+    nk = (int)(4 * A.I / C::BK);
     return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BK * 2);
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
-    const uint32_t so = (uint32_t)(((int64_t)kt * BK % (2 * ar->I)) * 2);
+    const uint32_t so = (uint32_t)(((int64_t)kt * C::BK % (2 * ar->I)) * 2);
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], so);
   }
@@ -424,7 +424,7 @@ struct DwF32 : PlainCols<Cc> {
     n0 = c * C::BN;
     p0 = A.offsets[e];
     p1 = A.offsets[e + 1];
-    nk1 = (p1 - p0 + BK - 1) / BK;
+    nk1 = (p1 - p0 + C::BK - 1) / C::BK;
     nk = PASSES * nk1;
     ra_ = make_rsrc(A.A, A.a_rows * A.lda * 2);
     rb_ = make_rsrc(A.B, A.b_rows * A.ldb * 2);
@@ -440,7 +440,7 @@ struct DwF32 : PlainCols<Cc> {
     constexpr int CPR = R / 8;
 #pragma unroll
     for (int i = 0; i < CN; ++i) {
-      const int p = min(p0 + kk * BK + (tid + i * C::NTHR) / CPR, p1 - 1);
+      const int p = min(p0 + kk * C::BK + (tid + i * C::NTHR) / CPR, p1 - 1);
       raw[i] = ar->tok_of_row[p];
     }
   }
@@ -459,7 +459,7 @@ struct DwF32 : PlainCols<Cc> {
     for (int i = 0; i < CN; ++i) {
       const int c = tid + i * C::NTHR;
       const int kr = c / CPR, c8 = c % CPR;
-      const int p = p0 + kk * BK + kr;
+      const int p = p0 + kk * C::BK + kr;
       const uint32_t col = (uint32_t)c0 + c8 * 8;  // every offset fits 32 bits (resources < 4 GiB)
       uint32_t row = (uint32_t)p;
       if constexpr (GATHER) row = (uint32_t)raw[i];

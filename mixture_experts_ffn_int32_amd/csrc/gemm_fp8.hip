@@ -93,11 +93,13 @@ struct Gmm1F8 {
     if (logical >= R * A.n_ntiles) return false;
     int j;
     raster(logical, R, A.n_ntiles, j, nt);
-    if (j >= g.tiles[SMALL ? 1 : 0]) return false;
     const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-    e = tab[2 * j];
+    const int cnt = g.tiles[SMALL ? 1 : 0];
+    const int32_t w = tab[2 * j];
     row0 = tab[2 * j + 1];
-    rows = min(C::BM, g.offsets[e + 1] - row0);
+    if (j >= cnt) return false;
+    e = tile_expert(w);
+    rows = min(C::BM, tile_rows(w));
     i0 = nt * (C::BN / 2);
     const int tid = threadIdx.x;
     ra_ = make_rsrc(A.xq, A.T * A.H);

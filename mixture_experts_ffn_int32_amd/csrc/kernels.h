@@ -17,6 +17,13 @@ constexpr int RT_ONE_MAX_EXPERTS = 256;
 
 constexpr int TILE_BIG = 256;         // rows of a big row-grouped product tile
 constexpr int TILE_SMALL = 64;        // rows of a small tile (expert remainders, small experts)
+// A tile table entry is two int32 words: (expert | rows << 16, first row).  The
+// tile's row count rides with its expert id (E <= 1024, rows <= 256), so a
+// product reads one entry and not also the expert's end in the offsets array: a
+// dependent load fewer before its first data load.
+__host__ __device__ inline int32_t tile_word(int e, int rows) { return (int32_t)(e | (rows << 16)); }
+__host__ __device__ inline int tile_expert(int32_t w) { return w & 0xffff; }
+__host__ __device__ inline int tile_rows(int32_t w) { return (int)((uint32_t)w >> 16); }
 
 // Upper bounds of the tile-table lengths for S routed rows over E experts.
 // An expert with c rows gets floor(c/256) big tiles, one more if the remainder

@@ -36,13 +36,14 @@ __device__ __forceinline__ void shared_entry(const SharedTables& st, int64_t i) 
   st.idx[i] = (int32_t)i;
   st.ones[i] = 1.f;
   if (i < nbig) {
-    st.tiles[4 + 2 * i] = 0;
+    st.tiles[4 + 2 * i] = tile_word(0, (int)min((int64_t)TILE_BIG, st.T - i * TILE_BIG));
     st.tiles[4 + 2 * i + 1] = (int32_t)(i * TILE_BIG);
   }
   if (i < nsmall) {
     int32_t* small = st.tiles + 4 + 2 * (int64_t)st.max_big;
-    small[2 * i] = 0;
-    small[2 * i + 1] = (int32_t)(nbig * TILE_BIG + i * TILE_SMALL);
+    const int64_t r0 = nbig * TILE_BIG + i * TILE_SMALL;
+    small[2 * i] = tile_word(0, (int)min((int64_t)TILE_SMALL, st.T - r0));
+    small[2 * i + 1] = (int32_t)r0;
   }
 }
 __device__ __forceinline__ void shared_header(const SharedTables& st) {
@@ -89,8 +90,9 @@ __global__ void __launch_bounds__(RT_THREADS) route_hist(const int32_t* __restri
 // covered by TILE_BIG-row tiles, and a remainder of at most TILE_BIG/2 rows by
 // TILE_SMALL-row tiles (a larger remainder gets one more, partly filled, big
 // tile).  With big_on = 0 (small problems) every row goes to TILE_SMALL-row
-// tiles.  Layout: tiles[0] = #big, tiles[1] = #small, then max_big (expert,
-// first row) pairs from tiles[4], then the small pairs from tiles[4 + 2*max_big].
+// tiles.  Layout: tiles[0] = #big, tiles[1] = #small, then max_big entries
+// (expert | rows << 16, first row) from tiles[4], then the small entries from
+// tiles[4 + 2*max_big].
 __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __restrict__ blockhist,
                                                               const int32_t* __restrict__ blockerr, int nblk,
                                                               int E, int max_big, int big_on,
@@ -139,13 +141,13 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
     counts[e] = c;
     offsets[e] = off;
     for (int i = 0; i < nbig; ++i) {
-      tiles[4 + 2 * (b0 + i)] = e;
+      tiles[4 + 2 * (b0 + i)] = tile_word(e, min(TILE_BIG, c - i * TILE_BIG));
       tiles[4 + 2 * (b0 + i) + 1] = off + i * TILE_BIG;
     }
     int32_t* small = tiles + 4 + 2 * max_big;
     const int srow = off + nbig * TILE_BIG;
     for (int i = 0; i < nsmall; ++i) {
-      small[2 * (s0 + i)] = e;
+      small[2 * (s0 + i)] = tile_word(e, min(TILE_SMALL, c - nbig * TILE_BIG - i * TILE_SMALL));
       small[2 * (s0 + i) + 1] = srow + i * TILE_SMALL;
     }
   }

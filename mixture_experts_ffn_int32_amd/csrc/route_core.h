@@ -138,13 +138,13 @@ __device__ __forceinline__ void route_block(RouteLds<NT>& L, const int32_t* __re
       put<COH>(offsets + tid, off);
       offs[tid] = off;
       for (int i = 0; i < nbig; ++i) {
-        put<COH>(tiles + 4 + 2 * (b0 + i), tid);
+        put<COH>(tiles + 4 + 2 * (b0 + i), tile_word(tid, min(TILE_BIG, c - i * TILE_BIG)));
         put<COH>(tiles + 4 + 2 * (b0 + i) + 1, off + i * TILE_BIG);
       }
       int32_t* small = tiles + 4 + 2 * max_big;
       const int srow = off + nbig * TILE_BIG;
       for (int i = 0; i < nsmall; ++i) {
-        put<COH>(small + 2 * (sm0 + i), tid);
+        put<COH>(small + 2 * (sm0 + i), tile_word(tid, min(TILE_SMALL, c - nbig * TILE_BIG - i * TILE_SMALL)));
         put<COH>(small + 2 * (sm0 + i) + 1, srow + i * TILE_SMALL);
       }
     }
