@@ -84,6 +84,14 @@ with C_F8 = 2^14; measured errors of such an instruction on random E4M3 data
 stay below 3300 * 2^-24 * sqrt(sum of squares), and below 1400 for Gaussian
 data (a margin of about 5 over the worst case seen).
 
+The per-group variant (``gmm1="group"``) quantises tokens in groups of 128
+along the hidden dimension and the weight in blocks of 128 rows per column
+(see ``quant``).  Reading of the product: each group's E4M3 products are summed
+as the FP8 instruction does (the bound above, per group), the group sum is
+scaled by its token and weight descales in float32, and the scaled group sums
+are added in float32 in group order; the oracle sums exactly and carries those
+three errors in its deviation.
+
 The MX variant (``gmm1="mx"``) quantises tokens and weights in blocks of 32
 along the hidden dimension with a power-of-two scale per block (see
 ``quant``); the up-projection sums the dequantised products exactly, and the
@@ -94,7 +102,8 @@ powers of two, so they add no rounding of their own).
 import numpy as np
 
 from .numerics import round_bf16, sigmoid, silu
-from .quant import quantize_columns, quantize_columns_mx, quantize_rows, quantize_rows_mx
+from .quant import (GROUP, quantize_columns, quantize_columns_groups, quantize_columns_mx, quantize_rows,
+                    quantize_rows_groups, quantize_rows_mx)
 from .routing import check_ids
 
 U32 = 2.0 ** -24     # unit roundoff of float32
@@ -123,7 +132,7 @@ class MoEFFN:
                  dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None):
         if mode not in ("pure", "faithful"):
             raise ValueError(mode)
-        if gmm1 not in ("bf16", "fp8", "mx"):
+        if gmm1 not in ("bf16", "fp8", "mx", "group"):
             raise ValueError(gmm1)
         self.x = np.asarray(x)
         self.ids = np.asarray(topk_ids, dtype=np.int64)
@@ -181,6 +190,8 @@ class MoEFFN:
         if e not in self._w1q:
             if self.gmm1 == "mx":   # (q, e): dequantised value q * 2^e, blocks of 32 rows
                 self._w1q[e] = quantize_columns_mx(self.W1[e])
+            elif self.gmm1 == "group":  # (q, scale, descale [H / 128, 2I])
+                self._w1q[e] = quantize_columns_groups(self.W1[e])
             else:                   # (q, scale, descale)
                 self._w1q[e] = quantize_columns(self.W1[e])
         return self._w1q[e]
@@ -202,6 +213,25 @@ class MoEFFN:
             h = (q @ wqc) * scale
             sq = (q * q) @ (wqc * wqc)
             eps = (acc_eps(sq, self.H) + C_F8 * U32 * np.sqrt(sq)) * scale + 2 * C_EL * U32 * np.abs(h)
+        elif self.gmm1 == "group":
+            q, _, dsx = quantize_rows_groups(xrows)
+            wq, _, dsw = self._W1q(e)
+            wqc, dswc = wq[:, cols], dsw[:, cols].astype(np.float64)
+            ng = self.H // GROUP
+            h = np.zeros((q.shape[0], wqc.shape[1]))
+            eps = np.zeros_like(h)
+            terms_sq = np.zeros_like(h)
+            for g in range(ng):                                     # groups in contraction order
+                k = slice(g * GROUP, (g + 1) * GROUP)
+                part = q[:, k] @ wqc[k]                             # exact sum of the group's E4M3 products
+                sq = (q[:, k] * q[:, k]) @ (wqc[k] * wqc[k])
+                sc = dsx[:, g].astype(np.float64)[:, None] * dswc[g][None, :]
+                term = part * sc
+                h += term
+                terms_sq += term * term
+                # the group sum's instruction error, then its scaling (two float32 products)
+                eps += (acc_eps(sq, GROUP) + C_F8 * U32 * np.sqrt(sq)) * np.abs(sc) + 2 * C_EL * U32 * np.abs(term)
+            eps += acc_eps(terms_sq, ng)                            # the float32 running sum over the groups
         elif self.gmm1 == "mx":
             q, ex = quantize_rows_mx(xrows)
             wq, ew = self._W1q(e)

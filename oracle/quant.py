@@ -112,3 +112,52 @@ def quantize_columns_mx(w):
     e = mx_exponent(np.max(np.abs(wb), axis=1))
     q = round_e4m3(wb / np.exp2(e)[:, None, :].astype(np.float64))
     return q.reshape(H, N), e
+
+
+# ---------------------------------------------------------------- per group
+# MoeDistributeDispatchV2, case 4 (quantMode 3, "pergroup" / "pertile" dynamic
+# quantisation): the same formula as case 3 (scale = dstTypeMax / max|x|, codes
+# = cast(x * scale), 1 / scale travelling with them), taken over a group of a
+# token row instead of the whole row.  Readings (the page leaves them open):
+# * a group is 128 consecutive elements along the hidden (contraction)
+#   dimension; the page gives no size, and 128 divides every hidden size here;
+# * the cast and the all-zero rule are case 3's (E4M3, 448; an all-zero group
+#   gets scale 1 and zero codes);
+# * the up-projection weight is quantised by the same rule per (expert, column,
+#   block of 128 rows along the hidden dimension), so each group of the
+#   contraction has one token scale and one weight scale per output column.
+
+GROUP = 128
+
+
+def quantize_rows_groups(x, group=GROUP):
+    """Per-group dynamic quantisation of ``x`` [..., H] in groups of ``group`` along H.
+
+    Returns (q [..., H] E4M3 values as float64, scale [..., H / group] float32,
+    descale = 1 / scale float32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    H = x32.shape[-1]
+    if H % group:
+        raise ValueError("H must be a multiple of %d" % group)
+    xg = x32.reshape(x32.shape[:-1] + (H // group, group))
+    scale = _scale_from_absmax(np.max(np.abs(xg), axis=-1))
+    prod = (xg * scale[..., None]).astype(np.float32)
+    q = round_e4m3(prod.astype(np.float64)).reshape(x32.shape)
+    descale = (np.float32(1.0) / scale).astype(np.float32)
+    return q, scale, descale
+
+
+def quantize_columns_groups(w, group=GROUP):
+    """Per-(block of ``group`` rows, column) quantisation of a weight ``w`` [H, N].
+
+    Returns (q [H, N], scale [H / group, N], descale [H / group, N])."""
+    w32 = np.asarray(w, dtype=np.float32)
+    H, N = w32.shape
+    if H % group:
+        raise ValueError("H must be a multiple of %d" % group)
+    wg = w32.reshape(H // group, group, N)
+    scale = _scale_from_absmax(np.max(np.abs(wg), axis=1))
+    prod = (wg * scale[:, None, :]).astype(np.float32)
+    q = round_e4m3(prod.astype(np.float64)).reshape(H, N)
+    descale = (np.float32(1.0) / scale).astype(np.float32)
+    return q, scale, descale

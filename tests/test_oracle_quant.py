@@ -199,3 +199,96 @@ def test_mx_up_projection_error_is_bounded():
         dw = dev(W1[e], np.exp2(ew).repeat(32, 0))
         bound = dx @ (np.abs(W1[e]) + dw) + np.abs(x) @ dw
         assert np.all(np.abs(mmx.up(e, x) - m16.up(e, x)) <= bound)
+
+
+# ----------------------------------------------------------------------------- per group (Dispatch case 4)
+from oracle.quant import GROUP, quantize_columns_groups, quantize_rows_groups  # noqa: E402
+
+
+def test_group_quant_matches_torch_float32_ops_and_cast():
+    """Every 128-element group of a row gets 448 / max|group| in float32 and the E4M3 cast of
+    x * scale; the groups are independent (magnitudes differ by up to 2^12 across them)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((16, 512)) * np.exp2(rng.integers(-6, 6, (16, 4))).repeat(GROUP, 1)
+    x = round_bf16(x).astype(np.float32)
+    q, scale, descale = quantize_rows_groups(x)
+    tx = torch.from_numpy(x).reshape(16, 4, GROUP)
+    tscale = torch.tensor(448.0, dtype=torch.float32) / tx.abs().amax(dim=2)
+    assert np.array_equal(scale, tscale.numpy())
+    tq = (tx * tscale[:, :, None]).to(torch.float8_e4m3fn).to(torch.float64).reshape(16, 512).numpy()
+    assert np.array_equal(q, tq)
+    assert np.array_equal(descale, (1.0 / tscale).numpy())
+    # the largest magnitude of every group lands on +-448
+    assert np.all(np.abs(q.reshape(16, 4, GROUP)).max(axis=2) == 448.0)
+
+
+def test_group_quant_special_cases():
+    """One group spanning the row is the per-token rule; an all-zero group gets scale 1."""
+    rng = np.random.default_rng(12)
+    x = round_bf16(rng.standard_normal((5, 256))).astype(np.float32)
+    q1, s1, d1 = quantize_rows_groups(x, group=256)
+    q0, s0, d0 = quantize_rows(x)
+    assert np.array_equal(q1, q0) and np.array_equal(s1[:, 0], s0) and np.array_equal(d1[:, 0], d0)
+    x[2, 128:] = 0.0
+    q, s, d = quantize_rows_groups(x)
+    assert s[2, 1] == 1.0 and d[2, 1] == 1.0 and not np.any(q[2, 128:])
+    w = round_bf16(rng.standard_normal((256, 24))).astype(np.float32)
+    qw, sw, dw = quantize_columns_groups(w)
+    assert sw.shape == (2, 24)
+    for b in range(2):   # a block of rows per column is that column's per-column rule
+        qb, sb, db = quantize_columns(w[b * GROUP:(b + 1) * GROUP])
+        assert np.array_equal(qw[b * GROUP:(b + 1) * GROUP], qb) and np.array_equal(sw[b], sb)
+
+
+def test_group_up_projection_equals_bf16_when_quantisation_is_exact():
+    """Entries +-2^j whose group (token) or block (weight column) maximum is a power of two
+    quantise exactly: scale = 448 / 2^m and the codes are 448 * 2^(j - m), exact in E4M3.
+    The descaled group sums then equal x . W1 up to the float32 rounding of the descales, so
+    the per-group and bf16 up-projections agree to ~1e-6.  Group maxima differ from group to
+    group and from row to row, so a scale applied to the wrong group would show."""
+    rng = np.random.default_rng(13)
+    T, H, I, E, K = 6, 256, 8, 2, 2
+    ng = H // GROUP
+    gmax = np.exp2(-rng.integers(0, 5, (T, ng)))
+    x = np.where(rng.random((T, H)) < 0.5, -1.0, 1.0) * 2.0 ** -rng.integers(0, 4, (T, H)) * gmax.repeat(GROUP, 1)
+    x[:, 0::GROUP] = gmax
+    bmax = np.exp2(-rng.integers(0, 5, (E, ng, 2 * I)))
+    W1 = np.where(rng.random((E, H, 2 * I)) < 0.5, -1.0, 1.0) * 2.0 ** -rng.integers(0, 4, (E, H, 2 * I))
+    W1 = W1 * bmax.repeat(GROUP, 1)
+    W1[:, 0::GROUP, :] = bmax
+    W2 = rng.standard_normal((E, I, H))
+    ids = np.array([[0, 1]] * T)
+    w = np.full((T, K), 0.5, np.float32)
+    mg = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="group")
+    m16 = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="bf16")
+    for e in range(E):
+        hg, h16 = mg.up(e, x), m16.up(e, x)
+        assert np.allclose(hg, h16, rtol=1e-6, atol=1e-9 * np.abs(h16).max())
+    q, s, d = quantize_rows_groups(x)   # the codes carry x exactly, up to the float32 descale
+    assert np.allclose(q * d.astype(np.float64).repeat(GROUP, 1), x, rtol=2e-7, atol=0)
+
+
+def test_group_up_projection_error_is_bounded():
+    """Generic data: each E4M3 code has relative error <= 2^-4 of its group's scaled value
+    (2^-10 of the group maximum below the normal range), so h moves by a bounded amount;
+    groups of very different magnitude are not dragged down to the largest one."""
+    rng = np.random.default_rng(14)
+    T, H, I, E, K = 8, 384, 16, 3, 2
+    x = round_bf16(rng.standard_normal((T, H)) * np.exp2(rng.integers(-8, 8, (T, H // GROUP))).repeat(GROUP, 1))
+    W1 = round_bf16(rng.standard_normal((E, H, 2 * I)) / 8)
+    W2 = round_bf16(rng.standard_normal((E, I, H)) / 4)
+    ids = np.array([rng.choice(E, K, replace=False) for _ in range(T)])
+    w = np.full((T, K), 0.5, np.float32)
+    mg = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="group")
+    m16 = MoEFFN(x, ids, w, W1, W2, mode="pure", gmm1="bf16")
+
+    def dev(v, gmax):
+        return 2.0 ** -4 * np.abs(v) + gmax * 2.0 ** -18
+
+    gx = np.abs(x).reshape(T, -1, GROUP).max(axis=2).repeat(GROUP, 1)
+    dx = dev(x, gx)
+    for e in range(E):
+        gw = np.abs(W1[e]).reshape(-1, GROUP, 2 * I).max(axis=1).repeat(GROUP, 0)
+        dw = dev(W1[e], gw)
+        bound = dx @ (np.abs(W1[e]) + dw) + np.abs(x) @ dw
+        assert np.all(np.abs(mg.up(e, x) - m16.up(e, x)) <= bound * (1 + 1e-6))
