@@ -288,6 +288,22 @@ hmm_status hmm_quant_cols_fp8(const void* w, int64_t E, int64_t H, int64_t N, ui
 hmm_status hmm_quant_rows_mx(const void* x, int64_t T, int64_t H, uint8_t* xq, uint8_t* xs, void* stream);
 hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws, void* stream);
 
+/* Per-group dynamic quantisation, MoeDistributeDispatchV2, function description,
+ * case 4 (quantMode 3): case 3's rule over groups of 128 consecutive hidden
+ * elements (the page gives no group size): scale = 448 / max|group| in float32
+ * (1 for an all-zero group), code = round-to-nearest-even E4M3 of v * scale,
+ * and the float32 descale 1 / scale is kept.  The weight gets the rule per
+ * (expert, column, block of 128 rows), so each group of the contraction has one
+ * token descale and one weight descale per column.
+ *   hmm_quant_rows_group: x bf16 [T,H] -> xq [T,H] E4M3 bytes, dsx [T,H/128] float32.
+ *   hmm_quant_cols_group: w bf16 [E,H,N] -> wq [E,H,N] E4M3 bytes, dsw [E,H/128,N] float32.
+ * H a multiple of 128, N of 8 and at most 2^24; arrays below 4 GiB; device pointers,
+ * 16-byte aligned; T = 0 is a no-op.  The library's forward does not consume these
+ * yet (gmm1_dtype has no per-group value). */
+hmm_status hmm_quant_rows_group(const void* x, int64_t T, int64_t H, uint8_t* xq, float* dsx, void* stream);
+hmm_status hmm_quant_cols_group(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
+                                void* stream);
+
 /* Names of statuses, and the calling thread's last error text. */
 const char* hmm_status_string(hmm_status s);
 const char* hmm_last_error_message(void);

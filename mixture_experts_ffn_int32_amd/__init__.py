@@ -8,8 +8,9 @@ load the library; the first call does, and raises if it has not been built.
 """
 
 from .moe import (HyperMegaMoEFunction, backward_from_saved, forward_with_saved, hyper_mega_moe,  # noqa: F401
-                  quantize_cols_fp8, quantize_cols_mx, quantize_rows_fp8, quantize_rows_mx, route,
-                  saved_views)
+                  quantize_cols_fp8, quantize_cols_group, quantize_cols_mx, quantize_rows_fp8,
+                  quantize_rows_group, quantize_rows_mx, route, saved_views)
 
 __all__ = ["hyper_mega_moe", "HyperMegaMoEFunction", "route", "forward_with_saved", "backward_from_saved",
-           "saved_views", "quantize_rows_fp8", "quantize_cols_fp8", "quantize_rows_mx", "quantize_cols_mx"]
+           "saved_views", "quantize_rows_fp8", "quantize_cols_fp8", "quantize_rows_mx", "quantize_cols_mx",
+           "quantize_rows_group", "quantize_cols_group"]

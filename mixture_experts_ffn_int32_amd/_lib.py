@@ -34,6 +34,7 @@ EXPORTS = (
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
     "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
     "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared", "hmm_quant_rows_mx", "hmm_quant_cols_mx",
+    "hmm_quant_rows_group", "hmm_quant_cols_group",
 )
 
 
@@ -74,6 +75,8 @@ _SIGS = {
     "hmm_quant_cols_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _SZ, _P],
     "hmm_quant_rows_mx": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_quant_cols_mx": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "hmm_quant_rows_group": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "hmm_quant_cols_group": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_status_string": [ctypes.c_int],
     "hmm_last_error_message": [],
     "hmm_build_info": [],

@@ -901,6 +901,29 @@ hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uin
   return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
 }
 
+hmm_status hmm_quant_rows_group(const void* x, int64_t T, int64_t H, uint8_t* xq, float* dsx, void* stream) {
+  if (T < 0 || T > (int64_t)0x7fffffff) return fail(HMM_ERR_BAD_SHAPE, "T must be in [0, 2^31) (got %lld)", (long long)T);
+  if (H < 128 || H % 128) return fail(HMM_ERR_BAD_SHAPE, "H must be a positive multiple of 128 (got %lld)", (long long)H);
+  hmm_status s = quant_dims(T > 0 ? T : 1, H, 8);
+  if (s != HMM_OK) return s;
+  const bool ne = T > 0;
+  if ((s = need(x, ne, "x")) || (s = need(xq, ne, "xq")) || (s = need(dsx, ne, "dsx"))) return s;
+  Stage stage("quant_x_group", (hipStream_t)stream);
+  const hipError_t e = hmm::launch_quant_rows_group((const uint16_t*)x, T, H, xq, dsx, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "token quantisation launch");
+}
+
+hmm_status hmm_quant_cols_group(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
+                                void* stream) {
+  hmm_status s = quant_dims(E, H, N);
+  if (s != HMM_OK) return s;
+  if (H % 128) return fail(HMM_ERR_BAD_SHAPE, "H must be a multiple of 128 (got %lld)", (long long)H);
+  if ((s = need(w, true, "w")) || (s = need(wq, true, "wq")) || (s = need(dsw, true, "dsw"))) return s;
+  Stage stage("quant_w1_group", (hipStream_t)stream);
+  const hipError_t e = hmm::launch_quant_cols_group((const uint16_t*)w, E, H, N, wq, dsw, (hipStream_t)stream);
+  return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
+}
+
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
                        const void* up_w, const void* down_w, void* y, void* saved, size_t saved_bytes,
                        void* workspace, size_t workspace_bytes, void* stream) {

@@ -172,6 +172,13 @@ hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t T, int64_t H, uint8_t
                                 hipStream_t stream);
 hipError_t launch_quant_cols_mx(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, uint8_t* ws,
                                 hipStream_t stream);
+// Per-group quantisation (quant.hip; MoeDistributeDispatchV2 case 4): groups of
+// 128 along H with a float32 scale each; H a multiple of 128.
+//   x [T][H] -> xq [T][H] E4M3, dsx [T][H/128];  w [E][H][N] -> wq, dsw [E][H/128][N]
+hipError_t launch_quant_rows_group(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, float* dsx,
+                                   hipStream_t stream);
+hipError_t launch_quant_cols_group(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
+                                   hipStream_t stream);
 // MX up-projection + SwiGLU (gemm_fp8.hip): h = bf16(sum_k xq 2^xs . wq 2^ws) by the
 // scaled instruction, then as launch_gmm1_swiglu.  H must be a multiple of 128.
 hipError_t launch_gmm1_mx(const RowGroups& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,

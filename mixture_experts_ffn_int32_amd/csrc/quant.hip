@@ -377,3 +377,91 @@ hipError_t launch_quant_cols_fp8(const uint16_t* w, int64_t E, int64_t H, int64_
 }
 
 }  // namespace hmm
+
+// ---------------------------------------------------------------- per group
+// MoeDistributeDispatchV2 case 4 (per-group dynamic quantisation): case 3's
+// rule over groups of QGROUP = 128 consecutive hidden elements of a token row,
+// and, for the weight, over blocks of 128 rows of one column.
+
+namespace hmm {
+
+constexpr int QGROUP = 128;
+
+// xq[t] = e4m3(x[t] * scale_g), dsx[t][g] = 1 / scale_g.  16 consecutive lanes
+// hold one group (8 elements each); H is a multiple of 128, so H / 8 is a
+// multiple of 16 and a group's lanes are active together.
+__global__ void __launch_bounds__(QT) quant_rows_group(const uint16_t* __restrict__ x, int64_t chunks, int64_t H,
+                                                       uint8_t* __restrict__ xq, float* __restrict__ dsx) {
+  for (int64_t c = (int64_t)blockIdx.x * QT + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * QT) {
+    float v[8];
+    unpack8(*reinterpret_cast<const u32x4*>(x + c * 8), v);
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+    const float sx = scale_of(m);
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = sx;
+    *reinterpret_cast<uint2*>(xq + c * 8) = to_e4m3x8(v, s);
+    if ((c & 15) == 0) dsx[c >> 4] = 1.f / sx;  // chunk c of the flat [T][H] array starts group c / 16
+  }
+}
+
+// wq[e][k][n] = e4m3(w[e][k][n] * scale), dsw[e][k / 128][n] = 1 / scale, the
+// scale from the column's 128-row block.  One thread per (expert, block, 8-column
+// chunk), consecutive threads on consecutive chunks (each row's loads of a wave
+// are one contiguous 1 KiB run); the block is read twice (its maxima, then its codes).
+__global__ void __launch_bounds__(QT) quant_cols_group(const uint16_t* __restrict__ w, int64_t E, int64_t H,
+                                                       int64_t N, uint8_t* __restrict__ wq, float* __restrict__ dsw) {
+  const int64_t n8s = N / 8, hb = H / QGROUP;
+  const int64_t total = E * hb * n8s;
+  for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
+    const int64_t c = i % n8s, r = i / n8s;
+    const int64_t b = r % hb, e = r / hb;
+    const int64_t off = (e * H + b * QGROUP) * N + c * 8;   // element (e, 128 b, 8 c)
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < QGROUP; ++k) {
+      float v[8];
+      unpack8(*reinterpret_cast<const u32x4*>(w + off + k * N), v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+    }
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = scale_of(m[j]);
+#pragma unroll 8
+    for (int k = 0; k < QGROUP; ++k) {
+      float v[8];
+      unpack8(*reinterpret_cast<const u32x4*>(w + off + k * N), v);
+      *reinterpret_cast<uint2*>(wq + off + k * N) = to_e4m3x8(v, s);
+    }
+    float* d = dsw + (e * hb + b) * N + c * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = 1.f / s[j];
+  }
+}
+
+hipError_t launch_quant_rows_group(const uint16_t* x, int64_t T, int64_t H, uint8_t* xq, float* dsx,
+                                   hipStream_t stream) {
+  const int64_t chunks = T * (H / 8);
+  if (chunks <= 0) return hipSuccess;
+  int64_t blocks = (chunks + QT - 1) / QT;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  hipLaunchKernelGGL(quant_rows_group, dim3((unsigned)blocks), dim3(QT), 0, stream, x, chunks, H, xq, dsx);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols_group(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
+                                   hipStream_t stream) {
+  const int64_t total = E * (H / QGROUP) * (N / 8);
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + QT - 1) / QT;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  hipLaunchKernelGGL(quant_cols_group, dim3((unsigned)blocks), dim3(QT), 0, stream, w, E, H, N, wq, dsw);
+  return hipGetLastError();
+}
+
+}  // namespace hmm

@@ -311,6 +311,34 @@ def quantize_cols_mx(w):
     return q, s
 
 
+def quantize_rows_group(x):
+    """Per-group quantisation of x bf16 [T,H] (groups of 128 along H):
+    (codes uint8 [T,H], float32 descales [T,H/128])."""
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [T,H] tensor on a HIP device")
+    x = _contig(x)
+    T, H = x.shape
+    q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    d = torch.empty((T, H // 128), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.load().hmm_quant_rows_group(_ptr(x), T, H, _ptr(q), _ptr(d), _stream(x.device)))
+    return q, d
+
+
+def quantize_cols_group(w):
+    """Per-group quantisation of w bf16 [E,H,N] in blocks of 128 rows per column:
+    (codes uint8 [E,H,N], float32 descales [E,H/128,N])."""
+    if w.device.type != "cuda" or w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("w must be a bf16 [E,H,N] tensor on a HIP device")
+    w = _contig(w)
+    E, H, N = w.shape
+    q = torch.empty((E, H, N), dtype=torch.uint8, device=w.device)
+    d = torch.empty((E, H // 128, N), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        _lib.check(_lib.load().hmm_quant_cols_group(_ptr(w), E, H, N, _ptr(q), _ptr(d), _stream(w.device)))
+    return q, d
+
+
 def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16", shared_I=0):
     """Typed views of the arrays a forward recorded in its saved buffer.
 

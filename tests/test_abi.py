@@ -160,3 +160,18 @@ def test_shared_expert_sizes_and_entry_points(lib):
                                    ok, ok, 1 << 40, z) == _lib.HMM_ERR_NULL_POINTER
     assert lib.hmm_forward_shared(ctypes.byref(base), ok, ok, ok, ok, ok, z, z, ok, ok, 16, ok, 16, z) == \
         _lib.HMM_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_group_quantisers_reject_bad_shapes_and_pointers(lib):
+    """Per-group quantisers: H must be a multiple of 128 (the group), N of 8; NULL
+    pointers are rejected; T = 0 is a no-op.  All before any HIP call."""
+    z = ctypes.c_void_p(0)
+    ok = ctypes.c_void_p(0x1000)
+    assert lib.hmm_quant_rows_group(ok, 4, 192, ok, ok, z) == _lib.HMM_ERR_BAD_SHAPE
+    assert lib.hmm_quant_rows_group(ok, -1, 256, ok, ok, z) == _lib.HMM_ERR_BAD_SHAPE
+    assert lib.hmm_quant_rows_group(z, 4, 256, ok, ok, z) == _lib.HMM_ERR_NULL_POINTER
+    assert lib.hmm_quant_rows_group(ok, 4, 256, ok, z, z) == _lib.HMM_ERR_NULL_POINTER
+    assert lib.hmm_quant_rows_group(z, 0, 256, z, z, z) == _lib.HMM_OK
+    assert lib.hmm_quant_cols_group(ok, 2, 192, 64, ok, ok, z) == _lib.HMM_ERR_BAD_SHAPE
+    assert lib.hmm_quant_cols_group(ok, 2, 256, 60, ok, ok, z) == _lib.HMM_ERR_BAD_SHAPE
+    assert lib.hmm_quant_cols_group(ok, 2, 256, 64, z, ok, z) == _lib.HMM_ERR_NULL_POINTER
