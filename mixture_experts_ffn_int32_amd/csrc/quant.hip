@@ -410,37 +410,53 @@ __global__ void __launch_bounds__(QT) quant_rows_group(const uint16_t* __restric
 }
 
 // wq[e][k][n] = e4m3(w[e][k][n] * scale), dsw[e][k / 128][n] = 1 / scale, the
-// scale from the column's 128-row block.  One thread per (expert, block, 8-column
-// chunk), consecutive threads on consecutive chunks (each row's loads of a wave
-// are one contiguous 1 KiB run); the block is read twice (its maxima, then its codes).
-__global__ void __launch_bounds__(QT) quant_cols_group(const uint16_t* __restrict__ w, int64_t E, int64_t H,
-                                                       int64_t N, uint8_t* __restrict__ wq, float* __restrict__ dsw) {
-  const int64_t n8s = N / 8, hb = H / QGROUP;
-  const int64_t total = E * hb * n8s;
-  for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
-    const int64_t c = i % n8s, r = i / n8s;
-    const int64_t b = r % hb, e = r / hb;
-    const int64_t off = (e * H + b * QGROUP) * N + c * 8;   // element (e, 128 b, 8 c)
-    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = 0; k < QGROUP; ++k) {
+// scale from the column's 128-row block.  A wave takes a 128-column by 128-row
+// tile (the column quantisers' wave tile, four 32-row slabs): the column maxima
+// of the slabs, met in two lane shuffles, then the slabs again for the codes
+// (the second read finds the tile in L2).
+__global__ void __launch_bounds__(64 * QW) quant_cols_group(const uint16_t* __restrict__ w, int64_t E, int64_t H,
+                                                            int64_t N, uint8_t* __restrict__ wq,
+                                                            float* __restrict__ dsw) {
+  const int64_t n8s = N / 8, cgs = (n8s + QG - 1) / QG, hb = H / QGROUP;
+  const int64_t task = wave_task();
+  if (task >= E * cgs * hb) return;
+  const ColTask t = col_task(task, cgs, hb);
+  const ColLane l = col_lane(t.cg, n8s);
+  const uint32_t pitch = (uint32_t)N * 2;
+  const char* wb = reinterpret_cast<const char*>(w + (t.e * H + t.hg * QGROUP) * N);
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < QGROUP / 32; ++sl) {
+    const char* row = wb + (int64_t)sl * 32 * pitch;
+    u32x4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[i] = load16(row, l.n8 * 16u + (uint32_t)(l.rs * 8 + i) * pitch);
+    rows_absmax(raw, m);
+  }
+  wave_colmax(m);
+  float s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = scale_of(m[j]);
+  if (l.rs == 0 && l.ok) {
+    float4* out = reinterpret_cast<float4*>(dsw + (t.e * hb + t.hg) * N + l.n8 * 8);
+    out[0] = make_float4(1.f / s[0], 1.f / s[1], 1.f / s[2], 1.f / s[3]);
+    out[1] = make_float4(1.f / s[4], 1.f / s[5], 1.f / s[6], 1.f / s[7]);
+  }
+  uint8_t* qb = wq + (t.e * H + t.hg * QGROUP) * N;
+#pragma unroll
+  for (int sl = 0; sl < QGROUP / 32; ++sl) {
+    const char* row = wb + (int64_t)sl * 32 * pitch;
+    uint8_t* qrow = qb + (int64_t)sl * 32 * N;
+    u32x4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[i] = load16(row, l.n8 * 16u + (uint32_t)(l.rs * 8 + i) * pitch);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       float v[8];
-      unpack8(*reinterpret_cast<const u32x4*>(w + off + k * N), v);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+      unpack8(raw[i], v);
+      if (l.ok)
+        *reinterpret_cast<uint2*>(qrow + (l.n8 * 8u + (uint32_t)(l.rs * 8 + i) * (uint32_t)N)) = to_e4m3x8(v, s);
     }
-    float s[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] = scale_of(m[j]);
-#pragma unroll 8
-    for (int k = 0; k < QGROUP; ++k) {
-      float v[8];
-      unpack8(*reinterpret_cast<const u32x4*>(w + off + k * N), v);
-      *reinterpret_cast<uint2*>(wq + off + k * N) = to_e4m3x8(v, s);
-    }
-    float* d = dsw + (e * hb + b) * N + c * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = 1.f / s[j];
   }
 }
 
@@ -456,11 +472,11 @@ hipError_t launch_quant_rows_group(const uint16_t* x, int64_t T, int64_t H, uint
 
 hipError_t launch_quant_cols_group(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
                                    hipStream_t stream) {
-  const int64_t total = E * (H / QGROUP) * (N / 8);
-  if (total <= 0) return hipSuccess;
-  int64_t blocks = (total + QT - 1) / QT;
-  if (blocks > (1 << 20)) blocks = 1 << 20;
-  hipLaunchKernelGGL(quant_cols_group, dim3((unsigned)blocks), dim3(QT), 0, stream, w, E, H, N, wq, dsw);
+  const int64_t tasks = E * ((N / 8 + QG - 1) / QG) * (H / QGROUP);
+  if (tasks <= 0) return hipSuccess;
+  if ((tasks + QW - 1) / QW > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_cols_group, dim3((unsigned)((tasks + QW - 1) / QW)), dim3(64 * QW), 0, stream, w, E, H, N,
+                     wq, dsw);
   return hipGetLastError();
 }
 
