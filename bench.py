@@ -11,10 +11,11 @@ Prints ONE JSON line on stdout; details go to stderr.
 
 Timing: W untimed warm-up steps (the first one's time is reported as
 first_step_ms), then K steps between two synchronisations, timed with HIP
-events on the stream the kernels run on -> ms_per_step and tokens/s.  A
-second pass of K steps records HIP events around every kernel launch (the
-library's stage timing) and gives each kernel's average duration for the
-roofline figures.  The CPU oracle is then timed on a bounded sample of the
+events on the stream the kernels run on -> ms_per_step and tokens/s.  A second
+pass of K steps, with an event after each call, gives the forward and backward
+times (fwd_ms, bwd_ms).  A third pass of K steps records HIP events around
+every kernel launch (the library's stage timing) and gives each kernel's
+average duration for the roofline figures.  The CPU oracle is then timed on a bounded sample of the
 same workload on the host's cores.
 """
 
@@ -197,6 +198,22 @@ class Runner:
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    def timed_split(self, n):
+        """Average forward and backward times (ms) over n steps, an event after each call."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
+        ev[0].record(self.stream)
+        for i in range(n):
+            self._lib.check(self.fwd(*self.fargs))
+            ev[2 * i + 1].record(self.stream)
+            self._lib.check(self.bwd(*self.bargs))
+            ev[2 * i + 2].record(self.stream)
+        torch.cuda.synchronize()
+        f = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)) / n
+        b = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n)) / n
+        return f, b
+
 
 def cpu_baseline(spec, seed, budget_s=12.0):
     """Time the oracle (faithful fwd + full bwd) on a bounded prefix of the workload's tokens."""
@@ -295,6 +312,10 @@ def main():
     log("[bench] %d steps: %.4f ms/step (host wall %.4f ms/step), first step %.3f ms"
         % (args.steps, ms, wall * 1e3 / args.steps, first_ms))
 
+    # forward and backward separately (an event between them in every step)
+    fwd_ms, bwd_ms = r.timed_split(args.steps)
+    log("[bench] forward %.4f ms, backward %.4f ms per step" % (fwd_ms, bwd_ms))
+
     # second pass: per-kernel device time from the library's stage events
     _lib.profile_read()
     _lib.profile_enable(True)
@@ -345,6 +366,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "first_step_ms": round(first_ms, 4),
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
