@@ -7,7 +7,7 @@ synthetic input already resident in HBM, through the C ABI of libhmm.
 
 Prints ONE JSON line on stdout; details go to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8|mx]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8|mx|group]
 
 Timing: W untimed warm-up steps (the first one's time is reported as
 first_step_ms), then K steps between two synchronisations, timed with HIP
@@ -71,7 +71,7 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
     Is > 0: a shared expert of that width (one more group of all T rows)."""
     S = T * K
     eb = 4 if f32 else 2
-    if stage in ("gmm1_fp8_swiglu", "gmm1_mx_swiglu"):
+    if stage in ("gmm1_fp8_swiglu", "gmm1_mx_swiglu", "gmm1_group_swiglu"):
         return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
     flops = {
         "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
@@ -105,6 +105,9 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
         # MX quantisers: the bf16 operand once, its codes and one exponent byte per 32 elements
         "quant_x_mx": T * H * 2 + T * H + T * H // 32,
         "quant_w1_mx": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * H // 32,
+        # per group of 128 along H: one float32 descale per token row / weight column
+        "quant_x_group": T * H * 2 + T * H + T * (H // 128) * 4,
+        "quant_w1_group": E * H * 2 * I * 2 + E * H * 2 * I + E * (H // 128) * 2 * I * 4,
     }
     if stage in nbytes:
         return "hbm", nbytes[stage], "GB/s", PEAK_HBM_GBS
@@ -139,7 +142,8 @@ class Runner:
         self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
         flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
-        gmm1 = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3}[spec.get("gmm1", "bf16")]
+        gmm1 = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3,
+                "group": _lib.HMM_FP8_E4M3_GROUP}[spec.get("gmm1", "bf16")]
         f32 = out_dtype == "f32"
         Is = spec.get("shared_I", 0)
         self.prob = _lib.Problem(T, H, I, E, K, _lib.HMM_F32 if f32 else _lib.HMM_BF16, gmm1, flags, Is)
@@ -371,7 +375,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "bf16+fp8", "mx": "bf16+mxfp8"}.get(
+        "dtype": {"fp8": "bf16+fp8", "mx": "bf16+mxfp8", "group": "bf16+fp8"}.get(
             gmm1_kind, "bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,

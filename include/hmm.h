@@ -68,7 +68,8 @@ typedef enum hmm_dtype {
   HMM_BF16 = 0,
   HMM_F32 = 1,
   HMM_FP8_E4M3 = 2,    /* E4M3 with one float32 scale per token row / weight column */
-  HMM_MXFP8_E4M3 = 3   /* E4M3 with one E8M0 exponent per 32 elements along H (MX) */
+  HMM_MXFP8_E4M3 = 3,  /* E4M3 with one E8M0 exponent per 32 elements along H (MX) */
+  HMM_FP8_E4M3_GROUP = 4  /* E4M3 with one float32 scale per 128 elements along H */
 } hmm_dtype;
 
 /* Check topk_ids: the routing kernel raises a flag for an id outside [0, E)
@@ -122,6 +123,11 @@ typedef enum hmm_dtype {
  *               per block (tokens per row, the weight per (expert, column)), see
  *               hmm_quant_rows_mx; the block exponents feed the scaled FP8
  *               matrix instruction directly.  H a multiple of 128.
+ *               HMM_FP8_E4M3_GROUP: the per-group quantisation of
+ *               MoeDistributeDispatchV2 case 4 (see hmm_quant_rows_group): each
+ *               128-deep group's E4M3 sums are scaled by its token and weight
+ *               descales and added in group order.  Runs the whole problem on
+ *               64x64 tiles (HMM_FLAG_TILES_LARGE is rejected).  H a multiple of 128.
  *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward.
  *   shared_I    0, or the intermediate size Is of a shared expert (a multiple of
  *               64 in [64, 65536]): then the calls are hmm_forward_shared and
@@ -298,8 +304,8 @@ hmm_status hmm_quant_cols_mx(const void* w, int64_t E, int64_t H, int64_t N, uin
  *   hmm_quant_rows_group: x bf16 [T,H] -> xq [T,H] E4M3 bytes, dsx [T,H/128] float32.
  *   hmm_quant_cols_group: w bf16 [E,H,N] -> wq [E,H,N] E4M3 bytes, dsw [E,H/128,N] float32.
  * H a multiple of 128, N of 8 and at most 2^24; arrays below 4 GiB; device pointers,
- * 16-byte aligned; T = 0 is a no-op.  The library's forward does not consume these
- * yet (gmm1_dtype has no per-group value). */
+ * 16-byte aligned; T = 0 is a no-op.  hmm_forward runs the same kernels with
+ * gmm1_dtype HMM_FP8_E4M3_GROUP. */
 hmm_status hmm_quant_rows_group(const void* x, int64_t T, int64_t H, uint8_t* xq, float* dsx, void* stream);
 hmm_status hmm_quant_cols_group(const void* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
                                 void* stream);

@@ -21,7 +21,7 @@ HMM_ERR_WORKSPACE_TOO_SMALL = 6
 HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7
 HMM_ERR_HIP = 8
 
-HMM_BF16, HMM_F32, HMM_FP8_E4M3, HMM_MXFP8_E4M3 = 0, 1, 2, 3
+HMM_BF16, HMM_F32, HMM_FP8_E4M3, HMM_MXFP8_E4M3, HMM_FP8_E4M3_GROUP = 0, 1, 2, 3, 4
 HMM_FLAG_VALIDATE_IDS = 1
 HMM_FLAG_TILES_LARGE = 2
 HMM_FLAG_TILES_NARROW = 4

@@ -44,6 +44,7 @@ struct Dims {
   bool small;  // small-problem mode (narrow tiles; see kernels.h)
   bool fp8;    // FP8 E4M3 up-projection (per-token scales, or MX block exponents)
   bool mx;     // ... with MX block exponents
+  bool group;  // ... with per-group (128 along H) float scales
   bool f32;    // float32 outputs (accuracy mode)
   bool fused;  // small problem whose forward runs as one fused launch (fused.hip)
 };
@@ -68,9 +69,13 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
   if (p->out_dtype != HMM_BF16 && p->out_dtype != HMM_F32)
     return fail(HMM_ERR_BAD_DTYPE, "out_dtype must be HMM_BF16 or HMM_F32 (got %d)", p->out_dtype);
-  if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3 && p->gmm1_dtype != HMM_MXFP8_E4M3)
-    return fail(HMM_ERR_BAD_DTYPE, "gmm1_dtype must be HMM_BF16, HMM_FP8_E4M3 or HMM_MXFP8_E4M3 (got %d)",
+  if (p->gmm1_dtype != HMM_BF16 && p->gmm1_dtype != HMM_FP8_E4M3 && p->gmm1_dtype != HMM_MXFP8_E4M3 &&
+      p->gmm1_dtype != HMM_FP8_E4M3_GROUP)
+    return fail(HMM_ERR_BAD_DTYPE,
+                "gmm1_dtype must be HMM_BF16, HMM_FP8_E4M3, HMM_MXFP8_E4M3 or HMM_FP8_E4M3_GROUP (got %d)",
                 p->gmm1_dtype);
+  if (p->gmm1_dtype == HMM_FP8_E4M3_GROUP && (p->flags & HMM_FLAG_TILES_LARGE))
+    return fail(HMM_ERR_UNSUPPORTED, "HMM_FP8_E4M3_GROUP runs on 64x64 tiles: HMM_FLAG_TILES_LARGE is not supported");
   {
     // every array a product reads through a buffer resource must stay below 4 GiB
     // (the float32-output mode reads [hi | lo] operands of twice the width)
@@ -93,10 +98,13 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->S = p->T * p->K;
   d->Is = p->shared_I;
   d->shared = p->shared_I != 0;
-  d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3 || p->gmm1_dtype == HMM_MXFP8_E4M3;
+  d->fp8 = p->gmm1_dtype == HMM_FP8_E4M3 || p->gmm1_dtype == HMM_MXFP8_E4M3 || p->gmm1_dtype == HMM_FP8_E4M3_GROUP;
   d->mx = p->gmm1_dtype == HMM_MXFP8_E4M3;
+  d->group = p->gmm1_dtype == HMM_FP8_E4M3_GROUP;
   d->f32 = p->out_dtype == HMM_F32;
-  d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
+  // the per-group product has 64x64 tiles only (two accumulator sets), and the
+  // routing's tile tables then hold every row in 64-row tiles
+  d->small = ((p->flags & HMM_FLAG_TILES_NARROW) || d->group) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
   d->fused = d->small && !d->fp8 && !d->f32 && !d->shared && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
@@ -193,6 +201,9 @@ FwdWork fwd_work(const Dims& d) {
   if (d.mx) {  // E8M0 block exponents: [T][H/32] and [E][2I][H/32]
     w.xs = o;   o += up(d.T * (d.H / 32));
     w.ws = o;   o += up(d.E * 2 * d.I * (d.H / 32));
+  } else if (d.group) {  // float32 descales: [T][H/128] and [E][H/128][2I]
+    w.dsx = o;  o += up(d.T * (d.H / 128) * 4);
+    w.dsw = o;  o += up(d.E * (d.H / 128) * 2 * d.I * 4);
   } else if (d.fp8) {
     w.dsx = o;  o += up(d.T * 4);
     w.dsw = o;  o += up(d.E * 2 * d.I * 4);
@@ -646,6 +657,26 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
     {
       Stage stage("gmm1_mx_swiglu", st);
       e = hmm::launch_gmm1_mx(g, xq, xs, wq, ws, topk_weights, d.H, d.I, h, a, aw, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  } else if (d.group) {
+    uint8_t* xq = at<uint8_t>(workspace, W.xq);
+    uint8_t* wq = at<uint8_t>(workspace, W.wq);
+    float* dsx = at<float>(workspace, W.dsx);
+    float* dsw = at<float>(workspace, W.dsw);
+    {
+      Stage stage("quant_x_group", st);
+      e = hmm::launch_quant_rows_group((const uint16_t*)x, d.T, d.H, xq, dsx, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "token quantisation launch");
+    {
+      Stage stage("quant_w1_group", st);
+      e = hmm::launch_quant_cols_group((const uint16_t*)up_w, d.E, d.H, 2 * d.I, wq, dsw, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
+    {
+      Stage stage("gmm1_group_swiglu", st);
+      e = hmm::launch_gmm1_group(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
     }
     if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
   } else if (d.fp8) {

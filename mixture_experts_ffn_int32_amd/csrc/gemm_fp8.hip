@@ -62,8 +62,12 @@ __device__ __forceinline__ int acc_row8(int wm, int mb, int r, int lane) {
   return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-template <class C, bool SMALL, bool MX = false>
+// Q: 0 per-token scales (applied in the epilogue), 1 MX block exponents (fed to
+// the instruction), 2 per-group float descales (applied to each K step's sums)
+template <class C, bool SMALL, int Q = 0>
 struct Gmm1F8 {
+  static constexpr bool MX = Q == 1;
+  static constexpr bool GROUP = Q == 2;
   struct Args {
     RowGroups g;
     const uint8_t* xq;   // [T][H] E4M3
@@ -76,11 +80,16 @@ struct Gmm1F8 {
     int n_ntiles;
     const uint8_t* xs = nullptr;  // [T][H/32] E8M0 (MX mode)
     const uint8_t* ws = nullptr;  // [E][2I][H/32] E8M0 (MX mode)
+    const float* gsx = nullptr;   // [T][H/128] token descales (per-group mode)
+    const float* gsw = nullptr;   // [E][H/128][2I] weight descales (per-group mode)
   };
-  // MX: one exponent word per tile row and column per step, SCR per thread
+  // MX: one exponent word per tile row and column per step; per group: one float
+  // descale per tile row and column per step (a K step is one 128-deep group)
   static constexpr bool MX_ = MX;
-  static constexpr int SCR = MX ? (C::BM + C::BN + C::NTHR - 1) / C::NTHR : 1;
-  static constexpr int SC_BYTES = MX ? (C::BM + C::BN) * 4 : 0;
+  static constexpr bool GROUP_ = GROUP;
+  static constexpr bool STAGED = MX || GROUP;
+  static constexpr int SCR = STAGED ? (C::BM + C::BN + C::NTHR - 1) / C::NTHR : 1;
+  static constexpr int SC_BYTES = STAGED ? (C::BM + C::BN) * 4 : 0;
   const Args* ar;
   int e, row0, rows, nt, i0, nk;
   rsrc_t ra_, rb_, rsx_, rsw_;
@@ -120,6 +129,23 @@ struct Gmm1F8 {
       boff[i] = (uint32_t)(kr * 2 * A.I + col);
     }
     nk = (int)(A.H / BKB);
+    if constexpr (GROUP) {
+      static_assert(BKB == 128, "a K step is one quantisation group");
+      const int64_t ng = A.H / BKB;
+      rsx_ = make_rsrc(A.gsx, A.T * ng * 4);
+      rsw_ = make_rsrc(A.gsw + (int64_t)e * ng * 2 * A.I, ng * 2 * A.I * 4);
+#pragma unroll
+      for (int j = 0; j < SCR; ++j) {
+        const int idx = tid + j * C::NTHR;
+        if (idx < C::BM) {
+          soff[j] = (uint32_t)((int64_t)g.tok_of_row[row0 + min(idx, rows - 1)] * ng * 4);
+        } else {
+          const int n = min(idx - C::BM, C::BN - 1);
+          const int64_t gi = min((int64_t)(i0 + n % (C::BN / 2)), A.I - 1);
+          soff[j] = (uint32_t)(((n < C::BN / 2) ? gi : A.I + gi) * 4);
+        }
+      }
+    }
     if constexpr (MX) {
       const int64_t nb = A.H / 32;  // exponent bytes per token row / weight column
       rsx_ = make_rsrc(A.xs, A.T * nb);
@@ -140,6 +166,18 @@ struct Gmm1F8 {
   }
   // MX: the exponent words of step kt (four blocks of 32 k) of this thread's rows / columns
   __device__ __forceinline__ void load_s(int kt, uint32_t (&r)[SCR]) {
+    if constexpr (GROUP) {
+      // group kt: the token descale at word kt of the row, the weight's at row kt of [H/128][2I]
+      const int tid = threadIdx.x;
+#pragma unroll
+      for (int j = 0; j < SCR; ++j) {
+        const int idx = tid + j * C::NTHR;
+        if (idx < C::BM)
+          r[j] = __builtin_amdgcn_raw_buffer_load_b32(rsx_, (int)soff[j], kt * 4, 0);
+        else if (idx < C::BM + C::BN)
+          r[j] = __builtin_amdgcn_raw_buffer_load_b32(rsw_, (int)soff[j], (int)(kt * 2 * ar->I * 4), 0);
+      }
+    }
     if constexpr (MX) {
       const int tid = threadIdx.x;
 #pragma unroll
@@ -174,16 +212,16 @@ struct Gmm1F8 {
     const int tid = threadIdx.x;
     const int64_t I = ar->I;
     // per-token mode: the row and column descales; MX: the instruction applied the
-    // block exponents already
+    // block exponents already; per group: every K step applied its descales
     for (int t = tid; t < C::BM; t += C::NTHR) {
       const bool v = t < rows;
       wrow[t] = v ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
-      rsc[t] = MX ? 1.f : (v ? ar->dsx[ar->g.tok_of_row[row0 + t]] : 0.f);
+      rsc[t] = STAGED ? 1.f : (v ? ar->dsx[ar->g.tok_of_row[row0 + t]] : 0.f);
     }
     for (int t = tid; t < C::BN; t += C::NTHR) {
       const int64_t gi = i0 + (t % (C::BN / 2));
       const int64_t col = (t < C::BN / 2) ? gi : I + gi;
-      csc[t] = MX ? 1.f : ((gi < I) ? ar->dsw[(int64_t)e * 2 * I + col] : 0.f);
+      csc[t] = STAGED ? 1.f : ((gi < I) ? ar->dsw[(int64_t)e * 2 * I + col] : 0.f);
     }
     __syncthreads();
 #pragma unroll
@@ -224,7 +262,7 @@ struct Gmm1F8 {
 
 template <class C, class P>
 __device__ __forceinline__ void store_scales(uint8_t* st, const uint32_t (&rs)[P::SCR]) {
-  if constexpr (P::MX_) {
+  if constexpr (P::STAGED) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < P::SCR; ++j) {
@@ -316,6 +354,17 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
       const uint8_t* sa = smem + (kt & 1) * ST;
       const uint8_t* sb = sa + C::A_BYTES;
       const uint32_t* scl = reinterpret_cast<const uint32_t*>(sa + C::STAGE);
+      // per group: this step's sums go to tmp, then into acc times the row's and the
+      // column's descale (float32 products and sum, in group order)
+      f32x16 tmp[P::GROUP_ ? C::MB : 1][P::GROUP_ ? C::NB : 1];
+      if constexpr (P::GROUP_) {
+#pragma unroll
+        for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmp[i][j][r] = 0.f;
+      }
 #pragma unroll
       for (int kk = 0; kk < BKB / 64; ++kk) {
         // B fragments for the whole wave tile, then one A fragment at a time
@@ -345,11 +394,30 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           const int asc = P::MX_ ? (int)(scl[wm * C::TM + mb * 32 + (lane & 31)] >> sh) : 127;
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, asc, 0,
-                                                                          bsc[nb]);
+          for (int nb = 0; nb < C::NB; ++nb) {
+            if constexpr (P::GROUP_)
+              tmp[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], tmp[mb][nb], 0, 0, 0, asc, 0,
+                                                                            bsc[nb]);
+            else
+              acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[nb], acc[mb][nb], 0, 0, 0, asc,
+                                                                            0, bsc[nb]);
+          }
         }
         if (SPREAD && st_ok) store_stage8<C, P>(dst, nxa, nxb, kk, BKB / 64);
+      }
+      if constexpr (P::GROUP_) {
+        const float* gsc = reinterpret_cast<const float*>(scl);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const float cs = gsc[C::BM + wn * C::TN + nb * 32 + (lane & 31)];
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float rsv = gsc[acc_row8<C>(wm, mb, r, lane)];
+              acc[mb][nb][r] = __builtin_fmaf(tmp[mb][nb][r], rsv * cs, acc[mb][nb][r]);
+            }
+        }
       }
       if (SPREAD && (full || kt + AHEAD < nk)) {
         pol.load_s(kt + AHEAD, nxs);
@@ -377,8 +445,8 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
   pol.epilogue(acc, wm, wn, lane, smem);
 }
 
-template <class C, bool SMALL, bool MX = false>
-struct Gmm1F8K : Gmm1F8<C, SMALL, MX> {
+template <class C, bool SMALL, int Q = 0>
+struct Gmm1F8K : Gmm1F8<C, SMALL, Q> {
   typedef C Cc;
   static constexpr int NTHR_ = C::NTHR;
 };
@@ -392,24 +460,32 @@ hipError_t launch8(const typename P::Args& args, int64_t logical_blocks, hipStre
   return hipGetLastError();
 }
 
-template <class C, bool SMALL, bool MX>
+template <class C, bool SMALL, int Q>
 hipError_t launch_one(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
                       const uint8_t* xs, const uint8_t* ws, const float* tw, int64_t H, int64_t I, uint16_t* h,
                       uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  typedef Gmm1F8K<C, SMALL, MX> P;
+  typedef Gmm1F8K<C, SMALL, Q> P;
   const int nnt = (int)((I + C::BN / 2 - 1) / (C::BN / 2));
   typename P::Args A{g, xq, dsx, wq, dsw, tw, g.T, H, I, h, a, aw, nnt, xs, ws};
+  if constexpr (Q == 2) {
+    A.gsx = dsx;
+    A.gsw = dsw;
+  }
   return launch8<P>(A, (SMALL ? g.max_small : g.max_big) * nnt, stream);
 }
 
-template <bool MX>
+template <int Q>
 hipError_t launch_all(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
                       const uint8_t* xs, const uint8_t* ws, const float* tw, int64_t H, int64_t I, uint16_t* h,
                       uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  if (g.narrow) return launch_one<Narrow8, true, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
-  hipError_t e = launch_one<Big8, false, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
-  if (e != hipSuccess) return e;
-  return launch_one<Small8, true, MX>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+  if (g.narrow) return launch_one<Narrow8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+  if constexpr (Q == 2) {
+    return hipErrorInvalidValue;  // per-group products run on 64x64 tiles only (two accumulator sets)
+  } else {
+    hipError_t e = launch_one<Big8, false, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+    if (e != hipSuccess) return e;
+    return launch_one<Small8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
+  }
 }
 
 }  // namespace
@@ -417,13 +493,19 @@ hipError_t launch_all(const RowGroups& g, const uint8_t* xq, const float* dsx, c
 hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
                            const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
                            uint16_t* aw, hipStream_t stream) {
-  return launch_all<false>(g, xq, dsx, wq, dsw, nullptr, nullptr, topk_w, H, I, h, a, aw, stream);
+  return launch_all<0>(g, xq, dsx, wq, dsw, nullptr, nullptr, topk_w, H, I, h, a, aw, stream);
+}
+
+hipError_t launch_gmm1_group(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
+                             const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                             uint16_t* aw, hipStream_t stream) {
+  return launch_all<2>(g, xq, dsx, wq, dsw, nullptr, nullptr, topk_w, H, I, h, a, aw, stream);
 }
 
 hipError_t launch_gmm1_mx(const RowGroups& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
                           const uint8_t* ws, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
                           uint16_t* aw, hipStream_t stream) {
-  return launch_all<true>(g, xq, nullptr, wq, nullptr, xs, ws, topk_w, H, I, h, a, aw, stream);
+  return launch_all<1>(g, xq, nullptr, wq, nullptr, xs, ws, topk_w, H, I, h, a, aw, stream);
 }
 
 }  // namespace hmm

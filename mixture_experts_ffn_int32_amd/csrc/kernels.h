@@ -179,6 +179,11 @@ hipError_t launch_quant_rows_group(const uint16_t* x, int64_t T, int64_t H, uint
                                    hipStream_t stream);
 hipError_t launch_quant_cols_group(const uint16_t* w, int64_t E, int64_t H, int64_t N, uint8_t* wq, float* dsw,
                                    hipStream_t stream);
+// Per-group FP8 up-projection + SwiGLU (gemm_fp8.hip): each 128-deep K step's sums
+// times dsx[tok][g] dsw[e][g][n], added in group order; 64x64 tiles only (narrow).
+hipError_t launch_gmm1_group(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
+                             const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
+                             uint16_t* aw, hipStream_t stream);
 // MX up-projection + SwiGLU (gemm_fp8.hip): h = bf16(sum_k xq 2^xs . wq 2^ws) by the
 // scaled instruction, then as launch_gmm1_swiglu.  H must be a multiple of 128.
 hipError_t launch_gmm1_mx(const RowGroups& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,

@@ -83,7 +83,8 @@ def _check_shared(x, shared_up_proj_weight, shared_down_proj_weight):
     return Is
 
 
-GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3}
+GMM1_DTYPES = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3,
+               "group": _lib.HMM_FP8_E4M3_GROUP}
 
 
 def _gmm1_code(gmm1_dtype):
@@ -209,7 +210,10 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     dynamic per-row / per-column scale (H must then be a multiple of 128); the
     rest of the forward and the whole backward stay bf16.  ``gmm1_dtype="mx"``
     uses MX quantisation instead (one power-of-two scale per 32 elements along
-    H, for tokens and for each weight column).  ``out_dtype=torch.float32``
+    H, for tokens and for each weight column); ``gmm1_dtype="group"`` uses
+    per-group quantisation (one float scale per 128 elements along H for tokens,
+    per 128-row block for each weight column; the problem then runs on 64x64
+    tiles).  ``out_dtype=torch.float32``
     is the accuracy mode: y (and dx and the weight gradients of the raw backward)
     are float32 and every intermediate is kept to about 16 significant bits
     (bf16 hi + lo pairs), for agreement with an unrounded computation to 1e-3;
@@ -339,15 +343,18 @@ def quantize_cols_group(w):
     return q, d
 
 
-def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16", shared_I=0):
+def saved_views(saved, T, H, I, E, K, tiles="auto", out_dtype="bf16", shared_I=0, gmm1_dtype="bf16"):
     """Typed views of the arrays a forward recorded in its saved buffer.
 
     In the float32-output mode h is float32 [S, 2I] and a, aw are bf16 [S, 2I]
     pairs (hi in the first I columns, lo in the last I).  With a shared expert
-    (shared_I = Is > 0) also shared_h [T, 2Is] and shared_a [T, Is] (same rules)."""
+    (shared_I = Is > 0) also shared_h [T, 2Is] and shared_a [T, Is] (same rules).
+    gmm1_dtype is the forward's: the per-group mode always runs on narrow tiles, whose
+    tables have another size."""
     lib = _lib.load()
     out = _out_code(out_dtype)
-    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles], out_dtype=out, shared_I=shared_I)
+    prob = _problem(T, H, I, E, K, _lib.TILE_FLAGS[tiles], out_dtype=out, shared_I=shared_I,
+                    gmm1_dtype=GMM1_DTYPES[gmm1_dtype])
     L = _lib.SavedLayout()
     _lib.check(lib.hmm_saved_layout_of(ctypes.byref(prob), ctypes.byref(L)))
     S = T * K

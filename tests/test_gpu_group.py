@@ -75,3 +75,63 @@ def test_group_quantisers_empty_and_repeatable():
     w = bf16_tensor(bits, "cuda")
     a, b = gpu_cols(w), gpu_cols(w)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- the per-group up-projection
+from _util import assert_close, gpu_inputs, oracle_inputs, to_f64  # noqa: E402
+from oracle.moe_ffn import MoEFFN  # noqa: E402
+from oracle.routing import route as oracle_route  # noqa: E402
+from test_gpu_parity import _sample_full, run_gpu  # noqa: E402
+
+GROUP_SMALL = [
+    ("tiny", dict(T=128, H=128, I=64, E=4, K=2)),
+    ("ragged", dict(T=300, H=256, I=192, E=6, K=3, routing="uniform")),
+    ("zipf", dict(T=411, H=384, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
+    ("outliers", dict(T=520, H=256, I=320, E=3, K=2, routing="hot", outlier_frac=0.02, outlier_scale=30.0)),
+]
+
+
+@pytest.mark.parametrize("name,over", GROUP_SMALL, ids=[s[0] for s in GROUP_SMALL])
+def test_group_forward_backward_parity(name, over):
+    """Forward intermediates, y and the whole backward against the FAITHFUL oracle in its
+    per-group mode (the mode runs on 64x64 tiles)."""
+    from mixture_experts_ffn_int32_amd import saved_views
+    spec = synth.spec_with("tiny", gmm1="group", **over)
+    inp = synth.make_inputs(spec, seed=29)
+    announce("group parity %s %s" % (name, {k: spec[k] for k in "THIEK"}))
+    g = gpu_inputs(inp, "cuda")
+    y, saved, dx, dW1, dW2, dw = run_gpu(g, "narrow", gmm1="group")
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful", gmm1="group")
+    v = saved_views(saved, *(spec[k] for k in "THIEK"), tiles="narrow")
+    ref_route = oracle_route(inp["topk_ids"], spec["E"])
+    (h, a, _), (hd, ad, _) = o.slot_intermediates_dev(ref_route["sorted_slot"])
+    assert_close(to_f64(v["h"]), h, name + " h", hd)
+    assert_close(to_f64(v["a"]), a, name + " a", ad)
+    ry, ryd = o.forward_dev()
+    assert_close(to_f64(y), ry, name + " y", ryd)
+    (rdx, rdw, rdW1, rdW2), (ddx, ddw, ddW1, ddW2) = o.backward_dev()
+    assert_close(to_f64(dx), rdx, name + " dx", ddx)
+    assert_close(to_f64(dw), rdw, name + " d_topk_weights", ddw)
+    assert_close(to_f64(dW1), rdW1, name + " d_up_proj_weight", ddW1)
+    assert_close(to_f64(dW2), rdW2, name + " d_down_proj_weight", ddW2)
+
+
+def test_group_differs_from_per_token_and_rejects_large_tiles():
+    """Per-group scales change the up-projection against per-token FP8 (groups of very
+    different magnitude), and the 256-row tiling is refused before any launch."""
+    spec = synth.spec_with("tiny", T=256, H=512, I=128, E=4, K=2)
+    inp = synth.make_inputs(spec, seed=31)
+    inp["x"] = synth.to_bf16_bits(synth.bits_to_f32(inp["x"]) *
+                                  np.repeat(np.exp2(np.arange(4) * 6.0 - 9.0), GROUP)[None, :].astype(np.float32))
+    announce("group against per-token")
+    g = gpu_inputs(inp, "cuda")
+    y_g = run_gpu(g, "narrow", gmm1="group")[0]
+    y_t = run_gpu(g, "narrow", gmm1="fp8")[0]
+    assert not np.array_equal(to_f64(y_g), to_f64(y_t))
+    with pytest.raises(Exception):
+        run_gpu(g, "large", gmm1="group")
+
+
+def test_full_size_group_sampled():
+    """The FP8-size workload with per-group scales, sampled (as the other full-size tests)."""
+    _sample_full("group")

@@ -172,7 +172,7 @@ def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):
     g = gpu_inputs(inp, "cuda")
     y, saved, dx, dW1, dW2, dw = run_gpu(g, gmm1=gmm1)
     from mixture_experts_ffn_int32_amd import saved_views
-    v = saved_views(saved, T, H, I, E, K)
+    v = saved_views(saved, T, H, I, E, K, gmm1_dtype=gmm1)
     ref_route = oracle_route(inp["topk_ids"], E)
     for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
         assert np.array_equal(v[k].cpu().numpy(), ref_route[k]), k
