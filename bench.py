@@ -99,6 +99,7 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
         "split_dy": T * H * 4 + T * H * 4,              # float32 dY -> bf16 hi | lo
         # ids read twice, histograms, sorted_slot + row_of_slot written
         "route": S * 4 * 2 + S * 8,
+        "route_narrow": S * 4 * 2 + S * 8,   # the per-group product's 64-row tile table
         # FP8 quantisers: read the bf16 operand once, write its codes and descales
         "quant_x": T * H * 2 + T * H + T * 4,
         "quant_w1": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * 4,

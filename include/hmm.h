@@ -126,8 +126,10 @@ typedef enum hmm_dtype {
  *               HMM_FP8_E4M3_GROUP: the per-group quantisation of
  *               MoeDistributeDispatchV2 case 4 (see hmm_quant_rows_group): each
  *               128-deep group's E4M3 sums are scaled by its token and weight
- *               descales and added in group order.  Runs the whole problem on
- *               64x64 tiles (HMM_FLAG_TILES_LARGE is rejected).  H a multiple of 128.
+ *               descales and added in group order.  The up-projection runs on
+ *               64x64 tiles only; with 256-row tiles for the other products a
+ *               second routing pass writes its tile table into the forward
+ *               workspace.  H a multiple of 128.
  *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward.
  *   shared_I    0, or the intermediate size Is of a shared expert (a multiple of
  *               64 in [64, 65536]): then the calls are hmm_forward_shared and

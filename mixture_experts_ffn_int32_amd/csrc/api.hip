@@ -74,8 +74,6 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_DTYPE,
                 "gmm1_dtype must be HMM_BF16, HMM_FP8_E4M3, HMM_MXFP8_E4M3 or HMM_FP8_E4M3_GROUP (got %d)",
                 p->gmm1_dtype);
-  if (p->gmm1_dtype == HMM_FP8_E4M3_GROUP && (p->flags & HMM_FLAG_TILES_LARGE))
-    return fail(HMM_ERR_UNSUPPORTED, "HMM_FP8_E4M3_GROUP runs on 64x64 tiles: HMM_FLAG_TILES_LARGE is not supported");
   {
     // every array a product reads through a buffer resource must stay below 4 GiB
     // (the float32-output mode reads [hi | lo] operands of twice the width)
@@ -102,9 +100,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   d->mx = p->gmm1_dtype == HMM_MXFP8_E4M3;
   d->group = p->gmm1_dtype == HMM_FP8_E4M3_GROUP;
   d->f32 = p->out_dtype == HMM_F32;
-  // the per-group product has 64x64 tiles only (two accumulator sets), and the
-  // routing's tile tables then hold every row in 64-row tiles
-  d->small = ((p->flags & HMM_FLAG_TILES_NARROW) || d->group) ? true
+  d->small = (p->flags & HMM_FLAG_TILES_NARROW) ? true
              : (p->flags & HMM_FLAG_TILES_LARGE) ? false
              : hmm::small_mode(d->S, d->H, d->I);
   d->fused = d->small && !d->fp8 && !d->f32 && !d->shared && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
@@ -184,7 +180,7 @@ RouteScratch route_scratch(const Dims& d, size_t base) {
 // maxima of the weight quantisation.
 struct FwdWork {
   RouteScratch rs;
-  size_t o, os, xq, dsx, wq, dsw, pmax, xs, ws, sync, total;
+  size_t o, os, xq, dsx, wq, dsw, pmax, xs, ws, sync, ntiles, total;
 };
 FwdWork fwd_work(const Dims& d) {
   FwdWork w{};
@@ -204,6 +200,9 @@ FwdWork fwd_work(const Dims& d) {
   } else if (d.group) {  // float32 descales: [T][H/128] and [E][H/128][2I]
     w.dsx = o;  o += up(d.T * (d.H / 128) * 4);
     w.dsw = o;  o += up(d.E * (d.H / 128) * 2 * d.I * 4);
+    if (!d.small) {  // the per-group product's own 64-row tile table
+      w.ntiles = o; o += up(hmm::tile_table_ints(d.S, d.E, true) * 4);
+    }
   } else if (d.fp8) {
     w.dsx = o;  o += up(d.T * 4);
     w.dsw = o;  o += up(d.E * 2 * d.I * 4);
@@ -674,9 +673,28 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
       e = hmm::launch_quant_cols_group((const uint16_t*)up_w, d.E, d.H, 2 * d.I, wq, dsw, st);
     }
     if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
+    // The per-group product runs on 64x64 tiles only (two accumulator sets).  With
+    // 256-row tiles for the other products a second routing pass, in the narrow
+    // mode, writes its tile table (every other array it writes is unchanged).
+    hmm::RowGroups gn = g;
+    if (!d.small) {
+      int32_t* nt = at<int32_t>(workspace, W.ntiles);
+      {
+        Stage stage("route_narrow", st);
+        e = hmm::launch_route(topk_ids, d.S, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E, true), 0,
+                              at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
+                              tok_of_row, nt, at<int32_t>(saved, L.id_error), at<int32_t>(workspace, W.rs.blockhist),
+                              at<int32_t>(workspace, W.rs.blockbase), at<int32_t>(workspace, W.rs.blockerr), nullptr,
+                              hmm::SharedTables{}, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "routing launch (64-row tiles)");
+      Dims dn = d;
+      dn.small = true;
+      gn = row_groups(dn, nt, offsets, sorted_slot, tok_of_row);
+    }
     {
       Stage stage("gmm1_group_swiglu", st);
-      e = hmm::launch_gmm1_group(g, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
+      e = hmm::launch_gmm1_group(gn, xq, dsx, wq, dsw, topk_weights, d.H, d.I, h, a, aw, st);
     }
     if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
   } else if (d.fp8) {

@@ -58,7 +58,7 @@ def _prob(**kw):
     (dict(gmm1_dtype=_lib.HMM_MXFP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(gmm1_dtype=5), _lib.HMM_ERR_BAD_DTYPE),
     (dict(gmm1_dtype=_lib.HMM_FP8_E4M3_GROUP, H=192), _lib.HMM_ERR_BAD_SHAPE),
     (dict(gmm1_dtype=_lib.HMM_FP8_E4M3_GROUP, flags=_lib.HMM_FLAG_VALIDATE_IDS | _lib.HMM_FLAG_TILES_LARGE),
-     _lib.HMM_ERR_UNSUPPORTED),
+     _lib.HMM_OK),
     (dict(out_dtype=_lib.HMM_F32, gmm1_dtype=_lib.HMM_FP8_E4M3_GROUP), _lib.HMM_ERR_UNSUPPORTED),
     (dict(out_dtype=_lib.HMM_F32, gmm1_dtype=_lib.HMM_MXFP8_E4M3), _lib.HMM_ERR_UNSUPPORTED),
     (dict(shared_I=1), _lib.HMM_ERR_BAD_SHAPE), (dict(shared_I=32), _lib.HMM_ERR_BAD_SHAPE),
