@@ -54,6 +54,9 @@ struct F8Cfg {
 typedef F8Cfg<256, 256, 2, 4, 1> Big8;
 typedef F8Cfg<64, 256, 1, 4, 2> Small8;
 typedef F8Cfg<64, 64, 2, 2, 2> Narrow8;
+// per group: eight waves on a 64x256 tile, two per SIMD, so one wave's rescaling
+// of its step sums overlaps the other's matrix instructions
+typedef F8Cfg<64, 256, 2, 4, 2> Group8;
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
@@ -478,10 +481,12 @@ template <int Q>
 hipError_t launch_all(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq, const float* dsw,
                       const uint8_t* xs, const uint8_t* ws, const float* tw, int64_t H, int64_t I, uint16_t* h,
                       uint16_t* a, uint16_t* aw, hipStream_t stream) {
-  if (g.narrow) return launch_one<Narrow8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
   if constexpr (Q == 2) {
-    return hipErrorInvalidValue;  // per-group products run on 64x64 tiles only (two accumulator sets)
+    // per group: 64-row tiles only (two accumulator sets)
+    if (!g.narrow) return hipErrorInvalidValue;
+    return launch_one<Group8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
   } else {
+    if (g.narrow) return launch_one<Narrow8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
     hipError_t e = launch_one<Big8, false, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
     if (e != hipSuccess) return e;
     return launch_one<Small8, true, Q>(g, xq, dsx, wq, dsw, xs, ws, tw, H, I, h, a, aw, stream);
