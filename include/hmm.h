@@ -127,7 +127,7 @@ typedef enum hmm_dtype {
  *               MoeDistributeDispatchV2 case 4 (see hmm_quant_rows_group): each
  *               128-deep group's E4M3 sums are scaled by its token and weight
  *               descales and added in group order.  The up-projection runs on
- *               64x64 tiles only; with 256-row tiles for the other products a
+ *               64-row tiles only; with 256-row tiles for the other products a
  *               second routing pass writes its tile table into the forward
  *               workspace.  H a multiple of 128.
  *   flags       HMM_FLAG_* bits; a backward takes the same value as its forward.

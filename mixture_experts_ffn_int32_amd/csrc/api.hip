@@ -673,7 +673,7 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
       e = hmm::launch_quant_cols_group((const uint16_t*)up_w, d.E, d.H, 2 * d.I, wq, dsw, st);
     }
     if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
-    // The per-group product runs on 64x64 tiles only (two accumulator sets).  With
+    // The per-group product runs on 64-row tiles only (two accumulator sets).  With
     // 256-row tiles for the other products a second routing pass, in the narrow
     // mode, writes its tile table (every other array it writes is unchanged).
     hmm::RowGroups gn = g;

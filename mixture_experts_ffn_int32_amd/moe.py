@@ -212,8 +212,8 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     uses MX quantisation instead (one power-of-two scale per 32 elements along
     H, for tokens and for each weight column); ``gmm1_dtype="group"`` uses
     per-group quantisation (one float scale per 128 elements along H for tokens,
-    per 128-row block for each weight column; the problem then runs on 64x64
-    tiles).  ``out_dtype=torch.float32``
+    per 128-row block for each weight column; its up-projection runs on
+    64-row tiles).  ``out_dtype=torch.float32``
     is the accuracy mode: y (and dx and the weight gradients of the raw backward)
     are float32 and every intermediate is kept to about 16 significant bits
     (bf16 hi + lo pairs), for agreement with an unrounded computation to 1e-3;

@@ -95,7 +95,7 @@ GROUP_SMALL = [
 @pytest.mark.parametrize("name,over", GROUP_SMALL, ids=[s[0] for s in GROUP_SMALL])
 def test_group_forward_backward_parity(name, over, tiles):
     """Forward intermediates, y and the whole backward against the FAITHFUL oracle in its
-    per-group mode.  The up-projection always runs on 64x64 tiles; with large tiles the
+    per-group mode.  The up-projection always runs on 64-row tiles; with large tiles the
     other products run on 256-row tiles and a second routing pass writes its table."""
     from mixture_experts_ffn_int32_amd import saved_views
     spec = synth.spec_with("tiny", gmm1="group", **over)
@@ -121,7 +121,7 @@ def test_group_forward_backward_parity(name, over, tiles):
 def test_group_differs_from_per_token_and_tilings_agree():
     """Per-group scales change the up-projection against per-token FP8 (groups of very
     different magnitude); both tilings give the same forward bit for bit (the per-group
-    product runs on 64x64 tiles in both, and the down-projection's sums do not depend on
+    product runs on 64-row tiles in both, and the down-projection's sums do not depend on
     the row tiling)."""
     spec = synth.spec_with("tiny", T=256, H=512, I=128, E=4, K=2)
     inp = synth.make_inputs(spec, seed=31)
