@@ -63,12 +63,23 @@ downstream.  Next to every faithful value the oracle therefore carries
   * rounding maps [v - d, v + d] onto the bfloat16 values between
     RNE(v - d) and RNE(v + d), so the rounded value's bound is
     max(|RNE(v + d) - RNE(v)|, |RNE(v) - RNE(v - d)|);
-  * downstream, bounds propagate to first order through |derivatives|, times
-    C_PROP = 1.25 to cover the curvature over the few-ulp steps involved.
+  * downstream, bounds propagate to first order, times C_PROP = 1.25 to cover
+    the curvature over the few-ulp steps involved.  Through an elementwise
+    formula the bound is sum_j |df/dv_j| d_j.  Through a reduction
+    sum_i c_i delta_i over many upstream values, each delta_i is an open
+    rounding decision of its own: it is 0 or +-d_i, decided by the evaluation
+    noise of its own element, with a sign unrelated to c_i.  The bound there is
+    min(sum_i |c_i| d_i, C_RMS sqrt(sum_i c_i^2 d_i^2)): the first term is the
+    worst case (every decision open and all aligned), the second C_RMS = 3
+    standard deviations of a sum of independent +-c_i d_i (every open decision
+    taken, at random sign); the actual spread is smaller, since an open decision
+    is taken only when the evaluation noise crosses the boundary.
 
-For almost every element dev is 0; it is one or a few ulps where a rounding
-decision is genuinely open.  Parity checks accept |gpu - ref| <= atol +
-rtol |ref| + dev.  In pure mode dev is 0.
+dev is nonzero only on elements whose value (or an upstream value) lies within
+its evaluation error of a bfloat16 rounding boundary; its size is pinned from
+above against the tolerance (tests/test_oracle_dev.py).  Parity checks accept
+|gpu - ref| <= atol + rtol |ref| + dev.  In pure mode dev is 0 and is not
+computed.
 
 The FP8 variant (``gmm1="fp8"``) quantises each token row and each
 (expert, column) of the up-projection weight to E4M3 (see ``quant``) before
@@ -80,9 +91,12 @@ accuracy: they sum small groups of products aligned to the group's largest
 one with about 13 bits below it, then combine the group sums.  The
 evaluation error of R1 in this variant is therefore taken as
 C_F8 * 2^-24 * sqrt(sum of squared products) (in the accumulator's units),
-with C_F8 = 2^14; measured errors of such an instruction on random E4M3 data
+with C_F8 = 2^12.  Errors of such an instruction measured on random E4M3 data
 stay below 3300 * 2^-24 * sqrt(sum of squares), and below 1400 for Gaussian
-data (a margin of about 5 over the worst case seen).
+data; a software model of it (groups of 8 products truncated 13 bits below the
+group's largest, tests/test_oracle_dev.py) has median 230, 99th percentile 900
+and maximum 2000 in the same units.  2^12 covers the worst of these with a
+margin of 1.24.
 
 The per-group variant (``gmm1="group"``) quantises tokens in groups of 128
 along the hidden dimension and the weight in blocks of 128 rows per column
@@ -110,12 +124,24 @@ U32 = 2.0 ** -24     # unit roundoff of float32
 C_ACC = 8.0          # margin on the typical accumulated rounding error of a float32 sum
 C_EL = 8.0           # float32 evaluation error of an elementwise formula, in ulps
 C_PROP = 1.25        # margin on first-order propagation (covers curvature over a few ulps)
-C_F8 = 2.0 ** 14     # evaluation error of an FP8 matrix-instruction sum, in 2^-24 * sqrt(sum t^2)
+C_F8 = 2.0 ** 12     # evaluation error of an FP8 matrix-instruction sum, in 2^-24 * sqrt(sum t^2)
+C_RMS = 3.0          # standard deviations allowed for a sum of independent open rounding decisions
 
 
 def acc_eps(sq_sum, n):
     """Evaluation-error estimate of a float32 sum of n terms whose squares sum to sq_sum."""
     return C_ACC * U32 * np.sqrt(max(n, 1) / 2.0) * np.sqrt(sq_sum)
+
+
+def prop_sum(abs_sum, sq_sum):
+    """Deviation of sum_i c_i delta_i, |delta_i| <= d_i, from abs_sum = sum |c_i| d_i and
+    sq_sum = sum c_i^2 d_i^2: the smaller of the worst case and C_RMS standard deviations."""
+    return np.minimum(abs_sum, C_RMS * np.sqrt(sq_sum))
+
+
+def prop_matmul(d, c):
+    """prop_sum over the contraction of d @ c (d: deviations, c: the coefficients)."""
+    return prop_sum(d @ np.abs(c), (d * d) @ (c * c))
 
 
 class MoEFFN:
@@ -125,18 +151,25 @@ class MoEFFN:
     up_proj_weight [E,H,2I], down_proj_weight [E,I,H], dY [T,H] (optional).
     Weights are converted to float64 one expert at a time, on first use.
     Methods return values; the ``*_dev`` variants also return the admissible
-    deviation bound described in the module text.
+    deviation bound described in the module text (zeros in pure mode).
+    ``acc="f32"`` (pure mode only) evaluates every product and sum in float32.
     """
 
     def __init__(self, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
-                 dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None):
+                 dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None,
+                 acc="f64"):
         if mode not in ("pure", "faithful"):
             raise ValueError(mode)
+        if acc not in ("f64", "f32") or (acc == "f32" and mode != "pure"):
+            raise ValueError("acc must be 'f64', or 'f32' in pure mode")
+        # float type of every product and sum: float64 for parity; float32 only for
+        # the pure mode's plain float32 per-token loop (a CPU timing baseline)
+        self.ft = np.float64 if acc == "f64" else np.float32
         if gmm1 not in ("bf16", "fp8", "mx", "group"):
             raise ValueError(gmm1)
         self.x = np.asarray(x)
         self.ids = np.asarray(topk_ids, dtype=np.int64)
-        self.w = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
+        self.w = np.asarray(topk_weights, dtype=np.float32).astype(self.ft)
         self.W1 = np.asarray(up_proj_weight)
         self.W2 = np.asarray(down_proj_weight)
         self.dY = None if dY is None else np.asarray(dY)
@@ -164,27 +197,34 @@ class MoEFFN:
             if ws1.ndim != 2 or ws1.shape[0] != self.H or ws2.shape != (ws1.shape[1] // 2, self.H):
                 raise ValueError("shared weights must be [H, 2Is] and [Is, H]")
             self.shared = MoEFFN(self.x, np.zeros((self.T, 1), np.int64), np.ones((self.T, 1), np.float32),
-                                 ws1[None], ws2[None], dY=self.dY, mode=mode)
+                                 ws1[None], ws2[None], dY=self.dY, mode=mode, acc=acc)
 
     # -- helpers ---------------------------------------------------------------
     def _round(self, v, d):
-        """Rounding point: (bf16(v), admissible deviation) in faithful mode; (v, 0) in pure mode."""
-        v = np.asarray(v, np.float64)
+        """Rounding point: (bf16(v), admissible deviation) in faithful mode; (v, None) in pure mode."""
         if not self.faithful:
-            return v, np.zeros_like(v)
+            return v, None
+        v = np.asarray(v, np.float64)
         r = round_bf16(v)
         dev = np.maximum(np.abs(round_bf16(v + d) - r), np.abs(r - round_bf16(v - d)))
         return r, dev
 
     def _W1(self, e):
         if e not in self._w1:
-            self._w1[e] = self.W1[e].astype(np.float64)
+            self._w1[e] = self.W1[e].astype(self.ft)
         return self._w1[e]
 
     def _W2(self, e):
         if e not in self._w2:
-            self._w2[e] = self.W2[e].astype(np.float64)
+            self._w2[e] = self.W2[e].astype(self.ft)
         return self._w2[e]
+
+    def _sig(self, g):
+        return sigmoid(g).astype(self.ft, copy=False)
+
+    def _zeros_like(self, d, v):
+        """d, or zeros shaped like v where d is None (pure mode)."""
+        return np.zeros(np.shape(v)) if d is None else d
 
     def _W1q(self, e):
         if e not in self._w1q:
@@ -204,7 +244,7 @@ class MoEFFN:
     def up_dev(self, e, xrows, cols=None):
         """R1: h = x . W1[e] for the given rows (optionally a subset of columns)."""
         cols = slice(None) if cols is None else cols
-        xr = np.asarray(xrows, np.float64)
+        xr = np.asarray(xrows, self.ft)
         if self.gmm1 == "fp8":
             q, _, dsx = quantize_rows(xrows)
             wq, _, dsw = self._W1q(e)
@@ -219,7 +259,7 @@ class MoEFFN:
             wqc, dswc = wq[:, cols], dsw[:, cols].astype(np.float64)
             ng = self.H // GROUP
             h = np.zeros((q.shape[0], wqc.shape[1]))
-            eps = np.zeros_like(h)
+            eps_sq = np.zeros_like(h)
             terms_sq = np.zeros_like(h)
             for g in range(ng):                                     # groups in contraction order
                 k = slice(g * GROUP, (g + 1) * GROUP)
@@ -230,8 +270,13 @@ class MoEFFN:
                 h += term
                 terms_sq += term * term
                 # the group sum's instruction error, then its scaling (two float32 products)
-                eps += (acc_eps(sq, GROUP) + C_F8 * U32 * np.sqrt(sq)) * np.abs(sc) + 2 * C_EL * U32 * np.abs(term)
-            eps += acc_eps(terms_sq, ng)                            # the float32 running sum over the groups
+                eg = (acc_eps(sq, GROUP) + C_F8 * U32 * np.sqrt(sq)) * np.abs(sc) + 2 * C_EL * U32 * np.abs(term)
+                eps_sq += eg * eg
+            # The groups' errors are independent.  C_F8 bounds the error of a whole
+            # instruction sum of any length in units of its sqrt(sum t^2), so the scaled
+            # group errors combine in quadrature, without a further margin; then the
+            # float32 running sum over the groups.
+            eps = np.sqrt(eps_sq) + acc_eps(terms_sq, ng)
         elif self.gmm1 == "mx":
             q, ex = quantize_rows_mx(xrows)
             wq, ew = self._W1q(e)
@@ -243,7 +288,7 @@ class MoEFFN:
         else:
             W = self._W1(e)[:, cols]
             h = xr @ W
-            eps = acc_eps((xr * xr) @ (W * W), self.H)
+            eps = acc_eps((xr * xr) @ (W * W), self.H) if self.faithful else None
         return self._round(h, eps)
 
     def up(self, e, xrows, cols=None):
@@ -254,9 +299,12 @@ class MoEFFN:
         icols = np.arange(self.I) if icols is None else np.asarray(icols)
         h, hd = self.up_dev(e, xrows, np.concatenate([icols, icols + self.I]))
         n = icols.size
-        g, u, gd, ud = h[:, :n], h[:, n:], hd[:, :n], hd[:, n:]
-        s = sigmoid(g)
+        g, u = h[:, :n], h[:, n:]
+        s = self._sig(g)
         v = g * s * u                                           # R2
+        if not self.faithful:
+            return (g, u, v), (None, None, None)
+        gd, ud = hd[:, :n], hd[:, n:]
         d = C_PROP * (np.abs(u * (s + g * s * (1 - s))) * gd + np.abs(g * s) * ud) + C_EL * U32 * np.abs(v)
         a, ad = self._round(v, d)
         return (g, u, a), (gd, ud, ad)
@@ -268,23 +316,29 @@ class MoEFFN:
         """R3: o = a . W2[e]."""
         W2 = self._W2(e)
         v = a @ W2
-        d = C_PROP * (ad @ np.abs(W2)) + acc_eps((a * a) @ (W2 * W2), self.I)
+        if not self.faithful:
+            return v, None
+        d = C_PROP * prop_matmul(ad, W2) + acc_eps((a * a) @ (W2 * W2), self.I)
         return self._round(v, d)
 
     def act_grad(self, e, dyrows, icols=None):
         """G = dY . W2[e]^T (unrounded) and its float32 evaluation error, for gate columns ``icols``."""
         W2 = self._W2(e)
         W2 = W2 if icols is None else W2[np.asarray(icols)]
-        dyr = np.asarray(dyrows, np.float64)
+        dyr = np.asarray(dyrows, self.ft)
+        if not self.faithful:
+            return dyr @ W2.T, None
         return dyr @ W2.T, acc_eps((dyr * dyr) @ (W2 * W2).T, self.H)
 
     def swiglu_grad_dev(self, w, G, Ge, g, u, gd, ud):
         """SwiGLUGrad with dA = w G; R5: dH = [dg | du] and deviations."""
-        s = sigmoid(g)
+        s = self._sig(g)
         q = s * (1.0 + g * (1.0 - s))              # d silu / dg
         dA = w * G
         vg = dA * u * q
         vu = dA * g * s
+        if not self.faithful:
+            return (vg, None), (vu, None)
         dq = s * (1 - s) * (2.0 + g * (1.0 - 2.0 * s))  # d q / dg
         dvg = C_PROP * (np.abs(dA * u * dq) * gd + np.abs(dA * q) * ud + np.abs(w * u * q) * Ge) + C_EL * U32 * np.abs(vg)
         dvu = C_PROP * (np.abs(dA * q) * gd + np.abs(w * g * s) * Ge) + C_EL * U32 * np.abs(vu)
@@ -299,23 +353,29 @@ class MoEFFN:
         if self.shared is not None:  # shared output o_s (R3 of the shared problem; its R4 of one term is exact)
             ys, ysd = self.shared.forward_dev(toks, out_dtype)
         for j, t in enumerate(toks):
-            acc = np.zeros(self.H)
+            acc = np.zeros(self.H, self.ft)
             accd = np.zeros(self.H)
+            accd2 = np.zeros(self.H)
             sq = np.zeros(self.H)
             for k in range(self.K):
                 e = self.ids[t, k]
                 (_, _, a), (_, _, ad) = self.hidden_dev(e, self.x[t:t + 1])
                 o, od = self.down_dev(e, a, ad)
                 acc = acc + self.w[t, k] * o[0]
-                accd = accd + abs(self.w[t, k]) * od[0]
-                sq = sq + (self.w[t, k] * o[0]) ** 2
+                if self.faithful:
+                    accd = accd + abs(self.w[t, k]) * od[0]
+                    accd2 = accd2 + (self.w[t, k] * od[0]) ** 2
+                    sq = sq + (self.w[t, k] * o[0]) ** 2
             nterm = self.K
             if self.shared is not None:
-                acc, accd, sq, nterm = acc + ys[j], accd + ysd[j], sq + ys[j] ** 2, self.K + 1
-            if out_dtype == "bf16":
-                y[j], yd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, nterm))      # R4
+                acc, nterm = acc + ys[j], self.K + 1
+                accd, accd2, sq = accd + ysd[j], accd2 + ysd[j] ** 2, sq + ys[j] ** 2
+            if not self.faithful:
+                y[j] = acc
+            elif out_dtype == "bf16":
+                y[j], yd[j] = self._round(acc, C_PROP * prop_sum(accd, accd2) + acc_eps(sq, nterm))      # R4
             else:
-                y[j], yd[j] = acc, accd
+                y[j], yd[j] = acc, C_PROP * prop_sum(accd, accd2)
         return y, yd
 
     def forward(self, tokens=None, out_dtype="bf16"):
@@ -335,7 +395,8 @@ class MoEFFN:
             (g, u, a), (gd, ud, ad) = self.hidden_dev(e, self.x[t:t + 1])
             o, od = self.down_dev(e, a, ad)
             out[0][j, :self.I], out[0][j, self.I:], out[1][j], out[2][j] = g[0], u[0], a[0], o[0]
-            dev[0][j, :self.I], dev[0][j, self.I:], dev[1][j], dev[2][j] = gd[0], ud[0], ad[0], od[0]
+            if self.faithful:
+                dev[0][j, :self.I], dev[0][j, self.I:], dev[1][j], dev[2][j] = gd[0], ud[0], ad[0], od[0]
         return out, dev
 
     # -- backward --------------------------------------------------------------
@@ -351,31 +412,42 @@ class MoEFFN:
         if self.shared is not None:  # the shared dX rows (R6 of the shared problem)
             (dxs, _), (dxsd, _) = self.shared.backward_tokens_dev(toks, out_dtype)
         for j, t in enumerate(toks):
-            acc = np.zeros(self.H)
+            acc = np.zeros(self.H, self.ft)
             accd = np.zeros(self.H)
+            accd2 = np.zeros(self.H)
             sq = np.zeros(self.H)
             for k in range(self.K):
                 e = self.ids[t, k]
                 (g, u, a), (gd, ud, ad) = self.hidden_dev(e, self.x[t:t + 1])
                 G, Ge = self.act_grad(e, self.dY[t:t + 1])
                 dw[j, k] = float(np.sum(G * a))
-                dwd[j, k] = float(C_PROP * np.sum(np.abs(G) * ad + np.abs(a) * Ge) + acc_eps(np.sum((G * a) ** 2), self.I))
                 (dg, dgd), (du, dud) = self.swiglu_grad_dev(self.w[t, k], G, Ge, g, u, gd, ud)
                 dH = np.concatenate([dg, du], axis=1)
-                dHd = np.concatenate([dgd, dud], axis=1)
                 W1 = self._W1(e)
                 v = dH @ W1.T
-                xp, xpd = self._round(v, C_PROP * (dHd @ np.abs(W1.T)) + acc_eps((dH * dH) @ (W1 * W1).T, 2 * self.I))  # R6
+                if not self.faithful:
+                    acc = acc + v[0]
+                    continue
+                # d_topk_weights = sum_i G_i a_i: open decisions of a (ad) and the evaluation errors of G (Ge)
+                dwd[j, k] = float(C_PROP * prop_sum(np.sum(np.abs(G) * ad + np.abs(a) * Ge),
+                                                    np.sum((G * ad) ** 2 + (a * Ge) ** 2))
+                                  + acc_eps(np.sum((G * a) ** 2), self.I))
+                dHd = np.concatenate([dgd, dud], axis=1)
+                xp, xpd = self._round(v, C_PROP * prop_matmul(dHd, W1.T) + acc_eps((dH * dH) @ (W1 * W1).T, 2 * self.I))  # R6
                 acc = acc + xp[0]
                 accd = accd + xpd[0]
+                accd2 = accd2 + xpd[0] ** 2
                 sq = sq + xp[0] ** 2
             nterm = self.K
             if self.shared is not None:
-                acc, accd, sq, nterm = acc + dxs[j], accd + dxsd[j], sq + dxs[j] ** 2, self.K + 1
-            if out_dtype == "bf16":
-                dx[j], dxd[j] = self._round(acc, C_PROP * accd + acc_eps(sq, nterm))     # R7
+                acc, nterm = acc + dxs[j], self.K + 1
+                accd, accd2, sq = accd + dxsd[j], accd2 + dxsd[j] ** 2, sq + dxs[j] ** 2
+            if not self.faithful:
+                dx[j] = acc
+            elif out_dtype == "bf16":
+                dx[j], dxd[j] = self._round(acc, C_PROP * prop_sum(accd, accd2) + acc_eps(sq, nterm))     # R7
             else:
-                dx[j], dxd[j] = acc, accd
+                dx[j], dxd[j] = acc, C_PROP * prop_sum(accd, accd2)
         return (dx, dw), (dxd, dwd)
 
     def backward_tokens(self, tokens=None, out_dtype="bf16"):
@@ -401,19 +473,21 @@ class MoEFFN:
             return (z, z.copy(), zr), (z.copy(), z.copy(), zr.copy())
         t = slots // self.K
         k = slots % self.K
-        xr = self.x[t].astype(np.float64)
-        dyr = self.dY[t].astype(np.float64)
+        xr = self.x[t].astype(self.ft)
+        dyr = self.dY[t].astype(self.ft)
         w = self.w[t, k][:, None]
         (g, u, a), (gd, ud, ad) = self.hidden_dev(e, xr, icols)
         G, Ge = self.act_grad(e, dyr, icols)
         (dg, dgd), (du, dud) = self.swiglu_grad_dev(w, G, Ge, g, u, gd, ud)
+        if not self.faithful:
+            res = (xr.T @ dg, xr.T @ du, (w * a).T @ dyr)
+            return res, tuple(np.zeros(r.shape) for r in res)
         aw, awd = self._round(w * a, C_PROP * np.abs(w) * ad + C_EL * U32 * np.abs(w * a))    # R8
         m = slots.size
-        ax = np.abs(xr)
         res = [xr.T @ dg, xr.T @ du, aw.T @ dyr]                                      # R9
-        devs = [C_PROP * (ax.T @ dgd) + acc_eps((xr * xr).T @ (dg * dg), m),
-                C_PROP * (ax.T @ dud) + acc_eps((xr * xr).T @ (du * du), m),
-                C_PROP * (awd.T @ np.abs(dyr)) + acc_eps((aw * aw).T @ (dyr * dyr), m)]
+        devs = [C_PROP * prop_matmul(dgd.T, xr).T + acc_eps((xr * xr).T @ (dg * dg), m),
+                C_PROP * prop_matmul(dud.T, xr).T + acc_eps((xr * xr).T @ (du * du), m),
+                C_PROP * prop_matmul(awd.T, dyr) + acc_eps((aw * aw).T @ (dyr * dyr), m)]
         if out_dtype == "bf16":
             pairs = [self._round(v, d) for v, d in zip(res, devs)]
             res, devs = [p[0] for p in pairs], [p[1] for p in pairs]

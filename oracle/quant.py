@@ -23,9 +23,13 @@ from .numerics import E4M3_MAX, round_e4m3
 
 
 def _scale_from_absmax(absmax):
+    """448 / absmax in float32; 1 for an all-zero row.  The page's formula
+    overflows float32 when 0 < absmax < ~1.3e-36 (bfloat16 holds values down to
+    ~9e-41); the reading is that the quotient is clamped to the largest finite
+    float32, which keeps the codes finite."""
     absmax = np.asarray(absmax, dtype=np.float32)
-    with np.errstate(divide="ignore"):
-        scale = np.float32(E4M3_MAX) / absmax
+    with np.errstate(divide="ignore", over="ignore"):
+        scale = np.minimum(np.float32(E4M3_MAX) / absmax, np.finfo(np.float32).max)
     return np.where(absmax > 0, scale, np.float32(1.0)).astype(np.float32)
 
 

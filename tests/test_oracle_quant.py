@@ -292,3 +292,21 @@ def test_group_up_projection_error_is_bounded():
         dw = dev(W1[e], gw)
         bound = dx @ (np.abs(W1[e]) + dw) + np.abs(x) @ dw
         assert np.all(np.abs(mg.up(e, x) - m16.up(e, x)) <= bound * (1 + 1e-6))
+
+
+def test_scale_clamped_where_448_over_max_overflows():
+    """A row whose largest value is ~1e-38 (a bf16 subnormal range value): 448 / max
+    overflows float32; the scale is the largest finite float32, the codes stay finite
+    and equal torch's E4M3 cast of x * FLT_MAX, and zeros stay zero."""
+    import torch
+    x = np.zeros((2, 64), np.float32)
+    x[0, ::3] = np.float32(1e-38) * np.linspace(-1, 1, 22).astype(np.float32)
+    x[1, 5] = np.float32(9.2e-41)                      # the smallest bf16 subnormal magnitude
+    x = round_bf16(x).astype(np.float32)
+    q, scale, descale = quantize_rows(x)
+    fmax = np.finfo(np.float32).max
+    assert np.all(scale == fmax) and np.all(np.isfinite(q))
+    ref = (torch.tensor(x) * torch.tensor(fmax)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(q, ref)
+    assert np.all(q[x == 0] == 0)
+    assert np.all(descale == np.float32(1.0) / fmax) and np.all(descale > 0)
