@@ -22,14 +22,16 @@
  * - Pointers named as tensors are DEVICE pointers (HBM of the current HIP
  *   device); all are caller-owned and caller-allocated.  The library never
  *   allocates device memory.  Its only state is, per host thread and device,
- *   one pinned host word and event for the id check, and the optional
- *   stage-timing events.
+ *   one pinned host word and event for the id check (and for the fused
+ *   forward), and the optional stage-timing events.
  * - All tensors are dense, row-major (last index fastest), with no padding.
  *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
  *   be 16-byte aligned.
  * - ``stream`` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *   is enqueued asynchronously on it, in order; outputs are valid once the
- *   stream reaches that point.  Only HMM_FLAG_VALIDATE_IDS adds a host wait.
+ *   stream reaches that point.  Only HMM_FLAG_VALIDATE_IDS (a wait for the
+ *   routing's id check) and HMM_FLAG_FUSED_FORWARD (a wait for its launch) add
+ *   a host wait.
  * - Every check that needs only host data (null pointers, shapes, dtypes,
  *   alignment, workspace size) runs before any HIP call: on failure nothing is
  *   enqueued (RFC section 4.2: invalid input is rejected at the host boundary
@@ -61,7 +63,8 @@ typedef enum hmm_status {
   HMM_ERR_UNSUPPORTED = 5,           /* valid problem the library does not implement */
   HMM_ERR_WORKSPACE_TOO_SMALL = 6,   /* workspace_bytes below the *_sizes figure */
   HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7,/* some topk_ids value is outside [0, E) */
-  HMM_ERR_HIP = 8                    /* a HIP runtime call failed */
+  HMM_ERR_HIP = 8,                   /* a HIP runtime call failed */
+  HMM_ERR_TIMEOUT = 9                /* a bounded device wait gave up; the outputs are incomplete */
 } hmm_status;
 
 typedef enum hmm_dtype {
@@ -96,7 +99,14 @@ typedef enum hmm_dtype {
  * The results are identical to the kernel sequence.  On MI355X it is slower
  * today (every array one tile writes for another has to go through the
  * device-wide coherence point, because the eight XCDs have separate L2s), so it
- * is opt-in; ignored where it does not apply. */
+ * is opt-in; ignored where it does not apply.
+ * Every wait between its tiles is bounded (RFC 5.3 and 7.3: a failure must be
+ * diagnosable, not a hang).  A wait that gives up (possible only when not all
+ * of the launch's workgroups are resident at once, e.g. beside other work on
+ * the device) stops its workgroup and stores a flag into a pinned host word;
+ * hmm_forward then waits for the launch to finish and returns HMM_ERR_TIMEOUT,
+ * with y and the saved intermediates incomplete.  With this flag hmm_forward
+ * therefore returns only after its launch has completed. */
 #define HMM_FLAG_FUSED_FORWARD 8u
 
 /* Problem description.
@@ -318,6 +328,14 @@ const char* hmm_last_error_message(void);
 
 /* Build identification: the offload target the kernels were compiled for. */
 const char* hmm_build_info(void);
+
+/* Test and diagnosis hook: the number of polls after which a wait of the fused
+ * forward (HMM_FLAG_FUSED_FORWARD) gives up, for the launches that follow on
+ * any thread; 0 restores the default (about a second).  A small value makes the
+ * waits give up on purpose, so the error path can be exercised with every
+ * workgroup still ending normally.  Not for concurrent use with forwards in
+ * flight. */
+hmm_status hmm_set_fused_spin_limit(uint32_t polls);
 
 /* Stage timing, for benchmarks and tools.  While enabled on the calling
  * thread, every kernel launch (and the id read-back) of hmm_forward,

@@ -20,6 +20,7 @@ HMM_ERR_UNSUPPORTED = 5
 HMM_ERR_WORKSPACE_TOO_SMALL = 6
 HMM_ERR_EXPERT_ID_OUT_OF_RANGE = 7
 HMM_ERR_HIP = 8
+HMM_ERR_TIMEOUT = 9
 
 HMM_BF16, HMM_F32, HMM_FP8_E4M3, HMM_MXFP8_E4M3, HMM_FP8_E4M3_GROUP = 0, 1, 2, 3, 4
 HMM_FLAG_VALIDATE_IDS = 1
@@ -34,7 +35,7 @@ EXPORTS = (
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
     "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
     "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared", "hmm_quant_rows_mx", "hmm_quant_cols_mx",
-    "hmm_quant_rows_group", "hmm_quant_cols_group",
+    "hmm_quant_rows_group", "hmm_quant_cols_group", "hmm_set_fused_spin_limit",
 )
 
 
@@ -78,6 +79,7 @@ _SIGS = {
     "hmm_quant_rows_group": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_quant_cols_group": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "hmm_status_string": [ctypes.c_int],
+    "hmm_set_fused_spin_limit": [ctypes.c_uint32],
     "hmm_last_error_message": [],
     "hmm_build_info": [],
     "hmm_profile_enable": [ctypes.c_int32],

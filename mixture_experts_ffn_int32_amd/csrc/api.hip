@@ -299,6 +299,8 @@ struct DevState {
   bool ready = false;
   int32_t* word = nullptr;
   hipEvent_t id_ev = nullptr;
+  uint32_t* fused_status = nullptr;  // pinned: the fused forward stores 1 when a wait gave up
+  hipEvent_t fused_ev = nullptr;     // recorded after a fused forward launch
   int cus = 0;  // compute units (the fused kernel's workgroup count: all resident)
 };
 DevState* dev_state() {
@@ -308,11 +310,15 @@ DevState* dev_state() {
   DevState& c = st[dev];
   if (c.ready) return &c;
   bool ok = hipHostMalloc((void**)&c.word, sizeof(int32_t), hipHostMallocCoherent) == hipSuccess;
+  ok = ok && hipHostMalloc((void**)&c.fused_status, sizeof(uint32_t), hipHostMallocCoherent) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&c.id_ev, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c.fused_ev, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c.cus > 0;
   if (!ok) {  // release whatever was made; the next call tries again
     if (c.word) (void)hipHostFree(c.word);
+    if (c.fused_status) (void)hipHostFree(c.fused_status);
     if (c.id_ev) (void)hipEventDestroy(c.id_ev);
+    if (c.fused_ev) (void)hipEventDestroy(c.fused_ev);
     c = DevState{};
     return nullptr;
   }
@@ -399,11 +405,17 @@ const char* hmm_status_string(hmm_status s) {
     case HMM_ERR_WORKSPACE_TOO_SMALL: return "HMM_ERR_WORKSPACE_TOO_SMALL";
     case HMM_ERR_EXPERT_ID_OUT_OF_RANGE: return "HMM_ERR_EXPERT_ID_OUT_OF_RANGE";
     case HMM_ERR_HIP: return "HMM_ERR_HIP";
+    case HMM_ERR_TIMEOUT: return "HMM_ERR_TIMEOUT";
   }
   return "HMM_ERR_UNKNOWN";
 }
 
 const char* hmm_last_error_message(void) { return g_last_error.c_str(); }
+
+hmm_status hmm_set_fused_spin_limit(uint32_t polls) {
+  hmm::set_fused_spin_cap(polls);
+  return HMM_OK;
+}
 
 const char* hmm_build_info(void) {
   return "libhmm gfx950 (CDNA4) bf16 MFMA 32x32x16 and fp8 e4m3 MFMA 32x32x64; 256x256, 64x256 and 64x64 tiles, "
@@ -560,6 +572,7 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
     DevState* c = dev_state();
     if (!c) return fail(HMM_ERR_HIP, "could not create the per-device id-check word or event");
     if (validate_ids) *c->word = ID_PENDING;
+    *c->fused_status = 0;
     hipError_t e;
     {
       Stage stage("fused_forward", st);
@@ -570,13 +583,23 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
                                     at<int32_t>(saved, L.id_error), validate_ids ? c->word : nullptr,
                                     at<uint16_t>(saved, L.h), at<uint16_t>(saved, L.a), at<uint16_t>(saved, L.aw),
                                     at<uint16_t>(workspace, W.o), at<uint32_t>(workspace, W.sync), next_epoch(),
-                                    c->cus, st);
+                                    c->fused_status, c->cus, st);
     }
     if (e != hipSuccess) return hip_fail(e, "fused forward launch");
-    if (!validate_ids) return HMM_OK;
-    e = hipEventRecord(c->id_ev, st);
-    if (e != hipSuccess) return hip_fail(e, "id-validation event");
-    return finish_id_check(d);
+    e = hipEventRecord(c->fused_ev, st);
+    if (e != hipSuccess) return hip_fail(e, "fused forward event");
+    if (validate_ids) {
+      e = hipEventRecord(c->id_ev, st);
+      if (e != hipSuccess) return hip_fail(e, "id-validation event");
+      s = finish_id_check(d);
+    }
+    // the launch's waits are bounded; one that gave up has stored the flag
+    e = hipEventSynchronize(c->fused_ev);
+    if (e != hipSuccess) return hip_fail(e, "fused forward wait");
+    if (*(volatile uint32_t*)c->fused_status)
+      return fail(HMM_ERR_TIMEOUT, "fused forward: a tile-ready wait gave up (not all of its %d workgroups were "
+                  "resident at once?); y and the saved intermediates are incomplete", c->cus);
+    return validate_ids ? s : HMM_OK;
   }
   // the routing launch also writes the shared expert's tables (also for T = 0:
   // the backward's weight gradients read them)

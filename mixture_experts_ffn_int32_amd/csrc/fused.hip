@@ -16,8 +16,11 @@
 // wait is for an item of a smaller index.  With all G workgroups resident (G is
 // at most the number of CUs) the oldest unfinished item never waits, so the
 // kernel always progresses.  Every wait is nevertheless bounded: after about a
-// second it gives up, sets a status bit and goes on (the results are then
-// wrong; the host reports the error).
+// second (or the host's lower test limit) it gives up, stores 1 into the
+// caller's pinned host status word, and its workgroup skips every item it has
+// left (it never reads routing tables it has not seen published, so nothing
+// it touches is out of bounds).  The results are then incomplete; the host
+// waits for the launch, reads the word and returns an error.
 //
 // Counters live in the caller's workspace.  They are reset by the routing item
 // of each call before it publishes its per-call epoch in the flag word; no
@@ -39,6 +42,7 @@ typedef Gmm1<Narrow, true> FG1;
 typedef Gmm2<Narrow, true, true> FG2;
 constexpr int FT = Narrow::NTHR;
 constexpr uint32_t SPIN_CAP = 1u << 20;  // polls (an L2 round trip and s_sleep each): about a second
+uint32_t g_spin_cap = SPIN_CAP;          // the host's limit for the next launches (tests lower it)
 
 struct FusedFwdArgs {
   const int32_t* ids;
@@ -54,27 +58,36 @@ struct FusedFwdArgs {
   uint16_t* y;
   int64_t T, H;
   int ncomb, ct;
-  uint32_t* sync;  // [0] epoch flag, [1] down-projection tiles done, [2] status, [4 + j] up tiles done of row tile j
+  uint32_t* sync;  // [0] epoch flag, [1] down-projection tiles done, [4 + j] up tiles done of row tile j
   uint32_t epoch;
+  uint32_t spin_cap;     // polls before a wait gives up
+  uint32_t* host_status; // pinned host word: 1 once a wait has given up (the host clears it)
 };
 
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// the whole workgroup waits until *word == target
-__device__ __forceinline__ void block_wait(const uint32_t* word, uint32_t target, uint32_t* status) {
+// the whole workgroup waits until *word == target; false if the wait gave up
+// (then the host status word holds 1)
+__device__ __forceinline__ bool block_wait(const uint32_t* word, uint32_t target, const FusedFwdArgs& A, int* flag) {
   if (threadIdx.x == 0) {
     uint32_t spins = 0;
+    bool ok = true;
     while (load_agent(word) != target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > SPIN_CAP) {
-        __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (++spins > A.spin_cap) {
+        __hip_atomic_store(A.host_status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        ok = false;
         break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
+    *flag = ok;
   }
   __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();  // the flag is reused by the next wait
+  return ok;
 }
 
 // every thread's coherent stores have completed (reached the coherence point)
@@ -114,8 +127,8 @@ __global__ void __launch_bounds__(FT, 1) fused_forward(const FusedFwdArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Narrow::STAGE];
   static_assert(sizeof(RouteLds<FT>) <= sizeof(smem), "routing LDS fits in the product buffers");
   const int tid = threadIdx.x;
+  __shared__ int wait_flag;
   const int total = 1 + A.n1 + A.n2 + A.ncomb;
-  uint32_t* status = A.sync + 2;
   bool routed = false;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     if (item == 0) {
@@ -123,17 +136,14 @@ __global__ void __launch_bounds__(FT, 1) fused_forward(const FusedFwdArgs A) {
                             A.offsets, A.sorted_slot, A.row_of_slot, A.tok_of_row, A.tiles, A.err, A.host_err);
       for (int i = tid; i < A.max_small; i += FT)
         __hip_atomic_store(A.sync + 4 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tid == 0) {
-        __hip_atomic_store(A.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(A.sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (tid == 0) __hip_atomic_store(A.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       stores_done();
       if (tid == 0) __hip_atomic_store(A.sync, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       routed = true;
       continue;
     }
     if (!routed) {
-      block_wait(A.sync, A.epoch, status);
+      if (!block_wait(A.sync, A.epoch, A, &wait_flag)) return;  // the tables are not published
       routed = true;
     }
     int it = item - 1;
@@ -149,19 +159,21 @@ __global__ void __launch_bounds__(FT, 1) fused_forward(const FusedFwdArgs A) {
       int j, nt;
       raster(it, A.max_small, A.nnt2, j, nt);
       if (j < get(A.tiles + 1, true)) {
-        block_wait(A.sync + 4 + j, (uint32_t)A.nnt1, status);
+        if (!block_wait(A.sync + 4 + j, (uint32_t)A.nnt1, A, &wait_flag)) return;
         if (gemm_tile<FG2>(A.g2, it, smem)) block_signal_add(A.sync + 1);
       }
       __syncthreads();
       continue;
     }
     it -= A.n2;
-    block_wait(A.sync + 1, (uint32_t)(get(A.tiles + 1, true) * A.nnt2), status);
+    if (!block_wait(A.sync + 1, (uint32_t)(get(A.tiles + 1, true) * A.nnt2), A, &wait_flag)) return;
     combine_item(A, it);
   }
 }
 
 }  // namespace
+
+void set_fused_spin_cap(uint32_t polls) { g_spin_cap = polls ? polls : SPIN_CAP; }
 
 int64_t fused_forward_sync_words(int64_t S, int64_t E) { return 4 + max_small_tiles(S, E, true); }
 
@@ -169,8 +181,8 @@ hipError_t launch_fused_forward(const int32_t* ids, int64_t T, int64_t H, int64_
                                 const uint16_t* w1, const uint16_t* w2, const float* topk_w, uint16_t* y,
                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot,
                                 int32_t* tok_of_row, int32_t* tiles, int32_t* err, int32_t* host_err, uint16_t* h,
-                                uint16_t* a, uint16_t* aw, uint16_t* o, uint32_t* sync, uint32_t epoch, int max_groups,
-                                hipStream_t stream) {
+                                uint16_t* a, uint16_t* aw, uint16_t* o, uint32_t* sync, uint32_t epoch,
+                                uint32_t* host_status, int max_groups, hipStream_t stream) {
   const int64_t S = T * K;
   FusedFwdArgs A{};
   A.ids = ids;
@@ -198,6 +210,8 @@ hipError_t launch_fused_forward(const int32_t* ids, int64_t T, int64_t H, int64_
   A.ncomb = (int)((T + A.ct - 1) / A.ct);
   A.sync = sync;
   A.epoch = epoch;
+  A.spin_cap = g_spin_cap;
+  A.host_status = host_status;
   const int64_t total = 1 + (int64_t)A.n1 + A.n2 + A.ncomb;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = (int)(total < max_groups ? total : max_groups);

@@ -209,13 +209,17 @@ hipError_t launch_combine_dx(const uint16_t* rows, const int32_t* row_of_slot, i
 // (all resident), synchronised through fused_forward_sync_words(S, E) counters
 // in ``sync`` that the call resets itself (epoch: a nonzero per-call value).
 // Needs S <= RT_ONE_MAX_SLOTS, E <= RT_ONE_MAX_EXPERTS and the narrow tiling.
+// A wait that gives up stores 1 into *host_status (pinned host memory the caller
+// cleared) and that workgroup stops; set_fused_spin_cap sets the polls before a
+// wait gives up for later launches (0: the default, about a second).
 int64_t fused_forward_sync_words(int64_t S, int64_t E);
+void set_fused_spin_cap(uint32_t polls);
 hipError_t launch_fused_forward(const int32_t* ids, int64_t T, int64_t H, int64_t I, int E, int K, const uint16_t* x,
                                 const uint16_t* w1, const uint16_t* w2, const float* topk_w, uint16_t* y,
                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot,
                                 int32_t* tok_of_row, int32_t* tiles, int32_t* err, int32_t* host_err, uint16_t* h,
-                                uint16_t* a, uint16_t* aw, uint16_t* o, uint32_t* sync, uint32_t epoch, int max_groups,
-                                hipStream_t stream);
+                                uint16_t* a, uint16_t* aw, uint16_t* o, uint32_t* sync, uint32_t epoch,
+                                uint32_t* host_status, int max_groups, hipStream_t stream);
 
 // float32-output (accuracy) mode (gemm_f32.hip, pointwise.hip).  Operands that are
 // not exact bf16 inputs are bf16 [hi | lo] pairs of twice the width; see gemm_f32.hip.

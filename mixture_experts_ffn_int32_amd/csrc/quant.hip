@@ -19,7 +19,14 @@ namespace hmm {
 constexpr int QT = 256;  // threads per quantisation block
 constexpr int QH = 256;  // hidden rows per column-maximum chunk
 
-__device__ __forceinline__ float scale_of(float absmax) { return absmax > 0.f ? 448.f / absmax : 1.f; }
+// 448 / max|x| in float32; an all-zero row or group gets 1.  Below a largest
+// value of about 1.3e-36 (bf16 holds values down to ~9e-41) the quotient
+// overflows: it is clamped to the largest finite float32, so the codes stay
+// finite (x * scale is then at most ~448) and the descale 1 / scale is a
+// subnormal float32 (about 2.9e-39) instead of 0.
+__device__ __forceinline__ float scale_of(float absmax) {
+  return absmax > 0.f ? fminf(448.f / absmax, 3.40282347e38f) : 1.f;
+}
 
 // 8 floats * scale -> 8 E4M3 bytes
 __device__ __forceinline__ uint2 to_e4m3x8(const float (&v)[8], const float (&s)[8]) {

@@ -36,12 +36,24 @@ def _bf16_matrix(shape, seed, outliers=True):
     return synth.to_bf16_bits(a)
 
 
+def _tiny(shape, seed):
+    """bf16 values of magnitude up to ~1e-38 (bf16 subnormals included), a third of them zero."""
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(shape) * 4e-39).astype(np.float32)
+    a[rng.random(shape) < 1 / 3] = 0
+    return synth.to_bf16_bits(a)
+
+
 @pytest.mark.parametrize("T,H", [(1, 64), (37, 320), (300, 4096)])
 def test_row_quantiser_bit_exact(T, H):
     from mixture_experts_ffn_int32_amd import quantize_rows_fp8
     bits = _bf16_matrix((T, H), seed=T + H, outliers=T > 2)
     if T > 3:
         bits[3] = 0                              # an all-zero row: scale 1, codes 0
+    if T > 4:
+        # a row whose largest value (~1e-38, with zeros) makes 448 / max overflow float32:
+        # the scale is clamped to the largest finite float32, the codes stay finite
+        bits[4] = _tiny(bits[4].shape, seed=T)
     announce("row quantiser T=%d H=%d" % (T, H))
     q, ds = quantize_rows_fp8(bf16_tensor(bits, "cuda"))
     rq, _, rds = quantize_rows(synth.bits_to_f32(bits))
@@ -54,6 +66,7 @@ def test_column_quantiser_bit_exact(E, H, N):
     from mixture_experts_ffn_int32_amd import quantize_cols_fp8
     bits = _bf16_matrix((E, H, N), seed=E * H + N)
     bits[:, :, 5] = 0                            # an all-zero column in every expert
+    bits[:, :, 7] = _tiny(bits[:, :, 7].shape, seed=E)   # a column whose 448 / max overflows float32
     announce("column quantiser E=%d H=%d N=%d" % (E, H, N))
     q, ds = quantize_cols_fp8(bf16_tensor(bits, "cuda"))
     qv = _e4m3_values(q)

@@ -23,7 +23,8 @@ def _e4m3_values(q):
 
 def _bf16_groups(shape, seed):
     """Normal values with a different magnitude per 128-group (2^-30 .. 2^30), 1% outliers
-    x30, an all-zero group, a group of tiny values and one near the top of the bf16 range."""
+    x30, an all-zero group, groups of tiny values (one whose 448 / max overflows float32) and
+    one near the top of the bf16 range."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(shape).astype(np.float32)
     ng = shape[-1] // GROUP
@@ -34,6 +35,10 @@ def _bf16_groups(shape, seed):
     if flat.shape[0] > 2:
         flat[1, GROUP:2 * GROUP] *= 1e-25
         flat[2, :GROUP] = np.float32(2.0 ** 120) * np.sign(flat[2, :GROUP])
+    if flat.shape[0] > 3:
+        # a group whose largest value (~1e-38, with zeros) makes 448 / max overflow float32
+        flat[3, :GROUP] = rng.standard_normal(GROUP).astype(np.float32) * np.float32(4e-39)
+        flat[3, :GROUP:3] = 0.0
     return synth.to_bf16_bits(a)
 
 

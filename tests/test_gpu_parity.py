@@ -249,7 +249,9 @@ FUSED = [
 
 @pytest.mark.parametrize("name,over", FUSED, ids=[f[0] for f in FUSED])
 def test_fused_forward_equals_kernel_sequence(name, over):
-    """The one-launch forward gives bit-identical y and saved arrays to the kernel sequence."""
+    """The one-launch forward matches the FAITHFUL oracle (y, and the saved h and a
+    element by element; the routing arrays bit-exactly), and gives bit-identical y
+    and saved arrays to the kernel sequence."""
     import torch
     from mixture_experts_ffn_int32_amd import forward_with_saved, saved_views
     spec = synth.spec_with("tiny", **over)
@@ -260,11 +262,62 @@ def test_fused_forward_equals_kernel_sequence(name, over):
     y1, s1 = forward_with_saved(*args, tiles="narrow", fused=True)
     y0, s0 = forward_with_saved(*args, tiles="narrow", fused=False)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y0)
     v1 = saved_views(s1, *(spec[k] for k in "THIEK"), tiles="narrow")
+    ref_route = oracle_route(inp["topk_ids"], spec["E"])
+    for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
+        assert np.array_equal(v1[k].cpu().numpy(), ref_route[k]), k
+    announce("oracle forward and intermediates of %d slots" % ref_route["sorted_slot"].size)
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    ry, ryd = o.forward_dev()
+    assert_close(to_f64(y1), ry, "y", ryd)
+    (h, a, _), (hd, ad, _) = o.slot_intermediates_dev(ref_route["sorted_slot"])
+    assert_close(to_f64(v1["h"]), h, "h", hd)
+    assert_close(to_f64(v1["a"]), a, "a", ad)
+    assert torch.equal(y1, y0)
     v0 = saved_views(s0, *(spec[k] for k in "THIEK"), tiles="narrow")
     for k in v1:
         assert torch.equal(v1[k], v0[k]), k
+
+
+def test_fused_forward_reports_a_wait_that_gives_up():
+    """With the wait limit lowered from the host to one poll, the fused forward's waits
+    give up (the routing item still runs; every workgroup ends normally): the call
+    returns HMM_ERR_TIMEOUT.  The next call, at the default limit, is correct."""
+    import ctypes
+    import torch
+    from mixture_experts_ffn_int32_amd import _lib, forward_with_saved
+    spec = synth.spec_with("tiny", T=1024, H=512, I=128, E=4, K=2, routing="uniform")
+    T, H, I, E, K = (spec[k] for k in "THIEK")
+    lib = _lib.load()
+    prob = _lib.Problem(T, H, I, E, K, _lib.HMM_BF16, _lib.HMM_BF16,
+                        _lib.HMM_FLAG_VALIDATE_IDS | _lib.HMM_FLAG_FUSED_FORWARD | _lib.HMM_FLAG_TILES_NARROW, 0)
+    ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(lib.hmm_forward_sizes(ctypes.byref(prob), ctypes.byref(ws), ctypes.byref(sv)))
+    work = torch.zeros(ws.value, dtype=torch.uint8, device="cuda")
+    saved = torch.empty(sv.value, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    g = gpu_inputs(synth.make_inputs(spec, seed=60), "cuda")
+
+    def call():
+        return lib.hmm_forward(ctypes.byref(prob), P(g["x"]), P(g["topk_ids"]), P(g["topk_weights"]),
+                               P(g["up_proj_weight"]), P(g["down_proj_weight"]), P(y), P(saved), sv.value, P(work),
+                               ws.value, stream)
+    announce("fused forward with a one-poll wait limit")
+    try:
+        _lib.check(lib.hmm_set_fused_spin_limit(1))
+        st = call()
+    finally:
+        _lib.check(lib.hmm_set_fused_spin_limit(0))
+    assert st == _lib.HMM_ERR_TIMEOUT, lib.hmm_status_string(st)
+    assert b"gave up" in lib.hmm_last_error_message()
+    announce("fused forward after the failure, default limit")
+    _lib.check(call())
+    ref, _ = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
+                                g["down_proj_weight"], tiles="narrow", fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
 
 
 def test_fused_forward_reuses_its_workspace():
