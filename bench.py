@@ -7,7 +7,10 @@ synthetic input already resident in HBM, through the C ABI of libhmm.
 
 Prints ONE JSON line on stdout; details go to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sample|tiny|skewed|hotspot|fp8|mx|group]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload hotspot|skewed|sample|tiny|fp8|mx|group]
+
+The default workload is hotspot (T=8192, H=7168, I=2048, E=32, K=8: the
+largest bf16 workload of the list, one hot expert in every token).
 
 Timing: W untimed warm-up steps (the first one's time is reported as
 first_step_ms), then K steps between two synchronisations, timed with HIP
@@ -15,8 +18,11 @@ events on the stream the kernels run on -> ms_per_step and tokens/s.  A second
 pass of K steps, with an event after each call, gives the forward and backward
 times (fwd_ms, bwd_ms).  A third pass of K steps records HIP events around
 every kernel launch (the library's stage timing) and gives each kernel's
-average duration for the roofline figures.  The CPU oracle is then timed on a bounded sample of the
-same workload on the host's cores.
+average duration for the roofline figures.  A fourth pass writes a 1 GiB
+scratch buffer before every step (more than the 256 MB last-level cache holds)
+and times the HBM-bound kernels again (flushed figures, beside the warm ones).
+The CPU oracle (its pure mode, float32 sums: the plain per-token loop) is then
+timed on a bounded sample of the same workload on the host's cores.
 """
 
 import argparse
@@ -30,9 +36,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+from mixture_experts_ffn_int32_amd.roofline import PEAK_BF16_TFLOPS, PEAK_FP8_TFLOPS, PEAK_HBM_GBS, stage_work  # noqa: E402,F401
 
 
 def log(*a):
@@ -61,58 +65,6 @@ def recorded_traffic(workload, kernel):
         return None
     ent = rec.get("per_workload", {}).get(workload, {}).get(kernel)
     return None if ent is None else int(round(ent["bytes"]))
-
-
-def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
-    """Algorithmic work of one launch of a stage: (bound, amount, unit, peak).
-
-    The float32-output mode counts the same algorithmic flops (its hi/lo operand
-    pairs make the MFMAs do about 1.9x that work) and float32 rows in the combines.
-    Is > 0: a shared expert of that width (one more group of all T rows)."""
-    S = T * K
-    eb = 4 if f32 else 2
-    if stage in ("gmm1_fp8_swiglu", "gmm1_mx_swiglu", "gmm1_group_swiglu"):
-        return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
-    flops = {
-        "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
-        "gmm2": 2 * S * I * H,          # [S,I] x [I,H]
-        "act_grad": 2 * S * H * I,      # [S,H] x [H,I]
-        "input_grad": 4 * S * I * H,    # [S,2I] x [2I,H]
-        "dw2": 2 * S * I * H,           # [I,S] x [S,H]
-        "dw1": 4 * S * H * I,           # [H,S] x [S,2I]
-    }
-    flops["act_grad+dw2"] = flops["act_grad"] + flops["dw2"]      # two products in one launch
-    flops["input_grad+dw1"] = flops["input_grad"] + flops["dw1"]
-    # a shared expert: the same products over T rows of width Is, in the routed launches ("<stage>+shared")
-    shared = {k: v * T * Is // (S * I) for k, v in flops.items()}
-    for k, v in shared.items():
-        flops[k + "+shared"] = flops[k] + v
-        flops["shared_" + k] = v                      # its own launches (float32-output mode)
-    flops["shared_gmm1"] = shared["gmm1_swiglu"]
-    if stage in flops:
-        return "mfma", flops[stage], "TFLOP/s", PEAK_BF16_TFLOPS
-    nbytes = {
-        # read K gathered rows per token + row index + weight, write one row
-        "combine": S * H * eb + S * 8 + T * H * eb + (T * H * eb if Is else 0),   # (+ shared rows)
-        "combine_dx": S * H * eb + S * 4 + T * H * eb + (T * H * eb if Is else 0),  # (+ d_topk_weights partials)
-        "shared_tables": T * 12,
-        "split_dy": T * H * 4 + T * H * 4,              # float32 dY -> bf16 hi | lo
-        # ids read twice, histograms, sorted_slot + row_of_slot written
-        "route": S * 4 * 2 + S * 8,
-        "route_narrow": S * 4 * 2 + S * 8,   # the per-group product's 64-row tile table
-        # FP8 quantisers: read the bf16 operand once, write its codes and descales
-        "quant_x": T * H * 2 + T * H + T * 4,
-        "quant_w1": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * 4,
-        # MX quantisers: the bf16 operand once, its codes and one exponent byte per 32 elements
-        "quant_x_mx": T * H * 2 + T * H + T * H // 32,
-        "quant_w1_mx": E * H * 2 * I * 2 + E * H * 2 * I + E * 2 * I * H // 32,
-        # per group of 128 along H: one float32 descale per token row / weight column
-        "quant_x_group": T * H * 2 + T * H + T * (H // 128) * 4,
-        "quant_w1_group": E * H * 2 * I * 2 + E * H * 2 * I + E * (H // 128) * 2 * I * 4,
-    }
-    if stage in nbytes:
-        return "hbm", nbytes[stage], "GB/s", PEAK_HBM_GBS
-    return None, 0, None, None
 
 
 class Runner:
@@ -203,6 +155,18 @@ class Runner:
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    def timed_flushed(self, n, flush_mb):
+        """n steps, each preceded by a write of flush_mb MiB of scratch on the same stream
+        (the stage events of the library time the kernels; the write is not a stage)."""
+        torch = self.torch
+        if getattr(self, "_scratch", None) is None or self._scratch.numel() != flush_mb << 18:
+            self._scratch = torch.empty(flush_mb << 18, dtype=torch.float32, device=self.x.device)
+        torch.cuda.synchronize()
+        for i in range(n):
+            self._scratch.fill_(float(i))
+            self.step()
+        torch.cuda.synchronize()
+
     def timed_split(self, n):
         """Average forward and backward times (ms) over n steps, an event after each call."""
         torch = self.torch
@@ -221,7 +185,9 @@ class Runner:
 
 
 def cpu_baseline(spec, seed, budget_s=12.0):
-    """Time the oracle (faithful fwd + full bwd) on a bounded prefix of the workload's tokens."""
+    """Time the oracle's pure mode with float32 sums (forward + full backward: the plain
+    per-token loop over K experts, and each expert's weight gradients) on a bounded
+    prefix of the workload's tokens."""
     import numpy as np
     from mixture_experts_ffn_int32_amd import synth
     from oracle.moe_ffn import MoEFFN
@@ -241,7 +207,7 @@ def cpu_baseline(spec, seed, budget_s=12.0):
             if k in inp:
                 d[k] = synth.bits_to_f32(inp[k])
         t0 = time.perf_counter()
-        m = MoEFFN(**d, mode="faithful", gmm1=spec.get("gmm1", "bf16"))
+        m = MoEFFN(**d, mode="pure", gmm1=spec.get("gmm1", "bf16"), acc="f32")
         m.forward()
         m.backward()
         if m.shared is not None:
@@ -259,8 +225,8 @@ def cpu_baseline(spec, seed, budget_s=12.0):
         el += run(tp)
         passes += 1
     return {"value": passes * tp / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "first %d of %d tokens of the same workload x %d pass(es), FAITHFUL float64 forward + full "
-                      "backward (numpy, %d BLAS threads), %.1f s" % (tp, T, passes, cores, el)}
+            "sample": "first %d of %d tokens of the same workload x %d pass(es), oracle pure mode with float32 "
+                      "sums, forward + full backward (numpy, %d BLAS threads), %.1f s" % (tp, T, passes, cores, el)}
 
 
 def main():
@@ -268,7 +234,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sample")
+    ap.add_argument("--workload", default="hotspot")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-validate", action="store_true", help="skip the id check's device-to-host read-back")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"],
@@ -276,7 +242,10 @@ def main():
     ap.add_argument("--shared-I", type=int, default=0, metavar="IS",
                     help="add a shared expert of intermediate size IS (every token, weight 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=40.0,
+                    help="the oracle sample grows until it takes about a quarter of this (seconds)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="scratch written before each step of the flushed pass (0: no flushed pass)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -361,6 +330,26 @@ def main():
         "traffic": recorded_traffic(args.workload, dom[0]),
     }
 
+    # fourth pass: the HBM-bound kernels with the last-level cache flushed before every step
+    hbm_rows = [x for x in rows if x[3] == "hbm"]
+    flushed = {}
+    if args.flush_mb > 0 and hbm_rows:
+        _lib.profile_read()
+        _lib.profile_enable(True)
+        r.timed_flushed(args.steps, args.flush_mb)
+        _lib.profile_enable(False)
+        flushed, _ = _lib.profile_read()
+    hbm = {}
+    for name, n, avg, bound, work, rate, unit, frac, peak in hbm_rows:
+        ent = {"bytes": work, "warm_ms": round(avg, 5), "warm_GBs": round(rate, 1), "warm_frac": round(frac, 4)}
+        if name in flushed:
+            fn, ftot = flushed[name]
+            favg = ftot / max(fn, 1)
+            frate = work / (favg * 1e-3) / 1e9
+            ent.update({"flushed_ms": round(favg, 5), "flushed_GBs": round(frate, 1), "flushed_frac": round(frate / peak, 4)})
+            log("[bench]   %-16s flushed avg %9.4f ms  %.1f GB/s (%.1f%% of peak)" % (name, favg, frate, 100 * frate / peak))
+        hbm[name] = ent
+
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -391,6 +380,9 @@ def main():
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
         "gemm_frac_peak": round(gemm_ms_at_peak / gemm_ms, 5) if gemm_ms > 0 else None,
         "roofline": roofline,
+        "stage_ms": {x[0]: round(x[2], 5) for x in rows},
+        "hbm_kernels": hbm,
+        "flush_mb": args.flush_mb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -296,9 +296,13 @@ class MoEFFN:
 
     def hidden_dev(self, e, xrows, icols=None):
         """(g, u, a) and their deviations for gate columns ``icols`` (default all)."""
-        icols = np.arange(self.I) if icols is None else np.asarray(icols)
-        h, hd = self.up_dev(e, xrows, np.concatenate([icols, icols + self.I]))
-        n = icols.size
+        if icols is None:
+            h, hd = self.up_dev(e, xrows)
+            n = self.I
+        else:
+            icols = np.asarray(icols)
+            h, hd = self.up_dev(e, xrows, np.concatenate([icols, icols + self.I]))
+            n = icols.size
         g, u = h[:, :n], h[:, n:]
         s = self._sig(g)
         v = g * s * u                                           # R2
@@ -464,9 +468,9 @@ class MoEFFN:
         """
         if self.dY is None:
             raise ValueError("dY required")
-        icols = np.arange(self.I) if icols is None else np.asarray(icols)
+        icols = None if icols is None else np.asarray(icols)   # None: all columns, without an indexed copy
         slots = self.slots_of_expert(e)
-        n = icols.size
+        n = self.I if icols is None else icols.size
         if slots.size == 0:
             z = np.zeros((self.H, n))
             zr = np.zeros((n, self.H))
@@ -481,7 +485,7 @@ class MoEFFN:
         (dg, dgd), (du, dud) = self.swiglu_grad_dev(w, G, Ge, g, u, gd, ud)
         if not self.faithful:
             res = (xr.T @ dg, xr.T @ du, (w * a).T @ dyr)
-            return res, tuple(np.zeros(r.shape) for r in res)
+            return res, tuple(np.broadcast_to(0.0, r.shape) for r in res)
         aw, awd = self._round(w * a, C_PROP * np.abs(w) * ad + C_EL * U32 * np.abs(w * a))    # R8
         m = slots.size
         res = [xr.T @ dg, xr.T @ du, aw.T @ dyr]                                      # R9
@@ -499,8 +503,13 @@ class MoEFFN:
     def backward_dev(self, out_dtype="bf16"):
         """Full backward with deviations: ((dx, dw, dW1, dW2), (their devs))."""
         (dx, dw), (dxd, dwd) = self.backward_tokens_dev(None, out_dtype)
-        dW1 = np.zeros((self.E, self.H, 2 * self.I))
-        dW2 = np.zeros((self.E, self.I, self.H))
+        dW1 = np.zeros((self.E, self.H, 2 * self.I), self.ft)
+        dW2 = np.zeros((self.E, self.I, self.H), self.ft)
+        if not self.faithful:   # no deviations: zero views, nothing allocated
+            for e in range(self.E):
+                (g, u, r), _ = self.weight_grads_expert_dev(e, None, out_dtype)
+                dW1[e, :, :self.I], dW1[e, :, self.I:], dW2[e] = g, u, r
+            return (dx, dw, dW1, dW2), (dxd, dwd, np.broadcast_to(0.0, dW1.shape), np.broadcast_to(0.0, dW2.shape))
         dW1d, dW2d = np.zeros_like(dW1), np.zeros_like(dW2)
         for e in range(self.E):
             (g, u, r), (gd, ud, rd) = self.weight_grads_expert_dev(e, None, out_dtype)
