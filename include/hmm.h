@@ -23,7 +23,8 @@
  *   device); all are caller-owned and caller-allocated.  The library never
  *   allocates device memory.  Its only state is, per host thread and device,
  *   one pinned host word and event for the id check (and for the fused
- *   forward), and the optional stage-timing events.
+ *   forward), the optional stage-timing events, and the device array of
+ *   hmm_forward_noalloc (64 MiB per device, fixed at load).
  * - All tensors are dense, row-major (last index fastest), with no padding.
  *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
  *   be 16-byte aligned.
@@ -206,6 +207,32 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
                        const float* topk_weights, const void* up_w, const void* down_w, void* y,
                        void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* hmm_forward without a workspace argument, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same problem, inputs, outputs and
+ * saved buffer as hmm_forward (same kernels, identical results); the forward
+ * workspace comes from a device array inside the library instead.
+ * - That array holds 64 MiB (67108864 bytes).  It is allocated when the library
+ *   is loaded on a device (one copy per device, kept until the process ends)
+ *   and is never freed.  A problem whose hmm_forward_sizes workspace exceeds it
+ *   returns HMM_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Routed problems
+ *   need about S*H*2 bytes, plus small routing tables.  For example, T=256 and K=8
+ *   at H=7168 fit, and the skewed size T=4000, H=2048, K=8 does not (131 MB).
+ * - The call allocates no device or pinned host memory and creates no HIP
+ *   object (no hipMalloc, hipFree, hipHostMalloc or event creation); stage
+ *   timing is paused during it.  So it takes
+ *   neither HMM_FLAG_VALIDATE_IDS nor HMM_FLAG_FUSED_FORWARD (HMM_ERR_UNSUPPORTED):
+ *   invalid ids are dropped and flagged in ``saved`` instead.  No shared expert.
+ * - Nothing in the array has to start at any value: every call writes what it
+ *   later reads.  The array keeps the last call's contents.
+ * - All calls on one device share the one array: calls that overlap in time
+ *   on a device (several streams, or host threads) race on it and must be
+ *   ordered by the caller. */
+hmm_status hmm_forward_noalloc(const hmm_problem* p, const void* x, const int32_t* topk_ids,
+                               const float* topk_weights, const void* up_proj_weight,
+                               const void* down_proj_weight, void* y, void* saved, size_t saved_bytes,
+                               void* stream);
 
 /* Forward with a shared expert (RFC section 6.1: a shared expert fused into the
  * same pipeline, its output merged at the Combine).  Every token also goes

@@ -35,7 +35,7 @@ EXPORTS = (
     "hmm_route_workspace_size", "hmm_route", "hmm_status_string", "hmm_last_error_message", "hmm_build_info",
     "hmm_profile_enable", "hmm_profile_read", "hmm_quant_rows_fp8", "hmm_quant_cols_workspace_size",
     "hmm_quant_cols_fp8", "hmm_forward_shared", "hmm_backward_shared", "hmm_quant_rows_mx", "hmm_quant_cols_mx",
-    "hmm_quant_rows_group", "hmm_quant_cols_group", "hmm_set_fused_spin_limit",
+    "hmm_quant_rows_group", "hmm_quant_cols_group", "hmm_set_fused_spin_limit", "hmm_forward_noalloc",
 )
 
 
@@ -67,6 +67,7 @@ _SIGS = {
     "hmm_forward": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P],
     "hmm_backward_sizes": [_PROB, ctypes.POINTER(_SZ)],
     "hmm_backward": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _SZ, _P],
+    "hmm_forward_noalloc": [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "hmm_forward_shared": [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P],
     "hmm_backward_shared": [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "hmm_route_workspace_size": [_PROB, ctypes.POINTER(_SZ)],

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -994,6 +995,74 @@ hmm_status hmm_quant_cols_group(const void* w, int64_t E, int64_t H, int64_t N, 
   Stage stage("quant_w1_group", (hipStream_t)stream);
   const hipError_t e = hmm::launch_quant_cols_group((const uint16_t*)w, E, H, N, wq, dsw, (hipStream_t)stream);
   return e == hipSuccess ? HMM_OK : hip_fail(e, "weight quantisation launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------- no-allocation forward
+// hmm_forward_noalloc takes its workspace from this file-scope device array:
+// one copy per device, held from the library's load on that device until the
+// process ends.  In host code the name is only a host-side stand-in; the
+// array's device address comes from hipGetSymbolAddress, once per device, and
+// only that address is handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+struct NoallocScratch {
+  std::mutex m;
+  void* ptr[MAX_DEVICES] = {};
+};
+NoallocScratch g_noalloc;
+
+// The current device's address of ``scratch`` (looked up on its first use there).
+hmm_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(HMM_ERR_UNSUPPORTED, "device %d is beyond the %d tracked", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_noalloc.m);
+  if (!g_noalloc.ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "address of the no-allocation scratch");
+    if (!ptr) return fail(HMM_ERR_HIP, "the no-allocation scratch has no device address");
+    g_noalloc.ptr[dev] = ptr;
+  }
+  *out = g_noalloc.ptr[dev];
+  return HMM_OK;
+}
+
+// Stage timing off for the guard's lifetime (its events are created on first use).
+struct ProfPause {
+  bool was = g_prof.on;
+  ProfPause() { g_prof.on = false; }
+  ~ProfPause() { g_prof.on = was; }
+};
+}  // namespace
+
+extern "C" {
+
+hmm_status hmm_forward_noalloc(const hmm_problem* p, const void* x, const int32_t* topk_ids,
+                               const float* topk_weights, const void* up_w, const void* down_w, void* y, void* saved,
+                               size_t saved_bytes, void* stream) {
+  Dims d;
+  hmm_status s = validate(p, &d);
+  if (s != HMM_OK) return s;
+  if (d.shared) return fail(HMM_ERR_BAD_SHAPE, "shared_I != 0: the no-allocation forward has no shared expert");
+  if (p->flags & (HMM_FLAG_VALIDATE_IDS | HMM_FLAG_FUSED_FORWARD))
+    return fail(HMM_ERR_UNSUPPORTED, "the no-allocation forward takes neither HMM_FLAG_VALIDATE_IDS nor "
+                "HMM_FLAG_FUSED_FORWARD (both need pinned host memory and events created on first use); invalid "
+                "ids are dropped and flagged in saved's id_error word");
+  const size_t need_bytes = fwd_work(d).total;
+  if (need_bytes > NOALLOC_SCRATCH_BYTES)
+    return fail(HMM_ERR_WORKSPACE_TOO_SMALL, "the problem needs %zu bytes of forward workspace; the no-allocation "
+                "forward holds %zu (use hmm_forward with a workspace)", need_bytes, NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if ((s = noalloc_scratch(&ptr)) != HMM_OK) return s;
+  ProfPause pause;
+  return forward_impl(p, d, x, topk_ids, topk_weights, up_w, down_w, nullptr, nullptr, y, saved, saved_bytes, ptr,
+                      NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
