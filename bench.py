@@ -18,7 +18,9 @@ events on the stream the kernels run on -> ms_per_step and tokens/s.  A second
 pass of K steps, with an event after each call, gives the forward and backward
 times (fwd_ms, bwd_ms).  A third pass of K steps records HIP events around
 every kernel launch (the library's stage timing) and gives each kernel's
-average duration for the roofline figures.  A fourth pass writes a 1 GiB
+average duration for the roofline figures (this pass runs the backward's
+launches in series, so each kernel has the chip to itself; the timed steps use
+the default, with the weight gradients on a second stream).  A fourth pass writes a 1 GiB
 scratch buffer before every step (more than the 256 MB last-level cache holds)
 and times the HBM-bound kernels again (flushed figures, beside the warm ones).
 The CPU oracle (its pure mode, float32 sums: the plain per-token loop) is then
@@ -70,7 +72,7 @@ def recorded_traffic(workload, kernel):
 class Runner:
     """Preallocated buffers and raw C-ABI calls for one workload."""
 
-    def __init__(self, spec, seed, device, validate_ids=True, out_dtype="bf16"):
+    def __init__(self, spec, seed, device, validate_ids=True, out_dtype="bf16", serial_backward=False):
         import torch
         from mixture_experts_ffn_int32_amd import _lib, synth
         self.torch = torch
@@ -94,7 +96,8 @@ class Runner:
         self.W2 = bf(inp["down_proj_weight"])
         self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
-        flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+        flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | (
+            _lib.HMM_FLAG_SERIAL_BACKWARD if serial_backward else 0)
         gmm1 = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3,
                 "group": _lib.HMM_FP8_E4M3_GROUP}[spec.get("gmm1", "bf16")]
         f32 = out_dtype == "f32"
@@ -242,6 +245,8 @@ def main():
     ap.add_argument("--shared-I", type=int, default=0, metavar="IS",
                     help="add a shared expert of intermediate size IS (every token, weight 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial-backward", action="store_true",
+                    help="keep every backward launch on one stream (HMM_FLAG_SERIAL_BACKWARD)")
     ap.add_argument("--cpu-budget", type=float, default=40.0,
                     help="the oracle sample grows until it takes about a quarter of this (seconds)")
     ap.add_argument("--flush-mb", type=int, default=1024,
@@ -276,7 +281,8 @@ def main():
     T, H, I, E, K = (spec[k] for k in "THIEK")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate, out_dtype=args.out_dtype)
+    r = Runner(spec, args.seed, dev, validate_ids=not args.no_validate, out_dtype=args.out_dtype,
+               serial_backward=args.serial_backward)
     log("[bench] workload %s T=%d H=%d I=%d E=%d K=%d shared_I=%d; workspace fwd %.1f MB, saved %.1f MB, bwd %.1f MB"
         % (args.workload, T, H, I, E, K, Is, r.sizes[0] / 1e6, r.sizes[1] / 1e6, r.sizes[2] / 1e6))
 
@@ -295,10 +301,15 @@ def main():
     fwd_ms, bwd_ms = r.timed_split(args.steps)
     log("[bench] forward %.4f ms, backward %.4f ms per step" % (fwd_ms, bwd_ms))
 
-    # second pass: per-kernel device time from the library's stage events
+    # third pass: per-kernel device time from the library's stage events, with the
+    # backward's launches in series (each kernel alone on the chip, so the stage
+    # times add up and give each kernel's own rate)
     _lib.profile_read()
     _lib.profile_enable(True)
+    flags0 = r.prob.flags
+    r.prob.flags = flags0 | _lib.HMM_FLAG_SERIAL_BACKWARD
     prof_ms = r.timed(args.steps)
+    r.prob.flags = flags0
     _lib.profile_enable(False)
     stages, dropped = _lib.profile_read()
     log("[bench] profiled pass %.4f ms/step; %d launches untimed" % (prof_ms / args.steps, dropped))
@@ -375,7 +386,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
                    "routing": spec.get("routing"), "shared_I": Is, "seed": args.seed,
-                   "validate_ids": not args.no_validate,
+                   "validate_ids": not args.no_validate, "serial_backward": args.serial_backward,
                    "out_dtype": args.out_dtype},
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,
         "gemm_frac_peak": round(gemm_ms_at_peak / gemm_ms, 5) if gemm_ms > 0 else None,

@@ -110,6 +110,18 @@ typedef enum hmm_dtype {
  * therefore returns only after its launch has completed. */
 #define HMM_FLAG_FUSED_FORWARD 8u
 
+/* The backward of a large-tiled problem (not the narrow tiling, bf16 outputs)
+ * whose act_grad has fewer than 4 waves of 256-row tiles on the chip runs its
+ * weight gradients on a second stream of the library's (one per host thread and
+ * device, default priority), beside the dX chain on the caller's stream: W2Grad
+ * starts with act_grad, W1Grad starts once act_grad has written dH and runs
+ * beside input_grad and Combine(dX) (RFC 2.2).  The caller's stream waits for
+ * both through events, so the call's ordering on ``stream`` is unchanged.  (With
+ * longer products, two of them sharing the L2 caches are slower than one after
+ * the other.)  This flag keeps every launch on the caller's stream, in series;
+ * results are identical either way. */
+#define HMM_FLAG_SERIAL_BACKWARD 16u
+
 /* Problem description.
  *   T  tokens (>= 0; T = 0 is a no-op that still writes zero weight gradients)
  *   H  hidden size, multiple of 64, 64 <= H <= 65536

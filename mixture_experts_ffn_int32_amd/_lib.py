@@ -27,6 +27,7 @@ HMM_FLAG_VALIDATE_IDS = 1
 HMM_FLAG_TILES_LARGE = 2
 HMM_FLAG_TILES_NARROW = 4
 HMM_FLAG_FUSED_FORWARD = 8
+HMM_FLAG_SERIAL_BACKWARD = 16
 TILE_FLAGS = {"auto": 0, "large": HMM_FLAG_TILES_LARGE, "narrow": HMM_FLAG_TILES_NARROW}
 
 # every symbol include/hmm.h declares

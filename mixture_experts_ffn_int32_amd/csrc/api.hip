@@ -48,6 +48,7 @@ struct Dims {
   bool group;  // ... with per-group (128 along H) float scales
   bool f32;    // float32 outputs (accuracy mode)
   bool fused;  // small problem whose forward runs as one fused launch (fused.hip)
+  uint32_t flags;
 };
 
 hmm_status validate(const hmm_problem* p, Dims* d) {
@@ -64,7 +65,8 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_BAD_SHAPE, "I must be a multiple of 64 in [64, 65536] (got %lld)", (long long)p->I);
   if (p->T > (int64_t)0x7fffffff / p->K)
     return fail(HMM_ERR_BAD_SHAPE, "T*K must stay below 2^31 (T=%lld, K=%lld)", (long long)p->T, (long long)p->K);
-  if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW | HMM_FLAG_FUSED_FORWARD))
+  if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW | HMM_FLAG_FUSED_FORWARD |
+                   HMM_FLAG_SERIAL_BACKWARD))
     return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
   if ((p->flags & HMM_FLAG_TILES_LARGE) && (p->flags & HMM_FLAG_TILES_NARROW))
     return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
@@ -106,6 +108,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
              : hmm::small_mode(d->S, d->H, d->I);
   d->fused = d->small && !d->fp8 && !d->f32 && !d->shared && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
              d->E <= hmm::RT_ONE_MAX_EXPERTS && (p->flags & HMM_FLAG_FUSED_FORWARD);
+  d->flags = p->flags;
   return HMM_OK;
 }
 
@@ -303,6 +306,11 @@ struct DevState {
   uint32_t* fused_status = nullptr;  // pinned: the fused forward stores 1 when a wait gave up
   hipEvent_t fused_ev = nullptr;     // recorded after a fused forward launch
   int cus = 0;  // compute units (the fused kernel's workgroup count: all resident)
+  // the backward's second stream (default priority, non-blocking) and its fork,
+  // dH-ready and join events; created on the first large backward
+  bool side_ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, dh_ev = nullptr, join_ev = nullptr;
 };
 DevState* dev_state() {
   thread_local DevState st[MAX_DEVICES];
@@ -325,6 +333,28 @@ DevState* dev_state() {
   }
   c.ready = true;
   return &c;
+}
+
+// The backward's side stream and events of the current device (created once);
+// nullptr if they cannot be made (the backward then runs on one stream).
+DevState* side_state() {
+  DevState* c = dev_state();
+  if (!c) return nullptr;
+  if (c->side_ready) return c;
+  bool ok = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c->dh_ev, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    if (c->side) (void)hipStreamDestroy(c->side);
+    for (hipEvent_t* e : {&c->fork_ev, &c->dh_ev, &c->join_ev})
+      if (*e) (void)hipEventDestroy(*e);
+    c->side = nullptr;
+    c->fork_ev = c->dh_ev = c->join_ev = nullptr;
+    return nullptr;
+  }
+  c->side_ready = true;
+  return c;
 }
 
 // Enqueue the routing; with validate_ids the routing also stores its error flag
@@ -917,6 +947,57 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
                                  d_topk_weights, st);
     }
     return e == hipSuccess ? HMM_OK : hip_fail(e, "combine(dX) launch");
+  }
+  // The weight gradients run on a second stream beside the dX chain (RFC 2.2:
+  // W2Grad alongside act_grad, W1Grad alongside the rest of the dX chain) when
+  // the products are short, so neither chain's last wave of tiles leaves the
+  // chip idle and the HBM-bound Combine(dX) overlaps matrix work.  W2Grad needs
+  // only the forward's aw and dY; W1Grad waits for act_grad's dH.  The caller's
+  // stream waits for both.  With act_grad at 4 or more waves of 256-row tiles
+  // on the chip, two products sharing the XCDs' L2 caches lose more than the
+  // tails gain (measured: hotspot 18.25 -> 18.56 ms per step on two streams,
+  // skewed 2.37 -> 2.23 ms), so those stay on one stream.
+  DevState* side = nullptr;
+  if (ne && !(d.flags & HMM_FLAG_SERIAL_BACKWARD)) {
+    DevState* c = dev_state();
+    const int64_t tiles = ((d.S + hmm::TILE_BIG - 1) / hmm::TILE_BIG) * ((d.I + 255) / 256);
+    if (c && tiles < 4 * (int64_t)c->cus) side = side_state();
+  }
+  if (side) {
+    hipStream_t s2 = side->side;
+    if ((e = hipEventRecord(side->fork_ev, st)) != hipSuccess || (e = hipStreamWaitEvent(s2, side->fork_ev, 0)))
+      return hip_fail(e, "backward fork");
+    {
+      Stage stage(d.shared ? "dw2+shared" : "dw2", s2);
+      e = hmm::launch_dw2(dw2, nj, d.small, s2);
+    }
+    if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+    {
+      Stage stage(d.shared ? "act_grad+shared" : "act_grad", st);
+      e = hmm::launch_act_grad(ag, nj, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+    if ((e = hipEventRecord(side->dh_ev, st)) != hipSuccess || (e = hipStreamWaitEvent(s2, side->dh_ev, 0)))
+      return hip_fail(e, "dH event");
+    {
+      Stage stage(d.shared ? "dw1+shared" : "dw1", s2);
+      e = hmm::launch_dw1(dw1, nj, d.small, s2);
+    }
+    if (e != hipSuccess) return hip_fail(e, "W1Grad launch");
+    {
+      Stage stage(d.shared ? "input_grad+shared" : "input_grad", st);
+      e = hmm::launch_input_grad(ig, nj, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+    {
+      Stage stage("combine_dx", st);
+      e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
+                                 d_topk_weights, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
+    if ((e = hipEventRecord(side->join_ev, s2)) != hipSuccess || (e = hipStreamWaitEvent(st, side->join_ev, 0)))
+      return hip_fail(e, "backward join");
+    return HMM_OK;
   }
   if (ne) {
     {

@@ -412,11 +412,12 @@ def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weig
 
 def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto",
                         gmm1_dtype="bf16", out_dtype="bf16", shared_up_proj_weight=None,
-                        shared_down_proj_weight=None):
+                        shared_down_proj_weight=None, serial=False):
     """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights),
     then (d_shared_up_proj_weight, d_shared_down_proj_weight) with a shared expert.
 
-    With out_dtype float32, dy is taken in float32 and dx and the weight gradients are float32."""
+    With out_dtype float32, dy is taken in float32 and dx and the weight gradients are float32.
+    ``serial=True`` keeps every launch on the current stream (HMM_FLAG_SERIAL_BACKWARD)."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     Is = _check_shared(x, shared_up_proj_weight, shared_down_proj_weight)
     out = _out_code(out_dtype)
@@ -424,6 +425,7 @@ def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj
     with torch.cuda.device(x.device):
         return _backward_raw(_contig(dy, dyt), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
-                             _contig(down_proj_weight), saved, T, H, I, E, K, _lib.TILE_FLAGS[tiles],
+                             _contig(down_proj_weight), saved, T, H, I, E, K,
+                             _lib.TILE_FLAGS[tiles] | (_lib.HMM_FLAG_SERIAL_BACKWARD if serial else 0),
                              _gmm1_code(gmm1_dtype), out, _contig(shared_up_proj_weight) if Is else None,
                              _contig(shared_down_proj_weight) if Is else None)

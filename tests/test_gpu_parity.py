@@ -83,6 +83,28 @@ def test_saved_intermediates_match_oracle(tiles):
     assert_close(to_f64(v["aw"]), w[:, None] * to_f64(v["a"]), "aw")
 
 
+@pytest.mark.parametrize("Is", [0, 128])
+def test_backward_side_stream_equals_serial(Is):
+    """Large tiling: the weight gradients on the library's second stream give results
+    bit-identical to the same launches in series on one stream (with and without a
+    shared expert)."""
+    import torch
+    from mixture_experts_ffn_int32_amd import backward_from_saved, forward_with_saved
+    spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3, routing="uniform", shared_I=Is)
+    g = gpu_inputs(synth.make_inputs(spec, seed=9), "cuda")
+    sh = dict(shared_up_proj_weight=g.get("shared_up_proj_weight"), shared_down_proj_weight=g.get("shared_down_proj_weight"))
+    announce("backward on two streams against one, shared_I=%d" % Is)
+    y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
+                                  g["down_proj_weight"], tiles="large", **sh)
+    args = (g["dY"], g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"], saved)
+    a = backward_from_saved(*args, tiles="large", serial=False, **sh)
+    b = backward_from_saved(*args, tiles="large", serial=True, **sh)
+    torch.cuda.synchronize()
+    assert len(a) == len(b) == (6 if Is else 4)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
 def test_deterministic_and_t0():
     import torch
     spec = synth.spec_with("tiny", T=300, H=256, I=192, E=6, K=3)
