@@ -37,6 +37,7 @@ from .roofline import stage_work
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SIMDS = 1024            # 256 CUs x 4 SIMDs
+XCDS = 8                # GRBM_GUI_ACTIVE comes summed over the XCDs (one count each)
 MFMA_CTRS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
              "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
 
@@ -159,10 +160,14 @@ def summarise(wl, rundir):
            "Byte counters are scaled by what they read for a plain 1 GiB device copy: FETCH_SIZE x%s, WRITE_SIZE x%s "
            "bytes per KiB." % ("%.1f" % fs if fs else "n/a", "%.1f" % ws if ws else "n/a"),
            "Rate: algorithmic work (no tile padding; operands read once) / average duration, against the MI355X "
-           "peak (bf16 2.5 PFLOP/s, fp8 5.0, HBM 8 TB/s).  MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / "
-           "(GRBM_GUI_ACTIVE x 1024 SIMDs).  Clock: GRBM_GUI_ACTIVE / duration of the counter run.", "",
-           "| kernel | calls | avg us | % of GPU time | work | rate | of peak | HBM MB / dispatch | MFMA busy | clock GHz |",
-           "|---|---|---|---|---|---|---|---|---|---|"]
+           "peak (bf16 2.5 PFLOP/s, fp8 5.0, HBM 8 TB/s).  GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's "
+           "cycles are an eighth of it.  MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (XCD cycles x 1024 SIMDs).  "
+           "Clock: XCD cycles / duration of the dispatch in the counter run (kernels of 100 us or more).  "
+           "Dep. wait: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave time waiting on a dependency).  "
+           "Executed / work: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / algorithmic flops (tile padding).", "",
+           "| kernel | calls | avg us | % of GPU time | work | rate | of peak | HBM MB / dispatch | MFMA busy | "
+           "clock GHz | dep. wait | executed / work |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     per = {}
     for r in kernel_stats(os.path.join(rundir, "prof_" + wl)):
         name = r["Name"]
@@ -182,18 +187,25 @@ def summarise(wl, rundir):
             e["write_kib"] += w
             e["bytes"] += hbm
         mc = mfma.get(name, {})
-        busy = clock = None
+        busy = clock = wait = execd = None
         if mc.get("GRBM_GUI_ACTIVE"):
-            busy = mc.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (mc["GRBM_GUI_ACTIVE"] * SIMDS)
-            if mdur.get(name):
-                clock = mc["GRBM_GUI_ACTIVE"] / mdur[name]
-        out.append("| %s | %s | %.2f | %.2f | %s | %s | %s | %s | %s | %s |" % (
+            xcd_cycles = mc["GRBM_GUI_ACTIVE"] / XCDS
+            busy = mc.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (xcd_cycles * SIMDS)
+            if mdur.get(name, 0) >= 100e3:
+                clock = xcd_cycles / mdur[name]
+        if mc.get("SQ_WAVE_CYCLES"):
+            wait = mc.get("SQ_WAIT_INST_ANY", 0.0) / mc["SQ_WAVE_CYCLES"]
+        if bound == "mfma" and mc.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") and st in ("gmm1_swiglu", "gmm2", "act_grad",
+                                                                                  "input_grad", "dw1", "dw2"):
+            execd = mc["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / work
+        out.append("| %s | %s | %.2f | %.2f | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             label, r["Calls"], avg_us, float(r["Percentage"]),
             ("%.4g %s" % (work / (1e12 if bound == "mfma" else 1e6), "TFLOP" if bound == "mfma" else "MB"))
             if bound else "",
             ("%.1f %s" % (rate, unit)) if rate else "", ("%.3f" % frac) if frac else "",
             ("%.1f" % (hbm / 1e6)) if hbm is not None else "", ("%.3f" % busy) if busy is not None else "",
-            ("%.2f" % clock) if clock else ""))
+            ("%.2f" % clock) if clock else "", ("%.2f" % wait) if wait is not None else "",
+            ("%.3f" % execd) if execd else ""))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", "step_kernels_%s.md" % stem)
     with open(path, "w") as fh:
