@@ -31,7 +31,7 @@ def flags(debug=False):
     f = ["-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
-    f += ["-O1", "-g", "-DHMM_DEBUG=1"] if debug else ["-O3"]
+    f += ["-O1", "-g"] if debug else ["-O3"]
     return f
 
 
