@@ -106,6 +106,16 @@ scaled by its token and weight descales in float32, and the scaled group sums
 are added in float32 in group order; the oracle sums exactly and carries those
 three errors in its deviation.
 
+The FP8 backward (``bwd="fp8"``) runs the two products of the dX chain on E4M3,
+with case 3's per-row dynamic rule applied to every operand: act_grad
+G = (dYq . W2q^T) dsy dsw2 with dY quantised per token over H and W2[e] per
+row i over H; input_grad dXp = (dHq . W1q^T) dsh dsw1 with dH quantised per
+row over 2I and W1[e] per row h over 2I.  The weight gradients stay bfloat16.
+dY and the weights are exact inputs, so their codes are exact.  dH is an
+intermediate: where its bf16 decisions are open, its codes and its row descale
+may come out otherwise (quant.quantize_rows_dev), and dXp's deviation carries
+that.  The shared expert's backward stays bfloat16.
+
 The MX variant (``gmm1="mx"``) quantises tokens and weights in blocks of 32
 along the hidden dimension with a power-of-two scale per block (see
 ``quant``); the up-projection sums the dequantised products exactly, and the
@@ -117,7 +127,7 @@ import numpy as np
 
 from .numerics import round_bf16, sigmoid, silu
 from .quant import (GROUP, quantize_columns, quantize_columns_groups, quantize_columns_mx, quantize_rows,
-                    quantize_rows_groups, quantize_rows_mx)
+                    quantize_rows_dev, quantize_rows_groups, quantize_rows_mx)
 from .routing import check_ids
 
 U32 = 2.0 ** -24     # unit roundoff of float32
@@ -157,7 +167,7 @@ class MoEFFN:
 
     def __init__(self, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
                  dY=None, mode="faithful", gmm1="bf16", shared_up_proj_weight=None, shared_down_proj_weight=None,
-                 acc="f64"):
+                 acc="f64", bwd="bf16"):
         if mode not in ("pure", "faithful"):
             raise ValueError(mode)
         if acc not in ("f64", "f32") or (acc == "f32" and mode != "pure"):
@@ -167,6 +177,9 @@ class MoEFFN:
         self.ft = np.float64 if acc == "f64" else np.float32
         if gmm1 not in ("bf16", "fp8", "mx", "group"):
             raise ValueError(gmm1)
+        if bwd not in ("bf16", "fp8"):
+            raise ValueError(bwd)
+        self.bwd = bwd
         self.x = np.asarray(x)
         self.ids = np.asarray(topk_ids, dtype=np.int64)
         self.w = np.asarray(topk_weights, dtype=np.float32).astype(self.ft)
@@ -184,7 +197,7 @@ class MoEFFN:
         if two_i != 2 * self.I or self.W2.shape != (self.E, self.I, self.H):
             raise ValueError("weights must be [E,H,2I] and [E,I,H]")
         check_ids(self.ids, self.E)
-        self._w1, self._w2, self._w1q = {}, {}, {}
+        self._w1, self._w2, self._w1q, self._w2r, self._w1r = {}, {}, {}, {}, {}
         # Shared expert (RFC 6.1: an optional shared expert whose GMM1, SwiGLU and GMM2
         # run with the routed experts and whose output joins at the Combine).  Reading:
         # every token goes through it with weight 1; its output is added after the K
@@ -235,6 +248,18 @@ class MoEFFN:
             else:                   # (q, scale, descale)
                 self._w1q[e] = quantize_columns(self.W1[e])
         return self._w1q[e]
+
+    def _W2r(self, e):
+        """FP8 backward: W2[e] [I, H] quantised per row i (over H): (q, scale, descale)."""
+        if e not in self._w2r:
+            self._w2r[e] = quantize_rows(self.W2[e])
+        return self._w2r[e]
+
+    def _W1r(self, e):
+        """FP8 backward: W1[e] [H, 2I] quantised per row h (over 2I): (q, scale, descale)."""
+        if e not in self._w1r:
+            self._w1r[e] = quantize_rows(self.W1[e])
+        return self._w1r[e]
 
     def slots_of_expert(self, e):
         """Slots s = t*K + k routed to expert e, ascending."""
@@ -326,13 +351,53 @@ class MoEFFN:
         return self._round(v, d)
 
     def act_grad(self, e, dyrows, icols=None):
-        """G = dY . W2[e]^T (unrounded) and its float32 evaluation error, for gate columns ``icols``."""
+        """G = dY . W2[e]^T (unrounded) and its float32 evaluation error, for gate columns ``icols``.
+
+        FP8 backward: dY rows quantised per token over H and W2[e] per row i over H
+        (both exact inputs, so the codes are exact), G = (dYq . W2q^T) dsy dsw; the
+        evaluation error carries the FP8 instruction's term."""
+        if self.bwd == "fp8":
+            q, _, dsy = quantize_rows(dyrows)
+            wq, _, dsw = self._W2r(e)
+            if icols is not None:
+                wq, dsw = wq[np.asarray(icols)], dsw[np.asarray(icols)]
+            sc = dsy.astype(np.float64)[:, None] * dsw.astype(np.float64)[None, :]
+            G = (q @ wq.T) * sc
+            if not self.faithful:
+                return G, None
+            sq = (q * q) @ (wq * wq).T
+            return G, (acc_eps(sq, self.H) + C_F8 * U32 * np.sqrt(sq)) * sc + 2 * C_EL * U32 * np.abs(G)
         W2 = self._W2(e)
         W2 = W2 if icols is None else W2[np.asarray(icols)]
         dyr = np.asarray(dyrows, self.ft)
         if not self.faithful:
             return dyr @ W2.T, None
         return dyr @ W2.T, acc_eps((dyr * dyr) @ (W2 * W2).T, self.H)
+
+    def input_grad_dev(self, e, dH, dHd):
+        """R6: dXp = dH . W1[e]^T for the rows of dH (with deviations dHd).
+
+        FP8 backward: dH rows quantised per row over 2I and W1[e] per row h over 2I,
+        dXp = (dHq . W1q^T) dsh dsw.  dH is an intermediate: where its bf16 decisions
+        are open, its E4M3 codes and its row descale may be others (quantize_rows_dev);
+        code changes propagate like open decisions, a descale change scales the row."""
+        if self.bwd != "fp8":
+            W1 = self._W1(e)
+            v = dH @ W1.T
+            if not self.faithful:
+                return v, None
+            return self._round(v, C_PROP * prop_matmul(dHd, W1.T) + acc_eps((dH * dH) @ (W1 * W1).T, 2 * self.I))
+        q, _, dsh = quantize_rows(dH)
+        wq, _, dsw = self._W1r(e)
+        sc = dsh.astype(np.float64)[:, None] * dsw.astype(np.float64)[None, :]
+        v = (q @ wq.T) * sc
+        if not self.faithful:
+            return v, None
+        dq, rel = quantize_rows_dev(dH, dHd)
+        sq = (q * q) @ (wq * wq).T
+        d = (C_PROP * (prop_matmul(dq, wq.T) * sc + rel[:, None] * np.abs(v))
+             + (acc_eps(sq, 2 * self.I) + C_F8 * U32 * np.sqrt(sq)) * sc + 2 * C_EL * U32 * np.abs(v))
+        return self._round(v, d)
 
     def swiglu_grad_dev(self, w, G, Ge, g, u, gd, ud):
         """SwiGLUGrad with dA = w G; R5: dH = [dg | du] and deviations."""
@@ -427,17 +492,15 @@ class MoEFFN:
                 dw[j, k] = float(np.sum(G * a))
                 (dg, dgd), (du, dud) = self.swiglu_grad_dev(self.w[t, k], G, Ge, g, u, gd, ud)
                 dH = np.concatenate([dg, du], axis=1)
-                W1 = self._W1(e)
-                v = dH @ W1.T
                 if not self.faithful:
-                    acc = acc + v[0]
+                    acc = acc + self.input_grad_dev(e, dH, None)[0][0]
                     continue
                 # d_topk_weights = sum_i G_i a_i: open decisions of a (ad) and the evaluation errors of G (Ge)
                 dwd[j, k] = float(C_PROP * prop_sum(np.sum(np.abs(G) * ad + np.abs(a) * Ge),
                                                     np.sum((G * ad) ** 2 + (a * Ge) ** 2))
                                   + acc_eps(np.sum((G * a) ** 2), self.I))
                 dHd = np.concatenate([dgd, dud], axis=1)
-                xp, xpd = self._round(v, C_PROP * prop_matmul(dHd, W1.T) + acc_eps((dH * dH) @ (W1 * W1).T, 2 * self.I))  # R6
+                xp, xpd = self.input_grad_dev(e, dH, dHd)                                          # R6
                 acc = acc + xp[0]
                 accd = accd + xpd[0]
                 accd2 = accd2 + xpd[0] ** 2

@@ -165,3 +165,41 @@ def quantize_columns_groups(w, group=GROUP):
     q = round_e4m3(prod.astype(np.float64)).reshape(H, N)
     descale = (np.float32(1.0) / scale).astype(np.float32)
     return q, scale, descale
+
+
+# ----------------------------------------------------------- admissible rows
+def quantize_rows_dev(v, d):
+    """Deviation bounds of the per-row E4M3 quantisation of rows ``v`` [n, L] whose
+    elements may each lie anywhere in [v - d, v + d] (the open bf16 decisions of an
+    intermediate, see moe_ffn): returns (dq, rel), with dq [n, L] the largest change
+    of each E4M3 code and rel [n] the largest relative change of the row's float32
+    descale 1 / scale, over every admissible row.
+
+    The row maximum of an admissible row lies in [m_lo, m_hi] (m_lo = max(|v| - d),
+    m_hi = max(|v| + d)), so its scale lies between the scales of those two (the
+    largest finite float32 if m_lo is 0); each code is a monotone function of
+    float32(v' * s'), so its extremes are at the corners of that box.
+    """
+    v = np.asarray(v, np.float64)
+    d = np.asarray(d, np.float64)
+    a = np.abs(v)
+    m = a.max(axis=-1)
+    m_lo = np.maximum(a - d, 0.0).max(axis=-1)
+    m_hi = (a + d).max(axis=-1)
+    fmax = np.float32(np.finfo(np.float32).max)
+    s = _scale_from_absmax(m)
+    s_lo = _scale_from_absmax(m_hi)
+    s_hi = np.where(m_lo > 0, _scale_from_absmax(m_lo), fmax).astype(np.float32)
+    s_hi = np.where(m_hi > 0, s_hi, s)                       # an all-zero row stays all-zero
+    q = round_e4m3((v.astype(np.float32) * s[..., None]).astype(np.float64))
+    corners = [(np.float32(x) * sc[..., None]).astype(np.float64)
+               for x in ((v - d).astype(np.float32), (v + d).astype(np.float32)) for sc in (s_lo, s_hi)]
+    lo = round_e4m3(np.minimum.reduce(corners))
+    hi = round_e4m3(np.maximum.reduce(corners))
+    dq = np.maximum(np.abs(hi - q), np.abs(q - lo))
+    with np.errstate(divide="ignore", over="ignore"):
+        ds = (np.float32(1.0) / s).astype(np.float64)
+        ds_a = (np.float32(1.0) / s_lo).astype(np.float64)
+        ds_b = (np.float32(1.0) / s_hi).astype(np.float64)
+    rel = np.maximum(np.abs(ds_a - ds), np.abs(ds_b - ds)) / ds
+    return dq, rel

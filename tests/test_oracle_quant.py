@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from oracle.moe_ffn import MoEFFN
-from oracle.numerics import round_bf16
+from oracle.numerics import round_bf16, round_e4m3
 from oracle.quant import quantize_columns, quantize_rows
 
 
@@ -310,3 +310,66 @@ def test_scale_clamped_where_448_over_max_overflows():
     assert np.array_equal(q, ref)
     assert np.all(q[x == 0] == 0)
     assert np.all(descale == np.float32(1.0) / fmax) and np.all(descale > 0)
+
+
+# ------------------------------------------------ deviation bound of the row quantiser
+def _torch_rows(v):
+    """Per-row E4M3 quantisation with torch float32 ops and torch's float8 cast: (codes, descale)."""
+    t = torch.tensor(np.asarray(v, np.float32))
+    amax = t.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, torch.tensor(448.0) / amax, torch.ones_like(amax))
+    scale = torch.minimum(scale, torch.tensor(np.finfo(np.float32).max))
+    q = (t * scale).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return q, (1.0 / scale).to(torch.float64).numpy()[..., 0]
+
+
+def test_quantize_rows_dev_covers_every_sampled_admissible_row():
+    """Rows of bf16 values, some elements with an open decision of one bf16 ulp (the
+    row maximum open in some rows): every admissible row (each element one of the bf16
+    values within its deviation) quantises to codes within dq and a descale within rel."""
+    from oracle.quant import quantize_rows_dev
+    rng = np.random.default_rng(11)
+    n, L = 24, 96
+    v = round_bf16(rng.standard_normal((n, L)) * np.exp2(rng.integers(-3, 4, (n, 1))))
+    ulp = np.exp2(np.floor(np.log2(np.abs(v) + 1e-300)) - 7)
+    d = np.where(rng.random((n, L)) < 0.3, ulp, 0.0)
+    d[::3, np.argmax(np.abs(v[::3]), axis=1)] = ulp[::3, np.argmax(np.abs(v[::3]), axis=1)]   # open row maxima
+    dq, rel = quantize_rows_dev(v, d)
+    q0, ds0 = _torch_rows(v)
+    assert (dq > 0).any() and (rel > 0).any()
+    worst_q = np.zeros_like(dq)
+    worst_r = np.zeros(n)
+    for _ in range(300):
+        vp = v + d * rng.integers(-1, 2, (n, L))                   # each element: its value or a neighbour
+        q, ds = _torch_rows(vp)
+        worst_q = np.maximum(worst_q, np.abs(q - q0))
+        worst_r = np.maximum(worst_r, np.abs(ds - ds0) / ds0)
+    assert np.all(worst_q <= dq) and np.all(worst_r <= rel * (1 + 1e-12))
+    assert (worst_q > 0).any()                                     # the check is not vacuous
+    dq0, rel0 = quantize_rows_dev(v, np.zeros_like(v))
+    assert not dq0.any() and not rel0.any()
+
+
+def test_fp8_backward_act_grad_exact_when_rows_are_representable():
+    """dY and W2 rows made of E4M3 values whose row maxima are 448 * 2^k: the per-row
+    quantisation is exact, so the FP8 backward's G (seen through d_topk_weights and dH,
+    hence dW1) equals the bf16 backward's in pure mode; dx still differs (dH rows are
+    quantised) but stays within the E4M3 error of dH."""
+    rng = np.random.default_rng(12)
+    T, H, I, E, K = 24, 64, 64, 3, 2
+    codes = round_e4m3(rng.uniform(-448, 448, (T + E * I, H)))
+    codes[:, 0] = 448.0                                            # every row maximum is 448
+    dY = codes[:T] * np.exp2(rng.integers(-9, -3, (T, 1)))
+    W2 = (codes[T:] * np.exp2(rng.integers(-12, -8, (E * I, 1)))).reshape(E, I, H)
+    x = round_bf16(rng.standard_normal((T, H)))
+    W1 = round_bf16(rng.standard_normal((E, H, 2 * I)) / 8)
+    ids = np.array([rng.choice(E, K, replace=False) for _ in range(T)])
+    w = rng.random((T, K)).astype(np.float32)
+    a16 = MoEFFN(x, ids, w, W1, W2, dY=dY, mode="pure").backward()
+    a8 = MoEFFN(x, ids, w, W1, W2, dY=dY, mode="pure", bwd="fp8").backward()
+    np.testing.assert_allclose(a8[1], a16[1], rtol=1e-12, atol=1e-12)       # d_topk_weights
+    np.testing.assert_allclose(a8[2], a16[2], rtol=1e-10, atol=1e-12)       # dW1 (from dH)
+    np.testing.assert_allclose(a8[3], a16[3], rtol=1e-12, atol=1e-12)       # dW2 (dY, not quantised)
+    err = np.abs(a8[0] - a16[0])
+    assert err.max() > 0                                                   # dx: dH was quantised
+    assert np.all(err <= 0.15 * np.abs(a16[0]).max())
