@@ -97,7 +97,8 @@ class Runner:
         self.ids = torch.from_numpy(inp["topk_ids"]).to(device)
         self.w = torch.from_numpy(inp["topk_weights"]).to(device)
         flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | (
-            _lib.HMM_FLAG_SERIAL_BACKWARD if serial_backward else 0)
+            _lib.HMM_FLAG_SERIAL_BACKWARD if serial_backward else 0) | (
+            _lib.HMM_FLAG_FP8_BACKWARD if spec.get("fp8_backward") else 0)
         gmm1 = {"bf16": _lib.HMM_BF16, "fp8": _lib.HMM_FP8_E4M3, "mx": _lib.HMM_MXFP8_E4M3,
                 "group": _lib.HMM_FP8_E4M3_GROUP}[spec.get("gmm1", "bf16")]
         f32 = out_dtype == "f32"
@@ -210,7 +211,8 @@ def cpu_baseline(spec, seed, budget_s=12.0):
             if k in inp:
                 d[k] = synth.bits_to_f32(inp[k])
         t0 = time.perf_counter()
-        m = MoEFFN(**d, mode="pure", gmm1=spec.get("gmm1", "bf16"), acc="f32")
+        m = MoEFFN(**d, mode="pure", gmm1=spec.get("gmm1", "bf16"), acc="f32",
+                   bwd="fp8" if spec.get("fp8_backward") else "bf16")
         m.forward()
         m.backward()
         if m.shared is not None:
@@ -381,11 +383,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "bf16+fp8", "mx": "bf16+mxfp8", "group": "bf16+fp8"}.get(
+        "dtype": {"fp8": "bf16+fp8", "mx": "bf16+mxfp8", "group": "bf16+fp8", "fp8bwd": "bf16+fp8"}.get(
             gmm1_kind, "bf16 hi/lo pairs, f32 outputs" if args.out_dtype == "f32" else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "I": I, "E": E, "K": K,
                    "routing": spec.get("routing"), "shared_I": Is, "seed": args.seed,
+                   "gmm1": gmm1_kind, "fp8_backward": bool(spec.get("fp8_backward")),
                    "validate_ids": not args.no_validate, "serial_backward": args.serial_backward,
                    "out_dtype": args.out_dtype},
         "gemm_tflops": round(gemm_tflops, 3) if gemm_tflops else None,

@@ -122,6 +122,17 @@ typedef enum hmm_dtype {
  * results are identical either way. */
 #define HMM_FLAG_SERIAL_BACKWARD 16u
 
+/* FP8 backward: act_grad and input_grad, the two products of the dX chain, run on
+ * E4M3 with per-row dynamic scales (the MoeDistributeDispatchV2 page's case-3 rule,
+ * scale = 448 / max|row|, descale 1 / scale kept, applied to every operand): dy per
+ * token and each row of down_proj_weight[e] over H for act_grad; the intermediate
+ * dH per row and each row of up_proj_weight[e] over 2I for input_grad.  The weight
+ * gradients, the combine and a shared expert's products stay bf16.  Bf16 outputs
+ * only (else HMM_ERR_UNSUPPORTED); H a multiple of 128.  Needs the larger
+ * workspace that hmm_backward_sizes reports with the flag set; the forward
+ * ignores it. */
+#define HMM_FLAG_FP8_BACKWARD 32u
+
 /* Problem description.
  *   T  tokens (>= 0; T = 0 is a no-op that still writes zero weight gradients)
  *   H  hidden size, multiple of 64, 64 <= H <= 65536

@@ -28,6 +28,7 @@ HMM_FLAG_TILES_LARGE = 2
 HMM_FLAG_TILES_NARROW = 4
 HMM_FLAG_FUSED_FORWARD = 8
 HMM_FLAG_SERIAL_BACKWARD = 16
+HMM_FLAG_FP8_BACKWARD = 32
 TILE_FLAGS = {"auto": 0, "large": HMM_FLAG_TILES_LARGE, "narrow": HMM_FLAG_TILES_NARROW}
 
 # every symbol include/hmm.h declares

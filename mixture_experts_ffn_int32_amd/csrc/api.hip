@@ -48,6 +48,7 @@ struct Dims {
   bool group;  // ... with per-group (128 along H) float scales
   bool f32;    // float32 outputs (accuracy mode)
   bool fused;  // small problem whose forward runs as one fused launch (fused.hip)
+  bool fp8bwd; // the backward's act_grad and input_grad on E4M3 (HMM_FLAG_FP8_BACKWARD)
   uint32_t flags;
 };
 
@@ -66,7 +67,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
   if (p->T > (int64_t)0x7fffffff / p->K)
     return fail(HMM_ERR_BAD_SHAPE, "T*K must stay below 2^31 (T=%lld, K=%lld)", (long long)p->T, (long long)p->K);
   if (p->flags & ~(HMM_FLAG_VALIDATE_IDS | HMM_FLAG_TILES_LARGE | HMM_FLAG_TILES_NARROW | HMM_FLAG_FUSED_FORWARD |
-                   HMM_FLAG_SERIAL_BACKWARD))
+                   HMM_FLAG_SERIAL_BACKWARD | HMM_FLAG_FP8_BACKWARD))
     return fail(HMM_ERR_BAD_SHAPE, "unknown flag bits 0x%x", p->flags);
   if ((p->flags & HMM_FLAG_TILES_LARGE) && (p->flags & HMM_FLAG_TILES_NARROW))
     return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_TILES_LARGE and HMM_FLAG_TILES_NARROW are exclusive");
@@ -91,6 +92,10 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
     return fail(HMM_ERR_UNSUPPORTED, "out_dtype HMM_F32 is implemented with gmm1_dtype HMM_BF16 only");
   if (p->gmm1_dtype != HMM_BF16 && p->H % 128)
     return fail(HMM_ERR_BAD_SHAPE, "an FP8 gmm1_dtype needs H to be a multiple of 128 (got %lld)", (long long)p->H);
+  if ((p->flags & HMM_FLAG_FP8_BACKWARD) && p->out_dtype == HMM_F32)
+    return fail(HMM_ERR_UNSUPPORTED, "HMM_FLAG_FP8_BACKWARD is implemented with bf16 outputs only");
+  if ((p->flags & HMM_FLAG_FP8_BACKWARD) && p->H % 128)
+    return fail(HMM_ERR_BAD_SHAPE, "HMM_FLAG_FP8_BACKWARD needs H to be a multiple of 128 (got %lld)", (long long)p->H);
   d->T = p->T;
   d->H = p->H;
   d->I = p->I;
@@ -108,6 +113,7 @@ hmm_status validate(const hmm_problem* p, Dims* d) {
              : hmm::small_mode(d->S, d->H, d->I);
   d->fused = d->small && !d->fp8 && !d->f32 && !d->shared && d->S > 0 && d->S <= hmm::RT_ONE_MAX_SLOTS &&
              d->E <= hmm::RT_ONE_MAX_EXPERTS && (p->flags & HMM_FLAG_FUSED_FORWARD);
+  d->fp8bwd = (p->flags & HMM_FLAG_FP8_BACKWARD) != 0;
   d->flags = p->flags;
   return HMM_OK;
 }
@@ -223,6 +229,9 @@ FwdWork fwd_work(const Dims& d) {
 // mode, dY as a bf16 [hi | lo] pair (dH is then a pair too and dXp float32).
 struct BwdWork {
   size_t dy2, dh, dxp, dwpart, dhs, dxs, total;
+  // FP8 backward: E4M3 codes and float32 descales of dY [T][H], W2 rows [E*I][H],
+  // dH [S][2I] and W1 rows [E*H][2I]
+  size_t dyq, dsy, w2q, dsw2, dhq, dsh, w1q, dsw1;
   int dw_cols;
 };
 BwdWork bwd_work(const Dims& d) {
@@ -239,6 +248,16 @@ BwdWork bwd_work(const Dims& d) {
   if (d.shared) {  // the shared expert's dH and dX rows
     w.dhs = o;  o += up(d.T * 2 * d.Is * 2 * wide);
     w.dxs = o;  o += up(d.T * d.H * (d.f32 ? 4 : 2));
+  }
+  if (d.fp8bwd) {
+    w.dyq = o;  o += up(d.T * d.H);
+    w.dsy = o;  o += up(d.T * 4);
+    w.w2q = o;  o += up(d.E * d.I * d.H);
+    w.dsw2 = o; o += up(d.E * d.I * 4);
+    w.dhq = o;  o += up(d.S * 2 * d.I);
+    w.dsh = o;  o += up(d.S * 4);
+    w.w1q = o;  o += up(d.E * d.H * 2 * d.I);
+    w.dsw1 = o; o += up(d.E * d.H * 4);
   }
   w.total = o;
   return w;
@@ -927,6 +946,79 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
   const hmm::DwJob dw1[2] = {
       hmm::dw1_job(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w),
       hmm::dw1_job(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (uint16_t*)d_up_s)};
+  if (d.fp8bwd) {
+    // FP8 backward: dY and the rows of W2 quantised per row, act_grad on E4M3 (dH
+    // and the d_topk_weights partials as in bf16), dH and the rows of W1 quantised,
+    // input_grad on E4M3; the shared expert's products, the combine and the weight
+    // gradients in bf16.  One launch per product, on the caller's stream.
+    if (ne) {
+      uint8_t* dyq = at<uint8_t>(workspace, W.dyq);
+      uint8_t* w2q = at<uint8_t>(workspace, W.w2q);
+      uint8_t* dhq = at<uint8_t>(workspace, W.dhq);
+      uint8_t* w1q = at<uint8_t>(workspace, W.w1q);
+      float* dsy = at<float>(workspace, W.dsy);
+      float* dsw2 = at<float>(workspace, W.dsw2);
+      float* dsh = at<float>(workspace, W.dsh);
+      float* dsw1 = at<float>(workspace, W.dsw1);
+      {
+        Stage stage("quant_dy", st);
+        e = hmm::launch_quant_rows_fp8((const uint16_t*)dy, d.T, d.H, dyq, dsy, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "dY quantisation launch");
+      {
+        Stage stage("quant_w2", st);
+        e = hmm::launch_quant_rows_fp8((const uint16_t*)down_w, d.E * d.I, d.H, w2q, dsw2, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "W2 quantisation launch");
+      {
+        Stage stage("act_grad_fp8", st);
+        e = hmm::launch_act_grad_fp8(g, dyq, dsy, w2q, dsw2, topk_weights, h, a, d.H, d.I, dh, dwpart, W.dw_cols,
+                                     st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "act_grad launch");
+      if (d.shared) {
+        Stage stage("shared_act_grad", st);
+        e = hmm::launch_act_grad(&ag[1], 1, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "shared act_grad launch");
+      {
+        Stage stage("quant_dh", st);
+        e = hmm::launch_quant_rows_fp8(dh, d.S, 2 * d.I, dhq, dsh, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "dH quantisation launch");
+      {
+        Stage stage("quant_w1r", st);
+        e = hmm::launch_quant_rows_fp8((const uint16_t*)up_w, d.E * d.H, 2 * d.I, w1q, dsw1, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "W1 quantisation launch");
+      {
+        Stage stage("input_grad_fp8", st);
+        e = hmm::launch_input_grad_fp8(g, dhq, dsh, w1q, dsw1, d.H, d.I, dxp, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "input_grad launch");
+      if (d.shared) {
+        Stage stage("shared_input_grad", st);
+        e = hmm::launch_input_grad(&ig[1], 1, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "shared input_grad launch");
+      {
+        Stage stage("combine_dx", st);
+        e = hmm::launch_combine_dx(dxp, row_of_slot, d.T, (int)d.K, d.H, dxs, (uint16_t*)dx, dwpart, W.dw_cols,
+                                   d_topk_weights, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "combine(dX) launch");
+    }
+    {
+      Stage stage(d.shared ? "dw2+shared" : "dw2", st);
+      e = hmm::launch_dw2(dw2, nj, d.small, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "W2Grad launch");
+    {
+      Stage stage(d.shared ? "dw1+shared" : "dw1", st);
+      e = hmm::launch_dw1(dw1, nj, d.small, st);
+    }
+    return e == hipSuccess ? HMM_OK : hip_fail(e, "W1Grad launch");
+  }
   if (ne && d.small) {
     // small problems: each product fills only part of the chip, so the independent
     // ones share a launch (RFC 2.2: W2Grad alongside act_grad, W1Grad alongside the

@@ -208,76 +208,15 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 #pragma unroll
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * C::BK * 2);
   }
-  // G stays in float32: one wave column (TN columns) at a time it is staged in
-  // LDS, then each thread takes 8 consecutive columns of one row, reads g, u and
-  // a as 16-byte chunks, writes dH = [dg | du] as 16-byte chunks and adds its
-  // share of sum_i G a.  The row sums are reduced in a fixed order (8-lane
-  // butterfly, then wave columns in order): one partial per (row, N tile).
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
-    constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
-    constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
-    constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
-    static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
+    constexpr int LDF = C::TN + 4;
     static_assert((C::BM * LDF + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
     float* gst = reinterpret_cast<float*>(smem);
     float* wrow = gst + C::BM * LDF;
-    const int tid = threadIdx.x;
-    for (int t = tid; t < C::BM; t += C::NTHR)
+    for (int t = threadIdx.x; t < C::BM; t += C::NTHR)
       wrow[t] = this->row_weight(ar->tw, ar->g, t);
-    const int64_t I = ar->I;
-    float part[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) part[k] = 0.f;
-    for (int q = 0; q < C::WN; ++q) {
-      if (wn == q) {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              gst[acc_row<C>(wm, mb, r, lane) * LDF + nb * 32 + (lane & 31)] = acc[mb][nb][r];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int c = tid + k * C::NTHR;
-        const int row = c / CPR, c8 = c % CPR;
-        const int64_t i = n0 + q * C::TN + c8 * 8;
-        float s = 0.f;
-        if (row < rows && i < I) {
-          const int64_t p = row0 + row;
-          float g[8], u[8], av[8], dg[8], du[8];
-          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + i), g);
-          unpack8(*reinterpret_cast<const u32x4*>(ar->h + p * 2 * I + I + i), u);
-          unpack8(*reinterpret_cast<const u32x4*>(ar->a + p * I + i), av);
-          const float w = wrow[row];
-          const float* G = gst + row * LDF + c8 * 8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            s += G[j] * av[j];
-            const float dA = w * G[j];
-            const float sg = sigmoidf_(g[j]);
-            dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
-            du[j] = dA * g[j] * sg;
-          }
-          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + i) = pack8(dg);
-          *reinterpret_cast<u32x4*>(ar->dh + p * 2 * I + I + i) = pack8(du);
-        }
-        // the CPR threads of a row are consecutive lanes: fixed-order butterfly
-#pragma unroll
-        for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
-        part[k] += s;
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int c = tid + k * C::NTHR;
-      const int row = c / CPR;
-      if (ar->dwpart && c % CPR == 0 && row < rows)
-        ar->dwpart[(int64_t)(row0 + row) * ar->dw_cols + n0 / C::BN] = part[k];
-    }
+    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->a, ar->dh, ar->dwpart,
+                            ar->dw_cols);
   }
 };
 

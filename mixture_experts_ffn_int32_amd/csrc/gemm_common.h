@@ -1,5 +1,5 @@
 // Helpers shared by the grouped-product kernels (bf16 and FP8): workgroup to
-// XCD mapping, tile rasterisation, buffer resources.
+// XCD mapping, tile rasterisation, buffer resources, the act_grad epilogue.
 #pragma once
 
 #include "device.h"
@@ -36,6 +36,81 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
 // the same at the device-wide coherence point (sc1), for data written earlier in the same launch
 __device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 16));
+}
+
+// ------------------------------------------------------------- act_grad epilogue
+// SwiGLUGrad of one tile of G (fp32 accumulators): one wave column (TN columns)
+// at a time G is staged in LDS (gst, BM x (TN + 4) floats), then each thread takes
+// 8 consecutive columns of one row, reads g, u and a as 16-byte chunks, writes
+// dH = [dg | du] as 16-byte chunks and adds its share of sum_i G a.  The row sums
+// are reduced in a fixed order (8-lane butterfly, then wave columns in order):
+// one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
+// rows' topk weights (0 past the tile's rows), written by the caller before the
+// call (the first barrier here publishes it).  Shared by the bf16 and FP8 products.
+template <class C>
+__device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane,
+                                                     float* gst, const float* wrow, int rows, int64_t row0,
+                                                     int64_t n0, int64_t I, const uint16_t* hbuf,
+                                                     const uint16_t* abuf, uint16_t* dhbuf, float* dwpart,
+                                                     int dw_cols) {
+  constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
+  constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
+  constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
+  static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
+  const int tid = threadIdx.x;
+  float part[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) part[k] = 0.f;
+  for (int q = 0; q < C::WN; ++q) {
+    if (wn == q) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            gst[(wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDF + nb * 32 + (lane & 31)] =
+                acc[mb][nb][r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = tid + k * C::NTHR;
+      const int row = c / CPR, c8 = c % CPR;
+      const int64_t i = n0 + q * C::TN + c8 * 8;
+      float s = 0.f;
+      if (row < rows && i < I) {
+        const int64_t p = row0 + row;
+        float g[8], u[8], av[8], dg[8], du[8];
+        unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + i), g);
+        unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + I + i), u);
+        unpack8(*reinterpret_cast<const u32x4*>(abuf + p * I + i), av);
+        const float w = wrow[row];
+        const float* G = gst + row * LDF + c8 * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          s += G[j] * av[j];
+          const float dA = w * G[j];
+          const float sg = sigmoidf_(g[j]);
+          dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
+          du[j] = dA * g[j] * sg;
+        }
+        *reinterpret_cast<u32x4*>(dhbuf + p * 2 * I + i) = pack8(dg);
+        *reinterpret_cast<u32x4*>(dhbuf + p * 2 * I + I + i) = pack8(du);
+      }
+      // the CPR threads of a row are consecutive lanes: fixed-order butterfly
+#pragma unroll
+      for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+      part[k] += s;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = tid + k * C::NTHR;
+    const int row = c / CPR;
+    if (dwpart && c % CPR == 0 && row < rows) dwpart[(row0 + row) * dw_cols + n0 / C::BN] = part[k];
+  }
 }
 
 }  // namespace hmm

@@ -47,7 +47,8 @@ struct F8Cfg {
   static constexpr int CA = BM * BKB / 16 / NTHR;
   static constexpr int CB = BN * BKB / 16 / NTHR;
   static constexpr int LDB = BN + 32;
-  static constexpr int A_BYTES = BM * LDKB, B_BYTES = BKB * LDB;
+  // B N-major ([k][n], pitch LDB) or K-major ([n][k], pitch LDKB, the backward's weights)
+  static constexpr int A_BYTES = BM * LDKB, B_BYTES = (BKB * LDB > BN * LDKB) ? BKB * LDB : BN * LDKB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static_assert(CA >= 1 && CB >= 1 && STAGE % 16 == 0, "tile shape");
 };
@@ -91,6 +92,7 @@ struct Gmm1F8 {
   static constexpr bool MX_ = MX;
   static constexpr bool GROUP_ = GROUP;
   static constexpr bool STAGED = MX || GROUP;
+  static constexpr bool B_KMAJ_ = false;  // weights [H][2I]: N-major
   static constexpr int SCR = STAGED ? (C::BM + C::BN + C::NTHR - 1) / C::NTHR : 1;
   static constexpr int SC_BYTES = STAGED ? (C::BM + C::BN) * 4 : 0;
   const Args* ar;
@@ -287,7 +289,10 @@ __device__ __forceinline__ void store_stage8(uint8_t* st, const u32x4 (&ra)[C::C
 #pragma unroll
   for (int i = part; i < C::CB; i += nparts) {
     const int c = tid + i * C::NTHR;
-    *reinterpret_cast<u32x4*>(st + C::A_BYTES + (c / (C::BN / 16)) * C::LDB + (c % (C::BN / 16)) * 16) = rb[i];
+    if constexpr (P::B_KMAJ_)
+      *reinterpret_cast<u32x4*>(st + C::A_BYTES + (c >> 3) * LDKB + (c & 7) * 16) = rb[i];
+    else
+      *reinterpret_cast<u32x4*>(st + C::A_BYTES + (c / (C::BN / 16)) * C::LDB + (c % (C::BN / 16)) * 16) = rb[i];
   }
 }
 
@@ -377,14 +382,22 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
         int bsc[C::NB];
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          const int i = lane & 15;
-          const int n = wn * C::TN + nb * 32 + 16 * ((lane >> 4) & 1) + 8 * (i & 1);
+          if constexpr (P::B_KMAJ_) {
+            // K-major B: read like the A fragments (same k order)
+            const uint8_t* pb = sb + (wn * C::TN + nb * 32 + (lane & 31)) * LDKB + kk * 64 + 16 * (lane >> 5);
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(pb);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + 32);
+            fb[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          } else {
+            const int i = lane & 15;
+            const int n = wn * C::TN + nb * 32 + 16 * ((lane >> 4) & 1) + 8 * (i & 1);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int k = kk * 64 + 32 * (q >> 1) + 16 * (lane >> 5) + 8 * (q & 1) + (i >> 1);
-            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + k * C::LDB + n));
-            fb[nb][2 * q] = v[0];
-            fb[nb][2 * q + 1] = v[1];
+            for (int q = 0; q < 4; ++q) {
+              const int k = kk * 64 + 32 * (q >> 1) + 16 * (lane >> 5) + 8 * (q & 1) + (i >> 1);
+              const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + k * C::LDB + n));
+              fb[nb][2 * q] = v[0];
+              fb[nb][2 * q + 1] = v[1];
+            }
           }
           bsc[nb] = P::MX_ ? (int)(scl[C::BM + wn * C::TN + nb * 32 + (lane & 31)] >> sh) : 127;
         }
@@ -448,10 +461,200 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
   pol.epilogue(acc, wm, wn, lane, smem);
 }
 
+// ---------------------------------------------------------------- FP8 backward
+// The dX chain's products on E4M3 (per-row dynamic scales of every operand): the
+// row operand A is K-major as in the up-projection, the weight operand B is
+// K-major too (a weight row of [I][H] or [H][2I] is contiguous along K).
+
+// Row tile j of one of the routing's tables: expert, first row, rows, N tile.
+template <class C, bool SMALL>
+__device__ __forceinline__ bool f8_row_tile(const RowGroups& g, int logical, int n_ntiles, int& e, int& row0,
+                                            int& rows, int& nt) {
+  const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+  if (logical >= R * n_ntiles) return false;
+  int j;
+  raster(logical, R, n_ntiles, j, nt);
+  const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
+  const int cnt = g.tiles[SMALL ? 1 : 0];
+  const int32_t w = tab[2 * j];
+  row0 = tab[2 * j + 1];
+  if (j >= cnt) return false;
+  e = tile_expert(w);
+  rows = min(C::BM, tile_rows(w));
+  return true;
+}
+
+// shared by both backward products: no per-step scales, K-major weights
+template <class C>
+struct F8BwdBase {
+  typedef C Cc;
+  static constexpr int NTHR_ = C::NTHR;
+  static constexpr bool MX_ = false, GROUP_ = false, STAGED = false, B_KMAJ_ = true;
+  static constexpr int SCR = 1, SC_BYTES = 0;
+  int e, row0, rows, nt, n0, nk;
+  rsrc_t ra_, rb_;
+  uint32_t aoff[C::CA], boff[C::CB];
+  __device__ __forceinline__ void load_s(int, uint32_t (&)[SCR]) {}
+  __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) r[i] = bload(ra_, aoff[i], kt * BKB);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4 (&r)[C::CB]) {
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * BKB);
+  }
+  // B rows n0 + (c >> 3) (clamped to N - 1) of a [N][K] weight slice
+  __device__ __forceinline__ void b_rows(int64_t K, int64_t N) {
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int c = threadIdx.x + i * C::NTHR;
+      boff[i] = (uint32_t)(min((int64_t)(n0 + (c >> 3)), N - 1) * K + (c & 7) * 16);
+    }
+  }
+  // the accumulators times the row's and the column's descale (staged in LDS)
+  __device__ __forceinline__ void scale(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, const float* rsc,
+                                        const float* csc) const {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const float cs = csc[wn * C::TN + nb * 32 + (lane & 31)];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][nb][r] = acc[mb][nb][r] * rsc[acc_row8<C>(wm, mb, r, lane)] * cs;
+      }
+  }
+};
+
+// act_grad: G = (dYq[tok] . W2q[e]^T) dsy[tok] dsw2[e][i], then SwiGLUGrad -> dH and
+// the d_topk_weights partials, as the bf16 product's epilogue
+template <class C, bool SMALL>
+struct ActGradF8 : F8BwdBase<C> {
+  typedef F8BwdBase<C> B_;
+  using B_::e; using B_::row0; using B_::rows; using B_::nt; using B_::n0; using B_::nk;
+  struct Args {
+    RowGroups g;
+    const uint8_t* dyq;  // [T][H] E4M3
+    const float* dsy;    // [T]
+    const uint8_t* w2q;  // [E][I][H] E4M3 (rows i)
+    const float* dsw;    // [E][I]
+    const float* tw;
+    const uint16_t *h, *a;
+    int64_t T, H, I;
+    uint16_t* dh;
+    float* dwpart;
+    int dw_cols;
+    int n_ntiles;
+  };
+  const Args* ar;
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!f8_row_tile<C, SMALL>(A.g, logical, A.n_ntiles, e, row0, rows, nt)) return false;
+    n0 = nt * C::BN;
+    this->ra_ = make_rsrc(A.dyq, A.T * A.H);
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int c = threadIdx.x + i * C::NTHR;
+      const int p = row0 + min(c >> 3, rows - 1);
+      this->aoff[i] = (uint32_t)((int64_t)A.g.tok_of_row[p] * A.H + (c & 7) * 16);
+    }
+    this->rb_ = make_rsrc(A.w2q + (int64_t)e * A.I * A.H, A.I * A.H);
+    this->b_rows(A.H, A.I);
+    nk = (int)(A.H / BKB);
+    return true;
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint8_t* smemb) {
+    constexpr int LDF = C::TN + 4;
+    static_assert((C::BM * LDF + 2 * C::BM + C::BN) * 4 <= 2 * C::STAGE, "staging must fit");
+    float* gst = reinterpret_cast<float*>(smemb);
+    float* wrow = gst + C::BM * LDF;
+    float* rsc = wrow + C::BM;
+    float* csc = rsc + C::BM;
+    for (int t = threadIdx.x; t < C::BM; t += C::NTHR) {
+      const bool v = t < rows;
+      wrow[t] = v ? ar->tw[ar->g.sorted_slot[row0 + t]] : 0.f;
+      rsc[t] = v ? ar->dsy[ar->g.tok_of_row[row0 + t]] : 0.f;
+    }
+    for (int t = threadIdx.x; t < C::BN; t += C::NTHR)
+      csc[t] = (n0 + t < ar->I) ? ar->dsw[(int64_t)e * ar->I + n0 + t] : 0.f;
+    __syncthreads();
+    this->scale(acc, wm, wn, lane, rsc, csc);
+    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->a, ar->dh, ar->dwpart,
+                            ar->dw_cols);
+  }
+};
+
+// input_grad: dXp = bf16((dHq[p] . W1q[e]^T) dsh[p] dsw1[e][h])
+template <class C, bool SMALL>
+struct InputGradF8 : F8BwdBase<C> {
+  typedef F8BwdBase<C> B_;
+  using B_::e; using B_::row0; using B_::rows; using B_::nt; using B_::n0; using B_::nk;
+  struct Args {
+    RowGroups g;
+    const uint8_t* dhq;  // [S][2I] E4M3
+    const float* dsh;    // [S]
+    const uint8_t* w1q;  // [E][H][2I] E4M3 (rows h)
+    const float* dsw;    // [E][H]
+    int64_t S, H, I;
+    uint16_t* dxp;
+    int n_ntiles;
+  };
+  const Args* ar;
+  __device__ __forceinline__ bool init(const Args& A, int logical) {
+    ar = &A;
+    if (!f8_row_tile<C, SMALL>(A.g, logical, A.n_ntiles, e, row0, rows, nt)) return false;
+    n0 = nt * C::BN;
+    const int64_t K = 2 * A.I;
+    this->ra_ = make_rsrc(A.dhq, A.S * K);
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int c = threadIdx.x + i * C::NTHR;
+      this->aoff[i] = (uint32_t)((int64_t)(row0 + min(c >> 3, rows - 1)) * K + (c & 7) * 16);
+    }
+    this->rb_ = make_rsrc(A.w1q + (int64_t)e * A.H * K, A.H * K);
+    this->b_rows(K, A.H);
+    nk = (int)(K / BKB);
+    return true;
+  }
+  __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint8_t* smemb) {
+    constexpr int LD = C::BN + 8;
+    static_assert(C::BM * LD * 2 + (C::BM + C::BN) * 4 <= 2 * C::STAGE, "staging must fit");
+    uint16_t* st = reinterpret_cast<uint16_t*>(smemb);
+    float* rsc = reinterpret_cast<float*>(smemb + C::BM * LD * 2);
+    float* csc = rsc + C::BM;
+    const int64_t H = ar->H;
+    for (int t = threadIdx.x; t < C::BM; t += C::NTHR) rsc[t] = t < rows ? ar->dsh[row0 + t] : 0.f;
+    for (int t = threadIdx.x; t < C::BN; t += C::NTHR)
+      csc[t] = (n0 + t < H) ? ar->dsw[(int64_t)e * H + n0 + t] : 0.f;
+    __syncthreads();
+    this->scale(acc, wm, wn, lane, rsc, csc);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st[acc_row8<C>(wm, mb, r, lane) * LD + wn * C::TN + nb * 32 + (lane & 31)] = f2bf(acc[mb][nb][r]);
+    __syncthreads();
+    constexpr int CPR = C::BN / 8;
+    for (int c = threadIdx.x; c < C::BM * CPR; c += C::NTHR) {
+      const int row = c / CPR, c8 = c % CPR;
+      const int64_t col = n0 + c8 * 8;
+      if (row < rows && col < H)
+        *reinterpret_cast<u32x4*>(ar->dxp + (int64_t)(row0 + row) * H + col) =
+            *reinterpret_cast<const u32x4*>(st + row * LD + c8 * 8);
+    }
+  }
+};
+
 template <class C, bool SMALL, int Q = 0>
 struct Gmm1F8K : Gmm1F8<C, SMALL, Q> {
   typedef C Cc;
   static constexpr int NTHR_ = C::NTHR;
+};
+
+template <class T>
+struct TypeTag8 {
+  typedef T type;
 };
 
 template <class P>
@@ -493,7 +696,39 @@ hipError_t launch_all(const RowGroups& g, const uint8_t* xq, const float* dsx, c
   }
 }
 
+// big then small tiles (or narrow), one launch each
+template <template <class, bool> class P, class Fill>
+hipError_t launch_bwd8(const RowGroups& g, int64_t n_cols, Fill fill, hipStream_t stream) {
+  auto one = [&](auto tag, bool small) -> hipError_t {
+    typedef typename decltype(tag)::type PP;
+    typename PP::Args a{};
+    const int nnt = (int)((n_cols + PP::Cc::BN - 1) / PP::Cc::BN);
+    fill(a, nnt);
+    return launch8<PP>(a, (small ? g.max_small : g.max_big) * nnt, stream);
+  };
+  if (g.narrow) return one(TypeTag8<P<Narrow8, true>>{}, true);
+  const hipError_t e = one(TypeTag8<P<Big8, false>>{}, false);
+  return e != hipSuccess ? e : one(TypeTag8<P<Small8, true>>{}, true);
+}
+
 }  // namespace
+
+hipError_t launch_act_grad_fp8(const RowGroups& g, const uint8_t* dyq, const float* dsy, const uint8_t* w2q,
+                               const float* dsw2, const float* topk_w, const uint16_t* h, const uint16_t* a,
+                               int64_t H, int64_t I, uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream) {
+  return launch_bwd8<ActGradF8>(g, I, [&](auto& A, int nnt) {
+    A.g = g; A.dyq = dyq; A.dsy = dsy; A.w2q = w2q; A.dsw = dsw2; A.tw = topk_w; A.h = h; A.a = a;
+    A.T = g.T; A.H = H; A.I = I; A.dh = dh; A.dwpart = dwpart; A.dw_cols = dw_cols; A.n_ntiles = nnt;
+  }, stream);
+}
+
+hipError_t launch_input_grad_fp8(const RowGroups& g, const uint8_t* dhq, const float* dsh, const uint8_t* w1q,
+                                 const float* dsw1, int64_t H, int64_t I, uint16_t* dxp, hipStream_t stream) {
+  return launch_bwd8<InputGradF8>(g, H, [&](auto& A, int nnt) {
+    A.g = g; A.dhq = dhq; A.dsh = dsh; A.w1q = w1q; A.dsw = dsw1; A.S = g.S; A.H = H; A.I = I; A.dxp = dxp;
+    A.n_ntiles = nnt;
+  }, stream);
+}
 
 hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* dsx, const uint8_t* wq,
                            const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,

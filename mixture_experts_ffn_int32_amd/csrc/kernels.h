@@ -195,6 +195,20 @@ hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* d
                            const float* dsw, const float* topk_w, int64_t H, int64_t I, uint16_t* h, uint16_t* a,
                            uint16_t* aw, hipStream_t stream);
 
+// FP8 backward (gemm_fp8.hip): the dX chain's products on E4M3 with per-row
+// descales of both operands (codes from launch_quant_rows_fp8 on row views).
+//   act_grad:   G = (dyq[tok] . w2q[e]^T) dsy[tok] dsw2[e][i], then the SwiGLUGrad
+//               epilogue of launch_act_grad (dH, d_topk_weights partials);
+//               dyq [T][H], w2q [E][I][H] (rows i), dsw2 [E][I]; H a multiple of 128
+//   input_grad: dXp = bf16((dhq[p] . w1q[e]^T) dsh[p] dsw1[e][h]);
+//               dhq [S][2I], w1q [E][H][2I] (rows h), dsw1 [E][H]
+// Both on the tiling of ``g`` (256 + 64-row tiles, or 64x64 when narrow).
+hipError_t launch_act_grad_fp8(const RowGroups& g, const uint8_t* dyq, const float* dsy, const uint8_t* w2q,
+                               const float* dsw2, const float* topk_w, const uint16_t* h, const uint16_t* a,
+                               int64_t H, int64_t I, uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream);
+hipError_t launch_input_grad_fp8(const RowGroups& g, const uint8_t* dhq, const float* dsh, const uint8_t* w1q,
+                                 const float* dsw1, int64_t H, int64_t I, uint16_t* dxp, hipStream_t stream);
+
 // pointwise (pointwise.hip).  ``extra`` [T][H] (may be NULL): the shared expert's rows,
 // added with weight 1 after the K routed terms.
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of_slot, const float* topk_w, int64_t T,

@@ -197,7 +197,7 @@ class HyperMegaMoEFunction(torch.autograd.Function):
 
 def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *, validate_ids=True,
                    gmm1_dtype="bf16", out_dtype=torch.bfloat16, shared_up_proj_weight=None,
-                   shared_down_proj_weight=None):
+                   shared_down_proj_weight=None, fp8_backward=False):
     """y [T,H] = sum_k topk_weights[t,k] * SwiGLU-FFN_{topk_ids[t,k]}(x[t]), on the GPU.
 
     x bf16 [T,H]; topk_ids int32/int64 [T,K] (0 <= id < E); topk_weights float [T,K];
@@ -223,8 +223,11 @@ def hyper_mega_moe(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, 
     [Is,H] add a shared expert: every token also goes through that SwiGLU FFN,
     and its output is added to y with weight 1 (after the routed terms); both
     get gradients.  Its up-projection stays bf16 under ``gmm1_dtype="fp8"``.
+    ``fp8_backward=True`` runs the backward's act_grad and input_grad products on
+    FP8 E4M3 (per-row dynamic scales of dY, dH and the weight rows; H a multiple
+    of 128, bf16 outputs); the weight gradients stay bf16.
     """
-    flags = _lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0
+    flags = (_lib.HMM_FLAG_VALIDATE_IDS if validate_ids else 0) | (_lib.HMM_FLAG_FP8_BACKWARD if fp8_backward else 0)
     return HyperMegaMoEFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, flags,
                                       _gmm1_code(gmm1_dtype), _out_code(out_dtype), shared_up_proj_weight,
                                       shared_down_proj_weight)
@@ -412,12 +415,13 @@ def forward_with_saved(x, topk_ids, topk_weights, up_proj_weight, down_proj_weig
 
 def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, tiles="auto",
                         gmm1_dtype="bf16", out_dtype="bf16", shared_up_proj_weight=None,
-                        shared_down_proj_weight=None, serial=False):
+                        shared_down_proj_weight=None, serial=False, fp8_backward=False):
     """Backward without autograd; returns (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights),
     then (d_shared_up_proj_weight, d_shared_down_proj_weight) with a shared expert.
 
     With out_dtype float32, dy is taken in float32 and dx and the weight gradients are float32.
-    ``serial=True`` keeps every launch on the current stream (HMM_FLAG_SERIAL_BACKWARD)."""
+    ``serial=True`` keeps every launch on the current stream (HMM_FLAG_SERIAL_BACKWARD);
+    ``fp8_backward=True`` runs act_grad and input_grad on E4M3 (HMM_FLAG_FP8_BACKWARD)."""
     T, H, I, E, K = _check_inputs(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     Is = _check_shared(x, shared_up_proj_weight, shared_down_proj_weight)
     out = _out_code(out_dtype)
@@ -426,6 +430,7 @@ def backward_from_saved(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj
         return _backward_raw(_contig(dy, dyt), _contig(x), _contig(topk_ids, torch.int32),
                              _contig(topk_weights, torch.float32), _contig(up_proj_weight),
                              _contig(down_proj_weight), saved, T, H, I, E, K,
-                             _lib.TILE_FLAGS[tiles] | (_lib.HMM_FLAG_SERIAL_BACKWARD if serial else 0),
+                             _lib.TILE_FLAGS[tiles] | (_lib.HMM_FLAG_SERIAL_BACKWARD if serial else 0)
+                             | (_lib.HMM_FLAG_FP8_BACKWARD if fp8_backward else 0),
                              _gmm1_code(gmm1_dtype), out, _contig(shared_up_proj_weight) if Is else None,
                              _contig(shared_down_proj_weight) if Is else None)

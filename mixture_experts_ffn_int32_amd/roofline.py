@@ -23,6 +23,10 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
     eb = 4 if f32 else 2
     if stage in ("gmm1_fp8_swiglu", "gmm1_mx_swiglu", "gmm1_group_swiglu"):
         return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
+    if stage == "act_grad_fp8":     # FP8 backward: [S,H] x [H,I] on E4M3
+        return "mfma", 2 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
+    if stage == "input_grad_fp8":   # [S,2I] x [2I,H] on E4M3
+        return "mfma", 4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS
     flops = {
         "gmm1_swiglu": 4 * S * H * I,   # [S,H] x [H,2I]
         "gmm2": 2 * S * I * H,          # [S,I] x [I,H]
@@ -59,6 +63,11 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
         # per group of 128 along H: one float32 descale per token row / weight column
         "quant_x_group": T * H * 2 + T * H + T * (H // 128) * 4,
         "quant_w1_group": E * H * 2 * I * 2 + E * H * 2 * I + E * (H // 128) * 2 * I * 4,
+        # FP8 backward's per-row quantisers: bf16 rows in, E4M3 codes and one descale per row out
+        "quant_dy": T * H * 3 + T * 4,
+        "quant_w2": E * I * H * 3 + E * I * 4,
+        "quant_dh": S * 2 * I * 3 + S * 4,
+        "quant_w1r": E * H * 2 * I * 3 + E * H * 4,
     }
     if stage in nbytes:
         return "hbm", nbytes[stage], "GB/s", PEAK_HBM_GBS

@@ -48,6 +48,9 @@ WORKLOADS = {
     # the same shape with the MX (32-block) quantised up-projection
     "mx": dict(T=16384, H=4096, I=1536, E=64, K=6, routing="uniform",
                outlier_frac=0.01, outlier_scale=20.0, gmm1="mx"),
+    # the FP8 workload with the FP8 backward as well (act_grad and input_grad on E4M3)
+    "fp8bwd": dict(T=16384, H=4096, I=1536, E=64, K=6, routing="uniform",
+                   outlier_frac=0.01, outlier_scale=20.0, gmm1="fp8", fp8_backward=True),
     # the same shape with the per-group (128 along H) quantised up-projection
     "group": dict(T=16384, H=4096, I=1536, E=64, K=6, routing="uniform",
                   outlier_frac=0.01, outlier_scale=20.0, gmm1="group"),

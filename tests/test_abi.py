@@ -54,7 +54,9 @@ def _prob(**kw):
     (dict(T=-1), _lib.HMM_ERR_BAD_SHAPE), (dict(T=1 << 28, K=16), _lib.HMM_ERR_BAD_SHAPE),
     (dict(out_dtype=7), _lib.HMM_ERR_BAD_DTYPE), (dict(gmm1_dtype=9), _lib.HMM_ERR_BAD_DTYPE),
     (dict(out_dtype=_lib.HMM_F32, gmm1_dtype=_lib.HMM_FP8_E4M3), _lib.HMM_ERR_UNSUPPORTED),
-    (dict(gmm1_dtype=_lib.HMM_FP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=32), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(gmm1_dtype=_lib.HMM_FP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(flags=64), _lib.HMM_ERR_BAD_SHAPE),
+    (dict(flags=_lib.HMM_FLAG_FP8_BACKWARD, out_dtype=_lib.HMM_F32), _lib.HMM_ERR_UNSUPPORTED),
+    (dict(flags=_lib.HMM_FLAG_FP8_BACKWARD, H=192), _lib.HMM_ERR_BAD_SHAPE),
     (dict(gmm1_dtype=_lib.HMM_MXFP8_E4M3, H=192), _lib.HMM_ERR_BAD_SHAPE), (dict(gmm1_dtype=5), _lib.HMM_ERR_BAD_DTYPE),
     (dict(gmm1_dtype=_lib.HMM_FP8_E4M3_GROUP, H=192), _lib.HMM_ERR_BAD_SHAPE),
     (dict(gmm1_dtype=_lib.HMM_FP8_E4M3_GROUP, flags=_lib.HMM_FLAG_VALIDATE_IDS | _lib.HMM_FLAG_TILES_LARGE),

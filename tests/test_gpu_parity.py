@@ -18,14 +18,14 @@ from oracle.routing import route as oracle_route
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(g, tiles="auto", gmm1="bf16"):
+def run_gpu(g, tiles="auto", gmm1="bf16", fp8_backward=False):
     import torch
     from mixture_experts_ffn_int32_amd import backward_from_saved, forward_with_saved
     y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
                                   g["down_proj_weight"], tiles=tiles, gmm1_dtype=gmm1)
     dx, dW1, dW2, dw = backward_from_saved(g["dY"], g["x"], g["topk_ids"], g["topk_weights"],
                                            g["up_proj_weight"], g["down_proj_weight"], saved, tiles=tiles,
-                                           gmm1_dtype=gmm1)
+                                           gmm1_dtype=gmm1, fp8_backward=fp8_backward)
     torch.cuda.synchronize()
     return y, saved, dx, dW1, dW2, dw
 
@@ -189,16 +189,17 @@ def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):
     spec = synth.WORKLOADS[name]
     T, H, I, E, K = (spec[k] for k in "THIEK")
     gmm1 = spec.get("gmm1", "bf16")
+    fp8bwd = bool(spec.get("fp8_backward"))
     inp = synth.make_inputs(spec, seed=0)
     announce("full-size sampled parity %s" % name)
     g = gpu_inputs(inp, "cuda")
-    y, saved, dx, dW1, dW2, dw = run_gpu(g, gmm1=gmm1)
+    y, saved, dx, dW1, dW2, dw = run_gpu(g, gmm1=gmm1, fp8_backward=fp8bwd)
     from mixture_experts_ffn_int32_amd import saved_views
     v = saved_views(saved, T, H, I, E, K, gmm1_dtype=gmm1)
     ref_route = oracle_route(inp["topk_ids"], E)
     for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
         assert np.array_equal(v[k].cpu().numpy(), ref_route[k]), k
-    o = MoEFFN(**oracle_inputs(inp), mode="faithful", gmm1=gmm1)
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful", gmm1=gmm1, bwd="fp8" if fp8bwd else "bf16")
     rng = np.random.default_rng(1)
     toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_tok, replace=False)]))
     ti = torch.from_numpy(toks).cuda()
