@@ -232,6 +232,7 @@ struct BwdWork {
   // FP8 backward: E4M3 codes and float32 descales of dY [T][H], W2 rows [E*I][H],
   // dH [S][2I] and W1 rows [E*H][2I]
   size_t dyq, dsy, w2q, dsw2, dhq, dsh, w1q, dsw1;
+  size_t order;  // [E] int32: the experts by descending row count (weight gradients, large tiling)
   int dw_cols;
 };
 BwdWork bwd_work(const Dims& d) {
@@ -245,6 +246,9 @@ BwdWork bwd_work(const Dims& d) {
   w.dh = o;     o += up(d.S * 2 * d.I * 2 * wide);
   w.dxp = o;    o += up(d.S * d.H * (d.f32 ? 4 : 2));
   w.dwpart = o; o += up(d.S * w.dw_cols * 4);
+  if (d.S > 0 && !d.f32 && !d.small) {
+    w.order = o; o += up(d.E * 4);
+  }
   if (d.shared) {  // the shared expert's dH and dX rows
     w.dhs = o;  o += up(d.T * 2 * d.Is * 2 * wide);
     w.dxs = o;  o += up(d.T * d.H * (d.f32 ? 4 : 2));
@@ -940,12 +944,24 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
        nullptr, 0}};
   const hmm::InputGradJob ig[2] = {{g, dh, (const uint16_t*)up_w, d.H, d.I, dxp},
                                    {gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs}};
-  const hmm::DwJob dw2[2] = {
+  hmm::DwJob dw2[2] = {
       hmm::dw2_job(offsets, tok_of_row, d.T, d.S, d.E, aw, (const uint16_t*)dy, d.H, d.I, (uint16_t*)d_down_w),
       hmm::dw2_job(s_offsets, s_idx, d.T, d.T, 1, as, (const uint16_t*)dy, d.H, d.Is, (uint16_t*)d_down_s)};
-  const hmm::DwJob dw1[2] = {
+  hmm::DwJob dw1[2] = {
       hmm::dw1_job(offsets, tok_of_row, d.T, d.S, d.E, (const uint16_t*)x, dh, d.H, d.I, (uint16_t*)d_up_w),
       hmm::dw1_job(s_offsets, s_idx, d.T, d.T, 1, (const uint16_t*)x, dhs, d.H, d.Is, (uint16_t*)d_up_s)};
+  if (ne && !d.small) {
+    // large tiling: the routed weight gradients take the experts longest first
+    // (their cost grows with the row count; a large expert last would run alone
+    // at the launch's end)
+    int32_t* order = at<int32_t>(workspace, W.order);
+    {
+      Stage stage("expert_order", st);
+      e = hmm::launch_expert_order(at<int32_t>(saved, L.counts), (int)d.E, order, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "expert order launch");
+    dw1[0].order = dw2[0].order = order;
+  }
   if (d.fp8bwd) {
     // FP8 backward: dY and the rows of W2 quantised per row, act_grad on E4M3 (dH
     // and the d_topk_weights partials as in bf16), dH and the rows of W1 quantised,

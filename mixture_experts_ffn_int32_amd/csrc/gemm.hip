@@ -73,7 +73,7 @@ void fill_input_grad(A& a, const InputGradJob& j, int nnt) {
 template <class C, bool GA, bool GB>
 typename Dw<C, GA, GB>::Args dw_args(const DwJob& j) {
   return typename Dw<C, GA, GB>::Args{j.offsets, j.tok_of_row, j.E, j.A, j.B, j.a_rows, j.b_rows, j.M, j.N, j.out,
-                                      (int)((j.M + C::BM - 1) / C::BM), (int)((j.N + C::BN - 1) / C::BN)};
+                                      (int)((j.M + C::BM - 1) / C::BM), (int)((j.N + C::BN - 1) / C::BN), j.order};
 }
 template <class A>
 int64_t dw_blocks(const A& a) { return a.E * 8 * ((a.mt * a.nt + 7) / 8); }

@@ -282,6 +282,7 @@ struct Dw : PlainCols<Cc> {
     int64_t M, N;
     uint16_t* Cout;     // [E][M][N]
     int mt, nt;
+    const int32_t* order;  // [E] launch order of the experts, or NULL (0, 1, ...)
   };
   const Args* ar;
   rsrc_t ra_, rb_;
@@ -294,17 +295,20 @@ struct Dw : PlainCols<Cc> {
   };
   // The cost of a tile grows with its expert's row count, so every XCD gets an
   // equal slice of every expert's tiles (not a contiguous run of experts): XCD x
-  // (workgroups b with b % 8 == x) walks the experts in order and takes tiles
-  // [x * per, (x + 1) * per) of each, per = ceil(mt * nt / 8); inside a slice the
-  // tiles are rasterised in groups of GROUP_M row tiles.
+  // (workgroups b with b % 8 == x) walks the experts in launch order (``order``:
+  // longest reductions first, so the largest expert's tiles do not end the
+  // launch alone) and takes tiles [x * per, (x + 1) * per) of each, per =
+  // ceil(mt * nt / 8); inside a slice the tiles are rasterised in groups of
+  // GROUP_M row tiles.
   __device__ __forceinline__ bool init(const Args& A, int b) {
     ar = &A;
     const int per_e = A.mt * A.nt;
     const int per = (per_e + 7) / 8;
     const int j = b >> 3;
-    e = j / per;
-    if (e >= A.E) return false;
-    const int t = (b & 7) * per + (j - e * per);
+    const int rank = j / per;
+    if (rank >= A.E) return false;
+    e = A.order ? A.order[rank] : rank;
+    const int t = (b & 7) * per + (j - rank * per);
     if (t >= per_e) return false;
     int r, c;
     raster(t, A.mt, A.nt, r, c);

@@ -139,6 +139,7 @@ struct DwJob {
   const uint16_t* B;
   int64_t a_rows, b_rows, M, N;
   uint16_t* out;              // [E][M][N]
+  const int32_t* order = nullptr;  // [E]: the experts in launch order (NULL: 0, 1, ...)
 };
 inline DwJob dw1_job(const int32_t* offsets, const int32_t* tok_of_row, int64_t T, int64_t S, int64_t E,
                      const uint16_t* x, const uint16_t* dh, int64_t H, int64_t I, uint16_t* dw1) {
@@ -149,6 +150,9 @@ inline DwJob dw2_job(const int32_t* offsets, const int32_t* tok_of_row, int64_t 
   return DwJob{offsets, tok_of_row, E, aw, dy, S, T, I, H, dw2};
 }
 hipError_t launch_dw1(const DwJob* jobs, int n, bool narrow, hipStream_t stream);
+// order[r] = the expert of rank r by descending row count (ties: lower id first),
+// for the weight gradients to start the longest reductions first (route.hip)
+hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t stream);
 hipError_t launch_dw2(const DwJob* jobs, int n, bool narrow, hipStream_t stream);
 // Small problems (narrow tiles): the independent products share a launch,
 // act_grad with W2Grad, then input_grad with W1Grad (the same products as above;

@@ -243,7 +243,32 @@ __global__ void __launch_bounds__(RT_ONE_THREADS) route_one(const int32_t* __res
                               tok_of_row, tiles, err, host_err);
 }
 
+// The experts ranked by descending row count, ties by id (a permutation: every
+// expert gets a distinct rank).  One block of RT_SCAN_THREADS >= E threads;
+// thread e counts the experts that go before it.
+__global__ void __launch_bounds__(RT_SCAN_THREADS) expert_order(const int32_t* __restrict__ counts, int E,
+                                                                int32_t* __restrict__ order) {
+  __shared__ int32_t c[RT_SCAN_THREADS];
+  const int e = threadIdx.x;
+  if (e < E) c[e] = counts[e];
+  __syncthreads();
+  if (e >= E) return;
+  const int32_t ce = c[e];
+  int rank = 0;
+  for (int f = 0; f < E; ++f) {
+    const int32_t cf = c[f];
+    rank += (cf > ce || (cf == ce && f < e)) ? 1 : 0;
+  }
+  order[rank] = e;
+}
+
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_expert_order(const int32_t* counts, int E, int32_t* order, hipStream_t stream) {
+  if (E <= 0 || E > RT_SCAN_THREADS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_order, dim3(1), dim3(RT_SCAN_THREADS), 0, stream, counts, E, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int K, int max_big, int big_on, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* row_of_slot, int32_t* tok_of_row,
