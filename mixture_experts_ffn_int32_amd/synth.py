@@ -25,7 +25,10 @@ Routing structures:
   token (successive sampling without replacement, done as Gumbel-top-K);
 * ``hot``: one seeded hot expert sits in every token at a random position, the
   other K - 1 are distinct and uniform over the remaining experts
-  (``hot_dup`` puts the hot expert in two positions of every token).
+  (``hot_dup`` puts the hot expert in two positions of every token);
+* ``counts``: K = 1 and expert e receives exactly ``counts[e]`` tokens, in a
+  seeded random token order (T = sum of the counts), to place expert sizes on
+  chosen tile boundaries.
 """
 
 import math
@@ -123,6 +126,13 @@ def route_hot(rng, T, E, K, dup=False):
     return ids, hot
 
 
+def route_counts(rng, T, E, K, counts):
+    counts = np.asarray(counts, np.int64)
+    if K != 1 or counts.shape != (E,) or counts.sum() != T or (counts < 0).any():
+        raise ValueError("counts routing needs K = 1 and E non-negative counts summing to T")
+    return rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+
+
 def softmax_weights(rng, T, K):
     z = rng.standard_normal((T, K))
     z = np.exp(z - z.max(axis=1, keepdims=True))
@@ -142,6 +152,8 @@ def make_routing(spec, seed=0):
         ids = route_zipf(r_ids, T, E, K, spec.get("zipf_s", 1.2), spec.get("n_empty", 10))
     elif kind in ("hot", "hot_dup"):
         ids, info["hot_expert"] = route_hot(r_ids, T, E, K, dup=(kind == "hot_dup"))
+    elif kind == "counts":
+        ids = route_counts(r_ids, T, E, K, spec["counts"])
     else:
         raise ValueError(kind)
     return ids, softmax_weights(r_w, T, K), info

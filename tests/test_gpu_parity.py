@@ -38,6 +38,10 @@ SMALL = [
     ("hotdup", dict(T=130, H=128, I=64, E=4, K=3, routing="hot_dup")),
     ("k1", dict(T=200, H=128, I=128, E=3, K=1, routing="uniform")),
     ("zipf", dict(T=411, H=256, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
+    # expert sizes on the large tiling's boundaries: remainders of 1-64, 65-128
+    # (small tiles, one or two table entries) and 129-255 rows (a partial big tile)
+    ("bounds", dict(T=2278, H=128, I=64, E=14, K=1, routing="counts",
+                    counts=[0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 385, 228])),
 ]
 
 

@@ -106,3 +106,8 @@ def test_workload_routing_structures():
     u = synth.WORKLOADS["sample"]
     ids, _, _ = synth.make_routing(u, 0)
     assert all(len(set(row)) == u["K"] for row in ids)
+    c = [0, 3, 70, 1]
+    ids, _, _ = synth.make_routing(synth.spec_with("tiny", T=74, E=4, K=1, routing="counts", counts=c), 0)
+    assert ids.shape == (74, 1) and np.bincount(ids.reshape(-1), minlength=4).tolist() == c
+    with pytest.raises(ValueError):
+        synth.make_routing(synth.spec_with("tiny", T=75, E=4, K=1, routing="counts", counts=c), 0)
