@@ -63,11 +63,20 @@ __device__ __forceinline__ void route_block(RouteLds<NT>& L, const int32_t* __re
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int ev[R], rc[R];  // id; rank | count << 8 (both <= 64)
   int bad = 0;
+  // every round's id load is issued before the first ballot needs one, so the
+  // wave waits for its loads once, not once per round
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int64_t s = s0 + j * 64 + lane;
-    const bool in = (j * 64 < chunk) && s < S;
-    int e = in ? ids[s] : -1;
+    ev[j] = ((j * 64 < chunk) && s < S) ? ids[s] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    rc[j] = 0;
+    if (j * 64 >= chunk) continue;  // past the chunk (the same for every wave): no ballots
+    const int64_t s = s0 + j * 64 + lane;
+    const bool in = s < S;
+    int e = ev[j];
     const bool valid = in && e >= 0 && e < E;
     bad |= (in && !valid);
     uint64_t peers = __ballot(valid);
@@ -95,10 +104,13 @@ __device__ __forceinline__ void route_block(RouteLds<NT>& L, const int32_t* __re
   // per expert: exclusive prefix over the waves, total count
   int c = 0;
   if (tid < E) {
+    int v[NW];  // all reads issued before the first write
+#pragma unroll
+    for (int q = 0; q < NW; ++q) v[q] = cntw[q][tid];
+#pragma unroll
     for (int q = 0; q < NW; ++q) {
-      const int v = cntw[q][tid];
       cntw[q][tid] = c;
-      c += v;
+      c += v[q];
     }
   }
   // offsets and tile tables (the rule of route_scan): inclusive scans over the experts,
@@ -161,6 +173,7 @@ __device__ __forceinline__ void route_block(RouteLds<NT>& L, const int32_t* __re
   // phase 2: rows; cntw[w][e] runs through the earlier slots of e in this chunk
 #pragma unroll
   for (int j = 0; j < R; ++j) {
+    if (j * 64 >= chunk) continue;
     const int64_t s = s0 + j * 64 + lane;
     const int e = ev[j];
     const int rk = rc[j] & 0xff, cn = rc[j] >> 8;
