@@ -93,6 +93,10 @@ GROUP_SMALL = [
     ("ragged", dict(T=300, H=256, I=192, E=6, K=3, routing="uniform")),
     ("zipf", dict(T=411, H=384, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
     ("outliers", dict(T=520, H=256, I=320, E=3, K=2, routing="hot", outlier_frac=0.02, outlier_scale=30.0)),
+    # expert sizes of one to five 64-row entries, full and partial (the product's
+    # 128-row tiles take the entries in pairs)
+    ("bounds", dict(T=1092, H=256, I=64, E=9, K=1, routing="counts",
+                    counts=[0, 1, 64, 65, 128, 129, 192, 193, 320])),
 ]
 
 
