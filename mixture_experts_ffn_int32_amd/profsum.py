@@ -76,6 +76,10 @@ def stage_of(name):
     if "fused_forward" in name:
         return "fused_forward", "fused_forward"
     if "gemm_fp8_kernel" in name:
+        if "ActGradF8<" in name:
+            return "act_grad_fp8" + suf, "act_grad_fp8"
+        if "InputGradF8<" in name:
+            return "input_grad_fp8" + suf, "input_grad_fp8"
         m = re.search(r"F8Cfg<[^>]*>, (?:true|false), (\d)>", name)
         st = {"1": "gmm1_mx_swiglu", "2": "gmm1_group_swiglu"}.get(m.group(1) if m else "0", "gmm1_fp8_swiglu")
         return st + suf, st
@@ -105,6 +109,24 @@ def _one(pattern):
 def kernel_stats(d):
     f = _one(os.path.join(d, "**", "*kernel_stats.csv"))
     return list(csv.DictReader(open(f))) if f else []
+
+
+def overlapping(d):
+    """Names of kernels whose dispatches overlap another kernel's in the trace (two streams)."""
+    f = _one(os.path.join(d, "**", "*kernel_trace.csv"))
+    if not f:
+        return set()
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(open(f)))
+    # consecutive launches on one stream may overlap by the few microseconds of a
+    # kernel's end; count an overlap above 10 us and a tenth of the shorter kernel
+    out, beg, end, last = set(), -1, -1, None
+    for a, b, n in iv:
+        ov = min(end, b) - a
+        if ov > max(10000, 0.1 * min(b - a, end - beg)):
+            out.update((n, last))
+        if b > end:
+            beg, end, last = a, b, n
+    return out
 
 
 def counters(d):
@@ -169,13 +191,23 @@ def summarise(wl, rundir):
            "clock GHz | dep. wait | executed / work |",
            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     per = {}
-    for r in kernel_stats(os.path.join(rundir, "prof_" + wl)):
+    rows = kernel_stats(os.path.join(rundir, "prof_" + wl))
+    # kernels per stage (a stage of several launches, such as the FP8 up-projection's
+    # big-tile and small-tile launches, gets its rate in the per-stage table only)
+    nk = {}
+    for r in rows:
+        nk[stage_of(r["Name"])[1]] = nk.get(stage_of(r["Name"])[1], 0) + 1
+    calls = sorted(int(r["Calls"]) for r in rows)
+    steps = max(set(calls), key=calls.count) if calls else 1  # the product kernels run once per step
+    stage_ns = {}
+    for r in rows:
         name = r["Name"]
         label, st = stage_of(name)
+        stage_ns[st] = stage_ns.get(st, 0.0) + float(r["TotalDurationNs"])
         avg_us = float(r["AverageNs"]) / 1e3
         bound, work, unit, peak = stage_work(st, T, H, I, E, K)
         rate = frac = None
-        if bound and not label.startswith("route_"):
+        if bound and not label.startswith("route_") and nk[st] == 1:
             rate = work / (avg_us * 1e-6) / (1e12 if bound == "mfma" else 1e9)
             frac = rate / peak
         f, w = fetch.get(name, {}).get("FETCH_SIZE"), write.get(name, {}).get("WRITE_SIZE")
@@ -206,6 +238,22 @@ def summarise(wl, rundir):
             ("%.1f" % (hbm / 1e6)) if hbm is not None else "", ("%.3f" % busy) if busy is not None else "",
             ("%.2f" % clock) if clock else "", ("%.2f" % wait) if wait is not None else "",
             ("%.3f" % execd) if execd else ""))
+    ov = sorted({stage_of(n)[0] for n in overlapping(os.path.join(rundir, "prof_" + wl))})
+    if ov:
+        out += ["", "These kernels ran at the same time as another kernel in the traced steps (the backward's weight "
+                "gradients on a second stream beside the dX chain), so their durations include the sharing: "
+                + ", ".join(ov) + "."]
+    multi = sorted(st for st, n in nk.items() if n > 1 and stage_work(st, T, H, I, E, K)[0])
+    if multi:
+        out += ["", "Stages of several launches (time per step = the launches' total duration / %d steps):" % steps,
+                "", "| stage | launches per step | us per step | work | rate | of peak |", "|---|---|---|---|---|---|"]
+        for st in multi:
+            bound, work, unit, peak = stage_work(st, T, H, I, E, K)
+            us = stage_ns[st] / steps / 1e3
+            rate = work / (us * 1e-6) / (1e12 if bound == "mfma" else 1e9)
+            out.append("| %s | %d | %.2f | %.4g %s | %.1f %s | %.3f |" % (
+                st, nk[st], us, work / (1e12 if bound == "mfma" else 1e6), "TFLOP" if bound == "mfma" else "MB",
+                rate, unit, rate / peak))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", "step_kernels_%s.md" % stem)
     with open(path, "w") as fh:
