@@ -73,6 +73,8 @@ def stage_of(name):
         return "combine", "combine"
     if "combine_kernel<false" in name:
         return "combine_dx", "combine_dx"
+    if "expert_order" in name:
+        return "expert_order", "expert_order"
     if "fused_forward" in name:
         return "fused_forward", "fused_forward"
     if "gemm_fp8_kernel" in name:
