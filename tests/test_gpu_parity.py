@@ -40,6 +40,9 @@ SMALL = [
     ("zipf", dict(T=411, H=256, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
     # expert sizes on the large tiling's boundaries: remainders of 1-64, 65-128
     # (small tiles, one or two table entries) and 129-255 rows (a partial big tile)
+    # the most experts the routing takes, many of them empty or tied in size (the weight
+    # gradients' longest-first expert order ranks all 1024)
+    ("e1024", dict(T=512, H=128, I=64, E=1024, K=8, routing="zipf", zipf_s=0.6, n_empty=200)),
     ("bounds", dict(T=2278, H=128, I=64, E=14, K=1, routing="counts",
                     counts=[0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 385, 228])),
 ]
