@@ -23,8 +23,10 @@
  *   device); all are caller-owned and caller-allocated.  The library never
  *   allocates device memory.  Its only state is, per host thread and device,
  *   one pinned host word and event for the id check (and for the fused
- *   forward), the optional stage-timing events, and the device array of
- *   hmm_forward_noalloc (64 MiB per device, fixed at load).
+ *   forward), the backward's second stream (default priority) with its three
+ *   events, the optional stage-timing events, and the device array of
+ *   hmm_forward_noalloc (64 MiB per device, fixed at load).  That state is made
+ *   on the first call that needs it.
  * - All tensors are dense, row-major (last index fastest), with no padding.
  *   bf16 tensors are arrays of 16-bit bfloat16 values; every device pointer must
  *   be 16-byte aligned.
@@ -44,6 +46,11 @@
  * - Calls that share a workspace or saved buffer must be ordered by the caller
  *   (same stream, or events); concurrent calls from several host threads on the
  *   same buffers are not supported.
+ * - HIP graph capture: calls without HMM_FLAG_VALIDATE_IDS and
+ *   HMM_FLAG_FUSED_FORWARD allocate nothing, issue no memset and never wait on
+ *   the host, so they may be captured (the backward's second stream joins the
+ *   capture through its events).  Make one call of the same kind on the device
+ *   before capturing, so the per-device state above exists.
  */
 #ifndef HMM_H
 #define HMM_H
