@@ -37,4 +37,12 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// A 16-byte store of a product's output with the streaming (non-temporal) hint:
+// the outputs are far larger than the L2 caches and read back, if at all, by a
+// later launch, so they should not evict the operand tiles that the workgroups
+// of an XCD share (measured: hotspot -0.6%, skewed -1.6% per step).
+__device__ __forceinline__ void store16_stream(uint16_t* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 }  // namespace hmm

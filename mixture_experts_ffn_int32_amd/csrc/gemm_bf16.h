@@ -99,10 +99,10 @@ struct Gmm1 : RowTile<Cc, SMALL> {
         av[j] = round_bf(g[j] * sigmoidf_(g[j]) * u[j]);
         aw[j] = w * av[j];
       }
-      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
-      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
+      store16_stream(ar->h + p * 2 * I + i, gv);
+      store16_stream(ar->h + p * 2 * I + I + i, uv);
       put16(ar->a, ar->g.S * I * 2, p * I + i, pack8(av), ar->coh);
-      if (ar->aw) *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
+      if (ar->aw) store16_stream(ar->aw + p * I + i, pack8(aw));
     }
   }
 };

@@ -95,8 +95,8 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
           dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
           du[j] = dA * g[j] * sg;
         }
-        *reinterpret_cast<u32x4*>(dhbuf + p * 2 * I + i) = pack8(dg);
-        *reinterpret_cast<u32x4*>(dhbuf + p * 2 * I + I + i) = pack8(du);
+        store16_stream(dhbuf + p * 2 * I + i, pack8(dg));
+        store16_stream(dhbuf + p * 2 * I + I + i, pack8(du));
       }
       // the CPR threads of a row are consecutive lanes: fixed-order butterfly
 #pragma unroll

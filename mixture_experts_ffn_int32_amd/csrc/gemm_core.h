@@ -253,14 +253,14 @@ __device__ __forceinline__ int32_t get(const int32_t* p, bool coh) {
   return coh ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
 }
 
-// A 16-byte store of a result; with ``coh`` it goes to the device-wide coherence
-// point (sc1, as an agent-scope store), for a consumer on another XCD in the same
-// launch.  ``base``/``bytes`` describe the whole output array (below 4 GiB).
+// A 16-byte store of a result: streaming, or with ``coh`` to the device-wide
+// coherence point (sc1, as an agent-scope store), for a consumer on another XCD
+// in the same launch.  ``base``/``bytes`` describe the whole output array (below 4 GiB).
 __device__ __forceinline__ void put16(uint16_t* base, int64_t bytes, int64_t elem, u32x4 v, bool coh) {
   if (coh)
     __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(base, bytes), (uint32_t)(elem * 2), 0, 16);
   else
-    *reinterpret_cast<u32x4*>(base + elem) = v;
+    store16_stream(base + elem, v);
 }
 
 template <class C, class P>

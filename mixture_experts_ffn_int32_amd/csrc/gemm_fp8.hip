@@ -257,10 +257,10 @@ struct Gmm1F8 {
         av[j] = round_bf(g[j] * sigmoidf_(g[j]) * u[j]);
         aw[j] = w * av[j];
       }
-      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + i) = gv;
-      *reinterpret_cast<u32x4*>(ar->h + p * 2 * I + I + i) = uv;
-      *reinterpret_cast<u32x4*>(ar->a + p * I + i) = pack8(av);
-      *reinterpret_cast<u32x4*>(ar->aw + p * I + i) = pack8(aw);
+      store16_stream(ar->h + p * 2 * I + i, gv);
+      store16_stream(ar->h + p * 2 * I + I + i, uv);
+      store16_stream(ar->a + p * I + i, pack8(av));
+      store16_stream(ar->aw + p * I + i, pack8(aw));
     }
   }
 };
@@ -640,8 +640,7 @@ struct InputGradF8 : F8BwdBase<C> {
       const int row = c / CPR, c8 = c % CPR;
       const int64_t col = n0 + c8 * 8;
       if (row < rows && col < H)
-        *reinterpret_cast<u32x4*>(ar->dxp + (int64_t)(row0 + row) * H + col) =
-            *reinterpret_cast<const u32x4*>(st + row * LD + c8 * 8);
+        store16_stream(ar->dxp + (int64_t)(row0 + row) * H + col, *reinterpret_cast<const u32x4*>(st + row * LD + c8 * 8));
     }
   }
 };
