@@ -939,8 +939,8 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
   // jobs per product launch: the routed experts, then the shared expert
   const int nj = d.shared ? 2 : 1;
   const hmm::ActGradJob ag[2] = {
-      {g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, a, d.H, d.I, dh, dwpart, W.dw_cols},
-      {gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones, at<uint16_t>(saved, L.shared_h), as, d.H, d.Is, dhs,
+      {g, (const uint16_t*)dy, (const uint16_t*)down_w, topk_weights, h, d.H, d.I, dh, dwpart, W.dw_cols},
+      {gs, (const uint16_t*)dy, (const uint16_t*)down_s, ones, at<uint16_t>(saved, L.shared_h), d.H, d.Is, dhs,
        nullptr, 0}};
   const hmm::InputGradJob ig[2] = {{g, dh, (const uint16_t*)up_w, d.H, d.I, dxp},
                                    {gs, dhs, (const uint16_t*)up_s, d.H, d.Is, dxs}};
@@ -988,8 +988,7 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
       if (e != hipSuccess) return hip_fail(e, "W2 quantisation launch");
       {
         Stage stage("act_grad_fp8", st);
-        e = hmm::launch_act_grad_fp8(g, dyq, dsy, w2q, dsw2, topk_weights, h, a, d.H, d.I, dh, dwpart, W.dw_cols,
-                                     st);
+        e = hmm::launch_act_grad_fp8(g, dyq, dsy, w2q, dsw2, topk_weights, h, d.H, d.I, dh, dwpart, W.dw_cols, st);
       }
       if (e != hipSuccess) return hip_fail(e, "act_grad launch");
       if (d.shared) {

@@ -63,7 +63,7 @@ void fill_gmm2(A& a, const Gmm2Job& j, int nnt) {
 }
 template <class A>
 void fill_act_grad(A& a, const ActGradJob& j, int nnt) {
-  a.g = j.g; a.dy = j.dy; a.w2 = j.w2; a.tw = j.tw; a.h = j.h; a.a = j.a; a.T = j.g.T; a.H = j.H; a.I = j.I;
+  a.g = j.g; a.dy = j.dy; a.w2 = j.w2; a.tw = j.tw; a.h = j.h; a.T = j.g.T; a.H = j.H; a.I = j.I;
   a.dh = j.dh; a.dwpart = j.dwpart; a.dw_cols = j.dw_cols; a.n_ntiles = nnt;
 }
 template <class A>

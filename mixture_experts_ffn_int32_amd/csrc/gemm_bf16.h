@@ -180,7 +180,6 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     const uint16_t* w2;
     const float* tw;
     const uint16_t* h;
-    const uint16_t* a;
     int64_t T, H, I;
     uint16_t* dh;
     float* dwpart;  // may be NULL (the sums are not stored)
@@ -215,7 +214,7 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     float* wrow = gst + C::BM * LDF;
     for (int t = threadIdx.x; t < C::BM; t += C::NTHR)
       wrow[t] = this->row_weight(ar->tw, ar->g, t);
-    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->a, ar->dh, ar->dwpart,
+    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->dh, ar->dwpart,
                             ar->dw_cols);
   }
 };

@@ -41,8 +41,10 @@ __device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t sof
 // ------------------------------------------------------------- act_grad epilogue
 // SwiGLUGrad of one tile of G (fp32 accumulators): one wave column (TN columns)
 // at a time G is staged in LDS (gst, BM x (TN + 4) floats), then each thread takes
-// 8 consecutive columns of one row, reads g, u and a as 16-byte chunks, writes
-// dH = [dg | du] as 16-byte chunks and adds its share of sum_i G a.  The row sums
+// 8 consecutive columns of one row, reads g and u as 16-byte chunks, writes
+// dH = [dg | du] as 16-byte chunks and adds its share of sum_i G a.  a =
+// bf16(silu(g) u) is recomputed from g and u with the forward epilogue's float
+// operations, so it is the forward's a bit for bit, without a third load.  The row sums
 // are reduced in a fixed order (8-lane butterfly, then wave columns in order):
 // one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
 // rows' topk weights (0 past the tile's rows), written by the caller before the
@@ -51,8 +53,7 @@ template <class C>
 __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane,
                                                      float* gst, const float* wrow, int rows, int64_t row0,
                                                      int64_t n0, int64_t I, const uint16_t* hbuf,
-                                                     const uint16_t* abuf, uint16_t* dhbuf, float* dwpart,
-                                                     int dw_cols) {
+                                                     uint16_t* dhbuf, float* dwpart, int dw_cols) {
   constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
   constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
   constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
@@ -84,14 +85,14 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
         float g[8], u[8], av[8], dg[8], du[8];
         unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + i), g);
         unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + I + i), u);
-        unpack8(*reinterpret_cast<const u32x4*>(abuf + p * I + i), av);
         const float w = wrow[row];
         const float* G = gst + row * LDF + c8 * 8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+          const float sg = sigmoidf_(g[j]);
+          av[j] = round_bf(g[j] * sg * u[j]);  // as the up-projection's epilogue forms a
           s += G[j] * av[j];
           const float dA = w * G[j];
-          const float sg = sigmoidf_(g[j]);
           dg[j] = dA * u[j] * sg * (1.f + g[j] * (1.f - sg));
           du[j] = dA * g[j] * sg;
         }

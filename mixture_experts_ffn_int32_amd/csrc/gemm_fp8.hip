@@ -538,7 +538,7 @@ struct ActGradF8 : F8BwdBase<C> {
     const uint8_t* w2q;  // [E][I][H] E4M3 (rows i)
     const float* dsw;    // [E][I]
     const float* tw;
-    const uint16_t *h, *a;
+    const uint16_t* h;
     int64_t T, H, I;
     uint16_t* dh;
     float* dwpart;
@@ -578,7 +578,7 @@ struct ActGradF8 : F8BwdBase<C> {
       csc[t] = (n0 + t < ar->I) ? ar->dsw[(int64_t)e * ar->I + n0 + t] : 0.f;
     __syncthreads();
     this->scale(acc, wm, wn, lane, rsc, csc);
-    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->a, ar->dh, ar->dwpart,
+    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->dh, ar->dwpart,
                             ar->dw_cols);
   }
 };
@@ -713,10 +713,10 @@ hipError_t launch_bwd8(const RowGroups& g, int64_t n_cols, Fill fill, hipStream_
 }  // namespace
 
 hipError_t launch_act_grad_fp8(const RowGroups& g, const uint8_t* dyq, const float* dsy, const uint8_t* w2q,
-                               const float* dsw2, const float* topk_w, const uint16_t* h, const uint16_t* a,
-                               int64_t H, int64_t I, uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream) {
+                               const float* dsw2, const float* topk_w, const uint16_t* h, int64_t H, int64_t I,
+                               uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream) {
   return launch_bwd8<ActGradF8>(g, I, [&](auto& A, int nnt) {
-    A.g = g; A.dyq = dyq; A.dsy = dsy; A.w2q = w2q; A.dsw = dsw2; A.tw = topk_w; A.h = h; A.a = a;
+    A.g = g; A.dyq = dyq; A.dsy = dsy; A.w2q = w2q; A.dsw = dsw2; A.tw = topk_w; A.h = h;
     A.T = g.T; A.H = H; A.I = I; A.dh = dh; A.dwpart = dwpart; A.dw_cols = dw_cols; A.n_ntiles = nnt;
   }, stream);
 }

@@ -112,7 +112,7 @@ struct ActGradJob {
   const uint16_t* dy;
   const uint16_t* w2;
   const float* tw;
-  const uint16_t *h, *a;
+  const uint16_t* h;  // [S][2I]: g | u (a = bf16(silu(g) u) is recomputed from them)
   int64_t H, I;
   uint16_t* dh;
   float* dwpart;  // may be NULL (not stored)
@@ -208,8 +208,8 @@ hipError_t launch_gmm1_fp8(const RowGroups& g, const uint8_t* xq, const float* d
 //               dhq [S][2I], w1q [E][H][2I] (rows h), dsw1 [E][H]
 // Both on the tiling of ``g`` (256 + 64-row tiles, or 64x64 when narrow).
 hipError_t launch_act_grad_fp8(const RowGroups& g, const uint8_t* dyq, const float* dsy, const uint8_t* w2q,
-                               const float* dsw2, const float* topk_w, const uint16_t* h, const uint16_t* a,
-                               int64_t H, int64_t I, uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream);
+                               const float* dsw2, const float* topk_w, const uint16_t* h, int64_t H, int64_t I,
+                               uint16_t* dh, float* dwpart, int dw_cols, hipStream_t stream);
 hipError_t launch_input_grad_fp8(const RowGroups& g, const uint8_t* dhq, const float* dsh, const uint8_t* w1q,
                                  const float* dsw1, int64_t H, int64_t I, uint16_t* dxp, hipStream_t stream);
 
