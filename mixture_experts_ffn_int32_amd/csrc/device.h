@@ -35,7 +35,10 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// The logistic function on the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32: about one ulp each), not an IEEE division: a few ulps of float32,
+// far below the bf16 rounding that follows every use.
+__device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // A 16-byte store of a product's output with the streaming (non-temporal) hint:
 // the outputs are far larger than the L2 caches and read back, if at all, by a
