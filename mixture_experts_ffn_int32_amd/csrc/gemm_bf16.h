@@ -208,10 +208,9 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
     for (int i = 0; i < C::CB; ++i) r[i] = bload(rb_, boff[i], kt * C::BK * 2);
   }
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint16_t* smem) {
-    constexpr int LDF = C::TN + 4;
-    static_assert((C::BM * LDF + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
+    static_assert((sgrad_lds_floats<C>() + C::BM) * 4 <= 2 * C::STAGE * 2, "staging must fit in the LDS buffers");
     float* gst = reinterpret_cast<float*>(smem);
-    float* wrow = gst + C::BM * LDF;
+    float* wrow = gst + sgrad_lds_floats<C>();
     for (int t = threadIdx.x; t < C::BM; t += C::NTHR)
       wrow[t] = this->row_weight(ar->tw, ar->g, t);
     swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->dh, ar->dwpart,

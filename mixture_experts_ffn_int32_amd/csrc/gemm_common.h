@@ -39,46 +39,56 @@ __device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t sof
 }
 
 // ------------------------------------------------------------- act_grad epilogue
-// SwiGLUGrad of one tile of G (fp32 accumulators): one wave column (TN columns)
-// at a time G is staged in LDS (gst, BM x (TN + 4) floats), then each thread takes
-// 8 consecutive columns of one row, reads g and u as 16-byte chunks, writes
-// dH = [dg | du] as 16-byte chunks and adds its share of sum_i G a.  a =
-// bf16(silu(g) u) is recomputed from g and u with the forward epilogue's float
-// operations, so it is the forward's a bit for bit, without a third load.  The row sums
-// are reduced in a fixed order (8-lane butterfly, then wave columns in order):
+// SwiGLUGrad of one tile of G (fp32 accumulators), wave by wave: each wave stages
+// one 32-row block of its own G at a time in a private LDS block (32 x (TN + 4)
+// floats), then its lanes take 8 consecutive columns of one row each, read g and
+// u as 16-byte chunks, write dH = [dg | du] as 16-byte chunks and add their share
+// of sum_i G a.  No workgroup barrier separates the blocks, so one wave's loads
+// wait while the others compute.  a = bf16(silu(g) u) is recomputed from g and u
+// with the forward epilogue's float operations, so it is the forward's a bit for
+// bit, without a third load.  The row sums are reduced in a fixed order (8-lane
+// butterfly inside a wave column, then the wave columns in order, through LDS):
 // one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
 // rows' topk weights (0 past the tile's rows), written by the caller before the
 // call (the first barrier here publishes it).  Shared by the bf16 and FP8 products.
+//
+// LDS: the waves' staging blocks, then the row sums [BM][WN]; the caller's own
+// arrays (wrow, ...) go after sgrad_lds_floats<C>() floats.
+template <class C>
+constexpr int sgrad_lds_floats() { return (C::NTHR / 64) * 32 * (C::TN + 4) + C::BM * C::WN; }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <class C>
 __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane,
-                                                     float* gst, const float* wrow, int rows, int64_t row0,
+                                                     float* lds, const float* wrow, int rows, int64_t row0,
                                                      int64_t n0, int64_t I, const uint16_t* hbuf,
                                                      uint16_t* dhbuf, float* dwpart, int dw_cols) {
-  constexpr int LDF = C::TN + 4;                      // float pitch of the staged G
-  constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave column
-  constexpr int PER = C::BM * CPR / C::NTHR;          // chunks per thread per wave column
-  static_assert(C::BM * CPR % C::NTHR == 0 && C::NTHR % CPR == 0, "chunk mapping");
-  const int tid = threadIdx.x;
-  float part[PER];
+  constexpr int LDF = C::TN + 4;                      // float pitch of a staged block
+  constexpr int CPR = C::TN / 8;                      // 8-column chunks per row of a wave tile
+  constexpr int KP = 32 * CPR / 64;                   // chunks per lane per 32-row block
+  static_assert(32 * CPR % 64 == 0 && 64 % CPR == 0 && C::TM % 32 == 0, "chunk mapping");
+  float* gst = lds + (threadIdx.x >> 6) * 32 * LDF;   // this wave's staging block
+  float* rsum = lds + (C::NTHR / 64) * 32 * LDF;      // [BM][WN]
+  __syncthreads();  // wrow is published, and the main loop is done with the LDS
 #pragma unroll
-  for (int k = 0; k < PER; ++k) part[k] = 0.f;
-  for (int q = 0; q < C::WN; ++q) {
-    if (wn == q) {
+  for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
+      for (int r = 0; r < 16; ++r)
+        gst[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDF + nb * 32 + (lane & 31)] = acc[mb][nb][r];
+    wave_lds_sync();
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            gst[(wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDF + nb * 32 + (lane & 31)] =
-                acc[mb][nb][r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int c = tid + k * C::NTHR;
-      const int row = c / CPR, c8 = c % CPR;
-      const int64_t i = n0 + q * C::TN + c8 * 8;
+    for (int k = 0; k < KP; ++k) {
+      const int c = lane + 64 * k;
+      const int rr = c / CPR, c8 = c % CPR;
+      const int row = wm * C::TM + mb * 32 + rr;
+      const int64_t i = n0 + wn * C::TN + c8 * 8;
       float s = 0.f;
       if (row < rows && i < I) {
         const int64_t p = row0 + row;
@@ -86,7 +96,7 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
         unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + i), g);
         unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + I + i), u);
         const float w = wrow[row];
-        const float* G = gst + row * LDF + c8 * 8;
+        const float* G = gst + rr * LDF + c8 * 8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float sg = sigmoidf_(g[j]);
@@ -99,18 +109,21 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
         store16_stream(dhbuf + p * 2 * I + i, pack8(dg));
         store16_stream(dhbuf + p * 2 * I + I + i, pack8(du));
       }
-      // the CPR threads of a row are consecutive lanes: fixed-order butterfly
+      // the CPR lanes of a row are consecutive: fixed-order butterfly
 #pragma unroll
       for (int d = CPR / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d);
-      part[k] += s;
+      if (c8 == 0) rsum[row * C::WN + wn] = s;
     }
-    __syncthreads();
+    wave_lds_sync();  // every lane has read the block before the next one is staged
   }
+  __syncthreads();
+  if (dwpart) {
+    for (int t = threadIdx.x; t < rows && t < C::BM; t += C::NTHR) {
+      float part = 0.f;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int c = tid + k * C::NTHR;
-    const int row = c / CPR;
-    if (dwpart && c % CPR == 0 && row < rows) dwpart[(row0 + row) * dw_cols + n0 / C::BN] = part[k];
+      for (int q = 0; q < C::WN; ++q) part += rsum[t * C::WN + q];
+      dwpart[(row0 + t) * dw_cols + n0 / C::BN] = part;
+    }
   }
 }
 

@@ -563,10 +563,9 @@ struct ActGradF8 : F8BwdBase<C> {
     return true;
   }
   __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane, uint8_t* smemb) {
-    constexpr int LDF = C::TN + 4;
-    static_assert((C::BM * LDF + 2 * C::BM + C::BN) * 4 <= 2 * C::STAGE, "staging must fit");
+    static_assert((sgrad_lds_floats<C>() + 2 * C::BM + C::BN) * 4 <= 2 * C::STAGE, "staging must fit");
     float* gst = reinterpret_cast<float*>(smemb);
-    float* wrow = gst + C::BM * LDF;
+    float* wrow = gst + sgrad_lds_floats<C>();
     float* rsc = wrow + C::BM;
     float* csc = rsc + C::BM;
     for (int t = threadIdx.x; t < C::BM; t += C::NTHR) {
