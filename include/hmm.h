@@ -248,7 +248,7 @@ hmm_status hmm_forward(const hmm_problem* p, const void* x, const int32_t* topk_
  *   and is never freed.  A problem whose hmm_forward_sizes workspace exceeds it
  *   returns HMM_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Routed problems
  *   need about S*H*2 bytes, plus small routing tables.  For example, T=256 and K=8
- *   at H=7168 fit, and the skewed size T=4000, H=2048, K=8 does not (131 MB).
+ *   at H=7168 fit, and T=4000, H=2048, K=8 does not (131 MB).
  * - The call allocates no device or pinned host memory and creates no HIP
  *   object (no hipMalloc, hipFree, hipHostMalloc or event creation); stage
  *   timing is paused during it.  So it takes

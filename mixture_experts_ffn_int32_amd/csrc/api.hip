@@ -1062,8 +1062,9 @@ hmm_status backward_impl(const Dims& d, const void* dy, const void* x, const int
   // only the forward's aw and dY; W1Grad waits for act_grad's dH.  The caller's
   // stream waits for both.  With act_grad at 4 or more waves of 256-row tiles
   // on the chip, two products sharing the XCDs' L2 caches lose more than the
-  // tails gain (measured: hotspot 18.25 -> 18.56 ms per step on two streams,
-  // skewed 2.37 -> 2.23 ms), so those stay on one stream.
+  // tails gain (measured per step on two streams: 18.25 -> 18.56 ms at T=8192,
+  // H=7168, I=2048, E=32, K=8 with one hot expert; 2.37 -> 2.23 ms at T=4000,
+  // H=2048, I=768, E=128, K=8 with Zipf routing), so those stay on one stream.
   DevState* side = nullptr;
   if (ne && !(d.flags & HMM_FLAG_SERIAL_BACKWARD)) {
     DevState* c = dev_state();
