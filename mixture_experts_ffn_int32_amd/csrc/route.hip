@@ -110,10 +110,16 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
   if (st.idx && e == 0) shared_header(st);
   int c = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int v = blockhist[(int64_t)b * E + e];
-      blockbase[(int64_t)b * E + e] = c;
-      c += v;
+    // the per-block counts of expert e, 16 loads in flight at a time
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nblk) ? blockhist[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nblk) blockbase[(int64_t)(b0 + j) * E + e] = c;
+        c += v[j];
+      }
     }
   }
   const int rem = big_on ? c % TILE_BIG : c;
@@ -123,8 +129,8 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
   scan_b[e] = (e < E) ? nbig : 0;
   scan_s[e] = (e < E) ? nsmall : 0;
   __syncthreads();
-  // inclusive Hillis-Steele scans over the experts (integers: order-free)
-  for (int d = 1; d < RT_SCAN_THREADS; d <<= 1) {
+  // inclusive Hillis-Steele scans over the E experts (integers: order-free)
+  for (int d = 1; d < E; d <<= 1) {
     const int vc = (e >= d) ? scan_c[e - d] : 0;
     const int vb = (e >= d) ? scan_b[e - d] : 0;
     const int vs = (e >= d) ? scan_s[e - d] : 0;
@@ -151,7 +157,7 @@ __global__ void __launch_bounds__(RT_SCAN_THREADS) route_scan(const int32_t* __r
       small[2 * (s0 + i) + 1] = srow + i * TILE_SMALL;
     }
   }
-  if (e == RT_SCAN_THREADS - 1) {
+  if (e == E - 1) {  // holds the totals over all experts
     offsets[E] = scan_c[e];
     tiles[0] = scan_b[e];
     tiles[1] = scan_s[e];
