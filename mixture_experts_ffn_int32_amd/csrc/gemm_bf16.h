@@ -34,9 +34,9 @@ struct Gmm1 : RowTile<Cc, SMALL> {
   // the B tile holds BN/2 gate columns then the BN/2 matching up columns; the
   // epilogue pairs them through LDS
   __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     i0 = nt * (C::BN / 2);
     ra_ = make_rsrc(A.x, A.T * A.H * 2);
     this->template a_rows<true>(A.g, A.H, aoff);
@@ -129,9 +129,9 @@ struct Gmm2 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.a, A.S * A.I * 2);
     this->template a_rows<false>(A.g, A.I, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
@@ -189,9 +189,9 @@ struct ActGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.dy, A.T * A.H * 2);
     this->template a_rows<true>(A.g, A.H, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
@@ -237,9 +237,9 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.dh, A.S * 2 * A.I * 2);
     this->template a_rows<false>(A.g, 2 * A.I, aoff);
     rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);

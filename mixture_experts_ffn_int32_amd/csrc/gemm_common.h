@@ -25,6 +25,22 @@ __device__ __forceinline__ void raster(int idx, int R, int C, int& r, int& c) {
   c = w / gsz;
 }
 
+// Workgroup ``bid`` of a launch part (whose first workgroup sits on XCD 0 and
+// whose size is a multiple of 8 and at least cnt * C) -> tile (row tile r, column
+// tile c) of the cnt x C tiles a routing table really holds.  Each XCD takes an
+// equal contiguous share of them in raster order, however much of the table's
+// capacity (which sizes the launch) they fill; a share of the capacity instead
+// would leave the XCDs past the real tiles idle.  False past the XCD's share.
+__device__ __forceinline__ bool real_tile(int bid, int cnt, int C, int& r, int& c) {
+  const int n = cnt * C;
+  const int share = (n + 7) >> 3;
+  const int i = bid >> 3;
+  const int logical = (bid & 7) * share + i;
+  if (i >= share || logical >= n) return false;
+  raster(logical, cnt, C, r, c);
+  return true;
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // buffer resource over [base, base + bytes); bytes < 2^32
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -298,24 +298,40 @@ struct PlainCols {
 template <class Cc, bool SMALL>
 struct RowTile {
   typedef Cc C;
-  static constexpr bool RAW_INDEX = false;  // init takes the XCD-remapped logical index
+  // Tiles of 256 columns (the launches of large problems, many rounds of
+  // workgroups) spread the table's real tiles over the XCDs (real_tile: the count
+  // is loaded before the entry); the 64x64 tiles of small problems, one round or
+  // so, take the XCD-remapped index over the capacity and load the count and the
+  // entry together.
+  static constexpr bool DYN = C::BN > 64;
+  static constexpr bool RAW_INDEX = DYN;  // init takes the workgroup index itself
   static constexpr bool SCHED_HINT = true;  // see gemm_tile
   int e, row0, rows, n0, nk, nt;
   struct Raw {};  // K-major rows are fixed for the whole tile: no per-step indices
   __device__ __forceinline__ void fetch(int, Raw&) {}
   __device__ __forceinline__ void index(int, Raw&) {}
-  __device__ __forceinline__ bool init_rows(const RowGroups& g, int logical, int n_ntiles) {
+  __device__ __forceinline__ bool init_rows(const RowGroups& g, int idx, int n_ntiles) {
     const int R = SMALL ? (int)g.max_small : (int)g.max_big;
-    if (logical >= R * n_ntiles) return false;
-    int j;
-    raster(logical, R, n_ntiles, j, nt);
-    // the count and the entry are loaded together (entries j < R are in bounds;
-    // one past the count holds stale data and is not used)
     const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-    const int cnt = get(g.tiles + (SMALL ? 1 : 0), g.coh);
-    const int32_t w = get(tab + 2 * j, g.coh);
-    row0 = get(tab + 2 * j + 1, g.coh);
-    if (j >= cnt) return false;
+    int j;
+    int32_t w;
+    if constexpr (DYN) {
+      // the count is at most the capacity R; clamped anyway, so entries j < cnt
+      // are in bounds whatever the table holds
+      const int cnt = min(get(g.tiles + (SMALL ? 1 : 0), g.coh), R);
+      if (!real_tile(idx, cnt, n_ntiles, j, nt)) return false;
+      w = get(tab + 2 * j, g.coh);
+      row0 = get(tab + 2 * j + 1, g.coh);
+    } else {
+      if (idx >= R * n_ntiles) return false;
+      raster(idx, R, n_ntiles, j, nt);
+      // the count and the entry are loaded together (entries j < R are in bounds;
+      // one past the count holds stale data and is not used)
+      const int cnt = get(g.tiles + (SMALL ? 1 : 0), g.coh);
+      w = get(tab + 2 * j, g.coh);
+      row0 = get(tab + 2 * j + 1, g.coh);
+      if (j >= cnt) return false;
+    }
     e = tile_expert(w);
     rows = min(C::BM, tile_rows(w));
     n0 = nt * C::BN;

@@ -86,9 +86,9 @@ struct Gmm1F32 : RowTile<Cc, SMALL> {
   __device__ static __forceinline__ int ncol0(int wn, int nb) { return wn * C::TN + nb * 32; }
   // B tile: 32-column blocks alternate between gate and up columns of the same
   // intermediate columns: block b holds i0 + (b/2)*32 + [0, 32), gate if b is even
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     i0 = nt * (C::BN / 2);
     ra_ = make_rsrc(A.x, A.T * A.H * 2);
     this->template a_rows<true>(A.g, A.H, aoff);
@@ -167,9 +167,9 @@ struct Gmm2F32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.a2, A.S * 2 * A.I * 2);
     this->template a_rows<false>(A.g, 2 * A.I, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
@@ -231,9 +231,9 @@ struct ActGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.dy2, A.T * 2 * A.H * 2);
     this->template a_rows<true>(A.g, 2 * A.H, aoff);
     rb_ = make_rsrc(A.w2 + (int64_t)e * A.I * A.H, A.I * A.H * 2);
@@ -351,9 +351,9 @@ struct InputGradF32 : RowTile<Cc, SMALL>, PlainCols<Cc> {
   const Args* ar;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!this->init_rows(A.g, logical, A.n_ntiles)) return false;
+    if (!this->init_rows(A.g, idx, A.n_ntiles)) return false;
     ra_ = make_rsrc(A.dh2, A.S * 4 * A.I * 2);
     this->template a_rows<false>(A.g, 4 * A.I, aoff);
     rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);

@@ -66,6 +66,36 @@ __device__ __forceinline__ int acc_row8(int wm, int mb, int r, int lane) {
   return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// Row tile j of one of the routing's tables: expert, first row, rows, N tile.
+// Tiles of 256 columns (large problems) take the workgroup index ``idx`` and
+// spread the table's real tiles over the XCDs (real_tile; the count is loaded
+// before the entry); the 64x64 tiles of small problems take the XCD-remapped index
+// over the table's capacity and load the count and the entry together.
+template <class C, bool SMALL>
+__device__ __forceinline__ bool f8_row_tile(const RowGroups& g, int idx, int n_ntiles, int& e, int& row0,
+                                            int& rows, int& nt) {
+  const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+  const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
+  int j;
+  int32_t w;
+  if constexpr (C::BN > 64) {
+    const int cnt = min((int)g.tiles[SMALL ? 1 : 0], R);  // clamped: entries j < cnt are in bounds
+    if (!real_tile(idx, cnt, n_ntiles, j, nt)) return false;
+    w = tab[2 * j];
+    row0 = tab[2 * j + 1];
+  } else {
+    if (idx >= R * n_ntiles) return false;
+    raster(idx, R, n_ntiles, j, nt);
+    const int cnt = g.tiles[SMALL ? 1 : 0];
+    w = tab[2 * j];
+    row0 = tab[2 * j + 1];
+    if (j >= cnt) return false;
+  }
+  e = tile_expert(w);
+  rows = min(C::BM, tile_rows(w));
+  return true;
+}
+
 // Q: 0 per-token scales (applied in the epilogue), 1 MX block exponents (fed to
 // the instruction), 2 per-group float descales (applied to each K step's sums)
 template <class C, bool SMALL, int Q = 0>
@@ -100,20 +130,11 @@ struct Gmm1F8 {
   rsrc_t ra_, rb_, rsx_, rsw_;
   uint32_t aoff[C::CA], boff[C::CB], soff[SCR];
 
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  static constexpr bool RAW_INDEX = C::BN > 64;  // see f8_row_tile
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
     const RowGroups& g = A.g;
-    const int R = SMALL ? (int)g.max_small : (int)g.max_big;
-    if (logical >= R * A.n_ntiles) return false;
-    int j;
-    raster(logical, R, A.n_ntiles, j, nt);
-    const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-    const int cnt = g.tiles[SMALL ? 1 : 0];
-    const int32_t w = tab[2 * j];
-    row0 = tab[2 * j + 1];
-    if (j >= cnt) return false;
-    e = tile_expert(w);
-    rows = min(C::BM, tile_rows(w));
+    if (!f8_row_tile<C, SMALL>(g, idx, A.n_ntiles, e, row0, rows, nt)) return false;
     i0 = nt * (C::BN / 2);
     const int tid = threadIdx.x;
     ra_ = make_rsrc(A.xq, A.T * A.H);
@@ -302,7 +323,7 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
   constexpr int ST = C::STAGE + P::SC_BYTES;  // one LDS stage: operand tiles, then the MX exponents
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * ST];
   P pol;
-  if (!pol.init(args, xcd_remap(blockIdx.x, gridDim.x))) return;
+  if (!pol.init(args, P::RAW_INDEX ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x))) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -467,22 +488,6 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
 // K-major too (a weight row of [I][H] or [H][2I] is contiguous along K).
 
 // Row tile j of one of the routing's tables: expert, first row, rows, N tile.
-template <class C, bool SMALL>
-__device__ __forceinline__ bool f8_row_tile(const RowGroups& g, int logical, int n_ntiles, int& e, int& row0,
-                                            int& rows, int& nt) {
-  const int R = SMALL ? (int)g.max_small : (int)g.max_big;
-  if (logical >= R * n_ntiles) return false;
-  int j;
-  raster(logical, R, n_ntiles, j, nt);
-  const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
-  const int cnt = g.tiles[SMALL ? 1 : 0];
-  const int32_t w = tab[2 * j];
-  row0 = tab[2 * j + 1];
-  if (j >= cnt) return false;
-  e = tile_expert(w);
-  rows = min(C::BM, tile_rows(w));
-  return true;
-}
 
 // shared by both backward products: no per-step scales, K-major weights
 template <class C>
@@ -491,6 +496,7 @@ struct F8BwdBase {
   static constexpr int NTHR_ = C::NTHR;
   static constexpr bool MX_ = false, GROUP_ = false, STAGED = false, B_KMAJ_ = true;
   static constexpr int SCR = 1, SC_BYTES = 0;
+  static constexpr bool RAW_INDEX = C::BN > 64;  // see f8_row_tile
   int e, row0, rows, nt, n0, nk;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
@@ -546,9 +552,9 @@ struct ActGradF8 : F8BwdBase<C> {
     int n_ntiles;
   };
   const Args* ar;
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!f8_row_tile<C, SMALL>(A.g, logical, A.n_ntiles, e, row0, rows, nt)) return false;
+    if (!f8_row_tile<C, SMALL>(A.g, idx, A.n_ntiles, e, row0, rows, nt)) return false;
     n0 = nt * C::BN;
     this->ra_ = make_rsrc(A.dyq, A.T * A.H);
 #pragma unroll
@@ -598,9 +604,9 @@ struct InputGradF8 : F8BwdBase<C> {
     int n_ntiles;
   };
   const Args* ar;
-  __device__ __forceinline__ bool init(const Args& A, int logical) {
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
-    if (!f8_row_tile<C, SMALL>(A.g, logical, A.n_ntiles, e, row0, rows, nt)) return false;
+    if (!f8_row_tile<C, SMALL>(A.g, idx, A.n_ntiles, e, row0, rows, nt)) return false;
     n0 = nt * C::BN;
     const int64_t K = 2 * A.I;
     this->ra_ = make_rsrc(A.dhq, A.S * K);
