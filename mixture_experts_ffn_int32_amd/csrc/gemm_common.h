@@ -59,10 +59,10 @@ __device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t sof
 // one 32-row block of its own G at a time in a private LDS block (32 x (TN + 4)
 // floats), then its lanes take 8 consecutive columns of one row each, read g and
 // u as 16-byte chunks, write dH = [dg | du] as 16-byte chunks and add their share
-// of sum_i G a.  No workgroup barrier separates the blocks, so one wave's loads
-// wait while the others compute.  a = bf16(silu(g) u) is recomputed from g and u
-// with the forward epilogue's float operations, so it is the forward's a bit for
-// bit, without a third load.  The row sums are reduced in a fixed order (8-lane
+// of sum_i G a.  No workgroup barrier separates the blocks, and each wave loads a
+// block's g and u while it computes the block before (PF).  a = bf16(silu(g) u)
+// is recomputed from g and u with the forward epilogue's float operations, so it
+// is the forward's a bit for bit, without a third load.  The row sums are reduced in a fixed order (8-lane
 // butterfly inside a wave column, then the wave columns in order, through LDS):
 // one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
 // rows' topk weights (0 past the tile's rows), written by the caller before the
@@ -79,7 +79,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class C>
+// PF: load each block's g and u one block ahead (two blocks of chunks in
+// registers); without, right before the block (for tiles with no registers to spare).
+template <class C, bool PF = true>
 __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane,
                                                      float* lds, const float* wrow, int rows, int64_t row0,
                                                      int64_t n0, int64_t I, const uint16_t* hbuf,
@@ -90,9 +92,30 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
   static_assert(32 * CPR % 64 == 0 && 64 % CPR == 0 && C::TM % 32 == 0, "chunk mapping");
   float* gst = lds + (threadIdx.x >> 6) * 32 * LDF;   // this wave's staging block
   float* rsum = lds + (C::NTHR / 64) * 32 * LDF;      // [BM][WN]
+  // g and u of a block, as 16-byte chunks; the loads are unconditional, at a
+  // clamped row and column for lanes past the tile's rows or past I (results
+  // unused), so no wait has to assume a skipped load and drain the others.
+  u32x4 hb[2][2 * KP];
+  auto load_block = [&](int mb, u32x4 (&buf)[2 * KP]) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int c = lane + 64 * k;
+      const int row = min(wm * C::TM + mb * 32 + c / CPR, rows - 1);
+      const int64_t i = min(n0 + wn * C::TN + (c % CPR) * 8, I - 8);
+      const uint16_t* q = hbuf + (row0 + row) * 2 * I + i;
+      buf[2 * k] = *reinterpret_cast<const u32x4*>(q);
+      buf[2 * k + 1] = *reinterpret_cast<const u32x4*>(q + I);
+    }
+  };
+  if constexpr (PF) load_block(0, hb[0]);
   __syncthreads();  // wrow is published, and the main loop is done with the LDS
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
+    if constexpr (PF) {
+      if (mb + 1 < C::MB) load_block(mb + 1, hb[(mb + 1) & 1]);
+    } else {
+      load_block(mb, hb[mb & 1]);
+    }
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -109,8 +132,8 @@ __device__ __forceinline__ void swiglu_grad_epilogue(const f32x16 (&acc)[C::MB][
       if (row < rows && i < I) {
         const int64_t p = row0 + row;
         float g[8], u[8], av[8], dg[8], du[8];
-        unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + i), g);
-        unpack8(*reinterpret_cast<const u32x4*>(hbuf + p * 2 * I + I + i), u);
+        unpack8(hb[mb & 1][2 * k], g);
+        unpack8(hb[mb & 1][2 * k + 1], u);
         const float w = wrow[row];
         const float* G = gst + rr * LDF + c8 * 8;
 #pragma unroll

@@ -583,8 +583,9 @@ struct ActGradF8 : F8BwdBase<C> {
       csc[t] = (n0 + t < ar->I) ? ar->dsw[(int64_t)e * ar->I + n0 + t] : 0.f;
     __syncthreads();
     this->scale(acc, wm, wn, lane, rsc, csc);
-    swiglu_grad_epilogue<C>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->dh, ar->dwpart,
-                            ar->dw_cols);
+    // the 256x256 tile (one register set) has no registers for the prefetch
+    swiglu_grad_epilogue<C, C::SETS == 2>(acc, wm, wn, lane, gst, wrow, rows, row0, n0, ar->I, ar->h, ar->dh,
+                                          ar->dwpart, ar->dw_cols);
   }
 };
 
