@@ -41,6 +41,12 @@ __device__ __forceinline__ bool real_tile(int bid, int cnt, int C, int& r, int& 
   return true;
 }
 
+// Row-grouped launches of more than this many tiles (the table's capacity times
+// the column tiles) spread the real tiles with real_tile even on 64x64 tiles;
+// smaller ones run in about one round of workgroups, where the extra dependent
+// load of the count would cost more than the balance gains.
+constexpr int SPREAD_MIN_TILES = 1024;
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // buffer resource over [base, base + bytes); bytes < 2^32
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {

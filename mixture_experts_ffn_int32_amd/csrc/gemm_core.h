@@ -298,13 +298,14 @@ struct PlainCols {
 template <class Cc, bool SMALL>
 struct RowTile {
   typedef Cc C;
-  // Tiles of 256 columns (the launches of large problems, many rounds of
-  // workgroups) spread the table's real tiles over the XCDs (real_tile: the count
-  // is loaded before the entry); the 64x64 tiles of small problems, one round or
-  // so, take the XCD-remapped index over the capacity and load the count and the
-  // entry together.
-  static constexpr bool DYN = C::BN > 64;
-  static constexpr bool RAW_INDEX = DYN;  // init takes the workgroup index itself
+  // init takes the workgroup index of its launch part.  Tiles of 256 columns
+  // (large problems, many rounds of workgroups) and launches of more than
+  // SPREAD_MIN_TILES tiles spread the table's real tiles over the XCDs
+  // (real_tile; the count is loaded before the entry).  The others take the
+  // XCD-remapped index over the table's capacity (the launch part's size) and load
+  // the count and the entry together; inside the fused forward (coh) the index is
+  // that kernel's own tile index, used as is.
+  static constexpr bool RAW_INDEX = true;
   static constexpr bool SCHED_HINT = true;  // see gemm_tile
   int e, row0, rows, n0, nk, nt;
   struct Raw {};  // K-major rows are fixed for the whole tile: no per-step indices
@@ -312,10 +313,11 @@ struct RowTile {
   __device__ __forceinline__ void index(int, Raw&) {}
   __device__ __forceinline__ bool init_rows(const RowGroups& g, int idx, int n_ntiles) {
     const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+    const int cap = R * n_ntiles;
     const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
     int j;
     int32_t w;
-    if constexpr (DYN) {
+    if (C::BN > 64 || (!g.coh && cap > SPREAD_MIN_TILES)) {
       // the count is at most the capacity R; clamped anyway, so entries j < cnt
       // are in bounds whatever the table holds
       const int cnt = min(get(g.tiles + (SMALL ? 1 : 0), g.coh), R);
@@ -323,8 +325,9 @@ struct RowTile {
       w = get(tab + 2 * j, g.coh);
       row0 = get(tab + 2 * j + 1, g.coh);
     } else {
-      if (idx >= R * n_ntiles) return false;
-      raster(idx, R, n_ntiles, j, nt);
+      const int logical = g.coh ? idx : xcd_remap(idx, (cap + 7) & ~7);
+      if (logical >= cap) return false;
+      raster(logical, R, n_ntiles, j, nt);
       // the count and the entry are loaded together (entries j < R are in bounds;
       // one past the count holds stale data and is not used)
       const int cnt = get(g.tiles + (SMALL ? 1 : 0), g.coh);

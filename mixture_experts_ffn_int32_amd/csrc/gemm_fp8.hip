@@ -66,26 +66,29 @@ __device__ __forceinline__ int acc_row8(int wm, int mb, int r, int lane) {
   return wm * C::TM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Row tile j of one of the routing's tables: expert, first row, rows, N tile.
-// Tiles of 256 columns (large problems) take the workgroup index ``idx`` and
-// spread the table's real tiles over the XCDs (real_tile; the count is loaded
-// before the entry); the 64x64 tiles of small problems take the XCD-remapped index
-// over the table's capacity and load the count and the entry together.
+// Row tile j of one of the routing's tables: expert, first row, rows, N tile, for
+// workgroup ``idx`` of the launch.  Tiles of 256 columns (large problems) and
+// launches of more than SPREAD_MIN_TILES tiles spread the table's real tiles over
+// the XCDs (real_tile; the count is loaded before the entry); the others take the
+// XCD-remapped index over the table's capacity (the grid) and load the count and
+// the entry together.
 template <class C, bool SMALL>
 __device__ __forceinline__ bool f8_row_tile(const RowGroups& g, int idx, int n_ntiles, int& e, int& row0,
                                             int& rows, int& nt) {
   const int R = SMALL ? (int)g.max_small : (int)g.max_big;
+  const int cap = R * n_ntiles;
   const int32_t* tab = g.tiles + 4 + (SMALL ? 2 * g.max_big : 0);
   int j;
   int32_t w;
-  if constexpr (C::BN > 64) {
+  if (C::BN > 64 || cap > SPREAD_MIN_TILES) {
     const int cnt = min((int)g.tiles[SMALL ? 1 : 0], R);  // clamped: entries j < cnt are in bounds
     if (!real_tile(idx, cnt, n_ntiles, j, nt)) return false;
     w = tab[2 * j];
     row0 = tab[2 * j + 1];
   } else {
-    if (idx >= R * n_ntiles) return false;
-    raster(idx, R, n_ntiles, j, nt);
+    const int logical = xcd_remap(idx, (cap + 7) & ~7);
+    if (logical >= cap) return false;
+    raster(logical, R, n_ntiles, j, nt);
     const int cnt = g.tiles[SMALL ? 1 : 0];
     w = tab[2 * j];
     row0 = tab[2 * j + 1];
@@ -130,7 +133,7 @@ struct Gmm1F8 {
   rsrc_t ra_, rb_, rsx_, rsw_;
   uint32_t aoff[C::CA], boff[C::CB], soff[SCR];
 
-  static constexpr bool RAW_INDEX = C::BN > 64;  // see f8_row_tile
+  static constexpr bool RAW_INDEX = true;  // see f8_row_tile
   __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
     const RowGroups& g = A.g;
@@ -496,7 +499,7 @@ struct F8BwdBase {
   static constexpr int NTHR_ = C::NTHR;
   static constexpr bool MX_ = false, GROUP_ = false, STAGED = false, B_KMAJ_ = true;
   static constexpr int SCR = 1, SC_BYTES = 0;
-  static constexpr bool RAW_INDEX = C::BN > 64;  // see f8_row_tile
+  static constexpr bool RAW_INDEX = true;  // see f8_row_tile
   int e, row0, rows, nt, n0, nk;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];

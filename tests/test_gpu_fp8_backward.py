@@ -23,6 +23,8 @@ CASES = [
     ("ragged", dict(T=300, H=256, I=192, E=6, K=3, routing="uniform")),
     ("zipf", dict(T=411, H=384, I=128, E=16, K=4, routing="zipf", zipf_s=1.2, n_empty=5)),
     ("outliers", dict(T=520, H=256, I=320, E=3, K=2, routing="hot", outlier_frac=0.02, outlier_scale=30.0)),
+    # many experts: on 64x64 tiles the launches spread the real tiles over the XCDs
+    ("e1024", dict(T=512, H=128, I=64, E=1024, K=8, routing="zipf", zipf_s=0.6, n_empty=200)),
 ]
 PLAIN_SHARE = 0.01   # at most this share of an output's elements outside the plain bar
 

@@ -41,7 +41,9 @@ SMALL = [
     # expert sizes on the large tiling's boundaries: remainders of 1-64, 65-128
     # (small tiles, one or two table entries) and 129-255 rows (a partial big tile)
     # the most experts the routing takes, many of them empty or tied in size (the weight
-    # gradients' longest-first expert order ranks all 1024)
+    # gradients' longest-first expert order ranks all 1024; on 64x64 tiles the tables'
+    # capacity exceeds the size above which the launches spread the real tiles over
+    # the XCDs)
     ("e1024", dict(T=512, H=128, I=64, E=1024, K=8, routing="zipf", zipf_s=0.6, n_empty=200)),
     ("bounds", dict(T=2278, H=128, I=64, E=14, K=1, routing="counts",
                     counts=[0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 385, 228])),
