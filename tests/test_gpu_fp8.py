@@ -61,7 +61,9 @@ def test_row_quantiser_bit_exact(T, H):
     assert np.array_equal(ds.cpu().numpy(), rds)
 
 
-@pytest.mark.parametrize("E,H,N", [(1, 64, 128), (3, 320, 192), (2, 1024, 3072)])
+# the last case: many experts, H not a multiple of the 256-row chunks of the maxima,
+# N not a multiple of a wave's 128 columns
+@pytest.mark.parametrize("E,H,N", [(1, 64, 128), (3, 320, 192), (2, 1024, 3072), (6, 200, 3080)])
 def test_column_quantiser_bit_exact(E, H, N):
     from mixture_experts_ffn_int32_amd import quantize_cols_fp8
     bits = _bf16_matrix((E, H, N), seed=E * H + N)
