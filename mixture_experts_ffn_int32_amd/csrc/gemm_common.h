@@ -68,9 +68,9 @@ __device__ __forceinline__ u32x4 bload_coh(rsrc_t r, uint32_t voff, uint32_t sof
 // of sum_i G a.  No workgroup barrier separates the blocks, and each wave loads a
 // block's g and u while it computes the block before (PF).  a = bf16(silu(g) u)
 // is recomputed from g and u with the forward epilogue's float operations, so it
-// is the forward's a bit for bit, without a third load.  The row sums are reduced in a fixed order (8-lane
-// butterfly inside a wave column, then the wave columns in order, through LDS):
-// one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
+// is the forward's a bit for bit, without a third load.  The row sums are reduced
+// in a fixed order (8-lane butterfly inside a wave column, then the wave columns in
+// order, through LDS): one partial per (row, N tile) into dwpart (if not NULL).  wrow [BM] holds the
 // rows' topk weights (0 past the tile's rows), written by the caller before the
 // call (the first barrier here publishes it).  Shared by the bf16 and FP8 products.
 //
