@@ -266,7 +266,6 @@ struct InputGrad : RowTile<Cc, SMALL>, PlainCols<Cc> {
 template <class Cc, bool GATHER_A, bool GATHER_B>
 struct Dw : PlainCols<Cc> {
   typedef Cc C;
-  static constexpr bool RAW_INDEX = true;  // init maps the workgroup index to XCDs itself
   static constexpr bool SCHED_HINT = false;
   using PlainCols<Cc>::ncol0;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;

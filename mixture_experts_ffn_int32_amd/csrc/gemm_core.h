@@ -192,16 +192,17 @@ __device__ __forceinline__ bool gemm_tile(const typename P::Args& args, int idx,
   return true;
 }
 
-// ... for workgroup ``bid`` of ``nblocks`` of a launch
+// ... for workgroup ``bid`` of its launch part (every policy's init maps the
+// workgroup index onto its tiles and the XCDs itself)
 template <class P>
-__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, int nblocks, uint16_t* smem) {
-  (void)gemm_tile<P>(args, P::RAW_INDEX ? bid : xcd_remap(bid, nblocks), smem);
+__device__ __forceinline__ void gemm_body(const typename P::Args& args, int bid, uint16_t* smem) {
+  (void)gemm_tile<P>(args, bid, smem);
 }
 
 template <class P>
 __global__ void __launch_bounds__(P::C::NTHR, 1) gemm_kernel(const typename P::Args args) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * P::C::STAGE];
-  gemm_body<P>(args, blockIdx.x, gridDim.x, smem);
+  gemm_body<P>(args, blockIdx.x, smem);
 }
 
 // Two independent products in one launch (small problems, where each fills only
@@ -214,9 +215,9 @@ __global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_pair_kernel(const typenam
   constexpr int S1 = 2 * P1::C::STAGE, S2 = 2 * P2::C::STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S1 > S2 ? S1 : S2];
   if ((int)blockIdx.x < n1)
-    gemm_body<P1>(a1, blockIdx.x, n1, smem);
+    gemm_body<P1>(a1, blockIdx.x, smem);
   else
-    gemm_body<P2>(a2, blockIdx.x - n1, gridDim.x - n1, smem);
+    gemm_body<P2>(a2, blockIdx.x - n1, smem);
 }
 
 // Four independent products in one launch (small problems with a shared
@@ -234,13 +235,13 @@ __global__ void __launch_bounds__(P1::C::NTHR, 1) gemm_quad_kernel(const typenam
   __shared__ __attribute__((aligned(16))) uint16_t smem[S12 > S34 ? S12 : S34];
   const int b = blockIdx.x;
   if (b < s1)
-    gemm_body<P1>(a1, b, s1, smem);
+    gemm_body<P1>(a1, b, smem);
   else if (b < s2)
-    gemm_body<P2>(a2, b - s1, s2 - s1, smem);
+    gemm_body<P2>(a2, b - s1, smem);
   else if (b < s3)
-    gemm_body<P3>(a3, b - s2, s3 - s2, smem);
+    gemm_body<P3>(a3, b - s2, smem);
   else
-    gemm_body<P4>(a4, b - s3, gridDim.x - s3, smem);
+    gemm_body<P4>(a4, b - s3, smem);
 }
 
 // Plain epilogue: the tile's results, rounded to bf16, are staged in LDS as a
@@ -305,7 +306,6 @@ struct RowTile {
   // XCD-remapped index over the table's capacity (the launch part's size) and load
   // the count and the entry together; inside the fused forward (coh) the index is
   // that kernel's own tile index, used as is.
-  static constexpr bool RAW_INDEX = true;
   static constexpr bool SCHED_HINT = true;  // see gemm_tile
   int e, row0, rows, n0, nk, nt;
   struct Raw {};  // K-major rows are fixed for the whole tile: no per-step indices

@@ -384,7 +384,6 @@ template <class Cc, int MODE>
 struct DwF32 : PlainCols<Cc> {
   typedef Cc C;
   using PlainCols<Cc>::ncol0;
-  static constexpr bool RAW_INDEX = true;
   static constexpr bool SCHED_HINT = false;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
   static constexpr int PASSES = MODE == 1 ? 2 : 3;

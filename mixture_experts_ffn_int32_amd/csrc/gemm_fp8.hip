@@ -133,7 +133,6 @@ struct Gmm1F8 {
   rsrc_t ra_, rb_, rsx_, rsw_;
   uint32_t aoff[C::CA], boff[C::CB], soff[SCR];
 
-  static constexpr bool RAW_INDEX = true;  // see f8_row_tile
   __device__ __forceinline__ bool init(const Args& A, int idx) {
     ar = &A;
     const RowGroups& g = A.g;
@@ -326,7 +325,7 @@ __global__ void __launch_bounds__(P::NTHR_, 1) gemm_fp8_kernel(const typename P:
   constexpr int ST = C::STAGE + P::SC_BYTES;  // one LDS stage: operand tiles, then the MX exponents
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * ST];
   P pol;
-  if (!pol.init(args, P::RAW_INDEX ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x))) return;
+  if (!pol.init(args, (int)blockIdx.x)) return;  // init maps the workgroup onto its tile (f8_row_tile)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -499,7 +498,6 @@ struct F8BwdBase {
   static constexpr int NTHR_ = C::NTHR;
   static constexpr bool MX_ = false, GROUP_ = false, STAGED = false, B_KMAJ_ = true;
   static constexpr int SCR = 1, SC_BYTES = 0;
-  static constexpr bool RAW_INDEX = true;  // see f8_row_tile
   int e, row0, rows, nt, n0, nk;
   rsrc_t ra_, rb_;
   uint32_t aoff[C::CA], boff[C::CB];
