@@ -410,6 +410,29 @@ hmm_status run_route(const Dims& d, const int32_t* ids, int32_t* counts, int32_t
   return HMM_OK;
 }
 
+// The routing and the up-projection in one launch (small bf16 problems without
+// a shared expert; launch_route_gmm1_swiglu), with run_route's id check.
+hmm_status run_route_gmm1(hmm::RoutedGmm1Job j, bool validate_ids, hipStream_t stream) {
+  DevState* c = nullptr;
+  if (validate_ids) {
+    c = dev_state();
+    if (!c) return fail(HMM_ERR_HIP, "could not create the per-device id-check word or event");
+    *c->word = ID_PENDING;
+  }
+  j.host_err = c ? c->word : nullptr;
+  hipError_t e;
+  {
+    Stage stage("route+gmm1_swiglu", stream);
+    e = hmm::launch_route_gmm1_swiglu(j, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "routing + gmm1 launch");
+  if (c) {
+    e = hipEventRecord(c->id_ev, stream);
+    if (e != hipSuccess) return hip_fail(e, "id-validation event");
+  }
+  return HMM_OK;
+}
+
 // The routing stores 0 or 1 into the host word as soon as the ids are checked
 // (the word holds ID_PENDING until then); the host polls it, and falls back on
 // the event recorded after the launch that contains the routing.
@@ -662,9 +685,14 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
     sh = hmm::SharedTables{d.T, (int)hmm::max_big_tiles(d.T, 1, d.small), d.small ? 0 : 1,
                            at<int32_t>(saved, L.shared_offsets), at<int32_t>(saved, L.shared_idx),
                            at<float>(saved, L.shared_ones), at<int32_t>(saved, L.shared_tiles)};
-  s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
-                tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, sh, st);
-  if (s != HMM_OK) return s;
+  // small bf16 problems route inside the up-projection's launch (below)
+  const bool route_in_gmm1 = d.small && !d.fp8 && !d.f32 && !d.shared && d.S > 0 &&
+                             d.S <= hmm::ROUTED_MAX_SLOTS && d.E <= hmm::RT_ONE_MAX_EXPERTS;
+  if (!route_in_gmm1) {
+    s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
+                  tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, sh, st);
+    if (s != HMM_OK) return s;
+  }
   hipError_t e;
   const hmm::RowGroups gs =
       d.shared ? shared_groups(d, sh.tiles, sh.offsets, sh.idx) : hmm::RowGroups{};
@@ -804,6 +832,13 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
       e = hmm::launch_gmm1_swiglu(&js, 1, st);
     }
     if (e != hipSuccess) return hip_fail(e, "shared gmm1 launch");
+  } else if (route_in_gmm1) {
+    const hmm::RoutedGmm1Job j{{g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw},
+                               topk_ids, (int)d.E, (int)d.K, (int)hmm::max_big_tiles(d.S, d.E, d.small),
+                               at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
+                               tok_of_row, tiles, at<int32_t>(saved, L.id_error), nullptr};
+    s = run_route_gmm1(j, validate_ids, st);
+    if (s != HMM_OK) return s;
   } else {
     const hmm::Gmm1Job jobs[2] = {{g, (const uint16_t*)x, (const uint16_t*)up_w, topk_weights, d.H, d.I, h, a, aw},
                                   {gs, (const uint16_t*)x, (const uint16_t*)up_s, ones, d.H, d.Is, hs, as, nullptr}};

@@ -99,6 +99,216 @@ hipError_t launch_dw_jobs(const DwJob* j, int n, hipStream_t stream) {
 }
 }  // namespace
 
+namespace {
+// ------------------------------------------------------------- routed up-projection
+// An up-projection tile that routes the ids itself (launch_route_gmm1_swiglu).
+// The four waves count the ids of their chunks (slots [w chunk, (w+1) chunk)) per
+// expert with ballots, as the one-workgroup routing does; inclusive scans over
+// the experts give every expert's first row and first 64-row tile, so the
+// workgroup finds its tile (spread over the XCDs by real_tile, with the real
+// tile count in hand), then each wave walks its chunk again for the tile's
+// expert alone:
+//   row = (first row of the expert) + (its slots in earlier waves) + (its
+//         earlier slots in this wave's chunk),
+// the stable (expert, slot) order.  The tile's tokens and slots land in LDS and
+// take the place of the tables' loads.  The launch also stores the routing's
+// tables for the later launches: the tile of column 0 its rows (sorted_slot,
+// tok_of_row, row_of_slot) and its table entry, workgroup 0 (tile 0, or none
+// when no id is valid) every expert's count and first row, the table's header,
+// row_of_slot -1 for the slots whose id is out of range, and the error flags.
+struct TileRouteLds {
+  static constexpr int NW = Narrow::NTHR / 64;
+  int32_t cnt[NW][RT_ONE_MAX_EXPERTS];  // per wave, per expert
+  int32_t tot[2][NW];                   // per wave: inclusive rows and tiles over its experts
+  int32_t info[3 + NW];                 // expert, first row, rows; first row of each wave's slots
+  int32_t tok[TILE_SMALL], slot[TILE_SMALL];
+};
+
+struct Gmm1Routed : Gmm1<Narrow, true> {
+  typedef Gmm1<Narrow, true> G;
+  struct Args : G::Args {
+    const int32_t* ids;
+    int E, K, nbits, max_big;
+    int32_t *counts, *offsets, *sorted_slot, *row_of_slot, *tok_of_row, *tiles, *err, *host_err;
+  };
+  static_assert(C::BM == TILE_SMALL && C::NTHR >= RT_ONE_MAX_EXPERTS, "one thread per expert, one tile row each");
+
+  __device__ __forceinline__ bool init(const Args& A, int idx) {
+    __shared__ TileRouteLds L;
+    constexpr int NW = TileRouteLds::NW;
+    constexpr int R = ROUTED_MAX_SLOTS / C::NTHR;  // 64-slot rounds per wave at most
+    ar = &A;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int S = (int)A.g.S, E = A.E;
+    for (int i = lane; i < RT_ONE_MAX_EXPERTS; i += 64) L.cnt[w][i] = 0;  // each wave counts in its own row
+    const int chunk = ((S + NW - 1) / NW + 63) / 64 * 64;
+    const int s0 = w * chunk;
+    int ev[R];  // the id of each of this lane's slots; -1 past S or outside [0, E)
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int s = s0 + j * 64 + lane;
+      const int v = (j * 64 < chunk && s < S) ? A.ids[s] : -1;
+      ev[j] = (v >= 0 && v < E) ? v : -1;
+    }
+    wave_lds_sync();
+    const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j * 64 >= chunk) continue;  // the same for every wave
+      const int v = ev[j];
+      const bool valid = v >= 0;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < A.nbits; ++bit) {
+        const bool set = valid && ((v >> bit) & 1);
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+      }
+      // one leader per id; an LDS add, so the rounds do not wait on each other
+      if (valid && __popcll(peers & lt_mask) == 0) atomicAdd(&L.cnt[w][v], __popcll(peers));
+    }
+    __syncthreads();
+    // thread x < E: expert x's rows and 64-row tiles, scanned over the experts
+    int c = 0;
+    if (tid < E)
+#pragma unroll
+      for (int q = 0; q < NW; ++q) c += L.cnt[q][tid];
+    const int nt_x = (c + TILE_SMALL - 1) / TILE_SMALL;
+    int ic = c, is = nt_x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int vc = __shfl_up(ic, d), vs = __shfl_up(is, d);
+      if (lane >= d) {
+        ic += vc;
+        is += vs;
+      }
+    }
+    if (lane == 63) {
+      L.tot[0][w] = ic;
+      L.tot[1][w] = is;
+    }
+    __syncthreads();
+    int ntiles = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      if (q < w) {
+        ic += L.tot[0][q];
+        is += L.tot[1][q];
+      }
+      ntiles += L.tot[1][q];
+    }
+    if (idx == 0) {
+      if (tid < E) {
+        A.counts[tid] = c;
+        A.offsets[tid] = ic - c;
+      }
+      if (tid == C::NTHR - 1) {  // holds the totals over all experts
+        A.offsets[E] = ic;
+        A.tiles[0] = 0;
+        A.tiles[1] = ntiles;
+        A.tiles[2] = TILE_BIG;
+        A.tiles[3] = TILE_SMALL;
+      }
+      int bad = 0;
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) {
+        const int s = s0 + jj * 64 + lane;
+        if (jj * 64 < chunk && s < S && ev[jj] < 0) {
+          A.row_of_slot[s] = -1;
+          bad = 1;
+        }
+      }
+      bad = __syncthreads_or(bad);
+      if (tid == 0) {
+        *A.err = bad;
+        // the host reads this word only after the launch has completed: no release needed
+        if (A.host_err) __hip_atomic_store(A.host_err, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+    int j;
+    if (!real_tile(idx, ntiles, A.n_ntiles, j, nt)) return false;  // every thread alike
+    if (tid < E && j >= is - nt_x && j < is) {  // expert tid holds tile j
+      const int first = j - (is - nt_x);
+      int b = ic - c;
+      L.info[0] = tid;
+      L.info[1] = b + first * TILE_SMALL;
+      L.info[2] = min(TILE_SMALL, c - first * TILE_SMALL);
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        L.info[3 + q] = b;
+        b += L.cnt[q][tid];
+      }
+    }
+    __syncthreads();
+    e = L.info[0];
+    row0 = L.info[1];
+    rows = L.info[2];
+    int base = L.info[3 + w];
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) {
+      if (jj * 64 >= chunk) continue;
+      const bool mine = ev[jj] == e;
+      const uint64_t m = __ballot(mine);
+      if (mine) {
+        const int r = base + __popcll(m & lt_mask) - row0;
+        if (r >= 0 && r < rows) {
+          const int s = s0 + jj * 64 + lane;
+          L.tok[r] = s / A.K;
+          L.slot[r] = s;
+        }
+      }
+      base += __popcll(m);
+    }
+    __syncthreads();
+    if (nt == 0) {
+      if (tid < rows) {
+        const int p = row0 + tid;
+        A.sorted_slot[p] = L.slot[tid];
+        A.tok_of_row[p] = L.tok[tid];
+        A.row_of_slot[L.slot[tid]] = p;
+      }
+      if (tid == 0) {
+        int32_t* entry = A.tiles + 4 + 2 * A.max_big + 2 * j;
+        entry[0] = tile_word(e, rows);
+        entry[1] = row0;
+      }
+    }
+    // as Gmm1::init, with the tile's rows from LDS
+    slot_own = (tid < rows) ? L.slot[tid] : 0;
+    i0 = nt * (C::BN / 2);
+    ra_ = make_rsrc(A.x, A.T * A.H * 2);
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int cc = tid + i * C::NTHR;
+      const int r = min(cc / C::KCH, rows - 1);
+      aoff[i] = (uint32_t)(((int64_t)L.tok[r] * A.H + (cc % C::KCH) * 8) * 2);
+    }
+    init_b(A);
+    return true;
+  }
+};
+
+}  // namespace
+
+hipError_t launch_route_gmm1_swiglu(const RoutedGmm1Job& j, hipStream_t stream) {
+  const Gmm1Job& u = j.up;
+  if (u.g.S <= 0) return hipSuccess;
+  if (!u.g.narrow || u.g.S > ROUTED_MAX_SLOTS || j.E < 1 || j.E > RT_ONE_MAX_EXPERTS || j.K < 1 ||
+      u.g.S % j.K)
+    return hipErrorInvalidValue;
+  Gmm1Routed::Args a;
+  const int nnt = ntiles_half(u.I, Narrow::BN);
+  fill_gmm1(a, u, nnt);
+  a.ids = j.ids;
+  a.E = j.E;
+  a.K = j.K;
+  a.nbits = 0;
+  while ((1 << a.nbits) < j.E) ++a.nbits;
+  a.max_big = j.max_big;
+  a.counts = j.counts; a.offsets = j.offsets; a.sorted_slot = j.sorted_slot; a.row_of_slot = j.row_of_slot;
+  a.tok_of_row = j.tok_of_row; a.tiles = j.tiles; a.err = j.err; a.host_err = j.host_err;
+  return launch<Gmm1Routed>(a, u.g.max_small * nnt, stream);
+}
+
 hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream) {
   return launch_rows_jobs<Gmm1, Narrow>(jobs, n, [](const Gmm1Job& j, int bn) { return ntiles_half(j.I, bn); },
                                         [](auto& a, const Gmm1Job& j, int nnt) { fill_gmm1(a, j, nnt); }, stream);

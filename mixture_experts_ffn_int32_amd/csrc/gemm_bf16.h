@@ -40,6 +40,12 @@ struct Gmm1 : RowTile<Cc, SMALL> {
     i0 = nt * (C::BN / 2);
     ra_ = make_rsrc(A.x, A.T * A.H * 2);
     this->template a_rows<true>(A.g, A.H, aoff);
+    init_b(A);
+    return true;
+  }
+  // the weight side of tile (e, nt): its resource, the offsets of the tile's gate
+  // and up columns, and the K steps
+  __device__ __forceinline__ void init_b(const Args& A) {
     rb_ = make_rsrc(A.w1 + (int64_t)e * A.H * 2 * A.I, A.H * 2 * A.I * 2);
     const int tid = threadIdx.x;
     constexpr int CPR = C::BN / 8, HALF = C::BN / 16;
@@ -52,7 +58,6 @@ struct Gmm1 : RowTile<Cc, SMALL> {
       boff[i] = (uint32_t)((kr * 2 * A.I + col) * 2);
     }
     nk = (int)(A.H / C::BK);
-    return true;
   }
   __device__ __forceinline__ void load_a(int kt, u32x4 (&r)[C::CA]) {
 #pragma unroll

@@ -97,6 +97,19 @@ struct Gmm1Job {
   uint16_t *h, *a, *aw;  // aw may be NULL (not stored)
 };
 hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream);
+// The routing and the up-projection in one launch, for small problems (S <=
+// ROUTED_MAX_SLOTS, E <= RT_ONE_MAX_EXPERTS) on the narrow tiling, bf16, without
+// a shared expert: every up-projection workgroup routes the ids itself as far as
+// its own tile needs, and the launch stores every routing array launch_route
+// stores (the later launches read them).
+constexpr int ROUTED_MAX_SLOTS = 4096;
+struct RoutedGmm1Job {
+  Gmm1Job up;  // up.g: the narrow tables' capacities (its arrays are not read)
+  const int32_t* ids;
+  int E, K, max_big;
+  int32_t *counts, *offsets, *sorted_slot, *row_of_slot, *tok_of_row, *tiles, *err, *host_err;
+};
+hipError_t launch_route_gmm1_swiglu(const RoutedGmm1Job& j, hipStream_t stream);
 // o = a . W2[e]                                                (forward down-projection)
 struct Gmm2Job {
   RowGroups g;

@@ -64,6 +64,8 @@ def stage_of(name):
     """(label, stage) of a kernel name: the label adds the tile shapes of a product; the
     stage is the library's name for the launch (what bench.py's stage events time)."""
     suf = _tiles(name)
+    if "Gmm1Routed" in name:
+        return "route+gmm1_swiglu[64x64]", "route+gmm1_swiglu"
     if "route_one" in name:
         return "route_one", "route"
     for r in ("route_hist", "route_scan", "route_scatter"):

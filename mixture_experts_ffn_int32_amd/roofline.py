@@ -37,6 +37,7 @@ def stage_work(stage, T, H, I, E, K, f32=False, Is=0):
     }
     flops["act_grad+dw2"] = flops["act_grad"] + flops["dw2"]      # two products in one launch
     flops["input_grad+dw1"] = flops["input_grad"] + flops["dw1"]
+    flops["route+gmm1_swiglu"] = flops["gmm1_swiglu"]  # small problems: the routing rides in the up-projection
     # a shared expert: the same products over T rows of width Is, in the routed launches ("<stage>+shared")
     shared = {k: v * T * Is // (S * I) for k, v in flops.items()}
     for k, v in shared.items():

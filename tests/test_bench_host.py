@@ -34,6 +34,8 @@ def test_products_count_18_shi_flops():
     # small problems pair two products in one launch: both count
     for pair, a, b in (("act_grad+dw2", "act_grad", "dw2"), ("input_grad+dw1", "input_grad", "dw1")):
         assert stage_work(pair, T, H, I, E, K)[1] == work[a][1] + work[b][1]
+    # small problems route inside the up-projection's launch: the launch does its products
+    assert stage_work("route+gmm1_swiglu", T, H, I, E, K) == work["gmm1_swiglu"]
     # the FP8 products take the FP8 peak, with the same flop counts
     assert stage_work("gmm1_fp8_swiglu", T, H, I, E, K)[1:] == (4 * S * H * I, "TFLOP/s", PEAK_FP8_TFLOPS)
     assert stage_work("input_grad_fp8", T, H, I, E, K)[1] == work["input_grad"][1]

@@ -191,6 +191,66 @@ def test_bad_inputs_rejected_before_launch():
     assert torch.equal(y1, y2)
 
 
+ROUTED = [
+    # problems whose up-projection launch routes the ids itself (narrow tiles, S <= 4096,
+    # E <= 256), at its bounds: the most slots and experts, one expert, one slot, a slot
+    # count that splits unevenly over the four waves
+    ("max", dict(T=512, H=128, I=64, E=256, K=8, routing="zipf", zipf_s=0.8, n_empty=40)),
+    ("one_expert", dict(T=4096, H=128, I=64, E=1, K=1, routing="uniform")),
+    ("one_slot", dict(T=1, H=128, I=64, E=3, K=1, routing="uniform")),
+    ("uneven", dict(T=585, H=192, I=128, E=200, K=7, routing="zipf", zipf_s=1.1, n_empty=30)),
+]
+
+
+@pytest.mark.parametrize("name,over", ROUTED, ids=[r[0] for r in ROUTED])
+def test_routed_up_projection_at_its_bounds(name, over):
+    """The routing arrays of the launch that routes inside the up-projection match the
+    oracle's bit for bit; h, a and y match it element by element."""
+    from mixture_experts_ffn_int32_amd import forward_with_saved, saved_views
+    spec = synth.spec_with("tiny", **over)
+    inp = synth.make_inputs(spec, seed=23)
+    announce("routed up-projection %s %s" % (name, {k: spec[k] for k in "THIEK"}))
+    g = gpu_inputs(inp, "cuda")
+    y, saved = forward_with_saved(g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"],
+                                  g["down_proj_weight"], tiles="narrow")
+    v = saved_views(saved, *(spec[k] for k in "THIEK"), tiles="narrow")
+    ref_route = oracle_route(inp["topk_ids"], spec["E"])
+    for k in ("counts", "offsets", "sorted_slot", "row_of_slot"):
+        assert np.array_equal(v[k].cpu().numpy(), ref_route[k]), k
+    o = MoEFFN(**oracle_inputs(inp), mode="faithful")
+    ry, ryd = o.forward_dev()
+    assert_close(to_f64(y), ry, name + " y", ryd)
+    (h, a, _), (hd, ad, _) = o.slot_intermediates_dev(ref_route["sorted_slot"])
+    assert_close(to_f64(v["h"]), h, name + " h", hd)
+    assert_close(to_f64(v["a"]), a, name + " a", ad)
+
+
+def test_routed_up_projection_drops_out_of_range_ids():
+    """Without the id check, slots whose id lies outside [0, E) get no row (row_of_slot
+    -1) and the others keep the stable order; with it, the call fails."""
+    from mixture_experts_ffn_int32_amd import _lib, forward_with_saved, saved_views
+    spec = synth.spec_with("tiny", T=200, H=128, I=64, E=5, K=2, routing="uniform")
+    inp = synth.make_inputs(spec, seed=29)
+    ids = inp["topk_ids"].copy()
+    ids[5, 0] = 5
+    ids[77, 1] = -3
+    inp["topk_ids"] = ids
+    announce("routed up-projection with out-of-range ids")
+    g = gpu_inputs(inp, "cuda")
+    args = (g["x"], g["topk_ids"], g["topk_weights"], g["up_proj_weight"], g["down_proj_weight"])
+    y, saved = forward_with_saved(*args, validate_ids=False, tiles="narrow")
+    v = saved_views(saved, *(spec[k] for k in "THIEK"), tiles="narrow")
+    flat = ids.reshape(-1)
+    good = (flat >= 0) & (flat < spec["E"])
+    order = np.flatnonzero(good)[np.argsort(flat[good], kind="stable")]
+    assert np.array_equal(v["sorted_slot"].cpu().numpy()[:order.size], order)
+    assert v["row_of_slot"].cpu().numpy()[~good].tolist() == [-1, -1]
+    assert np.array_equal(v["counts"].cpu().numpy(), np.bincount(flat[good], minlength=spec["E"]))
+    with pytest.raises(ValueError) as ei:
+        forward_with_saved(*args, tiles="narrow")
+    assert ei.value.status == _lib.HMM_ERR_EXPERT_ID_OUT_OF_RANGE
+
+
 # ----------------------------------------------------------------------------- full-size workloads, sampled
 
 def _sample_full(name, n_tok=6, icols_frac=(0.0, 0.37, 1.0)):

@@ -26,6 +26,7 @@ def test_stage_names_of_the_library_kernels():
         ("void hmm::combine_kernel<true, unsigned short>(args)", "combine", "combine"),
         ("void hmm::combine_kernel<false, unsigned short>(args)", "combine_dx", "combine_dx"),
         ("hmm::route_scan(int const*, int)", "route_scan", "route"),
+        ("void %sgemm_kernel<%sGmm1Routed>(args)" % (NS, NS), "route+gmm1_swiglu", "route+gmm1_swiglu"),
         ("hmm::expert_order(int const*, int, int*)", "expert_order", "expert_order"),
         ("hmm::quant_rows_fp8(unsigned short const*, long)", "quant_rows_fp8", "quant_rows_fp8"),
     ]
