@@ -83,8 +83,9 @@ typedef enum hmm_dtype {
   HMM_FP8_E4M3_GROUP = 4  /* E4M3 with one float32 scale per 128 elements along H */
 } hmm_dtype;
 
-/* Check topk_ids: the routing kernel raises a flag for an id outside [0, E)
- * and also stores it into a pinned host word; the host reads that word and
+/* Check topk_ids: the routing (its own launch, or on small bf16 problems the
+ * up-projection's launch) raises a flag for an id outside [0, E) and also
+ * stores it into a pinned host word; the host reads that word and
  * returns HMM_ERR_EXPERT_ID_OUT_OF_RANGE.  The host waits for that copy only
  * after the call's kernels are enqueued, so the check adds no idle time on the
  * GPU; the products of a failing call run with the invalid slots dropped, and
