@@ -687,7 +687,8 @@ hmm_status forward_impl(const hmm_problem* p, const Dims& d, const void* x, cons
                            at<float>(saved, L.shared_ones), at<int32_t>(saved, L.shared_tiles)};
   // small bf16 problems route inside the up-projection's launch (below)
   const bool route_in_gmm1 = d.small && !d.fp8 && !d.f32 && !d.shared && d.S > 0 &&
-                             d.S <= hmm::ROUTED_MAX_SLOTS && d.E <= hmm::RT_ONE_MAX_EXPERTS;
+                             d.S <= hmm::ROUTED_MAX_SLOTS && d.E <= hmm::RT_ONE_MAX_EXPERTS &&
+                             hmm::max_small_tiles(d.S, d.E, true) * ((d.I + 31) / 32) <= hmm::ROUTED_MAX_TILES;
   if (!route_in_gmm1) {
     s = run_route(d, topk_ids, at<int32_t>(saved, L.counts), offsets, sorted_slot, at<int32_t>(saved, L.row_of_slot),
                   tok_of_row, tiles, at<int32_t>(saved, L.id_error), workspace, W.rs, validate_ids, sh, st);

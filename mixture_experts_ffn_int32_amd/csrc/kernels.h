@@ -103,6 +103,11 @@ hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream);
 // its own tile needs, and the launch stores every routing array launch_route
 // stores (the later launches read them).
 constexpr int ROUTED_MAX_SLOTS = 4096;
+// ... and at most this many tiles in the launch (the table's capacity times the
+// column tiles): every workgroup pays a few microseconds for its routing, which
+// the saved routing launch (about 7 us with its kernel boundary) covers only
+// while the launch runs in about one round of workgroups.
+constexpr int ROUTED_MAX_TILES = 1024;
 struct RoutedGmm1Job {
   Gmm1Job up;  // up.g: the narrow tables' capacities (its arrays are not read)
   const int32_t* ids;
