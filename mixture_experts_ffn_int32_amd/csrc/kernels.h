@@ -104,10 +104,12 @@ hipError_t launch_gmm1_swiglu(const Gmm1Job* jobs, int n, hipStream_t stream);
 // stores (the later launches read them).
 constexpr int ROUTED_MAX_SLOTS = 4096;
 // ... and at most this many tiles in the launch (the table's capacity times the
-// column tiles): every workgroup pays a few microseconds for its routing, which
-// the saved routing launch (about 7 us with its kernel boundary) covers only
-// while the launch runs in about one round of workgroups.
-constexpr int ROUTED_MAX_TILES = 1024;
+// column tiles), one workgroup per CU: every workgroup pays a few microseconds
+// for its routing, which the saved routing launch (about 7 us with its kernel
+// boundary) covers only while the launch runs in one round.  Measured forwards:
+// 140 and 188 tiles 2.7-3 us faster than with the routing launch, 508 the same,
+// 760 and 1016 tiles 7-10 us slower.
+constexpr int ROUTED_MAX_TILES = 256;
 struct RoutedGmm1Job {
   Gmm1Job up;  // up.g: the narrow tables' capacities (its arrays are not read)
   const int32_t* ids;

@@ -193,13 +193,14 @@ def test_bad_inputs_rejected_before_launch():
 
 ROUTED = [
     # problems whose up-projection launch routes the ids itself (narrow tiles, S <= 4096,
-    # E <= 256, at most 1024 tiles of 64x64 in the launch), at its bounds: the most slots
-    # and experts, one expert, one slot, a slot count that splits unevenly over the four
-    # waves
-    ("max", dict(T=512, H=128, I=64, E=256, K=8, routing="zipf", zipf_s=0.8, n_empty=40)),
+    # E <= 256, at most 256 tiles of 64x64 in the launch), at its bounds: the most slots,
+    # the most experts (and exactly 256 tiles), one expert, one slot, a slot count that
+    # splits unevenly over the four waves
+    ("max_slots", dict(T=512, H=128, I=64, E=8, K=8, routing="zipf", zipf_s=0.8, n_empty=0)),
+    ("max_experts", dict(T=16, H=128, I=64, E=256, K=8, routing="uniform")),
     ("one_expert", dict(T=4096, H=128, I=64, E=1, K=1, routing="uniform")),
     ("one_slot", dict(T=1, H=128, I=64, E=3, K=1, routing="uniform")),
-    ("uneven", dict(T=585, H=192, I=64, E=200, K=7, routing="zipf", zipf_s=1.1, n_empty=30)),
+    ("uneven", dict(T=585, H=192, I=64, E=20, K=7, routing="zipf", zipf_s=1.1, n_empty=5)),
 ]
 
 
